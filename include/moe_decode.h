@@ -1,0 +1,187 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) small-batch decode MoE FFN.
+ *
+ * One layer's FFN half at decode width M <= 48 token rows, on one GPU:
+ *
+ *   y    = RMSNorm(x) * norm_w, rounded to bf16                 (the FFN seam)
+ *   x8   = MXFP8(y): E4M3 values, one E8M0 code per 32 columns
+ *   s    = sigmoid(y . gate_w^T); picks = top-k of s + bias; w = s_pick / sum
+ *   per picked expert e and for the shared expert:
+ *     h  = x8 . W13[e]^T  (E4M3 x E4M3 with 32 x 32 E8M0 weight blocks)
+ *     a8 = MXFP8(SiLU(h[:, :I]) * h[:, I:])
+ *     ye = a8 . W2[e]^T
+ *   out  = bf16(sum_j w_j ye_j + y_shared)
+ *
+ * Sources (three API-reference pages of one decode-layer implementation):
+ *   "vllm.models.deepseek_v41.amd.mono.runner": DSV41MonoLayer.ffn (the FFN
+ *     launch and its MoE tensors), DSV41MonoLayer.supports (1 <= M <= 48),
+ *     DSV41MonoLayer.scratch (scratch allocated before any graph capture),
+ *     MonoLayerWeights.check (tensor shapes and dtypes; 32 x 32 E8M0 blocks),
+ *     _check_tensors (shape checks because loads are unbounded).
+ *   "vllm.models.deepseek_v41.amd.mono.layer": run_ffn (norm, then the MoE
+ *     and its output), store_normed (bf16 normed row), store_x8 (MXFP8).
+ *   "vllm.models.deepseek_v41.amd.mono.attention.device": mx_code, mx_mul,
+ *     fp8_pack4, mfma_scaled.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* are device pointers on the device that was current
+ *     when the plan was made; h_* are host pointers.
+ *   - The library never allocates, frees or synchronises inside
+ *     moe_decode_run: all device memory it needs is allocated by
+ *     moe_decode_plan.  moe_decode_run enqueues its kernels on `stream` and
+ *     returns; it may be captured into a HIP graph.
+ *   - Return values: 0 on success, a negative MOE_DECODE_E* code otherwise;
+ *     moe_decode_strerror() names it.  On an argument error nothing is
+ *     enqueued.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DECODE_OK 0
+#define MOE_DECODE_EINVAL (-1)   /* a dimension, size, pointer or alignment is invalid */
+#define MOE_DECODE_ENOMEM (-2)   /* device or host allocation failed */
+#define MOE_DECODE_EHIP (-3)     /* a HIP runtime call failed (see moe_decode_last_hip_error) */
+#define MOE_DECODE_ECAPTURE (-4) /* moe_decode_plan called while the stream is capturing */
+
+/* Largest decode width the pages' runner supports (DSV41MonoLayer.supports). */
+#define MOE_DECODE_MAX_TOKENS 48
+
+/* Layer dimensions, fixed when the plan is made.
+ *   hidden        H, a multiple of 128 (the scaled MFMA's K step), <= 16384
+ *   experts       E routed experts, 1..1024
+ *   topk          k experts per token, 1..min(E, 32)
+ *   inter         I, routed expert intermediate, a multiple of 128, <= 8192
+ *   shared_inter  Is, shared expert intermediate, a multiple of 128, <= 8192
+ *   max_tokens    largest m a run may pass, 1..48
+ *   rms_eps       RMSNorm epsilon (added to mean(x^2) in double precision)
+ *   routed_scale  factor applied to the renormalised routing weights */
+typedef struct moe_decode_dims {
+  int32_t hidden;
+  int32_t experts;
+  int32_t topk;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t max_tokens;
+  float rms_eps;
+  float routed_scale;
+} moe_decode_dims;
+
+typedef struct moe_decode_plan_s* moe_decode_handle;
+
+/* Validates dims, allocates the plan's device scratch (laid out for
+ * max_tokens rows) on the current device and zeroes it.  Must not be called
+ * while a stream is being captured (DSV41MonoLayer.scratch raises in that
+ * case; here: MOE_DECODE_ECAPTURE, checked on `stream`, which may be NULL for
+ * the legacy stream).  On success *out owns the scratch until
+ * moe_decode_destroy. */
+int moe_decode_plan(const moe_decode_dims* dims, void* stream,
+                    moe_decode_handle* out);
+
+/* Device bytes the plan owns. */
+size_t moe_decode_scratch_bytes(moe_decode_handle plan);
+
+/* One decode step of m token rows, 1 <= m <= max_tokens (DSV41MonoLayer.ffn's
+ * MoE pointers, with the norm weight, since the norm is on this path).
+ *
+ *   d_x       bf16 [m, H]            input rows (not modified)
+ *   d_norm_w  bf16 [H]               RMSNorm weight
+ *   d_gate_w  bf16 [E, H]            router weight
+ *   d_bias    f32  [E]               expert-selection bias (e_score_correction_bias)
+ *   d_w13     E4M3 [E, 2I, H]        rows [0, I) gate, [I, 2I) up
+ *   d_w13_s   E8M0 [E, 2I/32, H/32]  one code per 32 x 32 block, row-major
+ *   d_w2      E4M3 [E, H, I]
+ *   d_w2_s    E8M0 [E, H/32, I/32]
+ *   d_sgu     E4M3 [2Is, H]          shared expert gate/up
+ *   d_sgu_s   E8M0 [2Is/32, H/32]
+ *   d_sw2     E4M3 [H, Is]           shared expert down
+ *   d_sw2_s   E8M0 [H/32, Is/32]
+ *   d_out     bf16 [m, H]            written in full; must not alias any input
+ *   stream    hipStream_t (NULL: the legacy stream)
+ *
+ * All tensors are dense row-major.  Every pointer must be non-NULL and 16-byte
+ * aligned: the kernels' loads are unchecked against tensor bounds, so a tensor
+ * smaller than its shape above is read past its end (the pages check shapes
+ * on the host for the same reason, _check_tensors).  The caller keeps every
+ * buffer alive until the enqueued work completes.  A plan serves one stream
+ * at a time: two runs of one plan must not overlap (they share its scratch). */
+int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
+                   const void* d_norm_w, const void* d_gate_w,
+                   const float* d_bias, const void* d_w13,
+                   const void* d_w13_s, const void* d_w2, const void* d_w2_s,
+                   const void* d_sgu, const void* d_sgu_s, const void* d_sw2,
+                   const void* d_sw2_s, void* d_out, void* stream);
+
+/* Views of the last run's intermediates inside the plan's scratch (device
+ * pointers, valid until the next run or destroy; read them after the run's
+ * work completes).  Shapes use the last run's m; P = m * k pairs, R = P + m
+ * rows (routed rows first, then one shared-expert row per token).
+ *   NORMED    bf16 [m, H]       the RMSNorm output (store_normed)
+ *   X8        u8   [m, H]       E4M3 of NORMED (store_x8)
+ *   X8S       u8   [m, H/32]    E8M0 codes of X8
+ *   LOGITS    f64  [m, E]       router logits
+ *   TOPK_IDS  i32  [m, k]       picked experts in selection order
+ *   TOPK_W    f32  [m, k]       routing weights of the picks
+ *   COUNTS    i32  [E]          tokens per expert
+ *   PAIR_ROW  i32  [m, k]       row of pair (t, j): pairs listed by expert
+ *                               ascending, then token ascending
+ *   ROW_TOK   i32  [R]          token of each row
+ *   A8        u8   [R, Imax]    E4M3 SiLU*up intermediate (Imax = max(I, Is))
+ *   A8S       u8   [R, Imax/32] its E8M0 codes */
+enum moe_decode_tap {
+  MOE_DECODE_TAP_NORMED = 0,
+  MOE_DECODE_TAP_X8 = 1,
+  MOE_DECODE_TAP_X8S = 2,
+  MOE_DECODE_TAP_LOGITS = 3,
+  MOE_DECODE_TAP_TOPK_IDS = 4,
+  MOE_DECODE_TAP_TOPK_W = 5,
+  MOE_DECODE_TAP_COUNTS = 6,
+  MOE_DECODE_TAP_PAIR_ROW = 7,
+  MOE_DECODE_TAP_ROW_TOK = 8,
+  MOE_DECODE_TAP_A8 = 9,
+  MOE_DECODE_TAP_A8S = 10
+};
+int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
+                       const void** d_ptr, size_t* bytes);
+
+/* Per-kernel timing of runs (HIP events recorded around each kernel on the
+ * run's stream).  moe_decode_timing(plan, 1) starts recording (and clears the
+ * totals), 0 stops.  While on, moe_decode_run must not be captured into a
+ * graph.  moe_decode_timing_read sums the elapsed milliseconds of every
+ * recorded run for kernel `kernel` (0 seam, 1 w13, 2 w2); it synchronises
+ * with the recorded events. */
+int moe_decode_timing(moe_decode_handle plan, int32_t on);
+int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
+                           double* total_ms, int32_t* runs);
+
+/* Frees the plan's scratch.  NULL is allowed. */
+void moe_decode_destroy(moe_decode_handle plan);
+
+/* Weight preparation (not part of a decode step): quantise a dense row-major
+ * fp32 [rows, cols] matrix to E4M3 [rows, cols] with one E8M0 code per
+ * 32 x 32 block ([rows/32, cols/32] row-major) -- the layout the expert
+ * tensors above use (MonoLayerWeights.check: 32 x 32 E8M0 blocks).  Code per
+ * block = clamp(ceil(log2(amax/448)) + 127, 0, 254) (mx_code); values are
+ * rounded to nearest even after scaling by 2^(127 - code) (fp8_pack4).
+ * rows and cols multiples of 32; pointers 16-byte aligned; `count` matrices
+ * of that shape stored back to back are quantised in one call. */
+int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows,
+                               int32_t cols, void* d_q, void* d_scales,
+                               void* stream);
+
+/* Text of an error code. */
+const char* moe_decode_strerror(int code);
+/* The last HIP error a plan (or, with NULL, the library) saw, as text. */
+const char* moe_decode_last_hip_error(moe_decode_handle plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -1,0 +1,349 @@
+// api.hip -- the C ABI (include/moe_decode.h): plan (validation, scratch
+// layout, one allocation), run (argument checks, three launches on the
+// caller's stream, no allocation, no synchronisation), inspect, timing.
+//
+// Pages: "vllm.models.deepseek_v41.amd.mono.runner" DSV41MonoLayer.ffn (one
+// launch set per step on the caller's stream; every argument a device
+// pointer, so the launches can be captured in a HIP graph),
+// DSV41MonoLayer.scratch (scratch sized for a step width and allocated
+// before any capture), DSV41MonoLayer.supports (1 <= M <= 48),
+// _check_tensors (argument checks, since the kernels' loads are unchecked).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "moe_decode.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTimingRing = 256;  // runs whose events are held before folding
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct TimingSet {
+  hipEvent_t ev[4];
+};
+
+std::string g_last_error = "no error";
+
+}  // namespace
+
+struct moe_decode_plan_s {
+  LayerDims d{};
+  int device = 0;
+  int cus = 0;
+  int w13_per_cu = 1;
+  int max_vs = 0;
+  int R = 0;
+  size_t bytes = 0;
+  void* base = nullptr;
+  Scratch s{};
+  int last_m = 0;
+  std::string err = "no error";
+  // timing
+  bool timing = false;
+  std::vector<TimingSet> ring;
+  int ring_used = 0;
+  double total_ms[3] = {0, 0, 0};
+  int runs = 0;
+};
+
+namespace {
+
+int hip_fail(moe_decode_plan_s* p, hipError_t e, const char* what) {
+  std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+  if (p) p->err = msg;
+  g_last_error = msg;
+  return MOE_DECODE_EHIP;
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dims(const moe_decode_dims* d) {
+  if (!d) return false;
+  if (d->hidden < 128 || d->hidden > kMaxHidden || d->hidden % 128) return false;
+  if (d->experts < 1 || d->experts > kMaxExperts) return false;
+  if (d->topk < 1 || d->topk > kMaxTopk || d->topk > d->experts) return false;
+  if (d->inter < 128 || d->inter > kMaxInter || d->inter % 128) return false;
+  if (d->shared_inter < 128 || d->shared_inter > kMaxInter || d->shared_inter % 128) return false;
+  if (d->max_tokens < 1 || d->max_tokens > kMaxTokens) return false;
+  if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.0f) return false;
+  if (!std::isfinite(d->routed_scale)) return false;
+  return true;
+}
+
+// Fold finished timing events into the totals (oldest first).
+void fold_timing(moe_decode_plan_s* p) {
+  for (int i = 0; i < p->ring_used; ++i) {
+    TimingSet& t = p->ring[i];
+    (void)hipEventSynchronize(t.ev[3]);
+    for (int k = 0; k < 3; ++k) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, t.ev[k], t.ev[k + 1]) == hipSuccess) p->total_ms[k] += ms;
+    }
+    p->runs += 1;
+  }
+  p->ring_used = 0;
+}
+
+void free_timing(moe_decode_plan_s* p) {
+  for (auto& t : p->ring)
+    for (auto& e : t.ev) (void)hipEventDestroy(e);
+  p->ring.clear();
+  p->ring_used = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle* out) {
+  if (!out) return MOE_DECODE_EINVAL;
+  *out = nullptr;
+  if (!valid_dims(dims)) {
+    g_last_error = "invalid dimensions";
+    return MOE_DECODE_EINVAL;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) {
+    g_last_error = "moe_decode_plan called during stream capture";
+    return MOE_DECODE_ECAPTURE;
+  }
+  auto* p = new (std::nothrow) moe_decode_plan_s();
+  if (!p) return MOE_DECODE_ENOMEM;
+  LayerDims& d = p->d;
+  d.H = dims->hidden;
+  d.E = dims->experts;
+  d.K = dims->topk;
+  d.I = dims->inter;
+  d.Is = dims->shared_inter;
+  d.Imax = d.I > d.Is ? d.I : d.Is;
+  d.Mx = dims->max_tokens;
+  d.eps = dims->rms_eps;
+  d.routed_scale = dims->routed_scale;
+  p->max_vs = max_vslots(d.Mx, d.E, d.K);
+  p->R = d.Mx * d.K + d.Mx;
+
+  if ((e = hipGetDevice(&p->device)) != hipSuccess) {
+    int rc = hip_fail(p, e, "hipGetDevice");
+    delete p;
+    return rc;
+  }
+  if ((e = hipDeviceGetAttribute(&p->cus, hipDeviceAttributeMultiprocessorCount, p->device)) != hipSuccess) {
+    int rc = hip_fail(p, e, "hipDeviceGetAttribute");
+    delete p;
+    return rc;
+  }
+  p->w13_per_cu = w13_blocks_per_cu();
+
+  // scratch layout, every region 256-byte aligned
+  const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = p->R;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off = align_up(off + n);
+    return o;
+  };
+  const size_t o_normed = take(Mx * H * 2), o_x8 = take(Mx * H), o_x8s = take(Mx * H / 32);
+  const size_t o_logits = take(Mx * E * 8), o_ids = take(Mx * K * 4), o_wts = take(Mx * K * 4);
+  const size_t o_counts = take(E * 4), o_pair = take(Mx * K * 4), o_tok = take(R * 4), o_roww = take(R * 4);
+  const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
+  const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
+  p->bytes = off;
+  if ((e = hipMalloc(&p->base, p->bytes)) != hipSuccess) {
+    hip_fail(p, e, "hipMalloc");
+    delete p;
+    return MOE_DECODE_ENOMEM;
+  }
+  if ((e = hipMemset(p->base, 0, p->bytes)) != hipSuccess) {
+    int rc = hip_fail(p, e, "hipMemset");
+    (void)hipFree(p->base);
+    delete p;
+    return rc;
+  }
+  char* b = static_cast<char*>(p->base);
+  Scratch& s = p->s;
+  s.normed = reinterpret_cast<uint16_t*>(b + o_normed);
+  s.x8 = reinterpret_cast<uint8_t*>(b + o_x8);
+  s.x8s = reinterpret_cast<uint8_t*>(b + o_x8s);
+  s.logits = reinterpret_cast<double*>(b + o_logits);
+  s.ids = reinterpret_cast<int32_t*>(b + o_ids);
+  s.wts = reinterpret_cast<float*>(b + o_wts);
+  s.counts = reinterpret_cast<int32_t*>(b + o_counts);
+  s.pair_row = reinterpret_cast<int32_t*>(b + o_pair);
+  s.row_tok = reinterpret_cast<int32_t*>(b + o_tok);
+  s.row_w = reinterpret_cast<float*>(b + o_roww);
+  s.vslots = reinterpret_cast<int4*>(b + o_vs);
+  s.header = reinterpret_cast<int32_t*>(b + o_hdr);
+  s.counter = reinterpret_cast<uint32_t*>(b + o_ctr);
+  s.a8 = reinterpret_cast<uint8_t*>(b + o_a8);
+  s.a8s = reinterpret_cast<uint8_t*>(b + o_a8s);
+  *out = p;
+  return MOE_DECODE_OK;
+}
+
+size_t moe_decode_scratch_bytes(moe_decode_handle p) { return p ? p->bytes : 0; }
+
+int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* d_norm_w, const void* d_gate_w,
+                   const float* d_bias, const void* d_w13, const void* d_w13_s, const void* d_w2,
+                   const void* d_w2_s, const void* d_sgu, const void* d_sgu_s, const void* d_sw2,
+                   const void* d_sw2_s, void* d_out, void* stream) {
+  if (!p) return MOE_DECODE_EINVAL;
+  const LayerDims& d = p->d;
+  if (m < 1 || m > d.Mx) {
+    p->err = "m outside [1, max_tokens]";
+    return MOE_DECODE_EINVAL;
+  }
+  const void* ptrs[] = {d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s,
+                        d_sgu, d_sgu_s, d_sw2, d_sw2_s, d_out};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) {
+      p->err = "null or misaligned (not 16-byte) pointer";
+      return MOE_DECODE_EINVAL;
+    }
+  {
+    // out is written while x is still read by other blocks: no overlap
+    const uintptr_t xo = reinterpret_cast<uintptr_t>(d_x), oo = reinterpret_cast<uintptr_t>(d_out);
+    const uintptr_t n = (uintptr_t)m * d.H * 2;
+    if (xo < oo + n && oo < xo + n) {
+      p->err = "out overlaps x";
+      return MOE_DECODE_EINVAL;
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Inputs in;
+  in.x = static_cast<const uint16_t*>(d_x);
+  in.norm_w = static_cast<const uint16_t*>(d_norm_w);
+  in.gate_w = static_cast<const uint16_t*>(d_gate_w);
+  in.bias = d_bias;
+  in.w13 = static_cast<const uint8_t*>(d_w13);
+  in.w13_s = static_cast<const uint8_t*>(d_w13_s);
+  in.w2 = static_cast<const uint8_t*>(d_w2);
+  in.w2_s = static_cast<const uint8_t*>(d_w2_s);
+  in.sgu = static_cast<const uint8_t*>(d_sgu);
+  in.sgu_s = static_cast<const uint8_t*>(d_sgu_s);
+  in.sw2 = static_cast<const uint8_t*>(d_sw2);
+  in.sw2_s = static_cast<const uint8_t*>(d_sw2_s);
+  in.out = static_cast<uint16_t*>(d_out);
+
+  // w13 work items: at most max_vslots(m) * (Imax / 32); the grid is capped
+  // at the resident capacity and loops over the items the plan counted.
+  const int max_items = max_vslots(m, d.E, d.K) * (d.Imax / 32);
+  const int cap = p->cus * p->w13_per_cu;
+  const int grid13 = max_items < cap ? max_items : cap;
+
+  TimingSet* ts = nullptr;
+  if (p->timing) {
+    if (p->ring_used == kTimingRing) fold_timing(p);
+    ts = &p->ring[p->ring_used++];
+  }
+  hipError_t e;
+  if (ts && (e = hipEventRecord(ts->ev[0], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_seam(d, m, in, p->s, st)) != hipSuccess) return hip_fail(p, e, "seam launch");
+  if (ts && (e = hipEventRecord(ts->ev[1], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_w13(d, m, in, p->s, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 launch");
+  if (ts && (e = hipEventRecord(ts->ev[2], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_w2(d, m, in, p->s, p->max_vs, st)) != hipSuccess) return hip_fail(p, e, "w2 launch");
+  if (ts && (e = hipEventRecord(ts->ev[3], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  p->last_m = m;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_inspect(moe_decode_handle p, int32_t tap, const void** d_ptr, size_t* bytes) {
+  if (!p || !d_ptr || !bytes) return MOE_DECODE_EINVAL;
+  const LayerDims& d = p->d;
+  const size_t m = p->last_m > 0 ? p->last_m : d.Mx;
+  const size_t H = d.H, E = d.E, K = d.K, R = m * K + m;
+  const Scratch& s = p->s;
+  switch (tap) {
+    case MOE_DECODE_TAP_NORMED: *d_ptr = s.normed; *bytes = m * H * 2; break;
+    case MOE_DECODE_TAP_X8: *d_ptr = s.x8; *bytes = m * H; break;
+    case MOE_DECODE_TAP_X8S: *d_ptr = s.x8s; *bytes = m * H / 32; break;
+    case MOE_DECODE_TAP_LOGITS: *d_ptr = s.logits; *bytes = m * E * 8; break;
+    case MOE_DECODE_TAP_TOPK_IDS: *d_ptr = s.ids; *bytes = m * K * 4; break;
+    case MOE_DECODE_TAP_TOPK_W: *d_ptr = s.wts; *bytes = m * K * 4; break;
+    case MOE_DECODE_TAP_COUNTS: *d_ptr = s.counts; *bytes = E * 4; break;
+    case MOE_DECODE_TAP_PAIR_ROW: *d_ptr = s.pair_row; *bytes = m * K * 4; break;
+    case MOE_DECODE_TAP_ROW_TOK: *d_ptr = s.row_tok; *bytes = R * 4; break;
+    case MOE_DECODE_TAP_A8: *d_ptr = s.a8; *bytes = R * d.Imax; break;
+    case MOE_DECODE_TAP_A8S: *d_ptr = s.a8s; *bytes = R * d.Imax / 32; break;
+    default: return MOE_DECODE_EINVAL;
+  }
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_timing(moe_decode_handle p, int32_t on) {
+  if (!p) return MOE_DECODE_EINVAL;
+  if (on) {
+    if (p->ring.empty()) {
+      p->ring.resize(kTimingRing);
+      for (auto& t : p->ring)
+        for (auto& ev : t.ev) {
+          hipError_t e = hipEventCreate(&ev);
+          if (e != hipSuccess) {
+            free_timing(p);
+            return hip_fail(p, e, "hipEventCreate");
+          }
+        }
+    }
+    fold_timing(p);
+    p->total_ms[0] = p->total_ms[1] = p->total_ms[2] = 0.0;
+    p->runs = 0;
+    p->timing = true;
+  } else {
+    p->timing = false;
+  }
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_timing_read(moe_decode_handle p, int32_t kernel, double* total_ms, int32_t* runs) {
+  if (!p || kernel < 0 || kernel > 2 || !total_ms || !runs) return MOE_DECODE_EINVAL;
+  fold_timing(p);
+  *total_ms = p->total_ms[kernel];
+  *runs = p->runs;
+  return MOE_DECODE_OK;
+}
+
+void moe_decode_destroy(moe_decode_handle p) {
+  if (!p) return;
+  free_timing(p);
+  if (p->base) (void)hipFree(p->base);
+  delete p;
+}
+
+int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows, int32_t cols, void* d_q,
+                               void* d_scales, void* stream) {
+  if (count < 1 || rows < 32 || cols < 32 || rows % 32 || cols % 32) return MOE_DECODE_EINVAL;
+  if (!aligned16(d_w) || !aligned16(d_q) || d_scales == nullptr) return MOE_DECODE_EINVAL;
+  hipError_t e = launch_quant_weight(d_w, count, rows, cols, static_cast<uint8_t*>(d_q),
+                                     static_cast<uint8_t*>(d_scales), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "quantize launch");
+  return MOE_DECODE_OK;
+}
+
+const char* moe_decode_strerror(int code) {
+  switch (code) {
+    case MOE_DECODE_OK: return "success";
+    case MOE_DECODE_EINVAL: return "invalid argument";
+    case MOE_DECODE_ENOMEM: return "out of memory";
+    case MOE_DECODE_EHIP: return "HIP runtime error";
+    case MOE_DECODE_ECAPTURE: return "called during stream capture";
+    default: return "unknown error";
+  }
+}
+
+const char* moe_decode_last_hip_error(moe_decode_handle p) { return p ? p->err.c_str() : g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// kernels.hpp -- launch interface between the C ABI (api.hip) and the
+// kernels (seam.hip, experts.hip, quant.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Compile-time limits of the kernels (the C ABI validates against them).
+constexpr int kMaxTokens = 48;    // DSV41MonoLayer.supports: M <= 48
+constexpr int kMaxExperts = 1024;  // 16 sort groups of 64
+constexpr int kMaxTopk = 32;       // two top-k lists fit one 64-lane merge
+constexpr int kMaxHidden = 16384;
+constexpr int kMaxInter = 8192;
+constexpr int kTokTile = 16;       // token rows per MFMA tile (one "virtual slot")
+constexpr int kThreads = 256;      // seam and w13 blocks
+
+struct LayerDims {
+  int H, E, K, I, Is, Imax, Mx;
+  float eps, routed_scale;
+};
+
+// The plan's device scratch, laid out for Mx token rows.
+struct Scratch {
+  uint16_t* normed;   // [Mx, H] bf16
+  uint8_t* x8;        // [Mx, H] E4M3
+  uint8_t* x8s;       // [Mx, H/32] E8M0
+  double* logits;     // [Mx, E]
+  int32_t* ids;       // [Mx, K]
+  float* wts;         // [Mx, K]
+  int32_t* counts;    // [E]
+  int32_t* pair_row;  // [Mx, K]
+  int32_t* row_tok;   // [R] token of each row; R = Mx*K + Mx
+  float* row_w;       // [R] its routing weight (1 for the shared expert)
+  int4* vslots;       // [VS] {expert (-1: shared), first row, rows (<= 16), 0}
+  int32_t* header;    // [4] {virtual slots, shared virtual slots, w13 items, m}
+  uint32_t* counter;  // arrival counter of the seam blocks (zero between runs)
+  uint8_t* a8;        // [R, Imax] E4M3 SiLU*up intermediate
+  uint8_t* a8s;       // [R, Imax/32] E8M0
+};
+
+struct Inputs {
+  const uint16_t* x;
+  const uint16_t* norm_w;
+  const uint16_t* gate_w;
+  const float* bias;
+  const uint8_t *w13, *w13_s, *w2, *w2_s, *sgu, *sgu_s, *sw2, *sw2_s;
+  uint16_t* out;
+};
+
+// Upper bound on virtual slots (experts split into tiles of <= 16 rows, the
+// shared expert first) for m rows.
+inline int max_vslots(int m, int E, int K) {
+  int pairs = m * K;
+  int routed = (pairs < E ? pairs : E) + (pairs + kTokTile - 1) / kTokTile;
+  return routed + (m + kTokTile - 1) / kTokTile;
+}
+
+// Launchers; each returns the hipError_t of its launch.
+hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st);
+hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, hipStream_t st);
+hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int max_vs, hipStream_t st);
+int w13_blocks_per_cu();
+hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
+                               hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,55 @@
+"""The C ABI library loads on a machine without a GPU, exports every symbol
+its header declares, and rejects invalid plans before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_decode_layer_seam_amd as mdl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe_decode.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_decode_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 10, names
+    L = mdl.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mdl.EXPORTS)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=100), dict(hidden=0), dict(hidden=32768), dict(experts=0), dict(experts=2048),
+    dict(topk=0), dict(topk=9, experts=8), dict(topk=33, experts=64), dict(inter=96),
+    dict(shared_inter=0), dict(max_tokens=0), dict(max_tokens=49), dict(rms_eps=-1.0),
+    dict(rms_eps=float("nan")), dict(routed_scale=float("inf")),
+])
+def test_plan_rejects_invalid_dims(bad):
+    d = dict(hidden=256, experts=8, topk=2, inter=128, shared_inter=128, max_tokens=4,
+             rms_eps=1e-6, routed_scale=1.0)
+    d.update(bad)
+    dims = mdl.Dims(d["hidden"], d["experts"], d["topk"], d["inter"], d["shared_inter"],
+                    d["max_tokens"], d["rms_eps"], d["routed_scale"])
+    h = ctypes.c_void_p()
+    assert mdl.lib().moe_decode_plan(ctypes.byref(dims), None, ctypes.byref(h)) == mdl.EINVAL
+    assert h.value is None
+
+
+def test_null_handles_are_rejected():
+    L = mdl.lib()
+    assert mdl.run_ptrs(None, 1, [0] * 13, stream=0) == mdl.EINVAL
+    p, n = ctypes.c_void_p(), ctypes.c_size_t()
+    assert L.moe_decode_inspect(None, 0, ctypes.byref(p), ctypes.byref(n)) == mdl.EINVAL
+    assert L.moe_decode_timing(None, 1) == mdl.EINVAL
+    assert L.moe_decode_quantize_weight(None, 1, 32, 32, None, None, None) == mdl.EINVAL
+    L.moe_decode_destroy(None)
+    assert mdl.strerror(mdl.ECAPTURE) == "called during stream capture"

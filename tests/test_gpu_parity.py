@@ -1,0 +1,299 @@
+"""Parity of the HIP path with the oracle, through the C ABI.
+
+Bars: bit-exact for the normed bf16 rows, the MXFP8 activation bytes and
+codes, the picked experts and the plan; |gpu - ref| <= 1e-2 + 2e-2 |ref| for
+the bf16 output (ref: the oracle's double-precision sum before its rounding);
+routing weights within 1e-6 relative.  The SiLU*up intermediate is compared
+to the oracle's by fraction of equal bytes (its accumulation order differs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import data
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+import moe_decode_layer_seam_amd as mdl  # noqa: E402
+
+
+def _cfg(m, H, E, K, I, Is, **kw):
+    c = dict(name=f"m{m}_h{H}_e{E}_k{K}_i{I}_is{Is}", m=m, hidden=H, experts=E, topk=K,
+             inter=I, shared_inter=Is, rms_eps=1e-6, routed_scale=1.0)
+    c.update(kw)
+    return c
+
+
+SMALL = [
+    synth.CONFIGS[0],
+    _cfg(1, 256, 64, 6, 128, 128),
+    _cfg(5, 512, 64, 6, 256, 128),          # I != Is
+    _cfg(13, 640, 100, 8, 128, 256),        # H % 512 != 0, E not a multiple of 64
+    _cfg(16, 256, 256, 8, 128, 128),
+    _cfg(17, 384, 256, 8, 256, 256, routed_scale=2.5),
+    _cfg(33, 256, 8, 8, 128, 128),          # k = E
+    _cfg(48, 512, 64, 4, 256, 256),
+    _cfg(48, 256, 512, 16, 128, 128),       # 8 sort groups, k = 16
+    _cfg(7, 256, 1000, 32, 128, 128),       # 16 sort groups, k = 32
+]
+
+
+def _plan_for(cfg, max_tokens=None):
+    return mdl.plan(cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"],
+                    cfg["shared_inter"], max_tokens or cfg["m"], cfg["rms_eps"],
+                    cfg["routed_scale"])
+
+
+def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
+    """Compare every intermediate of the last run with the oracle."""
+    m, H, E, K = cfg["m"], cfg["hidden"], cfg["experts"], cfg["topk"]
+    dims = data.dims_of(cfg)
+    # norm, quant and router for every row (cheap on the CPU)
+    y = oracle.rmsnorm(inp["x"], inp["norm_w"], cfg["rms_eps"])
+    assert np.array_equal(gu.tap(handle, "normed", torch.int16).view(np.uint16).reshape(m, H), y)
+    x8 = np.empty((m, H), np.uint8)
+    x8s = np.empty((m, H // 32), np.uint8)
+    for t in range(m):
+        x8[t], x8s[t] = oracle.mx_quant_row(_bf16_f64(y[t]))
+    assert np.array_equal(gu.tap(handle, "x8").reshape(m, H), x8)
+    assert np.array_equal(gu.tap(handle, "x8s").reshape(m, H // 32), x8s)
+    r = oracle.router(y, inp["gate_w"], inp["bias"], K, cfg["routed_scale"])
+    logits = gu.tap(handle, "logits", torch.float64).reshape(m, E)
+    assert np.allclose(logits, r["logits"], rtol=1e-12, atol=1e-12)
+    ids = gu.tap(handle, "topk_ids", torch.int32).reshape(m, K)
+    assert np.array_equal(ids, r["ids"]), f"ids differ; oracle margins {r['margin']}"
+    wts = gu.tap(handle, "topk_w", torch.float32).reshape(m, K)
+    assert np.allclose(wts, r["wts"], rtol=1e-6, atol=0)
+    counts, row = oracle.plan(r["ids"], E)
+    assert np.array_equal(gu.tap(handle, "counts", torch.int32), counts)
+    assert np.array_equal(gu.tap(handle, "pair_row", torch.int32).reshape(m, K), row)
+    row_tok = gu.tap(handle, "row_tok", torch.int32)
+    want_tok = np.empty(m * K + m, np.int32)
+    want_tok[row.ravel()] = np.repeat(np.arange(m), K)
+    want_tok[m * K:] = np.arange(m)
+    assert np.array_equal(row_tok, want_tok)
+    # output rows (all, or a sample at full size)
+    rows = list(range(m)) if rows_ref is None else list(rows_ref)
+    if o is None:
+        o = oracle.layer_parallel(dims, inp, w, rows, workers=data.WORKERS)
+    got = gu.out_f64(out)[rows]
+    gu.assert_out_close(got, o["out_f64"], what=cfg["name"])
+    return r, o
+
+
+def _bf16_f64(bits):
+    """bf16 bit patterns -> their values as float64."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c["name"])
+def test_parity_small(cfg):
+    inp, w = data.build_layer(7, cfg)
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg, max_tokens=48)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        r, o = _check_layer(cfg, h, inp, w, out)
+        # the intermediate: nearly all bytes equal (fp32 vs double accumulation)
+        a8 = gu.tap(h, "a8")
+        Imax = max(cfg["inter"], cfg["shared_inter"])
+        a8 = a8.reshape(-1, Imax)
+        counts, row = oracle.plan(r["ids"], cfg["experts"])
+        same = tot = 0
+        for t in range(min(cfg["m"], 4)):
+            for j in range(cfg["topk"]):
+                e = r["ids"][t, j]
+                ref = oracle.expert(o["x8"][t], o["x8s"][t], w["w13"][e], w["w13_s"][e],
+                                    w["w2"][e], w["w2_s"][e])["a8"]
+                got = a8[row[t, j], :cfg["inter"]]
+                same += int((got == ref).sum())
+                tot += ref.size
+        assert same >= 0.995 * tot, f"a8 equal bytes {same}/{tot}"
+    finally:
+        mdl.destroy(h)
+
+
+def test_zero_tokens_give_exact_zero():
+    cfg = _cfg(9, 512, 64, 6, 128, 128)
+    inp, w = data.build_layer(8, cfg)
+    inp["x"] = np.zeros_like(inp["x"])
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        assert torch.all(out.view(torch.int16) == 0)
+        assert np.all(gu.tap(h, "x8") == 0) and np.all(gu.tap(h, "x8s") == 0)
+        want = np.argsort(-inp["bias"].astype(np.float64), kind="stable")[:6]
+        ids = gu.tap(h, "topk_ids", torch.int32).reshape(9, 6)
+        assert np.all(ids == want[None, :])
+    finally:
+        mdl.destroy(h)
+
+
+def test_concentrated_routing_splits_slots():
+    # every token picks the same experts: 48 rows per expert, three token tiles
+    cfg = _cfg(48, 256, 64, 4, 128, 128)
+    inp, w = data.build_layer(9, cfg)
+    inp["bias"] = inp["bias"].copy()
+    inp["bias"][[3, 17, 40, 63]] = 10.0
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        _check_layer(cfg, h, inp, w, out)
+    finally:
+        mdl.destroy(h)
+
+
+def test_runs_are_deterministic_and_plan_reusable_across_m():
+    cfg = _cfg(48, 512, 256, 8, 256, 256)
+    inp, w = data.build_layer(10, cfg)
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        a = gu.run(h, cfg, dinp, dw).clone()
+        b = gu.run(h, cfg, dinp, dw).clone()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        # a smaller step on the same plan, then the full one again
+        c = gu.run(h, cfg, dinp, dw, x=dinp["x"][:5].contiguous())
+        d = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), a[:5].view(torch.int16))
+        assert torch.equal(d.view(torch.int16), a.view(torch.int16))
+    finally:
+        mdl.destroy(h)
+
+
+def test_graph_capture_replays_match_eager():
+    cfg = _cfg(16, 512, 64, 6, 256, 128)
+    inp, w = data.build_layer(11, cfg)
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        xs = [gu.bf16_dev(synth.to_bf16_bits(synth.normal(100 + i, 1, (16, 512)))) for i in range(4)]
+        eager = []
+        for x in xs:
+            eager.append(gu.run(h, cfg, dinp, dw, x=x).clone())
+        torch.cuda.synchronize()
+        xin = torch.empty_like(xs[0])
+        out = torch.empty_like(xs[0])
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            gu.run(h, cfg, dinp, dw, x=xin, out=out)  # warm-up outside the graph
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gu.run(h, cfg, dinp, dw, x=xin, out=out)
+        for rep in range(3):
+            for i, x in enumerate(xs):
+                xin.copy_(x)
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out.view(torch.int16), eager[i].view(torch.int16)), (rep, i)
+        del g
+    finally:
+        mdl.destroy(h)
+
+
+def test_quantize_weight_matches_oracle():
+    w = synth.normal(12, 77, (3, 256, 320), 0.0, 0.02)
+    w[0, :32, :32] = 0.0                      # all-zero block: code 0
+    w[1, 32:64, 64:96] *= 1e-30               # tiny block
+    w[2, 100, 200] = 300.0                    # a spike
+    w[2, 5, 7] = -1e-41                       # a subnormal
+    q_ref = np.empty(w.shape, np.uint8)
+    s_ref = np.empty((3, 8, 10), np.uint8)
+    for i in range(3):
+        q_ref[i], s_ref[i] = oracle.quant_weight(w[i])
+    wd = torch.from_numpy(w).cuda()
+    q = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+    s = torch.empty((3, 8, 10), dtype=torch.uint8, device="cuda")
+    mdl.quantize_weight(wd, q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_run_rejects_bad_arguments_without_launching():
+    cfg = _cfg(4, 256, 8, 2, 128, 128)
+    inp, w = data.build_layer(13, cfg)
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        out = torch.empty_like(dinp["x"])
+        ptrs = [dinp["x"].data_ptr(), dinp["norm_w"].data_ptr(), dinp["gate_w"].data_ptr(),
+                dinp["bias"].data_ptr()] + [dw[n].data_ptr() for n in gu.WEIGHT_NAMES] + [out.data_ptr()]
+        assert mdl.run_ptrs(h, 0, ptrs) == mdl.EINVAL          # empty step
+        assert mdl.run_ptrs(h, 5, ptrs) == mdl.EINVAL          # m > max_tokens
+        for i in range(13):
+            bad = list(ptrs)
+            bad[i] = 0
+            assert mdl.run_ptrs(h, 4, bad) == mdl.EINVAL       # null
+            bad[i] = ptrs[i] + 8
+            assert mdl.run_ptrs(h, 4, bad) == mdl.EINVAL       # misaligned
+        alias = list(ptrs)
+        alias[12] = ptrs[0]
+        assert mdl.run_ptrs(h, 4, alias) == mdl.EINVAL         # out aliases x
+        assert mdl.run_ptrs(h, 4, ptrs) == mdl.OK
+        torch.cuda.synchronize()
+    finally:
+        mdl.destroy(h)
+
+
+def test_plan_refuses_during_capture():
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    codes = []
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        try:
+            torch.zeros(1, device="cuda").add_(1)  # keep the captured graph non-empty
+            d = mdl.Dims(256, 8, 2, 128, 128, 4, 1e-6, 1.0)
+            hh = mdl._P()
+            codes.append(mdl.lib().moe_decode_plan(mdl.ctypes.byref(d), s.cuda_stream, mdl.ctypes.byref(hh)))
+        finally:
+            g.capture_end()
+    assert codes == [mdl.ECAPTURE]
+
+
+# ---------------------------------------------------------------- full size ----
+
+_FULL = {}
+
+
+def _full_layer(idx):
+    """Configs 1-3 share one weight set (the picks of config 3's 48 rows cover
+    configs 1 and 2, whose rows are its first rows); config 4 has its own."""
+    key = "dsv41" if idx in (1, 2, 3) else "draft"
+    if key not in _FULL:
+        base = synth.CONFIGS[3] if key == "dsv41" else synth.CONFIGS[4]
+        inp, w = data.build_layer(0, base, experts="picked")
+        _FULL[key] = (base, inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
+    return _FULL[key]
+
+
+SAMPLES = {1: [0], 2: [0, 9, 15], 3: [0, 29, 47], 4: [0, 23, 47]}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_parity_full_size(idx):
+    cfg = synth.CONFIGS[idx]
+    base, inp_all, w, dinp_all, dw = _full_layer(idx)
+    m = cfg["m"]
+    inp = dict(inp_all, x=inp_all["x"][:m])
+    dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
+    h = _plan_for(cfg, max_tokens=48)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        print(f"[{cfg['name']}] ran; checking rows {SAMPLES[idx]}", flush=True)
+        _check_layer(cfg, h, inp, w, out, rows_ref=SAMPLES[idx])
+    finally:
+        mdl.destroy(h)
