@@ -154,11 +154,32 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * run's stream).  moe_decode_timing(plan, 1) starts recording (and clears the
  * totals), 0 stops.  While on, moe_decode_run must not be captured into a
  * graph.  moe_decode_timing_read sums the elapsed milliseconds of every
- * recorded run for kernel `kernel` (0 seam, 1 w13, 2 w2); it synchronises
+ * recorded run for kernel `kernel` (0 seam, 1 route, 2 w13, 3 w13 finish,
+ * 4 w2); it synchronises
  * with the recorded events. */
 int moe_decode_timing(moe_decode_handle plan, int32_t on);
 int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
                            double* total_ms, int32_t* runs);
+
+/* Timeline of runs (the pages' timeline build: "layer" run_ffn's mark and
+ * "device" stamp / memrealtime).  While on, thread 0 of every block of each
+ * kernel stores the 100 MHz device clock (s_memrealtime) at fixed points:
+ *   seam:  0 start, 1 squares summed, 2 logits stored
+ *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
+ *          4 plan written (3-4 only in the last block)
+ *   w13:   0 start, 1 first K segment done, 2 wave 0 done, 3 + w: wave w done
+ *   w13 finish: 0 start, 1 end (blocks with a split item)
+ *   w2:    0 start, 1 plan staged, 2 K loop done, 3 end
+ * Point 7 of every record holds where the block ran (XCC id << 32 | the
+ * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
+ * Unwritten points keep stale values.  moe_decode_timeline_read copies the
+ * last run's records of kernel `kernel` (0 seam, 1 route, 2 w13, 3 w13
+ * finish, 4 w2) as
+ * u64 [blocks][8] into h_out (n entries available), sets *blocks, and
+ * synchronises the device. */
+int moe_decode_timeline(moe_decode_handle plan, int32_t on);
+int moe_decode_timeline_read(moe_decode_handle plan, int32_t kernel,
+                             uint64_t* h_out, size_t n, int32_t* blocks);
 
 /* Frees the plan's scratch.  NULL is allowed. */
 void moe_decode_destroy(moe_decode_handle plan);

@@ -25,7 +25,7 @@ MAX_TOKENS = 48
 
 TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
         "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10}
-KERNELS = {"seam": 0, "w13": 1, "w2": 2}
+KERNELS = {"seam": 0, "route": 1, "w13": 2, "w13_finish": 3, "w2": 4}
 
 
 class Dims(ctypes.Structure):
@@ -69,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_timing_read.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int32)]
         L.moe_decode_timing_read.restype = ctypes.c_int
+        L.moe_decode_timeline.argtypes = [_P, ctypes.c_int32]
+        L.moe_decode_timeline.restype = ctypes.c_int
+        L.moe_decode_timeline_read.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_size_t,
+                                               ctypes.POINTER(ctypes.c_int32)]
+        L.moe_decode_timeline_read.restype = ctypes.c_int
         L.moe_decode_destroy.argtypes = [_P]
         L.moe_decode_destroy.restype = None
         L.moe_decode_quantize_weight.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
@@ -84,6 +89,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
            "moe_decode_inspect", "moe_decode_timing", "moe_decode_timing_read",
+           "moe_decode_timeline", "moe_decode_timeline_read",
            "moe_decode_destroy", "moe_decode_quantize_weight", "moe_decode_strerror",
            "moe_decode_last_hip_error")
 
@@ -211,6 +217,20 @@ def timing_read(handle: int, kernel: str) -> tuple[float, int]:
     _check(lib().moe_decode_timing_read(handle, KERNELS[kernel], ctypes.byref(ms), ctypes.byref(runs)),
            "moe_decode_timing_read", handle)
     return ms.value, runs.value
+
+
+def timeline(handle: int, on: bool) -> None:
+    _check(lib().moe_decode_timeline(handle, 1 if on else 0), "moe_decode_timeline", handle)
+
+
+def timeline_read(handle: int, kernel: str):
+    """The last run's stamps of one kernel: uint64 [blocks, 8] (100 MHz clock)."""
+    import numpy as np
+    buf = np.zeros(1024 * 8, np.uint64)
+    nb = ctypes.c_int32()
+    _check(lib().moe_decode_timeline_read(handle, KERNELS[kernel], buf.ctypes.data, buf.size,
+                                          ctypes.byref(nb)), "moe_decode_timeline_read", handle)
+    return buf[: nb.value * 8].reshape(nb.value, 8)
 
 
 def destroy(handle: int) -> None:

@@ -31,7 +31,7 @@ constexpr int kTimingRing = 256;  // runs whose events are held before folding
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct TimingSet {
-  hipEvent_t ev[4];
+  hipEvent_t ev[kKernels + 1];
 };
 
 std::string g_last_error = "no error";
@@ -49,12 +49,15 @@ struct moe_decode_plan_s {
   void* base = nullptr;
   Scratch s{};
   int last_m = 0;
+  int last_grid[kKernels] = {0, 0, 0, 0, 0};
+  bool timeline = false;
+  uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
   std::string err = "no error";
   // timing
   bool timing = false;
   std::vector<TimingSet> ring;
   int ring_used = 0;
-  double total_ms[3] = {0, 0, 0};
+  double total_ms[kKernels] = {0, 0, 0, 0, 0};
   int runs = 0;
 };
 
@@ -86,8 +89,8 @@ bool valid_dims(const moe_decode_dims* d) {
 void fold_timing(moe_decode_plan_s* p) {
   for (int i = 0; i < p->ring_used; ++i) {
     TimingSet& t = p->ring[i];
-    (void)hipEventSynchronize(t.ev[3]);
-    for (int k = 0; k < 3; ++k) {
+    (void)hipEventSynchronize(t.ev[kKernels]);
+    for (int k = 0; k < kKernels; ++k) {
       float ms = 0.0f;
       if (hipEventElapsedTime(&ms, t.ev[k], t.ev[k + 1]) == hipSuccess) p->total_ms[k] += ms;
     }
@@ -161,6 +164,9 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   const size_t o_counts = take(E * 4), o_pair = take(Mx * K * 4), o_tok = take(R * 4), o_roww = take(R * 4);
   const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
   const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
+  const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
+  const size_t w13_waves = (size_t)p->cus * p->w13_per_cu * 4;
+  const size_t o_part = take(2 * w13_waves * kTokTile * 64 * 4);
   p->bytes = off;
   if ((e = hipMalloc(&p->base, p->bytes)) != hipSuccess) {
     hip_fail(p, e, "hipMalloc");
@@ -190,6 +196,9 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.counter = reinterpret_cast<uint32_t*>(b + o_ctr);
   s.a8 = reinterpret_cast<uint8_t*>(b + o_a8);
   s.a8s = reinterpret_cast<uint8_t*>(b + o_a8s);
+  p->tl_base = reinterpret_cast<uint64_t*>(b + o_tl);
+  s.part = reinterpret_cast<float*>(b + o_part);
+  s.tl_seam = s.tl_route = s.tl_w13 = s.tl_w13f = s.tl_w2 = nullptr;
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -238,25 +247,41 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   in.sw2_s = static_cast<const uint8_t*>(d_sw2_s);
   in.out = static_cast<uint16_t*>(d_out);
 
-  // w13 work items: at most max_vslots(m) * (Imax / 32); the grid is capped
-  // at the resident capacity and loops over the items the plan counted.
-  const int max_items = max_vslots(m, d.E, d.K) * (d.Imax / 32);
-  const int cap = p->cus * p->w13_per_cu;
-  const int grid13 = max_items < cap ? max_items : cap;
+  // w13: every resident block slot of the device; the kernel cuts the
+  // plan's (item, K step) pairs into equal shares per wave
+  const int grid13 = p->cus * p->w13_per_cu;
 
   TimingSet* ts = nullptr;
   if (p->timing) {
     if (p->ring_used == kTimingRing) fold_timing(p);
     ts = &p->ring[p->ring_used++];
   }
+  Scratch sc = p->s;
+  if (p->timeline) {
+    sc.tl_seam = p->tl_base;
+    sc.tl_route = p->tl_base + (size_t)1 * kTlBlocks * kTlPoints;
+    sc.tl_w13 = p->tl_base + (size_t)2 * kTlBlocks * kTlPoints;
+    sc.tl_w13f = p->tl_base + (size_t)3 * kTlBlocks * kTlPoints;
+    sc.tl_w2 = p->tl_base + (size_t)4 * kTlBlocks * kTlPoints;
+  }
+  p->last_grid[0] = seam_blocks(d, m);
+  p->last_grid[1] = m;
+  p->last_grid[2] = grid13;
+  p->last_grid[3] = (max_vslots(m, d.E, d.K) * (d.Imax / 32) + 3) / 4;
+  p->last_grid[4] = d.H / 16;
   hipError_t e;
-  if (ts && (e = hipEventRecord(ts->ev[0], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_seam(d, m, in, p->s, st)) != hipSuccess) return hip_fail(p, e, "seam launch");
-  if (ts && (e = hipEventRecord(ts->ev[1], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_w13(d, m, in, p->s, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 launch");
-  if (ts && (e = hipEventRecord(ts->ev[2], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_w2(d, m, in, p->s, p->max_vs, st)) != hipSuccess) return hip_fail(p, e, "w2 launch");
-  if (ts && (e = hipEventRecord(ts->ev[3], st)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  auto rec = [&](int i) { return ts ? hipEventRecord(ts->ev[i], st) : hipSuccess; };
+  if ((e = rec(0)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_seam(d, m, in, sc, st)) != hipSuccess) return hip_fail(p, e, "seam launch");
+  if ((e = rec(1)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_route(d, m, in, sc, st)) != hipSuccess) return hip_fail(p, e, "route launch");
+  if ((e = rec(2)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_w13(d, m, in, sc, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 launch");
+  if ((e = rec(3)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_w13_finish(d, m, in, sc, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 finish launch");
+  if ((e = rec(4)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  if ((e = launch_w2(d, m, in, sc, p->max_vs, st)) != hipSuccess) return hip_fail(p, e, "w2 launch");
+  if ((e = rec(5)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
   p->last_m = m;
   return MOE_DECODE_OK;
 }
@@ -299,7 +324,7 @@ int moe_decode_timing(moe_decode_handle p, int32_t on) {
         }
     }
     fold_timing(p);
-    p->total_ms[0] = p->total_ms[1] = p->total_ms[2] = 0.0;
+    for (double& t : p->total_ms) t = 0.0;
     p->runs = 0;
     p->timing = true;
   } else {
@@ -309,10 +334,28 @@ int moe_decode_timing(moe_decode_handle p, int32_t on) {
 }
 
 int moe_decode_timing_read(moe_decode_handle p, int32_t kernel, double* total_ms, int32_t* runs) {
-  if (!p || kernel < 0 || kernel > 2 || !total_ms || !runs) return MOE_DECODE_EINVAL;
+  if (!p || kernel < 0 || kernel >= kKernels || !total_ms || !runs) return MOE_DECODE_EINVAL;
   fold_timing(p);
   *total_ms = p->total_ms[kernel];
   *runs = p->runs;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_timeline(moe_decode_handle p, int32_t on) {
+  if (!p) return MOE_DECODE_EINVAL;
+  p->timeline = on != 0;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_timeline_read(moe_decode_handle p, int32_t kernel, uint64_t* h_out, size_t n, int32_t* blocks) {
+  if (!p || kernel < 0 || kernel >= kKernels || !blocks) return MOE_DECODE_EINVAL;
+  const int nb = p->last_grid[kernel] < kTlBlocks ? p->last_grid[kernel] : kTlBlocks;
+  *blocks = nb;
+  const size_t want = (size_t)nb * kTlPoints;
+  if (!h_out || n < want) return MOE_DECODE_EINVAL;
+  hipError_t e = hipMemcpy(h_out, p->tl_base + (size_t)kernel * kTlBlocks * kTlPoints, want * 8,
+                           hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(p, e, "hipMemcpy");
   return MOE_DECODE_OK;
 }
 

@@ -20,8 +20,8 @@ constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
 // Lane exchange: value of lane (lane ^ mask).  Masks 1 and 2 are DPP quad
-// permutations, 4 and 8 a pair of DPP row shifts with bank masks, larger
-// masks go through ds_bpermute (device page, xshfl).
+// permutations, 4 and 8 a pair of DPP row shifts with bank masks, 16 and 32
+// permlane swaps across rows (device page, xshfl); others ds_bpermute.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int xor_lane(int v, int mask) {
   switch (mask) {
@@ -36,6 +36,18 @@ __device__ __forceinline__ int xor_lane(int v, int mask) {
     case 8: {
       int y = __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xC, false);  // row_shr:8, banks 2,3
       return __builtin_amdgcn_update_dpp(y, v, 0x108, 0xF, 0x3, false);   // row_shl:8, banks 0,1
+    }
+    case 16: {
+      // v_permlane16_swap: odd 16-lane rows of the first operand trade
+      // places with even rows of the second
+      const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+      return (int)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+    }
+    case 32: {
+      // v_permlane32_swap: upper 32 lanes of the first operand trade places
+      // with the lower 32 of the second
+      const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+      return (int)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
     }
     default:
       return __shfl_xor(v, mask, kWave);
@@ -136,5 +148,74 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *reinterpret_ca
 __device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+
+// ---------------------------------------------------------------------------
+// Buffer loads: a 128-bit descriptor (base, byte range) held in scalar
+// registers and a 32-bit per-lane offset.  Reads at or past the range return
+// zero, which is how lanes without a token row read their empty operand.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+// Non-temporal (streamed once) variant for weights read in whole cache lines.
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2 /* nt */);
+}
+
+// Weight tiles are read as two full-line loads: lane (g, j) of load X holds
+// row (j & 7) bytes [16 g, +16) when j < 8 and [64 + 16 g, +16) when j >= 8;
+// load Y the same for rows 8..15.  Two DPP row shifts per register turn the
+// pair into the scaled MFMA's operand halves of row j:
+//   lo = j < 8 ? X : Y(lane - 8),   hi = j < 8 ? X(lane + 8) : Y.
+__device__ __forceinline__ void lines_to_mfma(const u32x4& x, const u32x4& y, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)x[i], (int)y[i], 0x118, 0xF, 0xC, false);  // row_shr:8, lanes 8-15
+    hi[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)y[i], (int)x[i], 0x108, 0xF, 0x3, false);  // row_shl:8, lanes 0-7
+  }
+}
+
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// Timeline stamp (device page, memrealtime / stamp): thread 0 of the block
+// stores the 100 MHz device clock at record [block][point] (vector store).
+// tl == nullptr: no timeline.
+// Blocks are numbered x-fastest; records past kTlBlockCap are dropped.  The
+// last point of a record holds where the block ran: the XCC id in the upper
+// half, the HW_ID register (CU, shader array, SE) in the lower.
+constexpr int kTlBlockCap = 1024;
+
+__device__ __forceinline__ void stamp(uint64_t* tl, int points, int point) {
+  if (tl == nullptr || threadIdx.x != 0) return;
+  const uint32_t b = blockIdx.x + blockIdx.y * gridDim.x;
+  if (b >= (uint32_t)kTlBlockCap) return;
+  uint64_t* rec = tl + (size_t)b * points;
+  rec[point] = __builtin_amdgcn_s_memrealtime();
+  if (point == 0) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_REG_HW_ID, 32 bits
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // HW_REG_XCC_ID
+    rec[points - 1] = ((uint64_t)xcc << 32) | hw;
+  }
+}
+
+// Per-wave stamp: lane 0 of the calling wave stores the clock at `point`.
+__device__ __forceinline__ void stamp_wave(uint64_t* tl, int points, int point) {
+  if (tl == nullptr || (threadIdx.x & 63) != 0) return;
+  const uint32_t b = blockIdx.x + blockIdx.y * gridDim.x;
+  if (b >= (uint32_t)kTlBlockCap) return;
+  tl[(size_t)b * points + point] = __builtin_amdgcn_s_memrealtime();
+}
+
+// A lane offset no buffer of this library reaches: loads through it read 0.
+constexpr uint32_t kNoRow = 0x7FFFFF00u;
 
 }  // namespace moe

@@ -38,7 +38,19 @@ struct Scratch {
   uint32_t* counter;  // arrival counter of the seam blocks (zero between runs)
   uint8_t* a8;        // [R, Imax] E4M3 SiLU*up intermediate
   uint8_t* a8s;       // [R, Imax/32] E8M0
+  float* part;         // [2 * w13 waves][kTokTile][64] partial sums of split w13 items
+  // timeline records [block][kTlPoints] of each kernel (nullptr: off)
+  uint64_t* tl_seam;
+  uint64_t* tl_route;
+  uint64_t* tl_w13;
+  uint64_t* tl_w13f;
+  uint64_t* tl_w2;
 };
+
+constexpr int kKernels = 5;      // seam, route, w13, w13 finish, w2
+
+constexpr int kTlPoints = 8;     // stamps per block and kernel
+constexpr int kTlBlocks = 1024;  // blocks recorded per kernel (kTlBlockCap)
 
 struct Inputs {
   const uint16_t* x;
@@ -57,9 +69,20 @@ inline int max_vslots(int m, int E, int K) {
   return routed + (m + kTokTile - 1) / kTokTile;
 }
 
+// Experts per block of the seam launch (at most 256 expert slices).
+inline int seam_epb(int E) { return E <= 256 ? 1 : (E <= 512 ? 2 : 4); }
+// Token rows per block of the seam launch (rows held in registers).
+inline int seam_tb(int H) { return (H + 2047) / 2048 <= 4 ? 8 : 4; }
+inline int seam_blocks(const LayerDims& d, int m) {
+  return (d.E + seam_epb(d.E) - 1) / seam_epb(d.E) * ((m + seam_tb(d.H) - 1) / seam_tb(d.H));
+}
+
 // Launchers; each returns the hipError_t of its launch.
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st);
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st);
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, hipStream_t st);
+hipError_t launch_w13_finish(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w13_grid,
+                             hipStream_t st);
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int max_vs, hipStream_t st);
 int w13_blocks_per_cu();
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,

@@ -1,24 +1,210 @@
-// seam.hip -- the FFN seam and the router, one launch:
-//   RMSNorm -> bf16 normed rows -> MXFP8 (x8, x8s)
-//   router logits (double) -> sigmoid + bias -> top-k (sort network over
-//   expert groups of 64) -> routing weights -> token->expert plan.
+// seam.hip -- the FFN seam and the router, two launches:
+//   seam:  RMSNorm -> bf16 normed rows -> MXFP8 (x8, x8s); router logits in
+//          double precision.  Blocks tile (experts) x (token rows).
+//   route: per token, sigmoid + bias -> top-k by bitonic sort networks over
+//          expert groups of 64 (the four waves of a block sort groups in
+//          parallel, then merge) -> routing weights; the last block to
+//          finish writes the token->expert plan.
 //
 // Pages: "vllm.models.deepseek_v41.amd.mono.layer" run_ffn (the seam's norm,
 // then the MoE), store_normed (the normed row, bf16), store_x8 (MXFP8 of 8
 // columns per lane, amax over the 4 lanes of a 32-group, code, multiply,
 // E4M3 pack); "vllm.models.deepseek_v41.amd.mono.runner" MonoLayerWeights
 // (gate_w bf16 [E, H], bias f32 [E], the e_score_correction_bias);
-// build_mono_ffn (expert groups of 64 for the routing sort networks).
-//
-// Every block computes the norm of every token (a token row is 2H bytes, so
-// recomputing it is cheaper than a second launch at M <= 48) and the logits
-// of its own slice of experts.  The last block to finish -- found with an
-// arrival counter, no waiting -- picks the experts and writes the plan.
+// build_mono_ffn (expert groups of 64 for the routing sort networks);
+// "vllm.models.deepseek_v41.amd.mono.attention.device" atomic_add_dev
+// (relaxed device-scope counters: no L2 write-back or invalidate).
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
+
+// ===========================================================================
+// seam: norm, MXFP8, logits
+// ===========================================================================
+
+// Block (es, ts): experts [EPB es, +EPB) and token rows [TB ts, +TB).  Every
+// thread covers CPT chunks of 8 columns, the block 2048 consecutive columns
+// per chunk.  The norm weight and the gate rows are loaded once, up front,
+// when they fit in registers (PRE); the token rows are held in registers
+// between the sum of squares and the normed row.
+template <int EPB, int CPT, int TB>
+__global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inputs in, Scratch s) {
+  __shared__ double red_ss[TB][4];
+  __shared__ double red_lg[TB][EPB][4];
+  constexpr bool PRE = EPB * CPT <= 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int es = blockIdx.x, nES = gridDim.x;
+  const int t0 = blockIdx.y * TB;
+  const int nt = m - t0 < TB ? m - t0 : TB;
+  const int H = d.H, E = d.E;
+  const int e0 = es * EPB;
+  stamp(s.tl_seam, kTlPoints, 0);
+
+  int col[CPT];
+  bool live[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    col[q] = 8 * tid + 2048 * q;
+    live[q] = col[q] < H;
+  }
+  u32x4 wv[PRE ? CPT : 1], gv[PRE ? EPB : 1][PRE ? CPT : 1];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      if (live[q]) {
+        wv[q] = ld16(reinterpret_cast<const uint8_t*>(in.norm_w + col[q]));
+#pragma unroll
+        for (int e = 0; e < EPB; ++e)
+          if (e0 + e < E) gv[e][q] = ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + e) * H + col[q]));
+      }
+    }
+  }
+  u32x4 xv[TB][CPT];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      if (tt < nt && live[q]) xv[tt][q] = ld16(reinterpret_cast<const uint8_t*>(in.x + (size_t)(t0 + tt) * H + col[q]));
+
+  // sum of squares in double: each square of a bf16 is exact; lanes, then
+  // waves, are added in a fixed order
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+    double ss = 0.0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      if (tt < nt && live[q]) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const double lo = bf16_to_f32(xv[tt][q][z] & 0xFFFFu), hi = bf16_to_f32(xv[tt][q][z] >> 16);
+          ss += lo * lo;
+          ss += hi * hi;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red_ss[tt][wave] = ss;
+  }
+  __syncthreads();
+  stamp(s.tl_seam, kTlPoints, 1);
+
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+    if (tt >= nt) break;
+    const int t = t0 + tt;
+    const double ss = red_ss[tt][0] + red_ss[tt][1] + red_ss[tt][2] + red_ss[tt][3];
+    const float r = (float)(1.0 / sqrt(ss / (double)H + (double)d.eps));
+    const bool owner = (t % nES) == es;
+    double acc[EPB];
+#pragma unroll
+    for (int e = 0; e < EPB; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      float y[8];
+      uint32_t yb[8];
+      if (live[q]) {
+        u32x4 w;
+        if constexpr (PRE) w = wv[q];
+        else w = ld16(reinterpret_cast<const uint8_t*>(in.norm_w + col[q]));
+#pragma unroll
+        for (int z = 0; z < 8; ++z) {
+          const uint32_t xb = (z & 1) ? (xv[tt][q][z >> 1] >> 16) : (xv[tt][q][z >> 1] & 0xFFFFu);
+          const uint32_t wb = (z & 1) ? (w[z >> 1] >> 16) : (w[z >> 1] & 0xFFFFu);
+          const float xr = bf16_to_f32(xb) * r;   // fp32 product, rounded
+          const float yw = xr * bf16_to_f32(wb);  // fp32 product, rounded
+          yb[z] = f32_to_bf16(yw);
+          y[z] = bf16_to_f32(yb[z]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPB; ++e) {
+          if (e0 + e < E) {
+            u32x4 g;
+            if constexpr (PRE) g = gv[e][q];
+            else g = ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + e) * H + col[q]));
+#pragma unroll
+            for (int z = 0; z < 8; ++z) {
+              const uint32_t gb = (z & 1) ? (g[z >> 1] >> 16) : (g[z >> 1] & 0xFFFFu);
+              acc[e] += (double)y[z] * (double)bf16_to_f32(gb);  // exact products
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) {
+          y[z] = 0.0f;
+          yb[z] = 0;
+        }
+      }
+      if (owner) {
+        // store_normed: the bf16 row; store_x8: MXFP8 of each 32 columns,
+        // held by 4 consecutive lanes
+        float amax = 0.0f;
+#pragma unroll
+        for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
+        amax = group_max(amax, 4);
+        const int code = e8m0_code(amax);
+        const float mul = mx_mul(code);
+        if (live[q]) {
+          u32x4 nv;
+#pragma unroll
+          for (int z = 0; z < 4; ++z) nv[z] = yb[2 * z] | (yb[2 * z + 1] << 16);
+          *reinterpret_cast<u32x4*>(s.normed + (size_t)t * H + col[q]) = nv;
+          u32x2 qv;
+          qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
+          qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
+          *reinterpret_cast<u32x2*>(s.x8 + (size_t)t * H + col[q]) = qv;
+          if ((lane & 3) == 0) s.x8s[(size_t)t * (H / 32) + col[q] / 32] = (uint8_t)code;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPB; ++e) {
+      const double tot = wave_sum(acc[e]);
+      if (lane == 0) red_lg[tt][e][wave] = tot;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nt * EPB; i += kThreads) {
+    const int tt = i / EPB, e = i % EPB;
+    if (e0 + e < E)
+      s.logits[(size_t)(t0 + tt) * E + e0 + e] = red_lg[tt][e][0] + red_lg[tt][e][1] + red_lg[tt][e][2] + red_lg[tt][e][3];
+  }
+  stamp(s.tl_seam, kTlPoints, 2);
+}
+
+// Rows per block: a block holds TB rows of CPT chunks in registers.
+template <int CPT>
+constexpr int seam_tb() {
+  return CPT <= 4 ? 8 : 4;
+}
+
+template <int EPB, int CPT>
+hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+  constexpr int TB = seam_tb<CPT>();
+  const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
+  hipLaunchKernelGGL((seam_kernel<EPB, CPT, TB>), grid, dim3(kThreads), 0, st, d, m, in, s);
+  return hipGetLastError();
+}
+
+template <int EPB>
+hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+  switch ((d.H + 2047) / 2048) {
+    case 1: return launch_seam_t<EPB, 1>(d, m, in, s, st);
+    case 2: return launch_seam_t<EPB, 2>(d, m, in, s, st);
+    case 3: return launch_seam_t<EPB, 3>(d, m, in, s, st);
+    case 4: return launch_seam_t<EPB, 4>(d, m, in, s, st);
+    case 5: return launch_seam_t<EPB, 5>(d, m, in, s, st);
+    case 6: return launch_seam_t<EPB, 6>(d, m, in, s, st);
+    case 7: return launch_seam_t<EPB, 7>(d, m, in, s, st);
+    default: return launch_seam_t<EPB, 8>(d, m, in, s, st);
+  }
+}
+
+// ===========================================================================
+// route: top-k per token, weights, plan
+// ===========================================================================
 
 // Strict total order of the router: larger biased score first, the lower
 // expert index on equal scores.
@@ -27,9 +213,9 @@ __device__ __forceinline__ bool ranks_before(double b1, int e1, double b2, int e
 }
 
 // Bitonic sorting network over the 64 lanes, descending in the router order,
-// run on NG independent groups at once.
-template <int NG>
-__device__ __forceinline__ void sort64(double (&b)[NG], int (&e)[NG], int lane) {
+// run on G independent groups at once.
+template <int G>
+__device__ __forceinline__ void sort64(double (&b)[G], int (&e)[G], int lane) {
 #pragma unroll
   for (int k2 = 2; k2 <= 64; k2 <<= 1) {
 #pragma unroll
@@ -38,11 +224,10 @@ __device__ __forceinline__ void sort64(double (&b)[NG], int (&e)[NG], int lane) 
       const bool lower = (lane & j) == 0;
       const bool keep_first = (lower == up);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        double pb = xor_lane(b[g], j);
-        int pe = xor_lane(e[g], j);
-        bool mine_first = ranks_before(b[g], e[g], pb, pe);
-        if (mine_first != keep_first) {
+      for (int g = 0; g < G; ++g) {
+        const double pb = xor_lane(b[g], j);
+        const int pe = xor_lane(e[g], j);
+        if (ranks_before(b[g], e[g], pb, pe) != keep_first) {
           b[g] = pb;
           e[g] = pe;
         }
@@ -55,16 +240,16 @@ __device__ __forceinline__ void sort64(double (&b)[NG], int (&e)[NG], int lane) 
 // in a, sorted: the lane-wise better of a[i] and c[63 - i] is a bitonic
 // sequence holding them, which a half-cleaner cascade sorts.
 __device__ __forceinline__ void merge64(double& ab, int& ae, double cb, int ce, int lane) {
-  double rb = xor_lane(cb, 63);
-  int re = xor_lane(ce, 63);
+  const double rb = xor_lane(cb, 63);
+  const int re = xor_lane(ce, 63);
   if (ranks_before(rb, re, ab, ae)) {
     ab = rb;
     ae = re;
   }
 #pragma unroll
   for (int j = 32; j > 0; j >>= 1) {
-    double pb = xor_lane(ab, j);
-    int pe = xor_lane(ae, j);
+    const double pb = xor_lane(ab, j);
+    const int pe = xor_lane(ae, j);
     const bool lower = (lane & j) == 0;
     if (ranks_before(ab, ae, pb, pe) != lower) {
       ab = pb;
@@ -76,29 +261,29 @@ __device__ __forceinline__ void merge64(double& ab, int& ae, double cb, int ce, 
 // Exclusive prefix sum of arr[0, n) (n <= 4 * kThreads) in place; returns
 // the total.  Called by all kThreads threads.
 __device__ int block_scan(int* arr, int n, int* tmp4) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int v[4], sum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    int i = tid * 4 + q;
+    const int i = tid * 4 + q;
     v[q] = i < n ? arr[i] : 0;
     sum += v[q];
   }
   int inc = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(inc, o, 64);
+    const int y = __shfl_up(inc, o, 64);
     if (lane >= o) inc += y;
   }
   if (lane == 63) tmp4[wave] = inc;
   __syncthreads();
   int base = 0;
   for (int w = 0; w < wave; ++w) base += tmp4[w];
-  int total = tmp4[0] + tmp4[1] + tmp4[2] + tmp4[3];
+  const int total = tmp4[0] + tmp4[1] + tmp4[2] + tmp4[3];
   int run = base + inc - sum;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    int i = tid * 4 + q;
+    const int i = tid * 4 + q;
     if (i < n) arr[i] = run;
     run += v[q];
   }
@@ -106,91 +291,62 @@ __device__ int block_scan(int* arr, int n, int* tmp4) {
   return total;
 }
 
-struct PlanLds {
+struct RouteLds {
+  double cb[4][64];  // each wave's sorted candidates
+  int ce[4][64];
   int ids[kMaxTokens * kMaxTopk];
   float w[kMaxTokens * kMaxTopk];
-  int cnt[kMaxExperts];
+  uint32_t mlo[kMaxExperts], mhi[kMaxExperts];  // tokens 0-31 / 32-47 per expert
   int base[kMaxExperts];
   int vsb[kMaxExperts];
   int tmp4[4];
   int last;
 };
 
-// Top-k of every token, its weights, then the plan.  Run by the last block.
-template <int NG>
-__device__ void route_and_plan(const LayerDims& d, int m, const float* __restrict__ bias, const Scratch& s,
-                               PlanLds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = d.E, K = d.K;
-
-  for (int t = wave; t < m; t += kThreads / 64) {
-    double b[NG];
-    int e[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      int ex = 64 * g + lane;
-      if (ex < E) {
-        double l = __builtin_nontemporal_load(&s.logits[(size_t)t * E + ex]);
-        double bb = 1.0 / (1.0 + exp(-l)) + (double)bias[ex];
-        // a NaN score ranks last among the real experts, never below the
-        // padding, so the picks are always real experts
-        b[g] = (bb == bb) ? bb : -INFINITY;
-        e[g] = ex;
-      } else {
-        b[g] = -INFINITY;
-        e[g] = ex;  // distinct, above every real expert
-      }
-    }
-    sort64<NG>(b, e, lane);
-#pragma unroll
-    for (int width = NG / 2; width >= 1; width >>= 1) {
-#pragma unroll
-      for (int g = 0; g < width; ++g) merge64(b[g], e[g], b[g + width], e[g + width], lane);
-    }
-    // lanes [0, K) hold the picks in selection order
-    double sg = 0.0;
-    if (lane < K) sg = 1.0 / (1.0 + exp(-__builtin_nontemporal_load(&s.logits[(size_t)t * E + e[0]])));
-    double ssum = wave_sum(sg);
-    if (lane < K) {
-      float w = (float)((double)d.routed_scale * sg / ssum);
-      s.ids[t * K + lane] = e[0];
-      s.wts[t * K + lane] = w;
-      L.ids[t * K + lane] = e[0];
-      L.w[t * K + lane] = w;
-    }
+// The plan, from every token's picks: rows listed by expert ascending, then
+// token ascending; an expert's rows split into virtual slots of at most
+// kTokTile rows; the shared expert's m rows last, its slots first.  With at
+// most 48 tokens, the tokens of an expert form one 64-bit mask and a pair's
+// rank within its expert is the count of lower tokens in the mask.
+__device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds& L) {
+  const int tid = threadIdx.x;
+  const int E = d.E, K = d.K, P = m * K;
+  for (int p = tid; p < P; p += kThreads) {
+    L.ids[p] = __hip_atomic_load(&s.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.w[p] = __hip_atomic_load(&s.wts[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int e = tid; e < E; e += kThreads) L.mlo[e] = L.mhi[e] = 0u;
+  __syncthreads();
+  for (int p = tid; p < P; p += kThreads) {
+    const int t = p / K, e = L.ids[p];
+    if (t < 32) atomicOr(&L.mlo[e], 1u << t);
+    else atomicOr(&L.mhi[e], 1u << (t - 32));
   }
   __syncthreads();
-
-  // Tokens per expert, then rows (expert ascending, token ascending) and
-  // virtual slots of at most kTokTile rows.
-  const int P = m * K;
-  for (int ex = tid; ex < E; ex += kThreads) {
-    int c = 0;
-    for (int p = 0; p < P; ++p) c += (L.ids[p] == ex);
-    L.cnt[ex] = c;
-    L.base[ex] = c;
-    L.vsb[ex] = (c + kTokTile - 1) / kTokTile;
-    s.counts[ex] = c;
+  for (int e = tid; e < E; e += kThreads) {
+    const int c = __popc(L.mlo[e]) + __popc(L.mhi[e]);
+    L.base[e] = c;
+    L.vsb[e] = (c + kTokTile - 1) / kTokTile;
+    s.counts[e] = c;
   }
   __syncthreads();
   block_scan(L.base, E, L.tmp4);
   const int nR = block_scan(L.vsb, E, L.tmp4);
   const int nS = (m + kTokTile - 1) / kTokTile;
-  for (int ex = tid; ex < E; ex += kThreads) {
-    const int c = L.cnt[ex];
-    if (c == 0) continue;
-    int r = L.base[ex];
-    for (int p = 0; p < P; ++p) {
-      if (L.ids[p] == ex) {
-        s.row_tok[r] = p / K;
-        s.row_w[r] = L.w[p];
-        s.pair_row[p] = r;
-        ++r;
-      }
-    }
+  for (int p = tid; p < P; p += kThreads) {
+    const int t = p / K, e = L.ids[p];
+    const int rank = t < 32 ? __popc(L.mlo[e] & ((1u << t) - 1u))
+                            : __popc(L.mlo[e]) + __popc(L.mhi[e] & ((1u << (t - 32)) - 1u));
+    const int r = L.base[e] + rank;
+    s.row_tok[r] = t;
+    s.row_w[r] = L.w[p];
+    s.pair_row[p] = r;
+  }
+  for (int e = tid; e < E; e += kThreads) {
+    const int c = __popc(L.mlo[e]) + __popc(L.mhi[e]);
     for (int v = 0; v * kTokTile < c; ++v) {
-      int rows = c - v * kTokTile;
-      s.vslots[nS + L.vsb[ex] + v] = make_int4(ex, L.base[ex] + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+      const int rows = c - v * kTokTile;
+      s.vslots[nS + L.vsb[e] + v] = make_int4(e, L.base[e] + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
     }
   }
   for (int t = tid; t < m; t += kThreads) {
@@ -198,7 +354,7 @@ __device__ void route_and_plan(const LayerDims& d, int m, const float* __restric
     s.row_w[P + t] = 1.0f;
   }
   for (int v = tid; v < nS; v += kThreads) {
-    int rows = m - v * kTokTile;
+    const int rows = m - v * kTokTile;
     s.vslots[v] = make_int4(-1, P + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
   }
   if (tid == 0) {
@@ -210,131 +366,92 @@ __device__ void route_and_plan(const LayerDims& d, int m, const float* __restric
   }
 }
 
-template <int EPB, int NG>
-__global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inputs in, Scratch s) {
-  __shared__ PlanLds L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int blk = blockIdx.x, nblk = gridDim.x;
-  const int H = d.H, E = d.E;
-  const int e0 = blk * EPB;
-  const int nchunk = (H + 511) / 512;  // 8 columns per lane per chunk
+// Block t: token t.  Wave w sorts groups w, w + 4, ... (GPW of them) and
+// merges them; wave 0 merges the four waves' lists and writes the picks.
+template <int GPW>
+__global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, const float* __restrict__ bias,
+                                                         Scratch s) {
+  __shared__ RouteLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = blockIdx.x;
+  const int E = d.E, K = d.K;
+  const int groups = (E + 63) / 64;
+  stamp(s.tl_route, kTlPoints, 0);
 
-  for (int t = wave; t < m; t += kThreads / 64) {
-    const uint16_t* xr = in.x + (size_t)t * H;
-    // sum of squares in double: each square of a bf16 is exact
-    double ss = 0.0;
-    for (int it = 0; it < nchunk; ++it) {
-      const int c = it * 512 + lane * 8;
-      if (c < H) {
-        u32x4 v = ld16(reinterpret_cast<const uint8_t*>(xr + c));
+  double b[GPW];
+  int e[GPW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          double lo = bf16_to_f32(v[q] & 0xFFFFu), hi = bf16_to_f32(v[q] >> 16);
-          ss += lo * lo;
-          ss += hi * hi;
-        }
-      }
-    }
-    ss = wave_sum(ss);
-    const float r = (float)(1.0 / sqrt(ss / (double)H + (double)d.eps));
-    const bool owner = (t % nblk) == blk;
-
-    double acc[EPB];
-#pragma unroll
-    for (int q = 0; q < EPB; ++q) acc[q] = 0.0;
-    for (int it = 0; it < nchunk; ++it) {
-      const int c = it * 512 + lane * 8;
-      const bool live = c < H;
-      float y[8];
-      uint32_t yb[8];
-      if (live) {
-        u32x4 xv = ld16(reinterpret_cast<const uint8_t*>(xr + c));
-        u32x4 wv = ld16(reinterpret_cast<const uint8_t*>(in.norm_w + c));
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          uint32_t xb = (q & 1) ? (xv[q >> 1] >> 16) : (xv[q >> 1] & 0xFFFFu);
-          uint32_t wb = (q & 1) ? (wv[q >> 1] >> 16) : (wv[q >> 1] & 0xFFFFu);
-          float xr_ = bf16_to_f32(xb) * r;   // fp32 product, rounded
-          float yw = xr_ * bf16_to_f32(wb);  // fp32 product, rounded
-          yb[q] = f32_to_bf16(yw);
-          y[q] = bf16_to_f32(yb[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < EPB; ++q) {
-          if (e0 + q < E) {
-            u32x4 gv = ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + q) * H + c));
-#pragma unroll
-            for (int z = 0; z < 8; ++z) {
-              uint32_t gb = (z & 1) ? (gv[z >> 1] >> 16) : (gv[z >> 1] & 0xFFFFu);
-              acc[q] += (double)y[z] * (double)bf16_to_f32(gb);  // exact products
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          y[q] = 0.0f;
-          yb[q] = 0;
-        }
-      }
-      if (owner) {
-        // store_normed: the bf16 row; store_x8: MXFP8 of each 32 columns
-        float amax = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(y[q]));
-        amax = group_max(amax, 4);  // lanes 4i..4i+3 hold one 32-group
-        const int code = e8m0_code(amax);
-        const float mul = mx_mul(code);
-        if (live) {
-          u32x4 nv;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) nv[q] = yb[2 * q] | (yb[2 * q + 1] << 16);
-          *reinterpret_cast<u32x4*>(s.normed + (size_t)t * H + c) = nv;
-          u32x2 qv;
-          qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
-          qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
-          *reinterpret_cast<u32x2*>(s.x8 + (size_t)t * H + c) = qv;
-          if ((lane & 3) == 0) s.x8s[(size_t)t * (H / 32) + c / 32] = (uint8_t)code;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < EPB; ++q) {
-      double tot = wave_sum(acc[q]);
-      if (lane == 0 && e0 + q < E) s.logits[(size_t)t * E + e0 + q] = tot;
+  for (int i = 0; i < GPW; ++i) {
+    const int ex = 64 * (wave + 4 * i) + lane;
+    if (ex < E) {
+      const double bb = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex])) + (double)bias[ex];
+      // a NaN score ranks last among the real experts, never below the
+      // padding, so the picks are always real experts
+      b[i] = (bb == bb) ? bb : -INFINITY;
+      e[i] = ex;
+    } else {
+      b[i] = -INFINITY;
+      e[i] = ex;  // distinct, above every real expert
     }
   }
-
-  // Arrival: publish this block's writes, count it, and let the last block
-  // through to the routing.  Nothing waits.
-  __threadfence();
+  if (wave < groups) {
+    sort64<GPW>(b, e, lane);
+#pragma unroll
+    for (int width = GPW / 2; width >= 1; width >>= 1) {
+#pragma unroll
+      for (int i = 0; i < width; ++i) merge64(b[i], e[i], b[i + width], e[i + width], lane);
+    }
+  }
+  L.cb[wave][lane] = b[0];
+  L.ce[wave][lane] = e[0];
   __syncthreads();
-  if (tid == 0) L.last = (atomicAdd(s.counter, 1u) == (uint32_t)(nblk - 1));
+  stamp(s.tl_route, kTlPoints, 1);
+  if (wave == 0) {
+    const int nw = groups < 4 ? groups : 4;
+    for (int w = 1; w < nw; ++w) merge64(b[0], e[0], L.cb[w][lane], L.ce[w][lane], lane);
+    // lanes [0, K) hold the picks in selection order
+    double sg = 0.0;
+    if (lane < K) sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + e[0]]));
+    const double ssum = wave_sum(sg);
+    if (lane < K) {
+      const float w = (float)((double)d.routed_scale * sg / ssum);
+      // read by another block of this launch: stored device-coherent
+      __hip_atomic_store(&s.ids[t * K + lane], e[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&s.wts[t * K + lane], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  stamp(s.tl_route, kTlPoints, 2);
+
+  // Arrival: wait until this block's coherent stores completed, count the
+  // block, and let the last one through to the plan.  Nothing spins.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0)
+    L.last = (__hip_atomic_fetch_add(s.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(gridDim.x - 1));
   __syncthreads();
   if (!L.last) return;
-  __threadfence();
-  route_and_plan<NG>(d, m, in.bias, s, L);
-}
-
-template <int EPB>
-hipError_t launch_seam_ng(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
-  const int groups = (d.E + 63) / 64;
-  const int nblk = (d.E + EPB - 1) / EPB;
-  if (groups <= 1) hipLaunchKernelGGL((seam_kernel<EPB, 1>), dim3(nblk), dim3(kThreads), 0, st, d, m, in, s);
-  else if (groups <= 2) hipLaunchKernelGGL((seam_kernel<EPB, 2>), dim3(nblk), dim3(kThreads), 0, st, d, m, in, s);
-  else if (groups <= 4) hipLaunchKernelGGL((seam_kernel<EPB, 4>), dim3(nblk), dim3(kThreads), 0, st, d, m, in, s);
-  else if (groups <= 8) hipLaunchKernelGGL((seam_kernel<EPB, 8>), dim3(nblk), dim3(kThreads), 0, st, d, m, in, s);
-  else hipLaunchKernelGGL((seam_kernel<EPB, 16>), dim3(nblk), dim3(kThreads), 0, st, d, m, in, s);
-  return hipGetLastError();
+  stamp(s.tl_route, kTlPoints, 3);
+  build_plan(d, m, s, L);
+  stamp(s.tl_route, kTlPoints, 4);
 }
 
 }  // namespace
 
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
-  // one to four experts per block, at most 256 blocks
-  if (d.E <= 256) return launch_seam_ng<1>(d, m, in, s, st);
-  if (d.E <= 512) return launch_seam_ng<2>(d, m, in, s, st);
-  return launch_seam_ng<4>(d, m, in, s, st);
+  const int epb = seam_epb(d.E);
+  if (epb == 1) return launch_seam_epb<1>(d, m, in, s, st);
+  if (epb == 2) return launch_seam_epb<2>(d, m, in, s, st);
+  return launch_seam_epb<4>(d, m, in, s, st);
+}
+
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+  const int groups = (d.E + 63) / 64;  // sort groups; wave w takes w, w+4, ...
+  const int gpw = (groups + 3) / 4;
+  if (gpw <= 1) hipLaunchKernelGGL((route_kernel<1>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
+  else if (gpw <= 2) hipLaunchKernelGGL((route_kernel<2>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
+  else hipLaunchKernelGGL((route_kernel<4>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
+  return hipGetLastError();
 }
 
 }  // namespace moe

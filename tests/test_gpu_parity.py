@@ -117,6 +117,51 @@ def test_parity_small(cfg):
         mdl.destroy(h)
 
 
+def test_parity_with_widely_varying_block_codes():
+    """Block codes that differ from block to block by up to +-6 (weights and
+    activations), so a scale applied to the wrong 32-column block or the
+    wrong row block changes the output far beyond the tolerance."""
+    cfg = _cfg(6, 512, 16, 4, 256, 128)
+    H, E, I, Is = 512, 16, 256, 128
+    inp = synth.small_inputs(21, 6, H, E)
+    rng = np.random.default_rng(21)
+    # activations: each 32-column group of x scaled by its own power of two
+    xf = synth.normal(21, 1, (6, H)) * np.exp2(rng.integers(-6, 7, (6, H // 32))).repeat(32, 1)
+    inp["x"] = synth.to_bf16_bits(xf.astype(np.float32))
+    w = data.alloc_weights(cfg)
+
+    def q(name, shape):
+        f = synth.normal(21, synth.STREAM[name], shape, 0.0, 0.02)
+        f = f * np.exp2(rng.integers(-6, 7, (shape[0] // 32, shape[1] // 32))).repeat(32, 0).repeat(32, 1)
+        return oracle.quant_weight(f.astype(np.float32))
+
+    for e in range(E):
+        w["w13"][e], w["w13_s"][e] = q("w13", (2 * I, H))
+        w["w2"][e], w["w2_s"][e] = q("w2", (H, I))
+    w["sgu"], w["sgu_s"] = q("sgu", (2 * Is, H))
+    w["sw2"], w["sw2_s"] = q("sw2", (H, Is))
+    assert len(np.unique(w["w13_s"])) > 8 and len(np.unique(w["sw2_s"])) > 8
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        r, o = _check_layer(cfg, h, inp, w, out)
+        # the intermediate of every (token, pick) nearly byte-identical
+        a8 = gu.tap(h, "a8").reshape(-1, I)
+        a8s = gu.tap(h, "a8s").reshape(-1, I // 32)
+        counts, row = oracle.plan(r["ids"], E)
+        for t in range(6):
+            for j in range(4):
+                e = r["ids"][t, j]
+                ref = oracle.expert(o["x8"][t], o["x8s"][t], w["w13"][e], w["w13_s"][e],
+                                    w["w2"][e], w["w2_s"][e])
+                assert (a8[row[t, j]] == ref["a8"]).mean() >= 0.99, (t, j)
+                assert (a8s[row[t, j]] == ref["a8s"]).mean() >= 0.85, (t, j)
+    finally:
+        mdl.destroy(h)
+
+
 def test_zero_tokens_give_exact_zero():
     cfg = _cfg(9, 512, 64, 6, 128, 128)
     inp, w = data.build_layer(8, cfg)
