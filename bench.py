@@ -6,16 +6,17 @@ synthetic token rows already resident in HBM.  Default workload: the
 DeepSeek-V4.1-style layer at M = 1 (H 5120, 256 experts top-8, I = Is = 2048,
 E4M3 weights with 32 x 32 E8M0 blocks).
 
-The timed region replays captured HIP graphs of the step.  To keep the
-256 MB last-level cache from serving the expert weights, the steps rotate over
+The timed region replays captured HIP graphs, each holding several
+consecutive steps (as a decode graph holds many layers).  To keep the 256 MB
+last-level cache from serving the expert weights, the steps rotate over
 several device copies of the whole weight set, each with its own input rows
-(so each copy picks its own experts).  After the timed region a second pass of
-the same steps runs eagerly with the library's HIP events around each kernel
-(on the run's stream), which gives the dominant kernel's average duration for
-the roofline.
+(so each copy picks its own experts); a labelled cache-warm figure repeats one
+copy.  After the timed region the same steps run eagerly, each kernel's
+dispatch recording its own start/stop HIP events on the run's stream, which
+gives the dominant kernel's average duration for the roofline.
 
 Output: one JSON line (rank 0).  `python bench.py --gpus N` with N > 1 exits:
-this build measures one GPU.
+the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -86,6 +87,10 @@ def cpu_baseline(cfg: dict, budget_s: float = 12.0, workers: int = 16) -> dict:
 
     m = cfg["m"]
     inp, w = data.build_layer(0, cfg, experts="picked", workers=workers)
+    try:  # one host core, like the single-threaded oracle it times
+        os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
+    except (AttributeError, OSError):
+        pass
     dims = data.dims_of(cfg)
     reps, t0 = 0, time.perf_counter()
     rows = list(range(m))
@@ -95,10 +100,63 @@ def cpu_baseline(cfg: dict, budget_s: float = 12.0, workers: int = 16) -> dict:
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": reps * m / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cpu": cpu, "host_nproc": os.cpu_count(),
             "sample": f"{cfg['name']}: {reps} full-layer oracle pass(es) of the M={m} "
                       f"seed-0 step, one thread, {el:.1f} s; expert weights of the picked "
                       f"experts only (drawn outside the timing)"}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the expert kernels are built from: the traffic
+    figures measured with hardware counters hold only for this code."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in ("experts.hip", "device.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "moe_decode_layer_seam_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per w13 launch from the counter summary under profiles/
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none for this workload or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"w13_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_json: "):
+                rec = json.loads(line[len("traffic_json: "):])
+                if rec.get("kernel_src_sha256") == kernel_source_hash():
+                    return rec["bytes_per_launch"]
+    return None
+
+
+def copy_probe(mib: int, reps: int = 5) -> int:
+    """A plain device copy of known size (for calibrating the HBM byte
+    counters): dst = ~src over mib MiB of int32, reps times."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "reps": reps, "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -111,7 +169,12 @@ def main() -> int:
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -163,56 +226,99 @@ def main() -> int:
         step(i % copies)
     torch.cuda.synchronize()
 
-    graphs = []
+    # graphs of G consecutive steps (whole laps over the weight copies), as a
+    # decode graph holds many layers; a second graph takes K mod G steps
+    G = copies * max(1, -(-8 // copies))
+    graphs = {}
     if args.mode == "graph":
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for c in range(copies):
+            for n in sorted({G, args.steps % G} - {0}):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
-                    step(c)
-                graphs.append(g)
+                    for i in range(n):
+                        step(i % copies)
+                graphs[n] = g
         torch.cuda.current_stream().wait_stream(s)
-        for c in range(copies):
-            graphs[c].replay()
+        for g in graphs.values():
+            g.replay()
         torch.cuda.synchronize()
 
-    # ---- timed region
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def run_steps(n):
+        if graphs:
+            for _ in range(n // G):
+                graphs[G].replay()
+            if n % G:
+                graphs[n % G].replay()
+        else:
+            for i in range(n):
+                step(i % copies)
+
+    # ---- timed region: K steps in 5 batches (events between batches)
+    nb = 5 if args.steps >= 5 * G else 1
+    sizes = [args.steps // nb + (1 if b < args.steps % nb else 0) for b in range(nb)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % copies].replay()
-        else:
-            step(i % copies)
-    ev1.record()
+    evs[0].record()
+    for b in range(nb):
+        run_steps(sizes[b])
+        evs[b + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1)
+    ms = evs[0].elapsed_time(evs[nb])
     ms_step = ms / args.steps
+    batch_us = sorted(evs[b].elapsed_time(evs[b + 1]) / sizes[b] * 1e3 for b in range(nb))
 
-    # ---- per-kernel durations: the same steps, eager, HIP events per kernel
+    # ---- cache-warm figure (labelled, not the metric): one weight copy only
+    warm_us = None
+    if graphs:
+        gw = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(gw, stream=s):
+                for i in range(G):
+                    step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        gw.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // G)
+        e0.record()
+        for _ in range(reps):
+            gw.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_us = e0.elapsed_time(e1) / (reps * G) * 1e3
+        del gw
+
+    # ---- per-kernel durations: the same steps, eager, each kernel's dispatch
+    # recording its own start/stop HIP events (on the run's stream)
     mdl.timing(h, True)
     for i in range(args.steps):
         step(i % copies)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("seam", "route", "w13", "w13_finish", "w2"):
+    for k in ("seam", "route", "w13", "act", "w2", "combine"):
         tot, runs = mdl.timing_read(h, k)
         kern[k] = tot / max(1, runs)
     mdl.timing(h, False)
 
+    # MFMA row occupancy: useful token rows / issued 16-row tiles (last copy)
+    counts = mdl.inspect_tensor(h, "counts", torch.int32).cpu().numpy()
+    tiles = int(sum(-(-int(c) // 16) for c in counts if c > 0)) + -(-m // 16)
+    row_occupancy = (m * K + m) / (16 * tiles)
+
     # algorithmic bytes of the dominant kernel (w13) per launch: every active
-    # expert's gate/up weights and codes (shared expert included), the MXFP8
-    # rows it reads and the MXFP8 intermediate it writes
+    # expert's gate/up weights and codes (shared expert included) and the
+    # MXFP8 rows it multiplies them with
     steps_U = [U[i % copies] for i in range(args.steps)]
     avg_U = sum(steps_U) / len(steps_U)
-    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + m * (H + H // 32) + (m * K + m) * (max(I, Is) + max(I, Is) // 32)
+    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + m * (H + H // 32)
     expert_step_bytes = avg_U * (eb["w13"] + eb["w2"]) + ebs["w13"] + ebs["w2"]
     achieved = w13_bytes / (kern["w13"] * 1e-3) / 1e9
+    w2_bytes = avg_U * eb["w2"] + ebs["w2"] + (m * K + m) * (max(I, Is) + max(I, Is) // 32)
 
     res = {
         "metric": METRIC,
@@ -231,15 +337,23 @@ def main() -> int:
                                f"intermediate {I}, shared expert {Is}, E4M3 weights with 32x32 E8M0 blocks",
                    "tokens": m, "mode": args.mode, "weight_copies": copies},
         "us_per_layer": ms_step * 1e3,
+        "batch_us_per_layer": batch_us,
+        "median_batch_us_per_layer": batch_us[len(batch_us) // 2],
+        "cache_warm_us_per_layer": warm_us,
+        "steps_per_graph": G if graphs else None,
+        "mfma_row_occupancy": row_occupancy,
         "expert_hbm_frac": expert_step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "active_experts_avg": avg_U,
         "kernel_us": {k: v * 1e3 for k, v in kern.items()},
+        "kernel_gbs": {"w13": achieved, "w2": w2_bytes / (kern["w2"] * 1e-3) / 1e9},
         "wall_s": wall,
         "roofline": {"bound": "hbm", "kernel": "w13", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg["name"]), "algorithmic_bytes": w13_bytes},
     }
     mdl.destroy(h)
-    del graphs, wsets
+    graphs.clear()
+    del wsets
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

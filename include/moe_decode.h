@@ -150,13 +150,14 @@ enum moe_decode_tap {
 int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
                        const void** d_ptr, size_t* bytes);
 
-/* Per-kernel timing of runs (HIP events recorded around each kernel on the
- * run's stream).  moe_decode_timing(plan, 1) starts recording (and clears the
- * totals), 0 stops.  While on, moe_decode_run must not be captured into a
- * graph.  moe_decode_timing_read sums the elapsed milliseconds of every
- * recorded run for kernel `kernel` (0 seam, 1 route, 2 w13, 3 w13 finish,
- * 4 w2); it synchronises
- * with the recorded events. */
+/* Per-kernel timing of runs: each kernel is launched with a start and a stop
+ * HIP event that its dispatch itself records (hipExtLaunchKernelGGL), so an
+ * interval is that kernel's execution on the run's stream.
+ * moe_decode_timing(plan, 1) starts recording (and clears the totals), 0
+ * stops.  While on, moe_decode_run must not be captured into a graph.
+ * moe_decode_timing_read sums the elapsed milliseconds of every recorded run
+ * for kernel `kernel` (0 seam, 1 route, 2 w13, 3 act, 4 w2, 5 combine); it
+ * synchronises with the recorded events. */
 int moe_decode_timing(moe_decode_handle plan, int32_t on);
 int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
                            double* total_ms, int32_t* runs);
@@ -167,14 +168,13 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   seam:  0 start, 1 squares summed, 2 logits stored
  *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
  *          4 plan written (3-4 only in the last block)
- *   w13:   0 start, 1 first K segment done, 2 wave 0 done, 3 + w: wave w done
- *   w13 finish: 0 start, 1 end (blocks with a split item)
- *   w2:    0 start, 1 plan staged, 2 K loop done, 3 end
+ *   w13, w2:      0 start, 3 + w: wave w of the block done
+ *   act, combine: 0 start
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
  * Unwritten points keep stale values.  moe_decode_timeline_read copies the
- * last run's records of kernel `kernel` (0 seam, 1 route, 2 w13, 3 w13
- * finish, 4 w2) as
+ * last run's records of kernel `kernel` (0 seam, 1 route, 2 w13, 3 act,
+ * 4 w2, 5 combine) as
  * u64 [blocks][8] into h_out (n entries available), sets *blocks, and
  * synchronises the device. */
 int moe_decode_timeline(moe_decode_handle plan, int32_t on);

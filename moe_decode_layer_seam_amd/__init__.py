@@ -25,7 +25,7 @@ MAX_TOKENS = 48
 
 TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
         "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10}
-KERNELS = {"seam": 0, "route": 1, "w13": 2, "w13_finish": 3, "w2": 4}
+KERNELS = {"seam": 0, "route": 1, "w13": 2, "act": 3, "w2": 4, "combine": 5}
 
 
 class Dims(ctypes.Structure):

@@ -16,6 +16,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # keep fp32 subnormals (the norm and quantisers are bit-exact)
     "-fno-gpu-flush-denormals-to-zero",
+    # single-lane atomics stay single-lane: the expert kernels fetch their next
+    # work unit early and must not wait for the result where it is issued
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -31,7 +31,7 @@ constexpr int kTimingRing = 256;  // runs whose events are held before folding
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct TimingSet {
-  hipEvent_t ev[kKernels + 1];
+  hipEvent_t ev[2 * kKernels];  // start and stop of each kernel's dispatch
 };
 
 std::string g_last_error = "no error";
@@ -42,14 +42,14 @@ struct moe_decode_plan_s {
   LayerDims d{};
   int device = 0;
   int cus = 0;
-  int w13_per_cu = 1;
+  int grid13 = 0, grid2 = 0;  // blocks of the w13 and w2 launches
   int max_vs = 0;
   int R = 0;
   size_t bytes = 0;
   void* base = nullptr;
   Scratch s{};
   int last_m = 0;
-  int last_grid[kKernels] = {0, 0, 0, 0, 0};
+  int last_grid[kKernels] = {0, 0, 0, 0, 0, 0};
   bool timeline = false;
   uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
   std::string err = "no error";
@@ -57,7 +57,7 @@ struct moe_decode_plan_s {
   bool timing = false;
   std::vector<TimingSet> ring;
   int ring_used = 0;
-  double total_ms[kKernels] = {0, 0, 0, 0, 0};
+  double total_ms[kKernels] = {0, 0, 0, 0, 0, 0};
   int runs = 0;
 };
 
@@ -89,10 +89,10 @@ bool valid_dims(const moe_decode_dims* d) {
 void fold_timing(moe_decode_plan_s* p) {
   for (int i = 0; i < p->ring_used; ++i) {
     TimingSet& t = p->ring[i];
-    (void)hipEventSynchronize(t.ev[kKernels]);
+    (void)hipEventSynchronize(t.ev[2 * kKernels - 1]);
     for (int k = 0; k < kKernels; ++k) {
       float ms = 0.0f;
-      if (hipEventElapsedTime(&ms, t.ev[k], t.ev[k + 1]) == hipSuccess) p->total_ms[k] += ms;
+      if (hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]) == hipSuccess) p->total_ms[k] += ms;
     }
     p->runs += 1;
   }
@@ -149,7 +149,8 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
     delete p;
     return rc;
   }
-  p->w13_per_cu = w13_blocks_per_cu();
+  p->grid13 = p->cus * gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, p->max_vs, true));
+  p->grid2 = p->cus * gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false));
 
   // scratch layout, every region 256-byte aligned
   const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = p->R;
@@ -165,8 +166,19 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
   const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
-  const size_t w13_waves = (size_t)p->cus * p->w13_per_cu * 4;
-  const size_t o_part = take(2 * w13_waves * kTokTile * 64 * 4);
+  // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
+  // the step sizes that run in split mode
+  size_t part13 = 0, part2 = 0;
+  const size_t nseg13 = (H / 128 + kSegSteps - 1) / kSegSteps;
+  const size_t nseg2 = (d.Imax / 128 + kSegSteps - 1) / kSegSteps;
+  for (int mm = 1; mm <= d.Mx; ++mm) {
+    const size_t Rm = (size_t)mm * (K + 1);
+    const size_t a = (gemm_split(d, mm, p->grid13 * gemm_waves(true), true) ? nseg13 : 1) * Rm * 2 * d.Imax * 4;
+    const size_t c = (gemm_split(d, mm, p->grid2 * gemm_waves(false), false) ? nseg2 : 1) * Rm * H * 4;
+    part13 = a > part13 ? a : part13;
+    part2 = c > part2 ? c : part2;
+  }
+  const size_t o_part13 = take(part13), o_part2 = take(part2);
   p->bytes = off;
   if ((e = hipMalloc(&p->base, p->bytes)) != hipSuccess) {
     hip_fail(p, e, "hipMalloc");
@@ -197,8 +209,9 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.a8 = reinterpret_cast<uint8_t*>(b + o_a8);
   s.a8s = reinterpret_cast<uint8_t*>(b + o_a8s);
   p->tl_base = reinterpret_cast<uint64_t*>(b + o_tl);
-  s.part = reinterpret_cast<float*>(b + o_part);
-  s.tl_seam = s.tl_route = s.tl_w13 = s.tl_w13f = s.tl_w2 = nullptr;
+  s.part13 = reinterpret_cast<float*>(b + o_part13);
+  s.part2 = reinterpret_cast<float*>(b + o_part2);
+  s.tl_seam = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = nullptr;
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -247,10 +260,6 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   in.sw2_s = static_cast<const uint8_t*>(d_sw2_s);
   in.out = static_cast<uint16_t*>(d_out);
 
-  // w13: every resident block slot of the device; the kernel cuts the
-  // plan's (item, K step) pairs into equal shares per wave
-  const int grid13 = p->cus * p->w13_per_cu;
-
   TimingSet* ts = nullptr;
   if (p->timing) {
     if (p->ring_used == kTimingRing) fold_timing(p);
@@ -261,27 +270,31 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     sc.tl_seam = p->tl_base;
     sc.tl_route = p->tl_base + (size_t)1 * kTlBlocks * kTlPoints;
     sc.tl_w13 = p->tl_base + (size_t)2 * kTlBlocks * kTlPoints;
-    sc.tl_w13f = p->tl_base + (size_t)3 * kTlBlocks * kTlPoints;
+    sc.tl_act = p->tl_base + (size_t)3 * kTlBlocks * kTlPoints;
     sc.tl_w2 = p->tl_base + (size_t)4 * kTlBlocks * kTlPoints;
+    sc.tl_combine = p->tl_base + (size_t)5 * kTlBlocks * kTlPoints;
   }
   p->last_grid[0] = seam_blocks(d, m);
   p->last_grid[1] = m;
-  p->last_grid[2] = grid13;
-  p->last_grid[3] = (max_vslots(m, d.E, d.K) * (d.Imax / 32) + 3) / 4;
-  p->last_grid[4] = d.H / 16;
+  p->last_grid[2] = p->grid13;
+  p->last_grid[3] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
+  p->last_grid[4] = p->grid2;
+  p->last_grid[5] = (d.H / 4 + kThreads - 1) / kThreads * m;
   hipError_t e;
-  auto rec = [&](int i) { return ts ? hipEventRecord(ts->ev[i], st) : hipSuccess; };
-  if ((e = rec(0)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_seam(d, m, in, sc, st)) != hipSuccess) return hip_fail(p, e, "seam launch");
-  if ((e = rec(1)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_route(d, m, in, sc, st)) != hipSuccess) return hip_fail(p, e, "route launch");
-  if ((e = rec(2)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_w13(d, m, in, sc, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 launch");
-  if ((e = rec(3)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_w13_finish(d, m, in, sc, grid13, st)) != hipSuccess) return hip_fail(p, e, "w13 finish launch");
-  if ((e = rec(4)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
-  if ((e = launch_w2(d, m, in, sc, p->max_vs, st)) != hipSuccess) return hip_fail(p, e, "w2 launch");
-  if ((e = rec(5)) != hipSuccess) return hip_fail(p, e, "hipEventRecord");
+  auto ev = [&](int k) {
+    KernelEvents r;
+    if (ts) r.start = ts->ev[2 * k], r.stop = ts->ev[2 * k + 1];
+    return r;
+  };
+  if ((e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
+  if ((e = launch_route(d, m, in, sc, st, ev(1))) != hipSuccess) return hip_fail(p, e, "route launch");
+  if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(2))) != hipSuccess)
+    return hip_fail(p, e, "w13 launch");
+  if ((e = launch_act(d, m, sc, p->grid13, st, ev(3))) != hipSuccess) return hip_fail(p, e, "act launch");
+  if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(4))) != hipSuccess)
+    return hip_fail(p, e, "w2 launch");
+  if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(5))) != hipSuccess)
+    return hip_fail(p, e, "combine launch");
   p->last_m = m;
   return MOE_DECODE_OK;
 }

@@ -1,12 +1,12 @@
 // experts.hip -- the expert GEMMs on the gfx950 scaled MFMA (E4M3 x E4M3,
-// 32 x 32 E8M0 weight blocks, 16x16x128 per instruction).
+// 32 x 32 E8M0 weight blocks, 16x16x128 per instruction) and the two small
+// kernels that finish them:
 //
-//   w13: for every (virtual slot, 32-column chunk of the intermediate) item,
-//        h = x8 . W13^T over the chunk's 32 gate and 32 up rows, then
-//        a = SiLU(gate) * up and its MXFP8 (a8, a8s) per 32 columns.
-//   w2:  for every 16-row tile of the output, y = a8 . W2^T of every virtual
-//        slot, weighted by its rows' routing weights and summed into the
-//        token rows in a fixed order, then rounded to bf16 once.
+//   w13:     h = x8 . W13^T of every virtual slot (an expert's token rows,
+//            at most 16 of them, or the shared expert's), fp32
+//   act:     a = SiLU(h_gate) * h_up and its MXFP8 (a8, a8s) per 32 columns
+//   w2:      y = a8 . W2^T of every virtual slot, fp32
+//   combine: out[t] = bf16(sum_j w_tj y[row(t, j)] + y[shared row of t])
 //
 // Pages: "vllm.models.deepseek_v41.amd.mono.runner" MonoLayerWeights (w13
 // [E, 2I, H] gate/up, w2 [E, H, I], sgu, sw2, their 32 x 32 E8M0 scales);
@@ -14,435 +14,417 @@
 // layout of the scaled MFMA), mx_code / fp8_pack4 (the requantisation);
 // "vllm.models.deepseek_v41.amd.mono.layer" run_ffn (the MoE's output).
 //
-// Weights are streamed once, straight from HBM into MFMA operand registers:
-// each load instruction reads 64 contiguous bytes of 16 rows, the layout the
-// MFMA wants, so no LDS staging is needed for a tile that is used once.
+// Arithmetic.  Each GEMM output tile is 16 weight rows x a slot's token rows.
+// Its K range is cut into fixed segments of kSegSteps K steps; a segment's
+// sum starts from zero and runs through its MFMAs in K order, and the tile's
+// value is the segments' sums added in segment order.  That order depends
+// only on the layer's shape, never on m or on which wave did the work, so a
+// token's result is the same bits whatever batch it is in.
+//
+// Schedule.  The weights are streamed once, straight from HBM into MFMA
+// operand registers (whole 128-byte lines, rearranged with DPP), by one block
+// per CU.  Work is cut into units: a whole tile when there are many tiles
+// (its segment sums are added in registers), one segment of a tile when there
+// are few (at small m: then the segment sums are stored and the next kernel
+// adds them, in the same order).  Each CU takes an equal share of the units;
+// inside a CU, fast waves take more of them.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-// One 128-byte K window of one lane's row: the two 16-byte pieces the
-// scaled MFMA wants in its first and second register halves.
-struct Frag {
-  u32x4 lo, hi;
+// Geometry of one GEMM for one kind of slot (shared or routed expert).
+struct Geo {
+  int tiles;  // 16-row weight tiles
+  int K;      // bytes per weight row (the contraction length)
+  int nseg;   // K segments
 };
 
-// ---------------------------------------------------------------------------
-// w13 + SiLU*up + MXFP8
-// ---------------------------------------------------------------------------
-
-// Everything one K step (128 columns) of a w13 item needs, per lane.
-struct W13Step {
-  Frag b[4];       // weight tiles: gate rows 0-15, 16-31, up rows 0-15, 16-31
-  Frag a;          // activation rows (token rows of the slot; zero past them)
-  int sa, sg, su;  // E8M0 codes of the lane's K block: activation, gate, up
-};
-
-// One item's buffers: the expert's w13 and its codes, the MXFP8 rows.  Tile
-// t's rows start at soff[t] (bytes) inside the expert; lane (g, j) reads row
-// j of each tile at column kw + 16 g (+ 64).
-struct W13Item {
-  rsrc_t w, ws, x, xs;
-  uint32_t soff[4], sg_off, su_off;
-  uint32_t wlane, row8, slane, xlane, xslane;
-  int row0, c, chunk;
-};
-
-// Loads of K step `step` (kNoRow offsets past the segment: zeros, no traffic).
-// Weights come as whole 128-byte lines (b[t].lo = rows 0-7, b[t].hi = rows
-// 8-15, rearranged by lines_to_mfma before use).
-__device__ __forceinline__ void w13_load(W13Step& st, const W13Item& it, int step, bool ok) {
-  const uint32_t kw = step * 128;
-  const uint32_t wo = ok ? it.wlane + kw : kNoRow;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    st.b[t].lo = bload16_nt(it.w, wo, it.soff[t]);
-    st.b[t].hi = bload16_nt(it.w, wo, it.soff[t] + it.row8);
-  }
-  const uint32_t so = ok ? it.slane + 4 * step : kNoRow;
-  st.sg = bload8(it.ws, so, it.sg_off);
-  st.su = bload8(it.ws, so, it.su_off);
-  const uint32_t xo = ok ? it.xlane + kw : kNoRow;
-  st.a.lo = bload16(it.x, xo, 0);
-  st.a.hi = bload16(it.x, xo + 64, 0);
-  st.sa = bload8(it.xs, ok ? it.xslane + 4 * step : kNoRow, 0);
+template <bool W13>
+__device__ __forceinline__ Geo geo(const LayerDims& d, bool shared) {
+  const int Kv = shared ? d.Is : d.I;
+  Geo g;
+  g.tiles = W13 ? 2 * Kv / 16 : d.H / 16;
+  g.K = W13 ? d.H : Kv;
+  g.nseg = (g.K / 128 + kSegSteps - 1) / kSegSteps;
+  return g;
 }
 
-__device__ __forceinline__ void w13_mma(v4f (&acc)[4], const W13Step& st) {
-  const v8i a = join(st.a.lo, st.a.hi);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    u32x4 lo, hi;
-    lines_to_mfma(st.b[t].lo, st.b[t].hi, lo, hi);
-    acc[t] = mfma_e4m3(a, join(lo, hi), acc[t], st.sa, t < 2 ? st.sg : st.su);
-  }
-}
+// One K step of a lane for TT weight tiles: each tile's lines (x: rows 0-7,
+// y: rows 8-15), the activation fragment they share, and the E8M0 codes of
+// the lane group's K block (one weight code per pair of tiles).
+template <int TT>
+struct Step {
+  u32x4 x[TT], y[TT], alo, ahi;
+  int sa, sb[TT / 2];
+};
 
-// Item = (virtual slot, 32-column chunk of the intermediate): the chunk's 32
-// gate rows and 32 up rows of the slot's expert, for the slot's token rows.
-__device__ __forceinline__ W13Item w13_item(int item, const LayerDims& d, const Inputs& in, const Scratch& s,
-                                            int m, int g, int j) {
-  const int H = d.H, HB = H / 32;
-  const int nS = s.header[1], chS = d.Is / 32, chR = d.I / 32;
-  int vs, chunk;
-  if (item < nS * chS) {
-    vs = item / chS;
-    chunk = item % chS;
-  } else {
-    const int r = item - nS * chS;
-    vs = nS + r / chR;
-    chunk = r % chR;
-  }
-  const int4 slot = s.vslots[vs];
+// The operands of one unit, per lane (g, j): TT consecutive 16-row weight
+// tiles starting at row row_w0, and the slot's activation row j.
+struct UnitOps {
+  rsrc_t w, ws, a, as;
+  uint32_t wsoff, wlane, row8, tstride, ssoff, sstride, slane, alane, aslane;
+  int row0, c, col0, nsteps;
+};
+
+template <bool W13, int TT>
+__device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const LayerDims& d, const Inputs& in,
+                                            const Scratch& s, const int* s_tok, int m, int R, int g, int j) {
   const int ex = slot.x;
-  const int Kv = ex < 0 ? d.Is : d.I;
-  const uint8_t* W = ex < 0 ? in.sgu : in.w13 + (size_t)ex * 2 * d.I * H;
-  const uint8_t* WS = ex < 0 ? in.sgu_s : in.w13_s + (size_t)ex * (2 * d.I / 32) * HB;
-  W13Item it;
-  it.row0 = slot.y;
-  it.c = slot.z;
-  it.chunk = chunk;
-  it.w = make_rsrc(W, (uint32_t)(2 * Kv) * H);
-  it.ws = make_rsrc(WS, (uint32_t)(2 * Kv / 32) * HB);
-  it.x = make_rsrc(s.x8, (uint32_t)m * H);
-  it.xs = make_rsrc(s.x8s, (uint32_t)m * HB);
-  it.soff[0] = (uint32_t)(32 * chunk) * H;
-  it.soff[1] = (uint32_t)(32 * chunk + 16) * H;
-  it.soff[2] = (uint32_t)(Kv + 32 * chunk) * H;
-  it.soff[3] = (uint32_t)(Kv + 32 * chunk + 16) * H;
-  it.sg_off = (uint32_t)chunk * HB;
-  it.su_off = (uint32_t)(Kv / 32 + chunk) * HB;
-  it.wlane = (uint32_t)(j & 7) * H + (j < 8 ? 16 * g : 64 + 16 * g);
-  it.row8 = (uint32_t)8 * H;
-  it.slane = (uint32_t)g;  // the lane group's 32-column K block
-  const int tok = j < it.c ? s.row_tok[it.row0 + j] : -1;
-  it.xlane = tok >= 0 ? (uint32_t)tok * H + 16 * g : kNoRow;
-  it.xslane = tok >= 0 ? (uint32_t)tok * HB + g : kNoRow;
-  return it;
+  const bool shared = ex < 0;
+  const Geo G = geo<W13>(d, shared);
+  const int N = 16 * G.tiles;
+  const uint8_t* W;
+  const uint8_t* WS;
+  if (W13) {
+    W = shared ? in.sgu : in.w13 + (size_t)ex * 2 * d.I * d.H;
+    WS = shared ? in.sgu_s : in.w13_s + (size_t)ex * (2 * d.I / 32) * (d.H / 32);
+  } else {
+    W = shared ? in.sw2 : in.w2 + (size_t)ex * d.H * d.I;
+    WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * (d.H / 32) * (d.I / 32);
+  }
+  UnitOps u;
+  u.row0 = slot.y;
+  u.c = slot.z;
+  u.col0 = 16 * TT * tgroup;
+  u.nsteps = G.K / 128;
+  u.w = make_rsrc(W, (uint32_t)N * G.K);
+  u.ws = make_rsrc(WS, (uint32_t)(N / 32) * (G.K / 32));
+  u.wsoff = (uint32_t)u.col0 * G.K;
+  u.tstride = (uint32_t)16 * G.K;
+  u.wlane = (uint32_t)(j & 7) * G.K + (j < 8 ? 16 * g : 64 + 16 * g);
+  u.row8 = (uint32_t)8 * G.K;
+  u.ssoff = (uint32_t)(u.col0 / 32) * (G.K / 32);  // the first tile pair's 32-row code block
+  u.sstride = (uint32_t)(G.K / 32);
+  u.slane = (uint32_t)g;  // the lane group's 32-column K block
+  if (W13) {
+    const int tok = j < u.c ? s_tok[u.row0 + j] : -1;
+    u.a = make_rsrc(s.x8, (uint32_t)m * d.H);
+    u.as = make_rsrc(s.x8s, (uint32_t)m * (d.H / 32));
+    u.alane = tok >= 0 ? (uint32_t)tok * d.H + 16 * g : kNoRow;
+    u.aslane = tok >= 0 ? (uint32_t)tok * (d.H / 32) + g : kNoRow;
+  } else {
+    const uint32_t r = (uint32_t)(u.row0 + j);
+    u.a = make_rsrc(s.a8, (uint32_t)R * d.Imax);
+    u.as = make_rsrc(s.a8s, (uint32_t)R * (d.Imax / 32));
+    u.alane = j < u.c ? r * d.Imax + 16 * g : kNoRow;
+    u.aslane = j < u.c ? r * (d.Imax / 32) + g : kNoRow;
+  }
+  return u;
 }
 
-// SiLU(gate) * up of the item's 32 columns and their MXFP8, from the full
-// sums: lane (g, j) holds token rows 4g..4g+3 of gate columns j (tile 0) and
-// 16 + j (tile 1) and the same up columns (tiles 2, 3); the 16 lanes of a
-// lane group hold one token row's 32 columns.
-__device__ __forceinline__ void w13_epilogue(const v4f (&acc)[4], const W13Item& it, const LayerDims& d,
-                                             const Scratch& s, int g, int j) {
+// Loads of K step `st` (past the contraction: zeros, no traffic).
+template <int TT>
+__device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st) {
+  const bool ok = st < u.nsteps;
+  const uint32_t kw = (uint32_t)st * 128;
+  const uint32_t wo = ok ? u.wlane + kw : kNoRow;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float g0 = acc[0][v], g1 = acc[1][v];
-    const float a0 = g0 / (1.0f + __expf(-g0)) * acc[2][v];
-    const float a1 = g1 / (1.0f + __expf(-g1)) * acc[3][v];
-    const float amax = group_max(fmaxf(fabsf(a0), fabsf(a1)), 16);
-    const int code = e8m0_code(amax);
-    const float mul = mx_mul(code);
-    const int i = 4 * g + v;
-    if (i < it.c) {
-      const uint32_t q = fp8x2(a0 * mul, a1 * mul);
-      const size_t row = (size_t)(it.row0 + i);
-      uint8_t* dst = s.a8 + row * d.Imax + 32 * it.chunk;
-      dst[j] = (uint8_t)(q & 0xFF);
-      dst[16 + j] = (uint8_t)(q >> 8);
-      if (j == 0) s.a8s[row * (d.Imax / 32) + it.chunk] = (uint8_t)code;
+  for (int t = 0; t < TT; ++t) {
+    f.x[t] = bload16_nt(u.w, wo, u.wsoff + t * u.tstride);
+    f.y[t] = bload16_nt(u.w, wo, u.wsoff + t * u.tstride + u.row8);
+  }
+  const uint32_t so = ok ? u.slane + 4 * st : kNoRow;
+#pragma unroll
+  for (int p = 0; p < TT / 2; ++p) f.sb[p] = bload8(u.ws, so, u.ssoff + p * u.sstride);
+  const uint32_t ao = ok ? u.alane + kw : kNoRow;
+  f.alo = bload16(u.a, ao, 0);
+  f.ahi = bload16(u.a, ao + 64, 0);
+  f.sa = bload8(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+}
+
+// One segment's sums for the TT tiles: the segment's loads all issued before
+// the first MFMA.
+template <int TT>
+__device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, int seg) {
+  Step<TT> f[kSegSteps];
+#pragma unroll
+  for (int q = 0; q < kSegSteps; ++q) load_step<TT>(f[q], u, seg * kSegSteps + q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < kSegSteps; ++q) {
+    const v8i a = join(f[q].alo, f[q].ahi);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      u32x4 lo, hi;
+      lines_to_mfma(f[q].x[t], f[q].y[t], lo, hi);
+      acc[t] = mfma_e4m3(a, join(lo, hi), acc[t], f[q].sa, f[q].sb[t / 2]);
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Units of one run, in order: the shared slots' units, then the routed ones;
+// inside a slot tile-group-major, segment-minor (split mode) or one per tile
+// group.
+struct UnitMap {
+  int nS, nvs, per_s, per_r, split;
+  int nseg_s, nseg_r;
+  uint32_t total;
+};
+
+template <bool W13, int TT>
+__device__ __forceinline__ UnitMap unit_map(const LayerDims& d, const Scratch& s, int split) {
+  UnitMap um;
+  um.nvs = s.header[0];
+  um.nS = s.header[1];
+  um.split = split;
+  const Geo gs = geo<W13>(d, true), gr = geo<W13>(d, false);
+  um.nseg_s = gs.nseg;
+  um.nseg_r = gr.nseg;
+  um.per_s = gs.tiles / TT * (split ? gs.nseg : 1);
+  um.per_r = gr.tiles / TT * (split ? gr.nseg : 1);
+  um.total = (uint32_t)(um.nS * um.per_s + (um.nvs - um.nS) * um.per_r);
+  return um;
+}
+
+// unit -> (slot, tile group, first segment, end segment)
+__device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& v, int& tg, int& s0, int& s1) {
+  int rem, nseg;
+  const uint32_t shared_units = (uint32_t)(um.nS * um.per_s);
+  if (u < shared_units) {
+    v = (int)(u / (uint32_t)um.per_s);
+    rem = (int)u - v * um.per_s;
+    nseg = um.nseg_s;
+  } else {
+    const uint32_t u2 = u - shared_units;
+    const int vr = (int)(u2 / (uint32_t)um.per_r);
+    v = um.nS + vr;
+    rem = (int)u2 - vr * um.per_r;
+    nseg = um.nseg_r;
+  }
+  if (um.split) {
+    tg = rem / nseg;
+    s0 = rem - tg * nseg;
+    s1 = s0 + 1;
+  } else {
+    tg = rem;
+    s0 = 0;
+    s1 = nseg;
   }
 }
 
-// The worker (wave) whose share of the T (item, K step) pairs holds pair p,
-// for W workers with shares [floor(T w / W), floor(T (w + 1) / W)).
-__device__ __forceinline__ int worker_of(int64_t p, int64_t T, int64_t W) { return (int)(((p + 1) * W - 1) / T); }
-__device__ __forceinline__ int64_t share_begin(int w, int64_t T, int64_t W) { return T * w / W; }
-
-// Stream-K over waves: the n_items x S (item, K step) pairs are cut into
-// equal contiguous shares, one per wave, so every CU streams the same bytes
-// whatever the routing.  A wave owning a whole item finishes it (SiLU*up and
-// the MXFP8 of the result); of an item split between waves each wave stores
-// its partial sums, which the next launch (w13_finish_kernel) adds up in wave
-// order.  Nothing in this kernel waits on another wave.
-// Three 256-thread blocks per CU (at most 168 VGPRs a lane).
-constexpr int kW13Burst = 2;
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void w13_kernel(LayerDims d, Inputs in, Scratch s) {
+// The GEMM, one block of NW waves per CU.  Block b takes the contiguous
+// share [T b / B, T (b + 1) / B) of the T units, so every CU streams the same
+// bytes; its waves take the share's units from a counter in LDS, so a slow
+// wave does not hold the CU back.  Lane (g, j) of a unit ends with rows
+// 4g..4g+3 of the slot and weight rows col0 + 16 t + j; rows past the slot's
+// c are not stored.  Split units store their segment sums in plane s0 of
+// `part`, whole units the tiles' totals in plane 0.  Part planes are
+// [R][width] fp32, R = m (k + 1).
+template <bool W13, int TT, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  __shared__ uint32_t s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int S = d.H / 128;
-  const int m = s.header[3];
-  const int64_t T = (int64_t)s.header[2] * S;
-  const int64_t Wl = (int64_t)gridDim.x * 4;
-  const int64_t W = T < Wl ? T : Wl;
-  const int w = blockIdx.x * 4 + wave;
-  stamp(s.tl_w13, kTlPoints, 0);
-  if (w >= W) return;  // no barrier in this kernel: waves are independent
-  const int64_t begin = share_begin(w, T, W), end = share_begin(w + 1, T, W);
-  const int first_item = (int)(begin / S);
+  uint64_t* tl = W13 ? s.tl_w13 : s.tl_w2;
+  stamp(tl, kTlPoints, 0);
+  const UnitMap um = unit_map<W13, TT>(d, s, split);
+  const int R = m * d.K + m;
+  int4* s_vs = reinterpret_cast<int4*>(lds_raw);
+  int* s_tok = reinterpret_cast<int*>(s_vs + um.nvs);
+  for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
+  if (W13)
+    for (int i = tid; i < R; i += NW * 64) s_tok[i] = s.row_tok[i];
+  if (tid == 0) s_next = 0;
+  __syncthreads();
 
-  for (int64_t pos = begin; pos < end;) {
-    const int item = (int)(pos / S);
-    const int sa = (int)(pos % S);
-    const int sb = (end - pos) < (int64_t)(S - sa) ? sa + (int)(end - pos) : S;
-    const W13Item it = w13_item(item, d, in, s, m, g, j);
-
-    v4f acc[4];
+  const int width = W13 ? 2 * d.Imax : d.H;
+  float* part = W13 ? s.part13 : s.part2;
+  const size_t plane = (size_t)R * width;
+  const uint32_t B = gridDim.x;
+  const uint32_t first = (uint32_t)(((uint64_t)um.total * blockIdx.x) / B);
+  const uint32_t last = (uint32_t)(((uint64_t)um.total * (blockIdx.x + 1)) / B);
+  // first unit by wave index, the rest from the block's counter; the next
+  // index is fetched while the current unit streams
+  uint32_t u = first + wave;
+  while (u < last) {
+    uint32_t nx = 0;
+    if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int v, tg, s0, s1;
+    unit_decode(um, u, v, tg, s0, s1);
+    const UnitOps ops = unit_ops<W13, TT>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
+    v4f tot[TT];
+    segment_sum<TT>(tot, ops, s0);
+    for (int sg = s0 + 1; sg < s1; ++sg) {
+      v4f p[TT];
+      segment_sum<TT>(p, ops, sg);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    // K loop in bursts of kW13Burst steps: every load of the burst is issued
-    // before its first MFMA (steps past the segment read zeros and add
-    // nothing), with no condition inside the loop body.
-    for (int st = sa; st < sb; st += kW13Burst) {
-      W13Step f[kW13Burst];
+      for (int t = 0; t < TT; ++t)
 #pragma unroll
-      for (int u = 0; u < kW13Burst; ++u) w13_load(f[u], it, st + u, st + u < sb);
-      __builtin_amdgcn_sched_barrier(0);  // the whole burst in flight first
-#pragma unroll
-      for (int u = 0; u < kW13Burst; ++u) w13_mma(acc, f[u]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
     }
-
-    if (sa == 0 && sb == S) {
-      w13_epilogue(acc, it, d, s, g, j);
-    } else {
-      // partial sums of the item's live token rows: slot 0 for the wave's
-      // first item, 1 for its last
-      float* mine = s.part + ((size_t)2 * w + (item == first_item ? 0 : 1)) * (kTokTile * 64);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (4 * g + v < it.c) mine[(4 * g + v) * 64 + 16 * t + j] = acc[t][v];
-    }
-    if (pos == begin) stamp(s.tl_w13, kTlPoints, 1);
-    pos += sb - sa;
-  }
-  stamp(s.tl_w13, kTlPoints, 2);
-  stamp_wave(s.tl_w13, kTlPoints, 3 + wave);
-}
-
-// One wave per item split by w13_kernel (w13_waves: that launch's waves):
-// the partial sums of its waves added in wave order, then SiLU*up and the
-// MXFP8 of the result.
-__global__ __launch_bounds__(kThreads) void w13_finish_kernel(LayerDims d, Inputs in, Scratch s, int w13_waves) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, j = lane & 15;
-  const int S = d.H / 128;
-  const int n_items = s.header[2], m = s.header[3];
-  const int64_t T = (int64_t)n_items * S;
-  const int64_t W = T < (int64_t)w13_waves ? T : (int64_t)w13_waves;
-  const int item = blockIdx.x * 4 + wave;
-  stamp(s.tl_w13f, kTlPoints, 0);
-  if (item >= n_items) return;
-  const int wf = worker_of((int64_t)item * S, T, W), wl = worker_of((int64_t)(item + 1) * S - 1, T, W);
-  if (wf == wl) return;  // finished by its one wave
-  const W13Item it = w13_item(item, d, in, s, m, g, j);
-  v4f tot[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) tot[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  // the shares' loads in batches of 4 waves, added in wave order
-  for (int w0 = wf; w0 <= wl; w0 += 4) {
-    float v[4][4][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ww = w0 + q;
-      const int fi = (int)(share_begin(ww <= wl ? ww : wl, T, W) / S);
-      const float* src = s.part + ((size_t)2 * (ww <= wl ? ww : wl) + (item == fi ? 0 : 1)) * (kTokTile * 64);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          v[q][t][r] = (ww <= wl && 4 * g + r < it.c) ? src[(4 * g + r) * 64 + 16 * t + j] : 0.0f;
-    }
+    float* dst = part + (size_t)(um.split ? s0 : 0) * plane + (size_t)ops.row0 * width + ops.col0 + j;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (w0 + q <= wl)
+      if (4 * g + q < ops.c)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tot[t][r] += v[q][t][r];
+        for (int t = 0; t < TT; ++t) dst[(size_t)(4 * g + q) * width + 16 * t] = tot[t][q];
+    u = first + NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
-  w13_epilogue(tot, it, d, s, g, j);
-  stamp(s.tl_w13f, kTlPoints, 1);
+  stamp_wave(tl, kTlPoints, 3 + (wave & 3));
+  __syncthreads();
+  stamp(tl, kTlPoints, 1);
 }
 
-// ---------------------------------------------------------------------------
-// w2 + weighted combine
-// ---------------------------------------------------------------------------
-
-template <int SPW>
-struct W2Part {
-  Frag b[SPW];
-  Frag a[SPW];
-  int sa[SPW], sb[SPW];
-  int ns, c, row0;
-};
-
-// Walks this wave's share of every virtual slot in parts of at most SPW K
-// steps: (slot v, first step of the part).
-struct W2Cursor {
-  int v, st, end;
-};
-
-template <int NW>
-__device__ __forceinline__ void w2_cursor_enter(W2Cursor& k, const int4* s_vs, int nvs, const LayerDims& d,
-                                                int wave) {
-  // advance to the next slot with work for this wave
-  while (k.v < nvs) {
-    const int Kv = s_vs[k.v].x < 0 ? d.Is : d.I;
-    const int S = Kv / 128;
-    k.st = S * wave / NW;
-    k.end = S * (wave + 1) / NW;
-    if (k.st < k.end) return;
-    ++k.v;
+// SiLU(gate) * up of row r (blockIdx.y), columns blockIdx.x * 256 + tid, and
+// the MXFP8 of each 32 columns (one lane group of 32 per code).
+__global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, int m, int split) {
+  const int r = blockIdx.y, c = blockIdx.x * kThreads + threadIdx.x;
+  const int P = m * d.K;
+  const int Kv = r < P ? d.I : d.Is;
+  stamp(s.tl_act, kTlPoints, 0);
+  if (c >= Kv) return;  // whole groups of 32 (Kv is a multiple of 128)
+  const int nseg = split ? (d.H / 128 + kSegSteps - 1) / kSegSteps : 1;
+  const size_t plane = (size_t)(m * d.K + m) * 2 * d.Imax;
+  const float* p = s.part13 + (size_t)r * 2 * d.Imax;
+  float hg = p[c], hu = p[Kv + c];
+  for (int sg = 1; sg < nseg; ++sg) {
+    hg = hg + p[sg * plane + c];
+    hu = hu + p[sg * plane + Kv + c];
   }
+  const float a = hg / (1.0f + __expf(-hg)) * hu;
+  const float amax = group_max(fabsf(a), 32);
+  const int code = e8m0_code(amax);
+  s.a8[(size_t)r * d.Imax + c] = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
+  if ((c & 31) == 0) s.a8s[(size_t)r * (d.Imax / 32) + c / 32] = (uint8_t)code;
 }
 
-template <int NW, int SPW>
-__device__ __forceinline__ bool w2_load(W2Part<SPW>& f, W2Cursor& k, const int4* s_vs, int nvs,
-                                        const LayerDims& d, const Inputs& in, const Scratch& s, int m, int n0,
-                                        int wave, int g, int j) {
-  if (k.v >= nvs) {
-    f.ns = 0;
-    return false;
-  }
-  const int4 slot = s_vs[k.v];
-  const int ex = slot.x;
-  f.row0 = slot.y;
-  f.c = slot.z;
-  const int Kv = ex < 0 ? d.Is : d.I;
-  const int rem = k.end - k.st;
-  f.ns = rem < SPW ? rem : SPW;
-  const rsrc_t wr = make_rsrc(ex < 0 ? in.sw2 : in.w2 + (size_t)ex * d.H * d.I, (uint32_t)d.H * Kv);
-  const rsrc_t sr = make_rsrc(ex < 0 ? in.sw2_s : in.w2_s + (size_t)ex * (d.H / 32) * (d.I / 32),
-                              (uint32_t)(d.H / 32) * (Kv / 32));
-  const uint32_t R = (uint32_t)(m * d.K + m);
-  const rsrc_t ar = make_rsrc(s.a8, R * d.Imax);
-  const rsrc_t asr = make_rsrc(s.a8s, R * (d.Imax / 32));
-  const uint32_t wlane = (uint32_t)(n0 + j) * Kv + 16 * g;
-  const uint32_t slane = (uint32_t)(n0 / 32) * (Kv / 32) + g;
-  const bool has = j < f.c;
-  const uint32_t alane = has ? (uint32_t)(f.row0 + j) * d.Imax + 16 * g : kNoRow;
-  const uint32_t aslane = has ? (uint32_t)(f.row0 + j) * (d.Imax / 32) + g : kNoRow;
+// out[t, n..n+3] (t = blockIdx.y): the routed rows' y weighted in selection
+// order, then the shared row, in fp32; one rounding to bf16.  The loads of
+// eight picks are issued before their sums.
+template <int NSEG>
+__device__ __forceinline__ float4 row_sum(const float* p, size_t plane, int nseg) {
+  float4 y = *reinterpret_cast<const float4*>(p);
 #pragma unroll
-  for (int q = 0; q < SPW; ++q) {
-    if (q < f.ns) {
-      const uint32_t st = k.st + q, kw = st * 128;
-      f.b[q].lo = bload16(wr, wlane + kw, 0);
-      f.b[q].hi = bload16(wr, wlane + kw + 64, 0);
-      f.sb[q] = bload8(sr, slane + 4 * st, 0);
-      f.a[q].lo = bload16(ar, alane + kw, 0);
-      f.a[q].hi = bload16(ar, alane + kw + 64, 0);
-      f.sa[q] = bload8(asr, aslane + 4 * st, 0);
+  for (int sg = 1; sg < NSEG; ++sg) {
+    if (sg < nseg) {
+      const float4 q = *reinterpret_cast<const float4*>(p + sg * plane);
+      y.x = y.x + q.x;
+      y.y = y.y + q.y;
+      y.z = y.z + q.z;
+      y.w = y.w + q.w;
     }
   }
-  k.st += f.ns;
-  if (k.st >= k.end) {
-    ++k.v;
-    w2_cursor_enter<NW>(k, s_vs, nvs, d, wave);
-  }
-  return true;
+  return y;
 }
 
-// MFMAs of a loaded part, then its weighted rows added into the wave's
-// per-token accumulator (lane (g, j) holds rows 4g..4g+3 of column n0 + j).
-template <int SPW>
-__device__ __forceinline__ void w2_use(const W2Part<SPW>& f, float* my, const int* s_tok, const float* s_w,
-                                       int g, int j) {
-  if (f.ns == 0) return;
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+template <int NSEG>
+__global__ __launch_bounds__(kThreads) void combine_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
+  const int t = blockIdx.y, n = 4 * (blockIdx.x * kThreads + threadIdx.x);
+  stamp(s.tl_combine, kTlPoints, 0);
+  if (n >= d.H) return;
+  const int P = m * d.K;
+  const int nseg_r = split ? (d.I / 128 + kSegSteps - 1) / kSegSteps : 1;
+  const int nseg_s = split ? (d.Is / 128 + kSegSteps - 1) / kSegSteps : 1;
+  const size_t plane = (size_t)(m * d.K + m) * d.H;
+  const float4 ysh = row_sum<NSEG>(s.part2 + (size_t)(P + t) * d.H + n, plane, nseg_s);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < d.K; k0 += 8) {
+    int r[8];
 #pragma unroll
-  for (int q = 0; q < SPW; ++q)
-    if (q < f.ns) acc = mfma_e4m3(join(f.a[q].lo, f.a[q].hi), join(f.b[q].lo, f.b[q].hi), acc, f.sa[q], f.sb[q]);
+    for (int i = 0; i < 8; ++i) r[i] = k0 + i < d.K ? s.pair_row[t * d.K + k0 + i] : -1;
+    float w[8];
+    float4 y[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = 4 * g + q;
-    if (i < f.c) {
-      const int t = s_tok[f.row0 + i];
-      my[t * 16 + j] += s_w[f.row0 + i] * acc[q];
+    for (int i = 0; i < 8; ++i) {
+      if (r[i] >= 0) {
+        w[i] = s.row_w[r[i]];
+        y[i] = row_sum<NSEG>(s.part2 + (size_t)r[i] * d.H + n, plane, nseg_r);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (r[i] >= 0) {
+        acc.x = fmaf(w[i], y[i].x, acc.x);
+        acc.y = fmaf(w[i], y[i].y, acc.y);
+        acc.z = fmaf(w[i], y[i].z, acc.z);
+        acc.w = fmaf(w[i], y[i].w, acc.w);
+      }
     }
   }
+  acc.x = acc.x + ysh.x;
+  acc.y = acc.y + ysh.y;
+  acc.z = acc.z + ysh.z;
+  acc.w = acc.w + ysh.w;
+  u32x2 o;
+  o[0] = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+  o[1] = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+  *reinterpret_cast<u32x2*>(in.out + (size_t)t * d.H + n) = o;
 }
 
-template <int NW, int SPW>
-__global__ __launch_bounds__(NW * 64) void w2_kernel(LayerDims d, int m, Inputs in, Scratch s) {
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, j = lane & 15;
-  const int H = d.H, n0 = 16 * blockIdx.x;
-  const int nvs = s.header[0];
-  const int R = m * d.K + m;
-  stamp(s.tl_w2, kTlPoints, 0);
+// Tiles per unit and waves per block (one block per CU) of each GEMM: w13
+// shares one activation fragment among four weight tiles, w2 among two.
+constexpr int kTT13 = 4, kNW13 = 8;
+constexpr int kTT2 = 2, kNW2 = 12;
 
-  float* accl = reinterpret_cast<float*>(lds_raw);  // [NW][m][16]
-  int4* s_vs = reinterpret_cast<int4*>(accl + NW * m * 16);
-  int* s_tok = reinterpret_cast<int*>(s_vs + nvs);
-  float* s_w = reinterpret_cast<float*>(s_tok + R);
-  for (int i = tid; i < NW * m * 16; i += NW * 64) accl[i] = 0.0f;
-  for (int i = tid; i < nvs; i += NW * 64) s_vs[i] = s.vslots[i];
-  for (int i = tid; i < R; i += NW * 64) {
-    s_tok[i] = s.row_tok[i];
-    s_w[i] = s.row_w[i];
-  }
-  __syncthreads();
-  stamp(s.tl_w2, kTlPoints, 1);
-  float* my = accl + wave * m * 16;
-
-  // two parts in flight: part p+1's loads are issued before part p's MFMAs
-  W2Cursor k{0, 0, 0};
-  w2_cursor_enter<NW>(k, s_vs, nvs, d, wave);
-  W2Part<SPW> f0, f1;
-  bool more = w2_load<NW, SPW>(f0, k, s_vs, nvs, d, in, s, m, n0, wave, g, j);
-  while (more) {
-    const bool more1 = w2_load<NW, SPW>(f1, k, s_vs, nvs, d, in, s, m, n0, wave, g, j);
-    w2_use<SPW>(f0, my, s_tok, s_w, g, j);
-    if (!more1) break;
-    more = w2_load<NW, SPW>(f0, k, s_vs, nvs, d, in, s, m, n0, wave, g, j);
-    w2_use<SPW>(f1, my, s_tok, s_w, g, j);
-  }
-  __syncthreads();
-  stamp(s.tl_w2, kTlPoints, 2);
-  for (int idx = tid; idx < m * 16; idx += NW * 64) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) sum += accl[w * m * 16 + idx];
-    const int t = idx >> 4, jj = idx & 15;
-    in.out[(size_t)t * H + n0 + jj] = (uint16_t)f32_to_bf16(sum);
-  }
-  stamp(s.tl_w2, kTlPoints, 3);
-}
-
-template <int NW, int SPW>
-hipError_t launch_w2_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int max_vs, hipStream_t st) {
-  const size_t lds = (size_t)NW * m * 16 * 4 + (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 8;
-  hipLaunchKernelGGL((w2_kernel<NW, SPW>), dim3(d.H / 16), dim3(NW * 64), lds, st, d, m, in, s);
-  return hipGetLastError();
+template <bool W13>
+size_t gemm_lds(const LayerDims& d, int m, int max_vs) {
+  return (size_t)max_vs * 16 + (W13 ? (size_t)(m * d.K + m) * 4 : 0);
 }
 
 }  // namespace
 
-hipError_t launch_w13(const LayerDims& d, int /*m*/, const Inputs& in, const Scratch& s, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(w13_kernel, dim3(grid), dim3(kThreads), 0, st, d, in, s);
-  return hipGetLastError();
+int gemm_waves(bool w13) { return w13 ? kNW13 : kNW2; }
+
+// Tiles of the larger expert kind times the slots a step of m rows can have
+// (distinct experts, plus the shared expert's slots), in units of the GEMM's
+// tile group; split mode when that is under four units per wave.
+bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
+  const int pairs = m * d.K;
+  const long slots = (long)(pairs < d.E ? pairs : d.E) + (m + kTokTile - 1) / kTokTile;
+  const long groups = w13 ? 2L * d.Imax / 16 / kTT13 : d.H / 16 / kTT2;
+  return slots * groups < 4L * waves;
 }
 
-hipError_t launch_w13_finish(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w13_grid,
-                             hipStream_t st) {
-  const int max_items = max_vslots(m, d.E, d.K) * (d.Imax / 32);
-  hipLaunchKernelGGL(w13_finish_kernel, dim3((max_items + 3) / 4), dim3(kThreads), 0, st, d, in, s, w13_grid * 4);
-  return hipGetLastError();
+hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                      hipStream_t st, const KernelEvents& ev) {
+  const int split = gemm_split(d, m, grid * kNW13, true) ? 1 : 0;
+  return launch_kernel(gemm_kernel<true, kTT13, kNW13>, dim3(grid), dim3(kNW13 * 64),
+                       (uint32_t)gemm_lds<true>(d, m, max_vs), st, ev, d, in, s, m, split);
 }
 
-int w13_blocks_per_cu() {
+hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
+                      const KernelEvents& ev) {
+  const int split = gemm_split(d, m, w13_grid * kNW13, true) ? 1 : 0;
+  const dim3 grid((d.Imax + kThreads - 1) / kThreads, m * d.K + m);
+  return launch_kernel(act_kernel, grid, dim3(kThreads), 0, st, ev, d, s, m, split);
+}
+
+hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                     hipStream_t st, const KernelEvents& ev) {
+  const int split = gemm_split(d, m, grid * kNW2, false) ? 1 : 0;
+  return launch_kernel(gemm_kernel<false, kTT2, kNW2>, dim3(grid), dim3(kNW2 * 64),
+                       (uint32_t)gemm_lds<false>(d, m, max_vs), st, ev, d, in, s, m, split);
+}
+
+hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
+                          hipStream_t st, const KernelEvents& ev) {
+  const int split = gemm_split(d, m, w2_grid * kNW2, false) ? 1 : 0;
+  const dim3 grid((d.H / 4 + kThreads - 1) / kThreads, m);
+  const int nseg = split ? (d.Imax / 128 + kSegSteps - 1) / kSegSteps : 1;
+  if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
+  if (nseg <= 4) return launch_kernel(combine_kernel<4>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
+  if (nseg <= 8) return launch_kernel(combine_kernel<8>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
+  return launch_kernel(combine_kernel<16>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
+}
+
+int gemm_blocks_per_cu(bool w13, size_t lds) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, w13_kernel, kThreads, 0) != hipSuccess || n < 1) n = 1;
+  const hipError_t e =
+      w13 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<true, kTT13, kNW13>, kNW13 * 64, lds)
+          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<false, kTT2, kNW2>, kNW2 * 64, lds);
+  if (e != hipSuccess || n < 1) n = 1;
   return n;
 }
 
-hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int max_vs, hipStream_t st) {
-  constexpr int NW = 8;
-  const int steps = (d.Imax / 128 + NW - 1) / NW;  // K steps per wave per slot
-  // parts of at most four K steps; longer shares are walked part by part
-  if (steps <= 1) return launch_w2_t<NW, 1>(d, m, in, s, max_vs, st);
-  if (steps <= 2) return launch_w2_t<NW, 2>(d, m, in, s, max_vs, st);
-  return launch_w2_t<NW, 4>(d, m, in, s, max_vs, st);
+size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {
+  return w13 ? gemm_lds<true>(d, m, max_vs) : gemm_lds<false>(d, m, max_vs);
 }
 
 }  // namespace moe

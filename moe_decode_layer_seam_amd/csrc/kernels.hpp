@@ -2,6 +2,7 @@
 // kernels (seam.hip, experts.hip, quant.hip).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,7 +15,7 @@ constexpr int kMaxTopk = 32;       // two top-k lists fit one 64-lane merge
 constexpr int kMaxHidden = 16384;
 constexpr int kMaxInter = 8192;
 constexpr int kTokTile = 16;       // token rows per MFMA tile (one "virtual slot")
-constexpr int kThreads = 256;      // seam and w13 blocks
+constexpr int kThreads = 256;      // blocks of the small kernels
 
 struct LayerDims {
   int H, E, K, I, Is, Imax, Mx;
@@ -34,20 +35,23 @@ struct Scratch {
   int32_t* row_tok;   // [R] token of each row; R = Mx*K + Mx
   float* row_w;       // [R] its routing weight (1 for the shared expert)
   int4* vslots;       // [VS] {expert (-1: shared), first row, rows (<= 16), 0}
-  int32_t* header;    // [4] {virtual slots, shared virtual slots, w13 items, m}
+  int32_t* header;    // [4] {virtual slots, shared virtual slots, routed virtual slots, m}
   uint32_t* counter;  // arrival counter of the seam blocks (zero between runs)
   uint8_t* a8;        // [R, Imax] E4M3 SiLU*up intermediate
   uint8_t* a8s;       // [R, Imax/32] E8M0
-  float* part;         // [2 * w13 waves][kTokTile][64] partial sums of split w13 items
+  float* part13;       // [planes][R][2 Imax] fp32 w13 sums (per K segment in split mode)
+  float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
   uint64_t* tl_seam;
   uint64_t* tl_route;
   uint64_t* tl_w13;
-  uint64_t* tl_w13f;
+  uint64_t* tl_act;
   uint64_t* tl_w2;
+  uint64_t* tl_combine;
 };
 
-constexpr int kKernels = 5;      // seam, route, w13, w13 finish, w2
+constexpr int kKernels = 6;      // seam, route, w13, act, w2, combine
+constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment
 
 constexpr int kTlPoints = 8;     // stamps per block and kernel
 constexpr int kTlBlocks = 1024;  // blocks recorded per kernel (kTlBlockCap)
@@ -77,14 +81,42 @@ inline int seam_blocks(const LayerDims& d, int m) {
   return (d.E + seam_epb(d.E) - 1) / seam_epb(d.E) * ((m + seam_tb(d.H) - 1) / seam_tb(d.H));
 }
 
+// Optional timing events of one launch: when `start` is set the dispatch
+// itself records them (hipExtLaunchKernelGGL), so their interval is the
+// kernel's execution, without the queue latency of separate event packets.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... A>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                                const KernelEvents& ev, A... args) {
+  if (ev.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  return hipGetLastError();
+}
+
 // Launchers; each returns the hipError_t of its launch.
-hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st);
-hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st);
-hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, hipStream_t st);
-hipError_t launch_w13_finish(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w13_grid,
-                             hipStream_t st);
-hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int max_vs, hipStream_t st);
-int w13_blocks_per_cu();
+hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                       const KernelEvents& ev);
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                        const KernelEvents& ev);
+hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                      hipStream_t st, const KernelEvents& ev);
+hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
+                      const KernelEvents& ev);
+hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                     hipStream_t st, const KernelEvents& ev);
+hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
+                          hipStream_t st, const KernelEvents& ev);
+// Whether a step of m rows runs the GEMM (w13 or w2) in split mode on
+// `waves` waves, the occupancy of its kernel and its dynamic LDS bytes.
+bool gemm_split(const LayerDims& d, int m, int waves, bool w13);
+int gemm_blocks_per_cu(bool w13, size_t lds);
+int gemm_waves(bool w13);  // waves per block of the GEMM
+size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13);
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
                                hipStream_t st);
 

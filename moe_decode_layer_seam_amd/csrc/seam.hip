@@ -181,24 +181,25 @@ constexpr int seam_tb() {
 }
 
 template <int EPB, int CPT>
-hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                         const KernelEvents& ev) {
   constexpr int TB = seam_tb<CPT>();
   const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
-  hipLaunchKernelGGL((seam_kernel<EPB, CPT, TB>), grid, dim3(kThreads), 0, st, d, m, in, s);
-  return hipGetLastError();
+  return launch_kernel(seam_kernel<EPB, CPT, TB>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
 }
 
 template <int EPB>
-hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                           const KernelEvents& ev) {
   switch ((d.H + 2047) / 2048) {
-    case 1: return launch_seam_t<EPB, 1>(d, m, in, s, st);
-    case 2: return launch_seam_t<EPB, 2>(d, m, in, s, st);
-    case 3: return launch_seam_t<EPB, 3>(d, m, in, s, st);
-    case 4: return launch_seam_t<EPB, 4>(d, m, in, s, st);
-    case 5: return launch_seam_t<EPB, 5>(d, m, in, s, st);
-    case 6: return launch_seam_t<EPB, 6>(d, m, in, s, st);
-    case 7: return launch_seam_t<EPB, 7>(d, m, in, s, st);
-    default: return launch_seam_t<EPB, 8>(d, m, in, s, st);
+    case 1: return launch_seam_t<EPB, 1>(d, m, in, s, st, ev);
+    case 2: return launch_seam_t<EPB, 2>(d, m, in, s, st, ev);
+    case 3: return launch_seam_t<EPB, 3>(d, m, in, s, st, ev);
+    case 4: return launch_seam_t<EPB, 4>(d, m, in, s, st, ev);
+    case 5: return launch_seam_t<EPB, 5>(d, m, in, s, st, ev);
+    case 6: return launch_seam_t<EPB, 6>(d, m, in, s, st, ev);
+    case 7: return launch_seam_t<EPB, 7>(d, m, in, s, st, ev);
+    default: return launch_seam_t<EPB, 8>(d, m, in, s, st, ev);
   }
 }
 
@@ -360,7 +361,7 @@ __device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds
   if (tid == 0) {
     s.header[0] = nS + nR;
     s.header[1] = nS;
-    s.header[2] = nS * (d.Is / 32) + nR * (d.I / 32);
+    s.header[2] = nR;
     s.header[3] = m;
     __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -438,20 +439,21 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
 
 }  // namespace
 
-hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                       const KernelEvents& ev) {
   const int epb = seam_epb(d.E);
-  if (epb == 1) return launch_seam_epb<1>(d, m, in, s, st);
-  if (epb == 2) return launch_seam_epb<2>(d, m, in, s, st);
-  return launch_seam_epb<4>(d, m, in, s, st);
+  if (epb == 1) return launch_seam_epb<1>(d, m, in, s, st, ev);
+  if (epb == 2) return launch_seam_epb<2>(d, m, in, s, st, ev);
+  return launch_seam_epb<4>(d, m, in, s, st, ev);
 }
 
-hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st) {
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                        const KernelEvents& ev) {
   const int groups = (d.E + 63) / 64;  // sort groups; wave w takes w, w+4, ...
   const int gpw = (groups + 3) / 4;
-  if (gpw <= 1) hipLaunchKernelGGL((route_kernel<1>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
-  else if (gpw <= 2) hipLaunchKernelGGL((route_kernel<2>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
-  else hipLaunchKernelGGL((route_kernel<4>), dim3(m), dim3(kThreads), 0, st, d, m, in.bias, s);
-  return hipGetLastError();
+  if (gpw <= 1) return launch_kernel(route_kernel<1>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
+  if (gpw <= 2) return launch_kernel(route_kernel<2>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
+  return launch_kernel(route_kernel<4>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
 }
 
 }  // namespace moe
