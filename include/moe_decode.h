@@ -169,7 +169,7 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
  *          4 plan written (3-4 only in the last block)
  *   w13, w2:      0 start, 3 + w: wave w of the block done
- *   act, combine: 0 start
+ *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
  * Unwritten points keep stale values.  moe_decode_timeline_read copies the

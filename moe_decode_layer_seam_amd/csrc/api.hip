@@ -163,6 +163,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   const size_t o_normed = take(Mx * H * 2), o_x8 = take(Mx * H), o_x8s = take(Mx * H / 32);
   const size_t o_logits = take(Mx * E * 8), o_ids = take(Mx * K * 4), o_wts = take(Mx * K * 4);
   const size_t o_counts = take(E * 4), o_pair = take(Mx * K * 4), o_tok = take(R * 4), o_roww = take(R * 4);
+  const size_t o_rowout = take(R * 4);
   const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
   const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
@@ -203,6 +204,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.pair_row = reinterpret_cast<int32_t*>(b + o_pair);
   s.row_tok = reinterpret_cast<int32_t*>(b + o_tok);
   s.row_w = reinterpret_cast<float*>(b + o_roww);
+  s.row_out = reinterpret_cast<int32_t*>(b + o_rowout);
   s.vslots = reinterpret_cast<int4*>(b + o_vs);
   s.header = reinterpret_cast<int32_t*>(b + o_hdr);
   s.counter = reinterpret_cast<uint32_t*>(b + o_ctr);
@@ -279,7 +281,7 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   p->last_grid[2] = p->grid13;
   p->last_grid[3] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
   p->last_grid[4] = p->grid2;
-  p->last_grid[5] = (d.H / 4 + kThreads - 1) / kThreads * m;
+  p->last_grid[5] = d.H / 64 * m;
   hipError_t e;
   auto ev = [&](int k) {
     KernelEvents r;

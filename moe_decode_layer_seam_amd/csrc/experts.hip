@@ -61,7 +61,7 @@ struct Step {
 };
 
 // The operands of one unit, per lane (g, j): TT consecutive 16-row weight
-// tiles starting at row row_w0, and the slot's activation row j.
+// tiles starting at weight row col0, and the slot's activation row j.
 struct UnitOps {
   rsrc_t w, ws, a, as;
   uint32_t wsoff, wlane, row8, tstride, ssoff, sstride, slane, alane, aslane;
@@ -227,10 +227,10 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
   const UnitMap um = unit_map<W13, TT>(d, s, split);
   const int R = m * d.K + m;
   int4* s_vs = reinterpret_cast<int4*>(lds_raw);
-  int* s_tok = reinterpret_cast<int*>(s_vs + um.nvs);
+  int* s_tok = reinterpret_cast<int*>(s_vs + um.nvs);  // w13: token of a row; w2: its output row
+  const int* row_map = W13 ? s.row_tok : s.row_out;
   for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
-  if (W13)
-    for (int i = tid; i < R; i += NW * 64) s_tok[i] = s.row_tok[i];
+  for (int i = tid; i < R; i += NW * 64) s_tok[i] = row_map[i];
   if (tid == 0) s_next = 0;
   __syncthreads();
 
@@ -259,12 +259,17 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
     }
-    float* dst = part + (size_t)(um.split ? s0 : 0) * plane + (size_t)ops.row0 * width + ops.col0 + j;
+    // w13 sums go to the slot's rows; w2 sums to the rows' output rows
+    float* dst = part + (size_t)(um.split ? s0 : 0) * plane + ops.col0 + j;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (4 * g + q < ops.c)
+    for (int q = 0; q < 4; ++q) {
+      if (4 * g + q < ops.c) {
+        const int r = ops.row0 + 4 * g + q;
+        const size_t orow = (size_t)(W13 ? r : s_tok[r]);
 #pragma unroll
-        for (int t = 0; t < TT; ++t) dst[(size_t)(4 * g + q) * width + 16 * t] = tot[t][q];
+        for (int t = 0; t < TT; ++t) dst[orow * width + 16 * t] = tot[t][q];
+      }
+    }
     u = first + NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
   stamp_wave(tl, kTlPoints, 3 + (wave & 3));
@@ -273,7 +278,10 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
 }
 
 // SiLU(gate) * up of row r (blockIdx.y), columns blockIdx.x * 256 + tid, and
-// the MXFP8 of each 32 columns (one lane group of 32 per code).
+// the MXFP8 of each 32 columns (one lane group of 32 per code).  The NSEG
+// bound makes every load unconditional (planes past the run's count are read
+// from its last plane and not added), so they are all in flight at once.
+template <int NSEG>
 __global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, int m, int split) {
   const int r = blockIdx.y, c = blockIdx.x * kThreads + threadIdx.x;
   const int P = m * d.K;
@@ -283,79 +291,74 @@ __global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, i
   const int nseg = split ? (d.H / 128 + kSegSteps - 1) / kSegSteps : 1;
   const size_t plane = (size_t)(m * d.K + m) * 2 * d.Imax;
   const float* p = s.part13 + (size_t)r * 2 * d.Imax;
-  float hg = p[c], hu = p[Kv + c];
-  for (int sg = 1; sg < nseg; ++sg) {
-    hg = hg + p[sg * plane + c];
-    hu = hu + p[sg * plane + Kv + c];
+  float vg[NSEG], vu[NSEG];
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    const size_t o = (size_t)(sg < nseg ? sg : nseg - 1) * plane;
+    vg[sg] = p[o + c];
+    vu[sg] = p[o + Kv + c];
+  }
+  float hg = vg[0], hu = vu[0];
+#pragma unroll
+  for (int sg = 1; sg < NSEG; ++sg) {
+    hg = sg < nseg ? hg + vg[sg] : hg;
+    hu = sg < nseg ? hu + vu[sg] : hu;
   }
   const float a = hg / (1.0f + __expf(-hg)) * hu;
   const float amax = group_max(fabsf(a), 32);
   const int code = e8m0_code(amax);
   s.a8[(size_t)r * d.Imax + c] = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
   if ((c & 31) == 0) s.a8s[(size_t)r * (d.Imax / 32) + c / 32] = (uint8_t)code;
+  stamp(s.tl_act, kTlPoints, 1);
 }
 
-// out[t, n..n+3] (t = blockIdx.y): the routed rows' y weighted in selection
-// order, then the shared row, in fp32; one rounding to bf16.  The loads of
-// eight picks are issued before their sums.
+// out[t, n] (t = blockIdx.y, one column per lane): the routed rows' y
+// weighted in selection order, then the shared row, in fp32; one rounding to
+// bf16.  The w2 sums of pick (t, j) sit in row t k + j, the shared row's in
+// row m k + t, so every load is issued at once.  Narrow blocks spread the
+// reads over many CUs.
+constexpr int kCombineThreads = 64;
+
 template <int NSEG>
-__device__ __forceinline__ float4 row_sum(const float* p, size_t plane, int nseg) {
-  float4 y = *reinterpret_cast<const float4*>(p);
+__device__ __forceinline__ float row_sum(const float* p, size_t plane, int nseg) {
+  float v[NSEG];
 #pragma unroll
-  for (int sg = 1; sg < NSEG; ++sg) {
-    if (sg < nseg) {
-      const float4 q = *reinterpret_cast<const float4*>(p + sg * plane);
-      y.x = y.x + q.x;
-      y.y = y.y + q.y;
-      y.z = y.z + q.z;
-      y.w = y.w + q.w;
-    }
-  }
+  for (int sg = 0; sg < NSEG; ++sg) v[sg] = p[(size_t)(sg < nseg ? sg : nseg - 1) * plane];
+  float y = v[0];
+#pragma unroll
+  for (int sg = 1; sg < NSEG; ++sg) y = sg < nseg ? y + v[sg] : y;
   return y;
 }
 
+// NSEG bounds the run's segment counts; every load is unconditional (picks
+// past k and planes past the count re-read valid addresses and are not
+// added), so a lane's loads are all in flight at once.
 template <int NSEG>
-__global__ __launch_bounds__(kThreads) void combine_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
-  const int t = blockIdx.y, n = 4 * (blockIdx.x * kThreads + threadIdx.x);
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, Inputs in, Scratch s, int m,
+                                                                  int split) {
+  const int t = blockIdx.y, n = blockIdx.x * kCombineThreads + threadIdx.x;
   stamp(s.tl_combine, kTlPoints, 0);
   if (n >= d.H) return;
   const int P = m * d.K;
   const int nseg_r = split ? (d.I / 128 + kSegSteps - 1) / kSegSteps : 1;
   const int nseg_s = split ? (d.Is / 128 + kSegSteps - 1) / kSegSteps : 1;
   const size_t plane = (size_t)(m * d.K + m) * d.H;
-  const float4 ysh = row_sum<NSEG>(s.part2 + (size_t)(P + t) * d.H + n, plane, nseg_s);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float ysh = row_sum<NSEG>(s.part2 + (size_t)(P + t) * d.H + n, plane, nseg_s);
+  float acc = 0.0f;
   for (int k0 = 0; k0 < d.K; k0 += 8) {
-    int r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = k0 + i < d.K ? s.pair_row[t * d.K + k0 + i] : -1;
-    float w[8];
-    float4 y[8];
+    float w[8], y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (r[i] >= 0) {
-        w[i] = s.row_w[r[i]];
-        y[i] = row_sum<NSEG>(s.part2 + (size_t)r[i] * d.H + n, plane, nseg_r);
-      }
+      const int p = t * d.K + (k0 + i < d.K ? k0 + i : d.K - 1);
+      w[i] = s.wts[p];
+      y[i] = row_sum<NSEG>(s.part2 + (size_t)p * d.H + n, plane, nseg_r);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (r[i] >= 0) {
-        acc.x = fmaf(w[i], y[i].x, acc.x);
-        acc.y = fmaf(w[i], y[i].y, acc.y);
-        acc.z = fmaf(w[i], y[i].z, acc.z);
-        acc.w = fmaf(w[i], y[i].w, acc.w);
-      }
-    }
+    for (int i = 0; i < 8; ++i) acc = k0 + i < d.K ? fmaf(w[i], y[i], acc) : acc;
   }
-  acc.x = acc.x + ysh.x;
-  acc.y = acc.y + ysh.y;
-  acc.z = acc.z + ysh.z;
-  acc.w = acc.w + ysh.w;
-  u32x2 o;
-  o[0] = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
-  o[1] = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
-  *reinterpret_cast<u32x2*>(in.out + (size_t)t * d.H + n) = o;
+  acc = acc + ysh;
+  in.out[(size_t)t * d.H + n] = (uint16_t)f32_to_bf16(acc);
+  stamp(s.tl_combine, kTlPoints, 1);
 }
 
 // Tiles per unit and waves per block (one block per CU) of each GEMM: w13
@@ -365,7 +368,7 @@ constexpr int kTT2 = 2, kNW2 = 12;
 
 template <bool W13>
 size_t gemm_lds(const LayerDims& d, int m, int max_vs) {
-  return (size_t)max_vs * 16 + (W13 ? (size_t)(m * d.K + m) * 4 : 0);
+  return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4;
 }
 
 }  // namespace
@@ -392,8 +395,12 @@ hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch
 hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
                       const KernelEvents& ev) {
   const int split = gemm_split(d, m, w13_grid * kNW13, true) ? 1 : 0;
-  const dim3 grid((d.Imax + kThreads - 1) / kThreads, m * d.K + m);
-  return launch_kernel(act_kernel, grid, dim3(kThreads), 0, st, ev, d, s, m, split);
+  const dim3 grid((d.Imax + kThreads - 1) / kThreads, m * d.K + m), block(kThreads);
+  const int nseg = split ? (d.H / 128 + kSegSteps - 1) / kSegSteps : 1;
+  if (nseg <= 1) return launch_kernel(act_kernel<1>, grid, block, 0, st, ev, d, s, m, split);
+  if (nseg <= 4) return launch_kernel(act_kernel<4>, grid, block, 0, st, ev, d, s, m, split);
+  if (nseg <= 12) return launch_kernel(act_kernel<12>, grid, block, 0, st, ev, d, s, m, split);
+  return launch_kernel(act_kernel<32>, grid, block, 0, st, ev, d, s, m, split);
 }
 
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
@@ -406,12 +413,12 @@ hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch&
 hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
                           hipStream_t st, const KernelEvents& ev) {
   const int split = gemm_split(d, m, w2_grid * kNW2, false) ? 1 : 0;
-  const dim3 grid((d.H / 4 + kThreads - 1) / kThreads, m);
+  const dim3 grid(d.H / kCombineThreads, m), block(kCombineThreads);
   const int nseg = split ? (d.Imax / 128 + kSegSteps - 1) / kSegSteps : 1;
-  if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
-  if (nseg <= 4) return launch_kernel(combine_kernel<4>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
-  if (nseg <= 8) return launch_kernel(combine_kernel<8>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
-  return launch_kernel(combine_kernel<16>, grid, dim3(kThreads), 0, st, ev, d, in, s, m, split);
+  if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, block, 0, st, ev, d, in, s, m, split);
+  if (nseg <= 4) return launch_kernel(combine_kernel<4>, grid, block, 0, st, ev, d, in, s, m, split);
+  if (nseg <= 8) return launch_kernel(combine_kernel<8>, grid, block, 0, st, ev, d, in, s, m, split);
+  return launch_kernel(combine_kernel<16>, grid, block, 0, st, ev, d, in, s, m, split);
 }
 
 int gemm_blocks_per_cu(bool w13, size_t lds) {

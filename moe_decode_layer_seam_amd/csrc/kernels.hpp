@@ -34,6 +34,7 @@ struct Scratch {
   int32_t* pair_row;  // [Mx, K]
   int32_t* row_tok;   // [R] token of each row; R = Mx*K + Mx
   float* row_w;       // [R] its routing weight (1 for the shared expert)
+  int32_t* row_out;   // [R] the row of its w2 sums: pair t k + j, or P + t for the shared row
   int4* vslots;       // [VS] {expert (-1: shared), first row, rows (<= 16), 0}
   int32_t* header;    // [4] {virtual slots, shared virtual slots, routed virtual slots, m}
   uint32_t* counter;  // arrival counter of the seam blocks (zero between runs)
@@ -73,12 +74,20 @@ inline int max_vslots(int m, int E, int K) {
   return routed + (m + kTokTile - 1) / kTokTile;
 }
 
-// Experts per block of the seam launch (at most 256 expert slices).
-inline int seam_epb(int E) { return E <= 256 ? 1 : (E <= 512 ? 2 : 4); }
 // Token rows per block of the seam launch (rows held in registers).
 inline int seam_tb(int H) { return (H + 2047) / 2048 <= 4 ? 8 : 4; }
+// Experts per block of the seam launch: every block recomputes the norm of
+// its rows, so blocks take as many experts as keeps about 256 blocks (and at
+// most 256 expert slices).
+inline int seam_epb(const LayerDims& d, int m) {
+  const long tiles = (m + seam_tb(d.H) - 1) / seam_tb(d.H);
+  int epb = d.E <= 256 ? 1 : (d.E <= 512 ? 2 : 4);
+  while (epb < 8 && (long)(d.E / (2 * epb)) * tiles >= 256) epb *= 2;
+  return epb;
+}
 inline int seam_blocks(const LayerDims& d, int m) {
-  return (d.E + seam_epb(d.E) - 1) / seam_epb(d.E) * ((m + seam_tb(d.H) - 1) / seam_tb(d.H));
+  const int epb = seam_epb(d, m);
+  return (d.E + epb - 1) / epb * ((m + seam_tb(d.H) - 1) / seam_tb(d.H));
 }
 
 // Optional timing events of one launch: when `start` is set the dispatch

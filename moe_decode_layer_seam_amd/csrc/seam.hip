@@ -295,6 +295,7 @@ __device__ int block_scan(int* arr, int n, int* tmp4) {
 struct RouteLds {
   double cb[4][64];  // each wave's sorted candidates
   int ce[4][64];
+  double sig[kMaxExperts];  // this token's sigmoid scores
   int ids[kMaxTokens * kMaxTopk];
   float w[kMaxTokens * kMaxTopk];
   uint32_t mlo[kMaxExperts], mhi[kMaxExperts];  // tokens 0-31 / 32-47 per expert
@@ -342,6 +343,7 @@ __device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds
     s.row_tok[r] = t;
     s.row_w[r] = L.w[p];
     s.pair_row[p] = r;
+    s.row_out[r] = p;
   }
   for (int e = tid; e < E; e += kThreads) {
     const int c = __popc(L.mlo[e]) + __popc(L.mhi[e]);
@@ -353,6 +355,7 @@ __device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds
   for (int t = tid; t < m; t += kThreads) {
     s.row_tok[P + t] = t;
     s.row_w[P + t] = 1.0f;
+    s.row_out[P + t] = P + t;
   }
   for (int v = tid; v < nS; v += kThreads) {
     const int rows = m - v * kTokTile;
@@ -385,7 +388,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
   for (int i = 0; i < GPW; ++i) {
     const int ex = 64 * (wave + 4 * i) + lane;
     if (ex < E) {
-      const double bb = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex])) + (double)bias[ex];
+      const double sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex]));
+      L.sig[ex] = sg;
+      const double bb = sg + (double)bias[ex];
       // a NaN score ranks last among the real experts, never below the
       // padding, so the picks are always real experts
       b[i] = (bb == bb) ? bb : -INFINITY;
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
     for (int w = 1; w < nw; ++w) merge64(b[0], e[0], L.cb[w][lane], L.ce[w][lane], lane);
     // lanes [0, K) hold the picks in selection order
     double sg = 0.0;
-    if (lane < K) sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + e[0]]));
+    if (lane < K) sg = L.sig[e[0]];
     const double ssum = wave_sum(sg);
     if (lane < K) {
       const float w = (float)((double)d.routed_scale * sg / ssum);
@@ -441,10 +446,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
 
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                        const KernelEvents& ev) {
-  const int epb = seam_epb(d.E);
+  const int epb = seam_epb(d, m);
   if (epb == 1) return launch_seam_epb<1>(d, m, in, s, st, ev);
   if (epb == 2) return launch_seam_epb<2>(d, m, in, s, st, ev);
-  return launch_seam_epb<4>(d, m, in, s, st, ev);
+  if (epb == 4) return launch_seam_epb<4>(d, m, in, s, st, ev);
+  return launch_seam_epb<8>(d, m, in, s, st, ev);
 }
 
 hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
