@@ -300,7 +300,7 @@ def main() -> int:
         step(i % copies)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("seam", "route", "w13", "act", "w2", "combine"):
+    for k in ("seam", "logits", "route", "w13", "act", "w2", "combine"):
         tot, runs = mdl.timing_read(h, k)
         kern[k] = tot / max(1, runs)
     mdl.timing(h, False)

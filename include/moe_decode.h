@@ -155,9 +155,11 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * interval is that kernel's execution on the run's stream.
  * moe_decode_timing(plan, 1) starts recording (and clears the totals), 0
  * stops.  While on, moe_decode_run must not be captured into a graph.
- * moe_decode_timing_read sums the elapsed milliseconds of every recorded run
- * for kernel `kernel` (0 seam, 1 route, 2 w13, 3 act, 4 w2, 5 combine); it
- * synchronises with the recorded events. */
+ * moe_decode_timing_read sums the elapsed milliseconds of kernel `kernel` (0
+ * seam, 1 logits, 2 route, 3 w13, 4 act, 5 w2, 6 combine) over the recorded
+ * runs that launched it, and sets *runs to their number; it synchronises
+ * with the recorded events.  (Steps of m <= 4 rows compute the logits inside
+ * the seam launch and do not launch `logits`.) */
 int moe_decode_timing(moe_decode_handle plan, int32_t on);
 int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
                            double* total_ms, int32_t* runs);
@@ -165,7 +167,8 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
 /* Timeline of runs (the pages' timeline build: "layer" run_ffn's mark and
  * "device" stamp / memrealtime).  While on, thread 0 of every block of each
  * kernel stores the 100 MHz device clock (s_memrealtime) at fixed points:
- *   seam:  0 start, 1 squares summed, 2 logits stored
+ *   seam:  0 start, 1 squares summed, 2 logits (or rows) stored
+ *   logits: 0 start, 1 end
  *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
  *          4 plan written (3-4 only in the last block)
  *   w13, w2:      0 start, 3 + w: wave w of the block done
@@ -173,8 +176,8 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
  * Unwritten points keep stale values.  moe_decode_timeline_read copies the
- * last run's records of kernel `kernel` (0 seam, 1 route, 2 w13, 3 act,
- * 4 w2, 5 combine) as
+ * last run's records of kernel `kernel` (0 seam, 1 logits, 2 route, 3 w13,
+ * 4 act, 5 w2, 6 combine) as
  * u64 [blocks][8] into h_out (n entries available), sets *blocks, and
  * synchronises the device. */
 int moe_decode_timeline(moe_decode_handle plan, int32_t on);

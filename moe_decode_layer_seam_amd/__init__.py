@@ -18,14 +18,15 @@ import os
 import torch  # loads the HIP runtime first, so the library shares it
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_decode.so")
+# the in-tree library; MOE_DECODE_LIBRARY names another build of it instead
+LIB_PATH = os.environ.get("MOE_DECODE_LIBRARY") or os.path.join(_PKG, "libmoe_decode.so")
 
 OK, EINVAL, ENOMEM, EHIP, ECAPTURE = 0, -1, -2, -3, -4
 MAX_TOKENS = 48
 
 TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
         "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10}
-KERNELS = {"seam": 0, "route": 1, "w13": 2, "act": 3, "w2": 4, "combine": 5}
+KERNELS = {"seam": 0, "logits": 1, "route": 2, "w13": 3, "act": 4, "w2": 5, "combine": 6}
 
 
 class Dims(ctypes.Structure):

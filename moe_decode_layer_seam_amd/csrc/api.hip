@@ -32,6 +32,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct TimingSet {
   hipEvent_t ev[2 * kKernels];  // start and stop of each kernel's dispatch
+  uint32_t launched = 0;        // kernels of the run (bit k), whose events were recorded
 };
 
 std::string g_last_error = "no error";
@@ -49,7 +50,7 @@ struct moe_decode_plan_s {
   void* base = nullptr;
   Scratch s{};
   int last_m = 0;
-  int last_grid[kKernels] = {0, 0, 0, 0, 0, 0};
+  int last_grid[kKernels] = {0, 0, 0, 0, 0, 0, 0};
   bool timeline = false;
   uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
   std::string err = "no error";
@@ -57,8 +58,8 @@ struct moe_decode_plan_s {
   bool timing = false;
   std::vector<TimingSet> ring;
   int ring_used = 0;
-  double total_ms[kKernels] = {0, 0, 0, 0, 0, 0};
-  int runs = 0;
+  double total_ms[kKernels] = {0, 0, 0, 0, 0, 0, 0};
+  int runs[kKernels] = {0, 0, 0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -92,9 +93,12 @@ void fold_timing(moe_decode_plan_s* p) {
     (void)hipEventSynchronize(t.ev[2 * kKernels - 1]);
     for (int k = 0; k < kKernels; ++k) {
       float ms = 0.0f;
-      if (hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]) == hipSuccess) p->total_ms[k] += ms;
+      if (((t.launched >> k) & 1u) && hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]) == hipSuccess) {
+        p->total_ms[k] += ms;
+        p->runs[k] += 1;
+      }
     }
-    p->runs += 1;
+    t.launched = 0;
   }
   p->ring_used = 0;
 }
@@ -149,8 +153,14 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
     delete p;
     return rc;
   }
-  p->grid13 = p->cus * gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, p->max_vs, true));
-  p->grid2 = p->cus * gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false));
+  // the expert GEMMs run one block per CU; every variant must fit once
+  if (gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, p->max_vs, true)) < 1 ||
+      gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false)) < 1) {
+    p->err = g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
+    delete p;
+    return MOE_DECODE_EINVAL;
+  }
+  p->grid13 = p->grid2 = p->cus;
 
   // scratch layout, every region 256-byte aligned
   const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = p->R;
@@ -213,7 +223,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   p->tl_base = reinterpret_cast<uint64_t*>(b + o_tl);
   s.part13 = reinterpret_cast<float*>(b + o_part13);
   s.part2 = reinterpret_cast<float*>(b + o_part2);
-  s.tl_seam = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = nullptr;
+  s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = nullptr;
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -269,33 +279,42 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   }
   Scratch sc = p->s;
   if (p->timeline) {
-    sc.tl_seam = p->tl_base;
-    sc.tl_route = p->tl_base + (size_t)1 * kTlBlocks * kTlPoints;
-    sc.tl_w13 = p->tl_base + (size_t)2 * kTlBlocks * kTlPoints;
-    sc.tl_act = p->tl_base + (size_t)3 * kTlBlocks * kTlPoints;
-    sc.tl_w2 = p->tl_base + (size_t)4 * kTlBlocks * kTlPoints;
-    sc.tl_combine = p->tl_base + (size_t)5 * kTlBlocks * kTlPoints;
+    uint64_t* tl[kKernels];
+    for (int k = 0; k < kKernels; ++k) tl[k] = p->tl_base + (size_t)k * kTlBlocks * kTlPoints;
+    sc.tl_seam = tl[0];
+    sc.tl_logits = tl[1];
+    sc.tl_route = tl[2];
+    sc.tl_w13 = tl[3];
+    sc.tl_act = tl[4];
+    sc.tl_w2 = tl[5];
+    sc.tl_combine = tl[6];
   }
   p->last_grid[0] = seam_blocks(d, m);
-  p->last_grid[1] = m;
-  p->last_grid[2] = p->grid13;
-  p->last_grid[3] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
-  p->last_grid[4] = p->grid2;
-  p->last_grid[5] = d.H / 64 * m;
+  p->last_grid[1] = logits_blocks(d, m);
+  p->last_grid[2] = m;
+  p->last_grid[3] = p->grid13;
+  p->last_grid[4] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
+  p->last_grid[5] = p->grid2;
+  p->last_grid[6] = d.H / 64 * m;
   hipError_t e;
   auto ev = [&](int k) {
     KernelEvents r;
-    if (ts) r.start = ts->ev[2 * k], r.stop = ts->ev[2 * k + 1];
+    if (ts) {
+      r.start = ts->ev[2 * k], r.stop = ts->ev[2 * k + 1];
+      ts->launched |= 1u << k;
+    }
     return r;
   };
   if ((e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
-  if ((e = launch_route(d, m, in, sc, st, ev(1))) != hipSuccess) return hip_fail(p, e, "route launch");
-  if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(2))) != hipSuccess)
+  if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
+    return hip_fail(p, e, "logits launch");
+  if ((e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
+  if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(3))) != hipSuccess)
     return hip_fail(p, e, "w13 launch");
-  if ((e = launch_act(d, m, sc, p->grid13, st, ev(3))) != hipSuccess) return hip_fail(p, e, "act launch");
-  if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(4))) != hipSuccess)
+  if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
+  if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)
     return hip_fail(p, e, "w2 launch");
-  if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(5))) != hipSuccess)
+  if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(6))) != hipSuccess)
     return hip_fail(p, e, "combine launch");
   p->last_m = m;
   return MOE_DECODE_OK;
@@ -340,7 +359,7 @@ int moe_decode_timing(moe_decode_handle p, int32_t on) {
     }
     fold_timing(p);
     for (double& t : p->total_ms) t = 0.0;
-    p->runs = 0;
+    for (int& r : p->runs) r = 0;
     p->timing = true;
   } else {
     p->timing = false;
@@ -352,7 +371,7 @@ int moe_decode_timing_read(moe_decode_handle p, int32_t kernel, double* total_ms
   if (!p || kernel < 0 || kernel >= kKernels || !total_ms || !runs) return MOE_DECODE_EINVAL;
   fold_timing(p);
   *total_ms = p->total_ms[kernel];
-  *runs = p->runs;
+  *runs = p->runs[kernel];
   return MOE_DECODE_OK;
 }
 

@@ -65,11 +65,39 @@ __device__ __forceinline__ double xor_lane(double v, int mask) {
   return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
 }
 
-// Sum over the whole wave (every lane receives it).
+// Sum over the whole wave (every lane receives it): pairs of lanes 32
+// apart, then 16, ... then 1.  reduce_scatter below adds in the same tree.
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += xor_lane(v, m);
+  for (int m = kWave / 2; m >= 1; m >>= 1) v += xor_lane(v, m);
   return v;
+}
+
+// Wave sums of NV values at once (NV a power of two <= 32), each added in
+// the same tree as wave_sum.  The first log2(NV) steps halve the values a
+// lane carries (it keeps one half, adds its partner's copy of that half and
+// hands over the other); the rest are plain butterfly steps.  On return v[0]
+// of lane l holds the sum of value l >> (6 - log2(NV)).
+template <int NV>
+__device__ __forceinline__ void reduce_scatter(double (&v)[NV], int lane) {
+  int h = NV / 2;
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) {
+    if (h >= 1) {
+      const bool up = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < NV / 2; ++i) {
+        if (i < h) {
+          const double keep = up ? v[h + i] : v[i];
+          const double give = up ? v[i] : v[h + i];
+          v[i] = keep + xor_lane(give, m);
+        }
+      }
+      h >>= 1;
+    } else {
+      v[0] += xor_lane(v[0], m);
+    }
+  }
 }
 
 __device__ __forceinline__ float group_max(float v, int width) {

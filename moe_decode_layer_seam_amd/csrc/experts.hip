@@ -361,40 +361,69 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, I
   stamp(s.tl_combine, kTlPoints, 1);
 }
 
-// Tiles per unit and waves per block (one block per CU) of each GEMM: w13
-// shares one activation fragment among four weight tiles, w2 among two.
-constexpr int kTT13 = 4, kNW13 = 8;
-constexpr int kTT2 = 2, kNW2 = 12;
+// Tiles per unit and waves per block (one block per CU) of each GEMM and
+// mode.  More tiles per unit share one activation fragment among more weight
+// tiles and keep more weight bytes in flight per wave; fewer tiles give more
+// units to balance at small m.  Each tile's sums are the same whichever
+// variant runs it.
+#ifndef MOE_W13_WHOLE
+#define MOE_W13_WHOLE 4, 8
+#endif
+#ifndef MOE_W13_SPLIT
+#define MOE_W13_SPLIT 4, 8
+#endif
+#ifndef MOE_W2_WHOLE
+#define MOE_W2_WHOLE 4, 8
+#endif
+#ifndef MOE_W2_SPLIT
+#define MOE_W2_SPLIT 4, 8
+#endif
 
 template <bool W13>
 size_t gemm_lds(const LayerDims& d, int m, int max_vs) {
   return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4;
 }
 
+template <bool W13, int TT, int NW>
+hipError_t launch_gemm_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                         int split, hipStream_t st, const KernelEvents& ev) {
+  return launch_kernel(gemm_kernel<W13, TT, NW>, dim3(grid), dim3(NW * 64), (uint32_t)gemm_lds<W13>(d, m, max_vs),
+                       st, ev, d, in, s, m, split);
+}
+
+template <bool W13, int TT, int NW>
+int occupancy_t(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<W13, TT, NW>, NW * 64, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+
 }  // namespace
 
-int gemm_waves(bool w13) { return w13 ? kNW13 : kNW2; }
+// Nominal waves per block of each GEMM, for the split decision.
+int gemm_waves(bool w13) { return w13 ? 8 : 8; }
 
-// Tiles of the larger expert kind times the slots a step of m rows can have
-// (distinct experts, plus the shared expert's slots), in units of the GEMM's
-// tile group; split mode when that is under four units per wave.
+// Weight tiles of the larger expert kind times the slots a step of m rows
+// can have (distinct experts, plus the shared expert's slots); split mode
+// when whole-tile units would number under about four per wave.
 bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
   const int pairs = m * d.K;
   const long slots = (long)(pairs < d.E ? pairs : d.E) + (m + kTokTile - 1) / kTokTile;
-  const long groups = w13 ? 2L * d.Imax / 16 / kTT13 : d.H / 16 / kTT2;
-  return slots * groups < 4L * waves;
+  const long tiles = w13 ? 2L * d.Imax / 16 : d.H / 16;
+  return slots * tiles < (w13 ? 16L : 8L) * waves;
 }
 
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                       hipStream_t st, const KernelEvents& ev) {
-  const int split = gemm_split(d, m, grid * kNW13, true) ? 1 : 0;
-  return launch_kernel(gemm_kernel<true, kTT13, kNW13>, dim3(grid), dim3(kNW13 * 64),
-                       (uint32_t)gemm_lds<true>(d, m, max_vs), st, ev, d, in, s, m, split);
+  if (gemm_split(d, m, grid * gemm_waves(true), true))
+    return launch_gemm_t<true, MOE_W13_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
+  return launch_gemm_t<true, MOE_W13_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
 
 hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
                       const KernelEvents& ev) {
-  const int split = gemm_split(d, m, w13_grid * kNW13, true) ? 1 : 0;
+  const int split = gemm_split(d, m, w13_grid * gemm_waves(true), true) ? 1 : 0;
   const dim3 grid((d.Imax + kThreads - 1) / kThreads, m * d.K + m), block(kThreads);
   const int nseg = split ? (d.H / 128 + kSegSteps - 1) / kSegSteps : 1;
   if (nseg <= 1) return launch_kernel(act_kernel<1>, grid, block, 0, st, ev, d, s, m, split);
@@ -405,14 +434,14 @@ hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid,
 
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                      hipStream_t st, const KernelEvents& ev) {
-  const int split = gemm_split(d, m, grid * kNW2, false) ? 1 : 0;
-  return launch_kernel(gemm_kernel<false, kTT2, kNW2>, dim3(grid), dim3(kNW2 * 64),
-                       (uint32_t)gemm_lds<false>(d, m, max_vs), st, ev, d, in, s, m, split);
+  if (gemm_split(d, m, grid * gemm_waves(false), false))
+    return launch_gemm_t<false, MOE_W2_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
+  return launch_gemm_t<false, MOE_W2_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
 
 hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
                           hipStream_t st, const KernelEvents& ev) {
-  const int split = gemm_split(d, m, w2_grid * kNW2, false) ? 1 : 0;
+  const int split = gemm_split(d, m, w2_grid * gemm_waves(false), false) ? 1 : 0;
   const dim3 grid(d.H / kCombineThreads, m), block(kCombineThreads);
   const int nseg = split ? (d.Imax / 128 + kSegSteps - 1) / kSegSteps : 1;
   if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, block, 0, st, ev, d, in, s, m, split);
@@ -421,13 +450,18 @@ hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scr
   return launch_kernel(combine_kernel<16>, grid, block, 0, st, ev, d, in, s, m, split);
 }
 
+// Blocks per CU that every variant of the GEMM fits (one block per CU is
+// launched; 0 if a variant cannot run with this much LDS).
 int gemm_blocks_per_cu(bool w13, size_t lds) {
-  int n = 0;
-  const hipError_t e =
-      w13 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<true, kTT13, kNW13>, kNW13 * 64, lds)
-          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<false, kTT2, kNW2>, kNW2 * 64, lds);
-  if (e != hipSuccess || n < 1) n = 1;
-  return n;
+  int a, b;
+  if (w13) {
+    a = occupancy_t<true, MOE_W13_WHOLE>(lds);
+    b = occupancy_t<true, MOE_W13_SPLIT>(lds);
+  } else {
+    a = occupancy_t<false, MOE_W2_WHOLE>(lds);
+    b = occupancy_t<false, MOE_W2_SPLIT>(lds);
+  }
+  return a < b ? a : b;
 }
 
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {

@@ -44,6 +44,7 @@ struct Scratch {
   float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
   uint64_t* tl_seam;
+  uint64_t* tl_logits;
   uint64_t* tl_route;
   uint64_t* tl_w13;
   uint64_t* tl_act;
@@ -51,7 +52,7 @@ struct Scratch {
   uint64_t* tl_combine;
 };
 
-constexpr int kKernels = 6;      // seam, route, w13, act, w2, combine
+constexpr int kKernels = 7;      // seam, logits, route, w13, act, w2, combine
 constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment
 
 constexpr int kTlPoints = 8;     // stamps per block and kernel
@@ -85,9 +86,19 @@ inline int seam_epb(const LayerDims& d, int m) {
   while (epb < 8 && (long)(d.E / (2 * epb)) * tiles >= 256) epb *= 2;
   return epb;
 }
+// Up to 4 rows the seam launch also computes the router logits (each block
+// recomputes the norm of its rows); above, the norm runs once per row and a
+// separate launch computes the logits from the stored rows.
+inline bool seam_fused(int m) { return m <= 4; }
 inline int seam_blocks(const LayerDims& d, int m) {
   const int epb = seam_epb(d, m);
-  return (d.E + epb - 1) / epb * ((m + seam_tb(d.H) - 1) / seam_tb(d.H));
+  const int tiles = (m + seam_tb(d.H) - 1) / seam_tb(d.H);
+  return seam_fused(m) ? (d.E + epb - 1) / epb * tiles : m;
+}
+inline int logits_blocks(const LayerDims& d, int m) {
+  const int cpt = (d.H + 2047) / 2048;
+  const int tb = cpt <= 3 ? 8 : 4, epb = cpt <= 3 ? 4 : 2;
+  return seam_fused(m) ? 0 : (d.E + epb - 1) / epb * ((m + tb - 1) / tb);
 }
 
 // Optional timing events of one launch: when `start` is set the dispatch
@@ -110,6 +121,8 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, h
 // Launchers; each returns the hipError_t of its launch.
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                        const KernelEvents& ev);
+hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                         const KernelEvents& ev);
 hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                         const KernelEvents& ev);
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,

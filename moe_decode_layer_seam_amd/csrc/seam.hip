@@ -29,11 +29,13 @@ namespace {
 // per chunk.  The norm weight and the gate rows are loaded once, up front,
 // when they fit in registers (PRE); the token rows are held in registers
 // between the sum of squares and the normed row.
-template <int EPB, int CPT, int TB>
+// LOGITS false: the norm and MXFP8 only (one block column owns every row;
+// logits_kernel computes the logits from the stored rows).
+template <int EPB, int CPT, int TB, bool LOGITS>
 __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inputs in, Scratch s) {
   __shared__ double red_ss[TB][4];
   __shared__ double red_lg[TB][EPB][4];
-  constexpr bool PRE = EPB * CPT <= 4;
+  constexpr bool PRE = LOGITS && EPB * CPT <= 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int es = blockIdx.x, nES = gridDim.x;
   const int t0 = blockIdx.y * TB;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
         }
 #pragma unroll
         for (int e = 0; e < EPB; ++e) {
-          if (e0 + e < E) {
+          if (LOGITS && e0 + e < E) {
             u32x4 g;
             if constexpr (PRE) g = gv[e][q];
             else g = ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + e) * H + col[q]));
@@ -159,11 +161,17 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
         }
       }
     }
+    if (LOGITS) {
 #pragma unroll
-    for (int e = 0; e < EPB; ++e) {
-      const double tot = wave_sum(acc[e]);
-      if (lane == 0) red_lg[tt][e][wave] = tot;
+      for (int e = 0; e < EPB; ++e) {
+        const double tot = wave_sum(acc[e]);
+        if (lane == 0) red_lg[tt][e][wave] = tot;
+      }
     }
+  }
+  if (!LOGITS) {
+    stamp(s.tl_seam, kTlPoints, 2);
+    return;
   }
   __syncthreads();
   for (int i = tid; i < nt * EPB; i += kThreads) {
@@ -180,27 +188,117 @@ constexpr int seam_tb() {
   return CPT <= 4 ? 8 : 4;
 }
 
-template <int EPB, int CPT>
-hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
-                         const KernelEvents& ev) {
-  constexpr int TB = seam_tb<CPT>();
-  const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
-  return launch_kernel(seam_kernel<EPB, CPT, TB>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
+// Router logits from the stored bf16 rows: block (es, ts) takes experts
+// [EPB es, +EPB) and rows [TB ts, +TB).  Every logit is summed exactly as in
+// seam_kernel (a thread's columns in the same order, the same wave sum, the
+// four waves in order), so both paths give the same bits.
+template <int EPB, int CPT, int TB>
+__global__ __launch_bounds__(kThreads) void logits_kernel(LayerDims d, int m, Inputs in, Scratch s) {
+  __shared__ double red_lg[TB][EPB][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.y * TB;
+  const int nt = m - t0 < TB ? m - t0 : TB;
+  const int H = d.H, E = d.E;
+  const int e0 = blockIdx.x * EPB;
+  stamp(s.tl_logits, kTlPoints, 0);
+  int col[CPT];
+  bool live[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    col[q] = 8 * tid + 2048 * q;
+    live[q] = col[q] < H;
+  }
+  u32x4 yv[TB][CPT], gv[EPB][CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt)
+      yv[tt][q] = (tt < nt && live[q]) ? ld16(reinterpret_cast<const uint8_t*>(s.normed + (size_t)(t0 + tt) * H + col[q]))
+                                       : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < EPB; ++e)
+      gv[e][q] = (e0 + e < E && live[q]) ? ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + e) * H + col[q]))
+                                         : u32x4{0u, 0u, 0u, 0u};
+  }
+  double acc[TB][EPB];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int e = 0; e < EPB; ++e) acc[tt][e] = 0.0;
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    if (!live[q]) continue;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+      double yd[TB];
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const uint32_t yb = (z & 1) ? (yv[tt][q][z >> 1] >> 16) : (yv[tt][q][z >> 1] & 0xFFFFu);
+        yd[tt] = (double)bf16_to_f32(yb);
+      }
+#pragma unroll
+      for (int e = 0; e < EPB; ++e) {
+        const uint32_t gb = (z & 1) ? (gv[e][q][z >> 1] >> 16) : (gv[e][q][z >> 1] & 0xFFFFu);
+        const double gd = (double)bf16_to_f32(gb);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) acc[tt][e] += yd[tt] * gd;  // exact products
+      }
+    }
+  }
+  // every (row, expert) sum over the wave at once; lane l ends with value
+  // l >> shift, value i = tt * EPB + e
+  constexpr int NV = TB * EPB;
+  constexpr int shift = NV >= 32 ? 1 : NV >= 16 ? 2 : NV >= 8 ? 3 : NV >= 4 ? 4 : NV >= 2 ? 5 : 6;
+  double v[NV];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int e = 0; e < EPB; ++e) v[tt * EPB + e] = acc[tt][e];
+  reduce_scatter<NV>(v, lane);
+  if ((lane & ((1 << shift) - 1)) == 0) {
+    const int i = lane >> shift;
+    red_lg[i / EPB][i % EPB][wave] = v[0];
+  }
+  __syncthreads();
+  for (int i = tid; i < nt * EPB; i += kThreads) {
+    const int tt = i / EPB, e = i % EPB;
+    if (e0 + e < E)
+      s.logits[(size_t)(t0 + tt) * E + e0 + e] = red_lg[tt][e][0] + red_lg[tt][e][1] + red_lg[tt][e][2] + red_lg[tt][e][3];
+  }
+  stamp(s.tl_logits, kTlPoints, 1);
 }
 
-template <int EPB>
+template <int EPB, int CPT, bool LOGITS>
+hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                         const KernelEvents& ev) {
+  constexpr int TB = LOGITS ? seam_tb<CPT>() : 1;
+  const dim3 grid(LOGITS ? (d.E + EPB - 1) / EPB : 1, (m + TB - 1) / TB);
+  return launch_kernel(seam_kernel<EPB, CPT, TB, LOGITS>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
+}
+
+template <int EPB, bool LOGITS>
 hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                            const KernelEvents& ev) {
   switch ((d.H + 2047) / 2048) {
-    case 1: return launch_seam_t<EPB, 1>(d, m, in, s, st, ev);
-    case 2: return launch_seam_t<EPB, 2>(d, m, in, s, st, ev);
-    case 3: return launch_seam_t<EPB, 3>(d, m, in, s, st, ev);
-    case 4: return launch_seam_t<EPB, 4>(d, m, in, s, st, ev);
-    case 5: return launch_seam_t<EPB, 5>(d, m, in, s, st, ev);
-    case 6: return launch_seam_t<EPB, 6>(d, m, in, s, st, ev);
-    case 7: return launch_seam_t<EPB, 7>(d, m, in, s, st, ev);
-    default: return launch_seam_t<EPB, 8>(d, m, in, s, st, ev);
+    case 1: return launch_seam_t<EPB, 1, LOGITS>(d, m, in, s, st, ev);
+    case 2: return launch_seam_t<EPB, 2, LOGITS>(d, m, in, s, st, ev);
+    case 3: return launch_seam_t<EPB, 3, LOGITS>(d, m, in, s, st, ev);
+    case 4: return launch_seam_t<EPB, 4, LOGITS>(d, m, in, s, st, ev);
+    case 5: return launch_seam_t<EPB, 5, LOGITS>(d, m, in, s, st, ev);
+    case 6: return launch_seam_t<EPB, 6, LOGITS>(d, m, in, s, st, ev);
+    case 7: return launch_seam_t<EPB, 7, LOGITS>(d, m, in, s, st, ev);
+    default: return launch_seam_t<EPB, 8, LOGITS>(d, m, in, s, st, ev);
   }
+}
+
+// Logits tiles: 4 experts x 4 rows when the row is up to 2048 columns per
+// thread chunk budget allows it (registers), else 2 x 4.
+template <int CPT>
+hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                           const KernelEvents& ev) {
+  constexpr int TB = CPT <= 3 ? 8 : 4, EPB = CPT <= 3 ? 4 : 2;
+  const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
+  return launch_kernel(logits_kernel<EPB, CPT, TB>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
 }
 
 // ===========================================================================
@@ -446,11 +544,26 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
 
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                        const KernelEvents& ev) {
+  if (!seam_fused(m)) return launch_seam_epb<1, false>(d, m, in, s, st, ev);
   const int epb = seam_epb(d, m);
-  if (epb == 1) return launch_seam_epb<1>(d, m, in, s, st, ev);
-  if (epb == 2) return launch_seam_epb<2>(d, m, in, s, st, ev);
-  if (epb == 4) return launch_seam_epb<4>(d, m, in, s, st, ev);
-  return launch_seam_epb<8>(d, m, in, s, st, ev);
+  if (epb == 1) return launch_seam_epb<1, true>(d, m, in, s, st, ev);
+  if (epb == 2) return launch_seam_epb<2, true>(d, m, in, s, st, ev);
+  if (epb == 4) return launch_seam_epb<4, true>(d, m, in, s, st, ev);
+  return launch_seam_epb<8, true>(d, m, in, s, st, ev);
+}
+
+hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+                         const KernelEvents& ev) {
+  switch ((d.H + 2047) / 2048) {
+    case 1: return launch_logits_t<1>(d, m, in, s, st, ev);
+    case 2: return launch_logits_t<2>(d, m, in, s, st, ev);
+    case 3: return launch_logits_t<3>(d, m, in, s, st, ev);
+    case 4: return launch_logits_t<4>(d, m, in, s, st, ev);
+    case 5: return launch_logits_t<5>(d, m, in, s, st, ev);
+    case 6: return launch_logits_t<6>(d, m, in, s, st, ev);
+    case 7: return launch_logits_t<7>(d, m, in, s, st, ev);
+    default: return launch_logits_t<8>(d, m, in, s, st, ev);
+  }
 }
 
 hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,

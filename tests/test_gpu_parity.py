@@ -205,11 +205,14 @@ def test_runs_are_deterministic_and_plan_reusable_across_m():
         a = gu.run(h, cfg, dinp, dw).clone()
         b = gu.run(h, cfg, dinp, dw).clone()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-        # a smaller step on the same plan, then the full one again
-        c = gu.run(h, cfg, dinp, dw, x=dinp["x"][:5].contiguous())
+        # smaller steps on the same plan (m = 3 computes the router logits in
+        # the seam launch, m = 5 and 48 in their own), then the full one again
+        c = gu.run(h, cfg, dinp, dw, x=dinp["x"][:5].contiguous()).clone()
+        c3 = gu.run(h, cfg, dinp, dw, x=dinp["x"][:3].contiguous()).clone()
         d = gu.run(h, cfg, dinp, dw)
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.int16), a[:5].view(torch.int16))
+        assert torch.equal(c3.view(torch.int16), a[:3].view(torch.int16))
         assert torch.equal(d.view(torch.int16), a.view(torch.int16))
     finally:
         mdl.destroy(h)
