@@ -134,27 +134,31 @@ __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st)
   f.sa = bload8(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
 }
 
-// One segment's sums for the TT tiles: the segment's loads all issued before
-// the first MFMA.
-template <int TT>
+// One segment's sums for the TT tiles, in bursts of BS K steps: a burst's
+// loads are all issued before its first MFMA.  Each tile's MFMAs run in K
+// order whatever BS is.
+template <int TT, int BS>
 __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, int seg) {
-  Step<TT> f[kSegSteps];
-#pragma unroll
-  for (int q = 0; q < kSegSteps; ++q) load_step<TT>(f[q], u, seg * kSegSteps + q);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < kSegSteps; ++q) {
-    const v8i a = join(f[q].alo, f[q].ahi);
+  for (int b0 = 0; b0 < kSegSteps; b0 += BS) {
+    Step<TT> f[BS];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      u32x4 lo, hi;
-      lines_to_mfma(f[q].x[t], f[q].y[t], lo, hi);
-      acc[t] = mfma_e4m3(a, join(lo, hi), acc[t], f[q].sa, f[q].sb[t / 2]);
+    for (int q = 0; q < BS; ++q) load_step<TT>(f[q], u, seg * kSegSteps + b0 + q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < BS; ++q) {
+      const v8i a = join(f[q].alo, f[q].ahi);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        u32x4 lo, hi;
+        lines_to_mfma(f[q].x[t], f[q].y[t], lo, hi);
+        acc[t] = mfma_e4m3(a, join(lo, hi), acc[t], f[q].sa, f[q].sb[t / 2]);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Units of one run, in order: the shared slots' units, then the routed ones;
@@ -218,6 +222,7 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
 template <bool W13, int TT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
+  constexpr int BS = TT >= 8 ? 2 : kSegSteps;  // K steps per load burst
   extern __shared__ __align__(16) unsigned char lds_raw[];
   __shared__ uint32_t s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -250,10 +255,10 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
     unit_decode(um, u, v, tg, s0, s1);
     const UnitOps ops = unit_ops<W13, TT>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
     v4f tot[TT];
-    segment_sum<TT>(tot, ops, s0);
+    segment_sum<TT, BS>(tot, ops, s0);
     for (int sg = s0 + 1; sg < s1; ++sg) {
       v4f p[TT];
-      segment_sum<TT>(p, ops, sg);
+      segment_sum<TT, BS>(p, ops, sg);
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -367,13 +372,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, I
 // units to balance at small m.  Each tile's sums are the same whichever
 // variant runs it.
 #ifndef MOE_W13_WHOLE
-#define MOE_W13_WHOLE 4, 8
+#define MOE_W13_WHOLE 8, 8
 #endif
 #ifndef MOE_W13_SPLIT
 #define MOE_W13_SPLIT 4, 8
 #endif
 #ifndef MOE_W2_WHOLE
-#define MOE_W2_WHOLE 4, 8
+#define MOE_W2_WHOLE 8, 8
 #endif
 #ifndef MOE_W2_SPLIT
 #define MOE_W2_SPLIT 4, 8
