@@ -211,10 +211,10 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
   }
 }
 
-// The GEMM, one block of NW waves per CU.  Block b takes the contiguous
-// share [T b / B, T (b + 1) / B) of the T units, so every CU streams the same
-// bytes; its waves take the share's units from a counter in LDS, so a slow
-// wave does not hold the CU back.  Lane (g, j) of a unit ends with rows
+// The GEMM, one block of NW waves per CU.  Block b of B takes units b,
+// b + B, b + 2B, ... of the T units, so every CU streams the same bytes and
+// gets its part of every slot; its waves take the block's units from a
+// counter in LDS, so a slow wave does not hold the CU back.  Lane (g, j) of a unit ends with rows
 // 4g..4g+3 of the slot and weight rows col0 + 16 t + j; rows past the slot's
 // c are not stored.  Split units store their segment sums in plane s0 of
 // `part`, whole units the tiles' totals in plane 0.  Part planes are
@@ -242,13 +242,15 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
   const int width = W13 ? 2 * d.Imax : d.H;
   float* part = W13 ? s.part13 : s.part2;
   const size_t plane = (size_t)R * width;
+  // the block's units are blockIdx.x + i B, i < count: units of one slot
+  // (costlier for slots with more rows) spread over every CU
   const uint32_t B = gridDim.x;
-  const uint32_t first = (uint32_t)(((uint64_t)um.total * blockIdx.x) / B);
-  const uint32_t last = (uint32_t)(((uint64_t)um.total * (blockIdx.x + 1)) / B);
+  const uint32_t count = um.total > blockIdx.x ? (um.total - blockIdx.x + B - 1) / B : 0;
   // first unit by wave index, the rest from the block's counter; the next
   // index is fetched while the current unit streams
-  uint32_t u = first + wave;
-  while (u < last) {
+  uint32_t i = wave;
+  while (i < count) {
+    const uint32_t u = blockIdx.x + i * B;
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int v, tg, s0, s1;
@@ -275,7 +277,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
         for (int t = 0; t < TT; ++t) dst[orow * width + 16 * t] = tot[t][q];
       }
     }
-    u = first + NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
+    i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
   stamp_wave(tl, kTlPoints, 3 + (wave & 3));
   __syncthreads();
