@@ -20,11 +20,16 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 
 
+# routed expert weight formats (the shared expert is always E4M3)
+FMT_E4M3, FMT_MXFP4 = 0, 1
+FORMATS = {"e4m3": FMT_E4M3, "mxfp4": FMT_MXFP4}
+
+
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("experts", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("routed_format", ctypes.c_int32)]
 
 
 def build() -> str:
@@ -54,11 +59,20 @@ def lib():
         L.orc_e4m3_rne.restype = ctypes.c_uint8
         L.orc_mx_code.argtypes = [ctypes.c_double]
         L.orc_mx_code.restype = _I
-        for f in ("orc_e4m3_rne_array", "orc_mx_code_array", "orc_bf16_rne_array"):
+        L.orc_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e2m1_rne.argtypes = [ctypes.c_double]
+        L.orc_e2m1_rne.restype = ctypes.c_uint8
+        L.orc_fp4_code.argtypes = [ctypes.c_double]
+        L.orc_fp4_code.restype = _I
+        for f in ("orc_e4m3_rne_array", "orc_mx_code_array", "orc_bf16_rne_array",
+                  "orc_e2m1_rne_array"):
             getattr(L, f).argtypes = [ctypes.c_int64, _P, _P]
             getattr(L, f).restype = None
         L.orc_mx_quant_row.argtypes = [_I, _P, _P, _P]
         L.orc_quant_weight.argtypes = [_I, _I, _P, _P, _P]
+        L.orc_quant_weight_fp4.argtypes = [_I, _I, _P, _P, _P]
+        L.orc_expert_fmt.argtypes = [_I, _I, _I] + [_P] * 9
         L.orc_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
         L.orc_router.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
                                  _P, _P, _P, _P]
@@ -66,8 +80,8 @@ def lib():
         L.orc_expert.argtypes = [_I, _I] + [_P] * 9
         L.orc_layer.argtypes = [ctypes.POINTER(Dims), _I] + [_P] * 20
         L.orc_layer.restype = _I
-        for f in ("orc_mx_quant_row", "orc_quant_weight", "orc_rmsnorm",
-                  "orc_router", "orc_plan", "orc_expert"):
+        for f in ("orc_mx_quant_row", "orc_quant_weight", "orc_quant_weight_fp4",
+                  "orc_rmsnorm", "orc_router", "orc_plan", "orc_expert", "orc_expert_fmt"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -97,6 +111,25 @@ def e4m3_rne(v: float) -> int:
 
 def mx_code(amax: float) -> int:
     return lib().orc_mx_code(amax)
+
+
+def e2m1_value(nibble: int) -> float:
+    return lib().orc_e2m1_value(nibble)
+
+
+def e2m1_rne(v: float) -> int:
+    return lib().orc_e2m1_rne(v)
+
+
+def fp4_code(amax: float) -> int:
+    return lib().orc_fp4_code(amax)
+
+
+def e2m1_rne_array(v) -> np.ndarray:
+    v = _c(v, np.float64).ravel()
+    out = np.empty(v.size, np.uint8)
+    lib().orc_e2m1_rne_array(v.size, _p(v), _p(out))
+    return out
 
 
 def e4m3_rne_array(v) -> np.ndarray:
@@ -149,6 +182,24 @@ def quant_weight_into(w, q_out: np.ndarray, s_out: np.ndarray) -> None:
     lib().orc_quant_weight(rows, cols, _p(w), _p(q_out), _p(s_out))
 
 
+def quant_weight_fp4(w) -> tuple[np.ndarray, np.ndarray]:
+    """fp32 [rows, cols] -> (E2M1 pairs [rows, cols/2] u8, E8M0 [rows, cols/32] u8)."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols // 2), np.uint8)
+    s = np.empty((rows, cols // 32), np.uint8)
+    lib().orc_quant_weight_fp4(rows, cols, _p(w), _p(q), _p(s))
+    return q, s
+
+
+def quant_weight_fp4_into(w, q_out: np.ndarray, s_out: np.ndarray) -> None:
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    assert q_out.flags.c_contiguous and s_out.flags.c_contiguous
+    assert q_out.shape == (rows, cols // 2) and s_out.shape == (rows, cols // 32)
+    lib().orc_quant_weight_fp4(rows, cols, _p(w), _p(q_out), _p(s_out))
+
+
 # ---- layer steps ---------------------------------------------------------
 
 def rmsnorm(x, w, eps: float) -> np.ndarray:
@@ -184,8 +235,9 @@ def plan(ids, experts: int) -> tuple[np.ndarray, np.ndarray]:
     return counts, row
 
 
-def expert(x8, x8s, w13, w13_s, w2, w2_s) -> dict:
-    """One token through one expert: returns y [H] (f64), a8 [I], a8s [I/32]."""
+def expert(x8, x8s, w13, w13_s, w2, w2_s, fmt: str = "e4m3") -> dict:
+    """One token through one expert whose weights are in format fmt ("e4m3"
+    or "mxfp4"): returns y [H] (f64), a8 [I], a8s [I/32]."""
     x8 = _c(x8, np.uint8).ravel()
     x8s = _c(x8s, np.uint8).ravel()
     w13 = _c(w13, np.uint8)
@@ -197,15 +249,16 @@ def expert(x8, x8s, w13, w13_s, w2, w2_s) -> dict:
     y = np.empty(h, np.float64)
     a8 = np.empty(inter, np.uint8)
     a8s = np.empty(inter // 32, np.uint8)
-    lib().orc_expert(h, inter, _p(x8), _p(x8s), _p(w13), _p(w13_s), _p(w2),
-                     _p(w2_s), _p(y), _p(a8), _p(a8s))
+    lib().orc_expert_fmt(h, inter, FORMATS[fmt], _p(x8), _p(x8s), _p(w13), _p(w13_s),
+                         _p(w2), _p(w2_s), _p(y), _p(a8), _p(a8s))
     return {"y": y, "a8": a8, "a8s": a8s}
 
 
 def layer(dims: dict, inp: dict, w: dict, rows=None) -> dict:
     """The whole layer on token rows ``rows`` of inp["x"] (default: all).
 
-    dims: hidden, experts, topk, inter, shared_inter, rms_eps, routed_scale.
+    dims: hidden, experts, topk, inter, shared_inter, rms_eps, routed_scale,
+          routed ("e4m3", the default, or "mxfp4": the routed experts' format).
     inp:  x [M,H] u16 (bf16 bits), norm_w [H] u16, gate_w [E,H] u16, bias [E] f32.
     w:    w13, w13_s, w2, w2_s, sgu, sgu_s, sw2, sw2_s (uint8 arrays)."""
     x = _c(inp["x"], np.uint16)
@@ -214,7 +267,8 @@ def layer(dims: dict, inp: dict, w: dict, rows=None) -> dict:
     m, H = x.shape
     E, K = dims["experts"], dims["topk"]
     d = Dims(H, E, K, dims["inter"], dims["shared_inter"],
-             dims.get("rms_eps", 1e-6), dims.get("routed_scale", 1.0))
+             dims.get("rms_eps", 1e-6), dims.get("routed_scale", 1.0),
+             FORMATS[dims.get("routed", "e4m3")])
     out = {
         "normed": np.empty((m, H), np.uint16),
         "x8": np.empty((m, H), np.uint8),

@@ -125,6 +125,53 @@ int32_t orc_mx_code(double amax) {
   return 254;
 }
 
+/* ------------------------------------------------------------------------ */
+/* E2M1 (float4_e2m1fn, two per byte) and its E8M0 scale code                */
+/* ------------------------------------------------------------------------ */
+
+double orc_e2m1_value(uint8_t nibble) {
+  /* [runner] MonoLayerWeights.check: the routed experts' torch.float4_e2m1fn_x2
+   * (the OCP MX FP4 element): 1 sign bit, 2 exponent bits (bias 1), 1
+   * mantissa bit; exponent 0 is subnormal (m * 2^-1); no infinities or NaN. */
+  int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+uint8_t orc_e2m1_rne(double v) {
+  /* Nearest of the eight magnitudes (codes 0..7 increase with their value),
+   * ties to the code with an even (zero) mantissa bit; |v| above 6, the
+   * largest, saturates; the sign bit follows v (a negative value that rounds
+   * to zero gives 0x8, as for E4M3). */
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  if (a > 6.0) a = 6.0;
+  int best = 0;
+  double bd = a;  /* distance to code 0 (value 0) */
+  for (int c = 1; c < 8; ++c) {
+    double dist = fabs(a - orc_e2m1_value((uint8_t)c));
+    if (dist < bd || (dist == bd && (c & 1) == 0)) {
+      best = c;
+      bd = dist;
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x8 : 0));
+}
+
+int32_t orc_fp4_code(double amax) {
+  /* The E8M0 code of a 32-value block of FP4 weights: the same rule as
+   * [device] mx_code with the FP4 maximum 6 in place of 448, i.e. the
+   * smallest integer c in [0, 254] with amax <= 6 * 2^(c - 127), so that no
+   * element of the block needs clamping. */
+  for (int32_t c = 0; c < 254; ++c)
+    if (amax <= ldexp(6.0, c - 127)) return c;
+  return 254;
+}
+
+void orc_e2m1_rne_array(int64_t n, const double* v, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_rne(v[i]);
+}
+
 void orc_e4m3_rne_array(int64_t n, const double* v, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_rne(v[i]);
 }
@@ -183,9 +230,47 @@ void orc_quant_weight(int32_t rows, int32_t cols, const float* w, uint8_t* q,
   free(amax);
 }
 
+void orc_quant_weight_fp4(int32_t rows, int32_t cols, const float* w, uint8_t* q,
+                          uint8_t* scales) {
+  /* MXFP4 of a [rows, cols] fp32 weight: one E8M0 code per row and 32
+   * consecutive columns (scales [rows, cols/32] row-major), elements
+   * E2M1(w * 2^(127 - code)), two per byte: column 2i in the low nibble,
+   * column 2i + 1 in the high one ([runner] MonoLayerWeights.check: w13
+   * [E, 2I, H/2] fp4x2 with [E 2I, H/32] codes, w2 [E, H, I/2]). */
+  int32_t cb = cols / 32;
+  for (int32_t r = 0; r < rows; ++r)
+    for (int32_t b = 0; b < cb; ++b) {
+      const float* src = w + (size_t)r * cols + (size_t)b * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)src[i]) > amax) amax = fabs((double)src[i]);
+      int32_t code = orc_fp4_code(amax);
+      scales[(size_t)r * cb + b] = (uint8_t)code;
+      uint8_t* dst = q + (size_t)r * (cols / 2) + (size_t)b * 16;
+      for (int i = 0; i < 16; ++i) {
+        uint8_t lo = orc_e2m1_rne((double)src[2 * i] * POW2[254 - code]);
+        uint8_t hi = orc_e2m1_rne((double)src[2 * i + 1] * POW2[254 - code]);
+        dst[i] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+}
+
 /* Dequantised E4M3 element with its E8M0 code: value * 2^(code - 127). */
 static double mx_value(uint8_t q, uint8_t code) {
   return E4M3[q] * POW2[code]; /* exact: a power-of-two scaling */
+}
+
+/* Weight element (n, k) of an [N, K] expert matrix, dequantised, in either
+ * routed format: E4M3 with 32 x 32 blocks (codes [N/32, K/32]) or MXFP4 with
+ * 1 x 32 blocks (two elements per byte, codes [N, K/32]). */
+static double weight_value(int32_t fmt, const uint8_t* w, const uint8_t* ws,
+                           int32_t K, int32_t n, int32_t k) {
+  if (fmt == ORC_FMT_MXFP4) {
+    uint8_t byte = w[(size_t)n * (K / 2) + k / 2];
+    uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+    return orc_e2m1_value(nib) * POW2[ws[(size_t)n * (K / 32) + k / 32]];
+  }
+  return mx_value(w[(size_t)n * K + k], ws[(size_t)(n / 32) * (K / 32) + k / 32]);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -295,13 +380,13 @@ void orc_plan(int32_t m, int32_t e, int32_t k, const int32_t* ids,
 /* Experts and the combine                                                  */
 /* ------------------------------------------------------------------------ */
 
-void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
-                const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
-                const uint8_t* w2, const uint8_t* w2_s, double* y, uint8_t* a8,
-                uint8_t* a8s) {
+void orc_expert_fmt(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
+                    const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                    const uint8_t* w2, const uint8_t* w2_s, double* y,
+                    uint8_t* a8, uint8_t* a8s) {
   /* w13 [2I, H]: rows [0, I) the gate, rows [I, 2I) the up projection;
-   * w2 [H, I]; scales per 32 x 32 block, [N/32, K/32] row-major. */
-  int32_t hb = h / 32, ib = inter / 32;
+   * w2 [H, I]; both in the weight format fmt (see weight_value). */
+  int32_t ib = inter / 32;
   double* xd = (double*)malloc(sizeof(double) * (size_t)h);
   double* hv = (double*)malloc(sizeof(double) * 2 * (size_t)inter);
   double* av = (double*)malloc(sizeof(double) * (size_t)inter);
@@ -311,9 +396,7 @@ void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
   for (int32_t i = 0; i < h; ++i) xd[i] = mx_value(x8[i], x8s[i / 32]);
   for (int32_t n = 0; n < 2 * inter; ++n) {
     double acc = 0.0;
-    for (int32_t i = 0; i < h; ++i)
-      acc += xd[i] *
-             mx_value(w13[(size_t)n * h + i], w13_s[(size_t)(n / 32) * hb + i / 32]);
+    for (int32_t i = 0; i < h; ++i) acc += xd[i] * weight_value(fmt, w13, w13_s, h, n, i);
     hv[n] = acc;
   }
   /* a = SiLU(gate) * up, held as fp32, then MXFP8 along the intermediate. */
@@ -326,8 +409,7 @@ void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
   for (int32_t n = 0; n < h; ++n) {
     double acc = 0.0;
     for (int32_t i = 0; i < inter; ++i)
-      acc += mx_value(q[i], qc[i / 32]) *
-             mx_value(w2[(size_t)n * inter + i], w2_s[(size_t)(n / 32) * ib + i / 32]);
+      acc += mx_value(q[i], qc[i / 32]) * weight_value(fmt, w2, w2_s, inter, n, i);
     y[n] = acc;
   }
   if (a8) memcpy(a8, q, (size_t)inter);
@@ -337,6 +419,13 @@ void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
   free(av);
   free(q);
   free(qc);
+}
+
+void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
+                const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                const uint8_t* w2, const uint8_t* w2_s, double* y, uint8_t* a8,
+                uint8_t* a8s) {
+  orc_expert_fmt(h, inter, ORC_FMT_E4M3, x8, x8s, w13, w13_s, w2, w2_s, y, a8, a8s);
 }
 
 int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
@@ -350,7 +439,8 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   int32_t H = d->hidden, E = d->experts, K = d->topk, I = d->inter,
           Is = d->shared_inter;
   if (m < 1 || H < 32 || H % 32 || I < 32 || I % 32 || Is < 32 || Is % 32 ||
-      E < 1 || K < 1 || K > E)
+      E < 1 || K < 1 || K > E ||
+      (d->routed_format != ORC_FMT_E4M3 && d->routed_format != ORC_FMT_MXFP4))
     return -1;
   size_t mh = (size_t)m * H;
   uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * mh);
@@ -373,16 +463,20 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   orc_router(m, H, E, K, y, gate_w, bias, d->routed_scale, logits, sel, w,
              NULL);
   /* 4-5. picked experts and the shared expert; weighted sum, one rounding. */
-  size_t w13_e = (size_t)2 * I * H, w13s_e = (size_t)(2 * I / 32) * (H / 32);
-  size_t w2_e = (size_t)H * I, w2s_e = (size_t)(H / 32) * (I / 32);
+  /* per-expert strides of the routed tensors in their format */
+  int32_t fmt = d->routed_format;
+  size_t w13_e = fmt == ORC_FMT_MXFP4 ? (size_t)2 * I * (H / 2) : (size_t)2 * I * H;
+  size_t w13s_e = fmt == ORC_FMT_MXFP4 ? (size_t)2 * I * (H / 32) : (size_t)(2 * I / 32) * (H / 32);
+  size_t w2_e = fmt == ORC_FMT_MXFP4 ? (size_t)H * (I / 2) : (size_t)H * I;
+  size_t w2s_e = fmt == ORC_FMT_MXFP4 ? (size_t)H * (I / 32) : (size_t)(H / 32) * (I / 32);
   for (int32_t t = 0; t < m; ++t) {
     const uint8_t* xq = q + (size_t)t * H;
     const uint8_t* xc = qc + (size_t)t * (H / 32);
     for (int32_t n = 0; n < H; ++n) acc[n] = 0.0;
     for (int32_t j = 0; j < K; ++j) {
       size_t ex = (size_t)sel[(size_t)t * K + j];
-      orc_expert(H, I, xq, xc, w13 + ex * w13_e, w13_s + ex * w13s_e,
-                 w2 + ex * w2_e, w2_s + ex * w2s_e, ye, NULL, NULL);
+      orc_expert_fmt(H, I, fmt, xq, xc, w13 + ex * w13_e, w13_s + ex * w13s_e,
+                     w2 + ex * w2_e, w2_s + ex * w2s_e, ye, NULL, NULL);
       for (int32_t n = 0; n < H; ++n) acc[n] += w[(size_t)t * K + j] * ye[n];
     }
     orc_expert(H, Is, xq, xc, sgu, sgu_s, sw2, sw2_s, ye, NULL, NULL);

@@ -28,6 +28,11 @@ extern "C" {
 
 /* Layer dimensions (the pages' MonoLayerWeights.check shapes, with the
  * expert count, top-k and intermediates as parameters). */
+/* Routed expert weight formats: E4M3 with one E8M0 code per 32 x 32 block,
+ * or MXFP4 (E2M1, two per byte) with one code per row and 32 columns. */
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_MXFP4 1
+
 typedef struct orc_dims {
   int32_t hidden;        /* H */
   int32_t experts;       /* E routed experts */
@@ -36,6 +41,7 @@ typedef struct orc_dims {
   int32_t shared_inter;  /* Is, shared expert intermediate */
   float rms_eps;         /* RMSNorm epsilon */
   float routed_scale;    /* factor on the renormalised routing weights */
+  int32_t routed_format; /* ORC_FMT_E4M3 or ORC_FMT_MXFP4 (the shared expert is E4M3) */
 } orc_dims;
 
 /* ---- number formats ---------------------------------------------------- */
@@ -57,8 +63,19 @@ uint8_t orc_e4m3_rne(double v);
  * at 0.  [device] mx_code. */
 int32_t orc_mx_code(double amax);
 
-/* Element-wise loops over the three scalar functions above (for tests that
+/* E2M1 (float4_e2m1fn) nibble -> exact value.  [runner] MonoLayerWeights
+ * (the routed experts' fp4x2 tensors). */
+double orc_e2m1_value(uint8_t nibble);
+/* The E2M1 nibble nearest to v, ties to the even (zero) mantissa bit; |v|
+ * saturates at 6; the sign bit follows v's sign. */
+uint8_t orc_e2m1_rne(double v);
+/* E8M0 code of a 32-value FP4 block: the smallest c in [0, 254] with
+ * amax <= 6 * 2^(c-127). */
+int32_t orc_fp4_code(double amax);
+
+/* Element-wise loops over the scalar functions above (for tests that
  * sweep many inputs). */
+void orc_e2m1_rne_array(int64_t n, const double* v, uint8_t* out);
 void orc_e4m3_rne_array(int64_t n, const double* v, uint8_t* out);
 void orc_mx_code_array(int64_t n, const double* amax, int32_t* out);
 void orc_bf16_rne_array(int64_t n, const double* v, uint16_t* out);
@@ -72,6 +89,11 @@ void orc_mx_quant_row(int32_t n, const double* v, uint8_t* q, uint8_t* codes);
  * [rows/32, cols/32].  [runner] MonoLayerWeights.check / AttnWeights.check. */
 void orc_quant_weight(int32_t rows, int32_t cols, const float* w, uint8_t* q,
                       uint8_t* scales);
+/* MXFP4 of a [rows, cols] fp32 weight: codes [rows, cols/32] (one per row and
+ * 32 columns, orc_fp4_code of their amax), elements E2M1 two per byte, column
+ * 2i in the low nibble.  [runner] MonoLayerWeights.check (w13, w2 fp4x2). */
+void orc_quant_weight_fp4(int32_t rows, int32_t cols, const float* w, uint8_t* q,
+                          uint8_t* scales);
 
 /* ---- the layer, step by step ------------------------------------------- */
 
@@ -95,6 +117,11 @@ void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
                 const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
                 const uint8_t* w2, const uint8_t* w2_s, double* y, uint8_t* a8,
                 uint8_t* a8s);
+/* The same for weights in format fmt (ORC_FMT_E4M3 or ORC_FMT_MXFP4). */
+void orc_expert_fmt(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
+                    const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                    const uint8_t* w2, const uint8_t* w2_s, double* y,
+                    uint8_t* a8, uint8_t* a8s);
 /* The whole layer for m token rows.  Outputs other than out may be NULL:
  * normed [m,H] bf16, x8 [m,H], x8s [m,H/32], logits [m,E], ids [m,k],
  * wts [m,k], out_f64 [m,H] (the sum before its bf16 rounding), out [m,H] bf16.

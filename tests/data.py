@@ -1,5 +1,7 @@
 """Test inputs: seeded draws from ``synth`` with the expert weights quantised
-by the oracle's MXFP8 quantiser (32 x 32 E8M0 blocks).
+by the oracle's quantisers: E4M3 with 32 x 32 E8M0 blocks, or, for routed
+experts of a config with ``routed="mxfp4"``, E2M1 pairs with one E8M0 code
+per row and 32 columns.
 
 Weights of experts no token picks are never read by either side, so a layer
 can be built with only the picked experts' weights drawn (the rest of the
@@ -18,18 +20,35 @@ import synth
 WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
+def routed_of(cfg: dict) -> str:
+    return cfg.get("routed", "e4m3")
+
+
 def dims_of(cfg: dict) -> dict:
-    return {k: cfg[k] for k in ("hidden", "experts", "topk", "inter",
-                                "shared_inter", "rms_eps", "routed_scale")}
+    d = {k: cfg[k] for k in ("hidden", "experts", "topk", "inter",
+                             "shared_inter", "rms_eps", "routed_scale")}
+    d["routed"] = routed_of(cfg)
+    return d
 
 
 def alloc_weights(cfg: dict) -> dict:
     E, H, I, Is = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["shared_inter"]
+    if routed_of(cfg) == "mxfp4":
+        routed = {
+            "w13": np.zeros((E, 2 * I, H // 2), np.uint8),
+            "w13_s": np.zeros((E, 2 * I, H // 32), np.uint8),
+            "w2": np.zeros((E, H, I // 2), np.uint8),
+            "w2_s": np.zeros((E, H, I // 32), np.uint8),
+        }
+    else:
+        routed = {
+            "w13": np.zeros((E, 2 * I, H), np.uint8),
+            "w13_s": np.zeros((E, 2 * I // 32, H // 32), np.uint8),
+            "w2": np.zeros((E, H, I), np.uint8),
+            "w2_s": np.zeros((E, H // 32, I // 32), np.uint8),
+        }
     return {
-        "w13": np.zeros((E, 2 * I, H), np.uint8),
-        "w13_s": np.zeros((E, 2 * I // 32, H // 32), np.uint8),
-        "w2": np.zeros((E, H, I), np.uint8),
-        "w2_s": np.zeros((E, H // 32, I // 32), np.uint8),
+        **routed,
         "sgu": np.zeros((2 * Is, H), np.uint8),
         "sgu_s": np.zeros((2 * Is // 32, H // 32), np.uint8),
         "sw2": np.zeros((H, Is), np.uint8),
@@ -41,15 +60,14 @@ def fill_weights(seed: int, cfg: dict, w: dict, experts, workers: int = WORKERS)
     """Draw and quantise the given routed experts' weights (and the shared
     expert's) into ``w`` in place."""
     H, I, Is = cfg["hidden"], cfg["inter"], cfg["shared_inter"]
+    rq = oracle.quant_weight_fp4_into if routed_of(cfg) == "mxfp4" else oracle.quant_weight_into
 
     def one(job):
         name, e = job
         if name == "w13":
-            oracle.quant_weight_into(synth.expert_f32(seed, "w13", e, 2 * I, H),
-                                     w["w13"][e], w["w13_s"][e])
+            rq(synth.expert_f32(seed, "w13", e, 2 * I, H), w["w13"][e], w["w13_s"][e])
         elif name == "w2":
-            oracle.quant_weight_into(synth.expert_f32(seed, "w2", e, H, I),
-                                     w["w2"][e], w["w2_s"][e])
+            rq(synth.expert_f32(seed, "w2", e, H, I), w["w2"][e], w["w2_s"][e])
         elif name == "sgu":
             oracle.quant_weight_into(synth.expert_f32(seed, "sgu", 0, 2 * Is, H),
                                      w["sgu"], w["sgu_s"])

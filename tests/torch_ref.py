@@ -1,5 +1,7 @@
 """An independent reference of the layer built from torch library primitives
-(fp8 and bf16 casts, float64 matmul, sigmoid, topk) for tiny shapes.
+(fp8 and bf16 casts, float64 matmul, sigmoid, topk) for tiny shapes.  FP4
+(E2M1) weights, which torch cannot cast, are decoded through the golden table
+tests/golden/e2m1_values.txt.
 
 It shares nothing with the oracle: it exists to pin the oracle's expert path,
 router and combine against a second implementation whose number-format
@@ -8,10 +10,25 @@ method defines are torch casts.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
 F64 = torch.float64
+
+
+def _e2m1_table() -> torch.Tensor:
+    vals = [0.0] * 16
+    with open(os.path.join(os.path.dirname(__file__), "golden", "e2m1_values.txt")) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                nib, v = line.split()
+                vals[int(nib, 16)] = float(v)
+    return torch.tensor(vals, dtype=F64)
+
+
+E2M1 = _e2m1_table()
 
 
 def bf16_bits_to_f64(bits) -> torch.Tensor:
@@ -54,14 +71,27 @@ def block_dequant(q, s) -> torch.Tensor:
     return v * torch.exp2(sc - 127)
 
 
-def expert(xq, xc, w13, w13_s, w2, w2_s):
+def fp4_dequant(q, s) -> torch.Tensor:
+    """[N, K/2] E2M1 pairs (column 2i in the low nibble) with [N, K/32] codes
+    -> float64 [N, K]."""
+    b = torch.from_numpy(np.ascontiguousarray(q, np.uint8)).to(torch.int64)
+    v = torch.stack([E2M1[b & 0xF], E2M1[b >> 4]], dim=-1).reshape(b.shape[0], -1)
+    sc = torch.from_numpy(np.ascontiguousarray(s, np.uint8)).to(F64).repeat_interleave(32, 1)
+    return v * torch.exp2(sc - 127)
+
+
+def dequant(q, s, fmt: str) -> torch.Tensor:
+    return fp4_dequant(q, s) if fmt == "mxfp4" else block_dequant(q, s)
+
+
+def expert(xq, xc, w13, w13_s, w2, w2_s, fmt: str = "e4m3"):
     """One token through one expert: (y [H] f64, a8 [I] u8, a8s [I/32] u8)."""
     xd = mx_dequant(xq, xc)
-    h = block_dequant(w13, w13_s) @ xd
+    h = dequant(w13, w13_s, fmt) @ xd
     inter = h.shape[0] // 2
     a = (torch.nn.functional.silu(h[:inter]) * h[inter:]).to(torch.float32).to(F64)
     aq, ac = mx_quant(a)
-    y = block_dequant(w2, w2_s) @ mx_dequant(aq, ac)
+    y = dequant(w2, w2_s, fmt) @ mx_dequant(aq, ac)
     return y, aq, ac
 
 
@@ -83,7 +113,8 @@ def layer(dims: dict, inp: dict, w: dict, y_bits) -> dict:
     for t in range(m):
         for j in range(K):
             e = int(ids[t, j])
-            ye, _, _ = expert(xq[t], xc[t], w["w13"][e], w["w13_s"][e], w["w2"][e], w["w2_s"][e])
+            ye, _, _ = expert(xq[t], xc[t], w["w13"][e], w["w13_s"][e], w["w2"][e], w["w2_s"][e],
+                              dims.get("routed", "e4m3"))
             out[t] += wts[t, j] * ye
         ys, _, _ = expert(xq[t], xc[t], w["sgu"], w["sgu_s"], w["sw2"], w["sw2_s"])
         out[t] += ys
