@@ -34,8 +34,12 @@ METRIC = "MoE decode layer µs & tokens/s at M=1/16/48; % HBM roofline on expert
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def expert_bytes(H: int, I: int) -> dict:
-    """Algorithmic bytes of one expert: weights and their E8M0 codes."""
+def expert_bytes(H: int, I: int, fmt: str = "e4m3") -> dict:
+    """Algorithmic bytes of one expert: weights and their E8M0 codes (E4M3
+    with 32 x 32 blocks, or MXFP4: E2M1 pairs with a code per row and 32
+    columns)."""
+    if fmt == "mxfp4":
+        return {"w13": 2 * I * (H // 2) + 2 * I * (H // 32), "w2": H * (I // 2) + H * (I // 32)}
     w13 = 2 * I * H + (2 * I // 32) * (H // 32)
     w2 = H * I + (H // 32) * (I // 32)
     return {"w13": w13, "w2": w2}
@@ -43,18 +47,31 @@ def expert_bytes(H: int, I: int) -> dict:
 
 def make_weights(cfg: dict, seed: int, dev):
     """One device copy of the expert weights: N(0, 0.02) fp32 drawn on the GPU,
-    quantised by the library's weight quantiser (32 x 32 E8M0 blocks)."""
+    quantised by the library's weight quantisers (E4M3 with 32 x 32 E8M0
+    blocks; routed experts as MXFP4 when cfg["routed"] == "mxfp4")."""
     import torch
     import moe_decode_layer_seam_amd as mdl
 
     E, H, I, Is = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["shared_inter"]
+    fp4 = cfg.get("routed", "e4m3") == "mxfp4"
     g = torch.Generator(device=dev)
     g.manual_seed(1000 + seed)
+    if fp4:
+        routed = {
+            "w13": torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev),
+            "w13_s": torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev),
+            "w2": torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev),
+            "w2_s": torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev),
+        }
+    else:
+        routed = {
+            "w13": torch.empty((E, 2 * I, H), dtype=torch.uint8, device=dev),
+            "w13_s": torch.empty((E, 2 * I // 32, H // 32), dtype=torch.uint8, device=dev),
+            "w2": torch.empty((E, H, I), dtype=torch.uint8, device=dev),
+            "w2_s": torch.empty((E, H // 32, I // 32), dtype=torch.uint8, device=dev),
+        }
     w = {
-        "w13": torch.empty((E, 2 * I, H), dtype=torch.uint8, device=dev),
-        "w13_s": torch.empty((E, 2 * I // 32, H // 32), dtype=torch.uint8, device=dev),
-        "w2": torch.empty((E, H, I), dtype=torch.uint8, device=dev),
-        "w2_s": torch.empty((E, H // 32, I // 32), dtype=torch.uint8, device=dev),
+        **routed,
         "sgu": torch.empty((2 * Is, H), dtype=torch.uint8, device=dev),
         "sgu_s": torch.empty((2 * Is // 32, H // 32), dtype=torch.uint8, device=dev),
         "sw2": torch.empty((H, Is), dtype=torch.uint8, device=dev),
@@ -65,7 +82,8 @@ def make_weights(cfg: dict, seed: int, dev):
         for e0 in range(0, E, per):
             n = min(per, E - e0)
             f = torch.randn((n, rows, cols), generator=g, device=dev, dtype=torch.float32) * 0.02
-            mdl.quantize_weight(f, w[name][e0:e0 + n], w[name + "_s"][e0:e0 + n])
+            quant = mdl.quantize_weight_fp4 if fp4 else mdl.quantize_weight
+            quant(f, w[name][e0:e0 + n], w[name + "_s"][e0:e0 + n])
             del f
     for name, rows, cols in (("sgu", 2 * Is, H), ("sw2", H, Is)):
         f = torch.randn((rows, cols), generator=g, device=dev, dtype=torch.float32) * 0.02
@@ -169,6 +187,8 @@ def main() -> int:
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--routed", choices=("e4m3", "mxfp4"), default="e4m3",
+                    help="routed experts' weight format (the shared expert is E4M3)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -191,9 +211,9 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    cfg = dict(synth.CONFIGS[args.config])
+    cfg = dict(synth.CONFIGS[args.config], routed=args.routed)
     m, H, E, K, I, Is = cfg["m"], cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"], cfg["shared_inter"]
-    eb = expert_bytes(H, I)
+    eb = expert_bytes(H, I, args.routed)
     ebs = expert_bytes(H, Is)
     per_step_expected = (min(E, m * K) + 1) * (eb["w13"] + eb["w2"])
     copies = args.copies or max(2, min(8, -(-2 * 512 * 2**20 // per_step_expected)))
@@ -208,7 +228,7 @@ def main() -> int:
     outs = [torch.empty((m, H), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     print(f"[bench] weights ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    h = mdl.plan(H, E, K, I, Is, m, cfg["rms_eps"], cfg["routed_scale"])
+    h = mdl.plan(H, E, K, I, Is, m, cfg["rms_eps"], cfg["routed_scale"], routed=args.routed)
     stream = torch.cuda.current_stream()
 
     def step(c):
@@ -331,10 +351,11 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3",
+        "dtype": "e4m3" if args.routed == "e4m3" else "e4m3 x e2m1 (routed), e4m3 (shared)",
         "data": "synthetic",
         "config": {"workload": f"{cfg['name']}: M={m} token rows, hidden {H}, {E} routed experts top-{K}, "
-                               f"intermediate {I}, shared expert {Is}, E4M3 weights with 32x32 E8M0 blocks",
+                               f"intermediate {I}, shared expert {Is}, " + ("E4M3 weights with 32x32 E8M0 blocks" if args.routed == "e4m3" else
+                                    "routed experts MXFP4 (E2M1, 1x32 E8M0), shared expert E4M3 32x32"),
                    "tokens": m, "mode": args.mode, "weight_copies": copies},
         "us_per_layer": ms_step * 1e3,
         "batch_us_per_layer": batch_us,
@@ -349,7 +370,8 @@ def main() -> int:
         "wall_s": wall,
         "roofline": {"bound": "hbm", "kernel": "w13", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg["name"]), "algorithmic_bytes": w13_bytes},
+                     "traffic": measured_traffic(cfg["name"] + ("" if args.routed == "e4m3" else "_mxfp4")),
+                     "algorithmic_bytes": w13_bytes},
     }
     mdl.destroy(h)
     graphs.clear()

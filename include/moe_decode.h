@@ -53,6 +53,14 @@ extern "C" {
 /* Largest decode width the pages' runner supports (DSV41MonoLayer.supports). */
 #define MOE_DECODE_MAX_TOKENS 48
 
+/* Routed expert weight formats (the shared expert is always E4M3 with
+ * 32 x 32 blocks). */
+#define MOE_DECODE_ROUTED_E4M3 0  /* E4M3 [N, K] with E8M0 codes [N/32, K/32] */
+#define MOE_DECODE_ROUTED_MXFP4 1 /* E2M1 pairs [N, K/2] (column 2i in the low
+                                     nibble) with E8M0 codes [N, K/32]: the
+                                     pages' A8W4 routed experts
+                                     (MonoLayerWeights.check, fp4x2) */
+
 /* Layer dimensions, fixed when the plan is made.
  *   hidden        H, a multiple of 128 (the scaled MFMA's K step), <= 16384
  *   experts       E routed experts, 1..1024
@@ -61,7 +69,8 @@ extern "C" {
  *   shared_inter  Is, shared expert intermediate, a multiple of 128, <= 8192
  *   max_tokens    largest m a run may pass, 1..48
  *   rms_eps       RMSNorm epsilon (added to mean(x^2) in double precision)
- *   routed_scale  factor applied to the renormalised routing weights */
+ *   routed_scale  factor applied to the renormalised routing weights
+ *   routed_format MOE_DECODE_ROUTED_E4M3 or MOE_DECODE_ROUTED_MXFP4 */
 typedef struct moe_decode_dims {
   int32_t hidden;
   int32_t experts;
@@ -71,6 +80,7 @@ typedef struct moe_decode_dims {
   int32_t max_tokens;
   float rms_eps;
   float routed_scale;
+  int32_t routed_format;
 } moe_decode_dims;
 
 typedef struct moe_decode_plan_s* moe_decode_handle;
@@ -98,6 +108,8 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  *   d_w13_s   E8M0 [E, 2I/32, H/32]  one code per 32 x 32 block, row-major
  *   d_w2      E4M3 [E, H, I]
  *   d_w2_s    E8M0 [E, H/32, I/32]
+ *             (MXFP4 routed experts: w13 [E, 2I, H/2] with codes
+ *             [E, 2I, H/32], w2 [E, H, I/2] with codes [E, H, I/32])
  *   d_sgu     E4M3 [2Is, H]          shared expert gate/up
  *   d_sgu_s   E8M0 [2Is/32, H/32]
  *   d_sw2     E4M3 [H, Is]           shared expert down
@@ -198,6 +210,16 @@ void moe_decode_destroy(moe_decode_handle plan);
 int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows,
                                int32_t cols, void* d_q, void* d_scales,
                                void* stream);
+
+/* Weight preparation for MXFP4 routed experts: quantise `count` back-to-back
+ * fp32 [rows, cols] matrices to E2M1 pairs [rows, cols/2] (column 2i in the
+ * low nibble) with one E8M0 code per row and 32 columns ([rows, cols/32]).
+ * Code = the smallest c in [0, 254] with amax <= 6 * 2^(c-127); values
+ * rounded to nearest, ties to the even mantissa bit, after scaling by
+ * 2^(127 - code).  cols a multiple of 32; pointers 16-byte aligned. */
+int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows,
+                                   int32_t cols, void* d_q, void* d_scales,
+                                   void* stream);
 
 /* Text of an error code. */
 const char* moe_decode_strerror(int code);

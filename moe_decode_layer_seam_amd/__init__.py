@@ -4,7 +4,7 @@ Argument marshalling only -- every step of the layer runs in the HIP kernels
 of ``libmoe_decode.so`` (declared in ``include/moe_decode.h``).  The functions
 keep the C names without the ``moe_decode_`` prefix: ``plan``, ``run``,
 ``inspect``, ``timing``, ``timing_read``, ``destroy``, ``quantize_weight``,
-``strerror``.  Tensors are torch tensors on the GPU (torch supplies device
+``quantize_weight_fp4``, ``strerror``.  Tensors are torch tensors on the GPU (torch supplies device
 memory and streams); shapes, dtypes and contiguity are checked here before
 the pointers cross the boundary, because the kernels' loads are unchecked.
 
@@ -29,12 +29,17 @@ TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
 KERNELS = {"seam": 0, "logits": 1, "route": 2, "w13": 3, "act": 4, "w2": 5, "combine": 6}
 
 
+# routed expert weight formats (moe_decode.h MOE_DECODE_ROUTED_*)
+ROUTED = {"e4m3": 0, "mxfp4": 1}
+
+
 class Dims(ctypes.Structure):
     """moe_decode_dims."""
     _fields_ = [("hidden", ctypes.c_int32), ("experts", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("routed_scale", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("routed_scale", ctypes.c_float),
+                ("routed_format", ctypes.c_int32)]
 
 
 class MoeDecodeError(RuntimeError):
@@ -80,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_quantize_weight.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, _P, _P, _P]
         L.moe_decode_quantize_weight.restype = ctypes.c_int
+        L.moe_decode_quantize_weight_fp4.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, _P, _P, _P]
+        L.moe_decode_quantize_weight_fp4.restype = ctypes.c_int
         L.moe_decode_strerror.argtypes = [ctypes.c_int]
         L.moe_decode_strerror.restype = ctypes.c_char_p
         L.moe_decode_last_hip_error.argtypes = [_P]
@@ -91,7 +99,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
            "moe_decode_inspect", "moe_decode_timing", "moe_decode_timing_read",
            "moe_decode_timeline", "moe_decode_timeline_read",
-           "moe_decode_destroy", "moe_decode_quantize_weight", "moe_decode_strerror",
+           "moe_decode_destroy", "moe_decode_quantize_weight",
+           "moe_decode_quantize_weight_fp4", "moe_decode_strerror",
            "moe_decode_last_hip_error")
 
 
@@ -119,9 +128,11 @@ def _check(rc: int, what: str, handle=None) -> None:
 
 def plan(hidden: int, experts: int, topk: int, inter: int, shared_inter: int,
          max_tokens: int = MAX_TOKENS, rms_eps: float = 1e-6,
-         routed_scale: float = 1.0, stream=None) -> int:
-    """moe_decode_plan: returns an opaque handle (int)."""
-    d = Dims(hidden, experts, topk, inter, shared_inter, max_tokens, rms_eps, routed_scale)
+         routed_scale: float = 1.0, stream=None, routed: str = "e4m3") -> int:
+    """moe_decode_plan: returns an opaque handle (int).  routed: the routed
+    experts' weight format, "e4m3" or "mxfp4"."""
+    d = Dims(hidden, experts, topk, inter, shared_inter, max_tokens, rms_eps, routed_scale,
+             ROUTED[routed])
     h = _P()
     _check(lib().moe_decode_plan(ctypes.byref(d), _stream_ptr(stream), ctypes.byref(h)),
            "moe_decode_plan")
@@ -144,9 +155,11 @@ def _tensor(t: torch.Tensor, name: str, shape, dtype) -> int:
 def run(handle: int, dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s,
         sgu, sgu_s, sw2, sw2_s, out, stream=None) -> None:
     """moe_decode_run on torch tensors.  dims: hidden, experts, topk, inter,
-    shared_inter (the plan's).  E4M3 tensors may be torch.float8_e4m3fn or
-    uint8; scales uint8."""
+    shared_inter and routed ("e4m3", the default, or "mxfp4") -- the plan's.
+    E4M3 tensors may be torch.float8_e4m3fn or uint8; E2M1 pairs and scales
+    uint8."""
     H, E, I, Is = dims["hidden"], dims["experts"], dims["inter"], dims["shared_inter"]
+    fp4 = dims.get("routed", "e4m3") == "mxfp4"
     m = x.shape[0]
 
     def q(t, name, shape):
@@ -158,8 +171,12 @@ def run(handle: int, dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s,
         _tensor(norm_w, "norm_w", (H,), torch.bfloat16),
         _tensor(gate_w, "gate_w", (E, H), torch.bfloat16),
         _tensor(bias, "bias", (E,), torch.float32),
-        q(w13, "w13", (E, 2 * I, H)), _tensor(w13_s, "w13_s", (E, 2 * I // 32, H // 32), torch.uint8),
-        q(w2, "w2", (E, H, I)), _tensor(w2_s, "w2_s", (E, H // 32, I // 32), torch.uint8),
+        *((_tensor(w13, "w13", (E, 2 * I, H // 2), torch.uint8),
+           _tensor(w13_s, "w13_s", (E, 2 * I, H // 32), torch.uint8),
+           _tensor(w2, "w2", (E, H, I // 2), torch.uint8),
+           _tensor(w2_s, "w2_s", (E, H, I // 32), torch.uint8)) if fp4 else
+          (q(w13, "w13", (E, 2 * I, H)), _tensor(w13_s, "w13_s", (E, 2 * I // 32, H // 32), torch.uint8),
+           q(w2, "w2", (E, H, I)), _tensor(w2_s, "w2_s", (E, H // 32, I // 32), torch.uint8))),
         q(sgu, "sgu", (2 * Is, H)), _tensor(sgu_s, "sgu_s", (2 * Is // 32, H // 32), torch.uint8),
         q(sw2, "sw2", (H, Is)), _tensor(sw2_s, "sw2_s", (H // 32, Is // 32), torch.uint8),
         _tensor(out, "out", (m, H), torch.bfloat16),
@@ -236,6 +253,22 @@ def timeline_read(handle: int, kernel: str):
 
 def destroy(handle: int) -> None:
     lib().moe_decode_destroy(handle)
+
+
+def quantize_weight_fp4(w: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """moe_decode_quantize_weight_fp4: fp32 [..., rows, cols] -> E2M1 pairs q
+    (uint8 [..., rows, cols/2]) and E8M0 scales (uint8 [..., rows, cols/32])."""
+    rows, cols = w.shape[-2], w.shape[-1]
+    count = w.numel() // (rows * cols)
+    if w.dtype != torch.float32 or not w.is_contiguous() or not w.is_cuda:
+        raise ValueError("w: contiguous float32 on the GPU required")
+    if tuple(q.shape) != tuple(w.shape[:-1]) + (cols // 2,) or q.dtype != torch.uint8 or not q.is_contiguous():
+        raise ValueError("q: uint8 [..., rows, cols/2]")
+    if tuple(scales.shape) != tuple(w.shape[:-1]) + (cols // 32,) or scales.dtype != torch.uint8:
+        raise ValueError("scales: uint8 [..., rows, cols/32]")
+    rc = lib().moe_decode_quantize_weight_fp4(w.data_ptr(), count, rows, cols, q.data_ptr(),
+                                              scales.data_ptr(), _stream_ptr(stream))
+    _check(rc, "moe_decode_quantize_weight_fp4")
 
 
 def quantize_weight(w: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:

@@ -83,6 +83,7 @@ bool valid_dims(const moe_decode_dims* d) {
   if (d->max_tokens < 1 || d->max_tokens > kMaxTokens) return false;
   if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.0f) return false;
   if (!std::isfinite(d->routed_scale)) return false;
+  if (d->routed_format != MOE_DECODE_ROUTED_E4M3 && d->routed_format != MOE_DECODE_ROUTED_MXFP4) return false;
   return true;
 }
 
@@ -140,6 +141,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   d.Mx = dims->max_tokens;
   d.eps = dims->rms_eps;
   d.routed_scale = dims->routed_scale;
+  d.rfmt = dims->routed_format;
   p->max_vs = max_vslots(d.Mx, d.E, d.K);
   p->R = d.Mx * d.K + d.Mx;
 
@@ -406,6 +408,17 @@ int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows, in
   if (!aligned16(d_w) || !aligned16(d_q) || d_scales == nullptr) return MOE_DECODE_EINVAL;
   hipError_t e = launch_quant_weight(d_w, count, rows, cols, static_cast<uint8_t*>(d_q),
                                      static_cast<uint8_t*>(d_scales), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "quantize launch");
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows, int32_t cols, void* d_q,
+                                   void* d_scales, void* stream) {
+  if (count < 1 || rows < 1 || cols < 32 || cols % 32) return MOE_DECODE_EINVAL;
+  if (!aligned16(d_w) || !aligned16(d_q) || d_scales == nullptr) return MOE_DECODE_EINVAL;
+  const int64_t ngroups = (int64_t)count * rows * (cols / 32);
+  hipError_t e = launch_quant_weight_fp4(d_w, ngroups, static_cast<uint8_t*>(d_q),
+                                         static_cast<uint8_t*>(d_scales), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "quantize launch");
   return MOE_DECODE_OK;
 }

@@ -134,6 +134,30 @@ __device__ __forceinline__ int e8m0_code(float amax) {
   return c < 0 ? 0 : (c > 254 ? 254 : c);
 }
 
+// E8M0 code of a 32-value block of FP4 (E2M1) weights: the smallest c in
+// [0, 254] with amax <= 6 * 2^(c - 127) (mx_code's rule with the FP4 maximum).
+// With amax = M * 2^(e - 150) and 6 = 3 * 2^1 the condition reads
+// M <= 3 * 2^(c + 24 - e); M in [2^23, 2^24) makes that c = e - 2, or e - 1
+// when M > 3 * 2^22 (mantissa > 0x400000).
+__device__ __forceinline__ int fp4_code(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  int e = (int)(u >> 23);
+  if (e == 0) return 0;
+  int c = e - 2 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+// E2M1 nibble of x, round to nearest with ties to the even mantissa bit,
+// |x| saturating at 6, the sign bit following x.  The midpoints of the
+// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are .25, .75, 1.25, 1.75, 2.5, 3.5, 5;
+// a tie goes to the neighbour whose code is even.
+__device__ __forceinline__ uint32_t e2m1_rne(float x) {
+  const float a = fabsf(x);
+  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 // 2^(127 - code) as fp32, exact for code in [0, 253] (device page, mx_mul).
 __device__ __forceinline__ float mx_mul(int code) { return __uint_as_float((uint32_t)(254 - code) << 23); }
 
@@ -161,6 +185,42 @@ __device__ __forceinline__ uint32_t fp8x2(float a, float b) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ v4f mfma_e4m3(const v8i& a, const v8i& b, v4f c, int scale_a, int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// E4M3 A x E2M1 B (format 4).  B's lane l serves column l % 16 with the 32
+// consecutive K values [32 (l / 16), +32) of the window in its first four
+// registers (value 2i in the low nibble of byte i); the other four are not
+// read.  Scales as for E4M3: lane 16 kb + j holds the code of K block kb of
+// row / column j.  (Measured on gfx950; a scale the compiler proves uniform
+// across lanes does not reach every column, so scales are per-lane values.)
+__device__ __forceinline__ v4f mfma_e4m3_e2m1(const v8i& a, const u32x4& b, v4f c, int scale_a, int scale_b) {
+  v8i bb;
+  bb[0] = (int)b[0]; bb[1] = (int)b[1]; bb[2] = (int)b[2]; bb[3] = (int)b[3];
+  bb[4] = 0; bb[5] = 0; bb[6] = 0; bb[7] = 0;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, scale_a, 0, scale_b);
+}
+
+// The same with the B scale taken from byte SEL of its operand (opsel).
+template <int SEL>
+__device__ __forceinline__ v4f mfma_e4m3_e2m1_sel(const v8i& a, const u32x4& b, v4f c, int scale_a,
+                                                  uint32_t scale_b) {
+  v8i bb;
+  bb[0] = (int)b[0]; bb[1] = (int)b[1]; bb[2] = (int)b[2]; bb[3] = (int)b[3];
+  bb[4] = 0; bb[5] = 0; bb[6] = 0; bb[7] = 0;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb, c, 0, 4, 0, scale_a, SEL, (int)scale_b);
+}
+
+// 4 x 4 byte transpose across the lane groups of a wave: lane (g, j) holds
+// word w with byte b = M[g][b]; it returns byte b = M[b][g], where M[h][.]
+// is the word of lane (h, j).  Two exchange stages, lane groups g ^ 1 then
+// g ^ 2, each keeping two bytes and taking two from the partner.
+__device__ __forceinline__ uint32_t transpose4_groups(uint32_t w, int g) {
+  const uint32_t p1 = (uint32_t)xor_lane((int)w, 16);
+  // even g: [w0, p0, w2, p2]; odd g: [p1, w1, p3, w3]
+  w = __builtin_amdgcn_perm(p1, w, (g & 1) ? 0x03070105u : 0x06020400u);
+  const uint32_t p2 = (uint32_t)xor_lane((int)w, 32);
+  // g & 2 == 0: [w0, w1, p0, p1]; else [p2, p3, w2, w3]
+  return __builtin_amdgcn_perm(p2, w, (g & 2) ? 0x03020706u : 0x05040100u);
 }
 
 __device__ __forceinline__ v8i join(const u32x4& lo, const u32x4& hi) {

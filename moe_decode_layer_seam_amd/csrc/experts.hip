@@ -66,6 +66,7 @@ struct UnitOps {
   rsrc_t w, ws, a, as;
   uint32_t wsoff, wlane, row8, tstride, ssoff, sstride, slane, alane, aslane;
   int row0, c, col0, nsteps;
+  int fp4;  // weights as E2M1 pairs with per-row 32-column codes
 };
 
 template <bool W13, int TT>
@@ -77,27 +78,37 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
   const int N = 16 * G.tiles;
   const uint8_t* W;
   const uint8_t* WS;
-  if (W13) {
-    W = shared ? in.sgu : in.w13 + (size_t)ex * 2 * d.I * d.H;
-    WS = shared ? in.sgu_s : in.w13_s + (size_t)ex * (2 * d.I / 32) * (d.H / 32);
-  } else {
-    W = shared ? in.sw2 : in.w2 + (size_t)ex * d.H * d.I;
-    WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * (d.H / 32) * (d.I / 32);
-  }
   UnitOps u;
+  u.fp4 = !shared && d.rfmt == MOE_DECODE_ROUTED_MXFP4;
+  // bytes per weight row and codes per weight row block (E4M3: one per 32
+  // rows; E2M1: one per row)
+  const uint32_t rowb = u.fp4 ? G.K / 2 : G.K;
+  if (W13) {
+    W = shared ? in.sgu : in.w13 + (size_t)ex * 2 * d.I * (d.H / (u.fp4 ? 2 : 1));
+    WS = shared ? in.sgu_s : in.w13_s + (size_t)ex * 2 * d.I * (d.H / 32) / (u.fp4 ? 1 : 32);
+  } else {
+    W = shared ? in.sw2 : in.w2 + (size_t)ex * d.H * (d.I / (u.fp4 ? 2 : 1));
+    WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * d.H * (d.I / 32) / (u.fp4 ? 1 : 32);
+  }
   u.row0 = slot.y;
   u.c = slot.z;
   u.col0 = 16 * TT * tgroup;
   u.nsteps = G.K / 128;
-  u.w = make_rsrc(W, (uint32_t)N * G.K);
-  u.ws = make_rsrc(WS, (uint32_t)(N / 32) * (G.K / 32));
-  u.wsoff = (uint32_t)u.col0 * G.K;
-  u.tstride = (uint32_t)16 * G.K;
-  u.wlane = (uint32_t)(j & 7) * G.K + (j < 8 ? 16 * g : 64 + 16 * g);
-  u.row8 = (uint32_t)8 * G.K;
-  u.ssoff = (uint32_t)(u.col0 / 32) * (G.K / 32);  // the first tile pair's 32-row code block
-  u.sstride = (uint32_t)(G.K / 32);
-  u.slane = (uint32_t)g;  // the lane group's 32-column K block
+  u.w = make_rsrc(W, (uint32_t)N * rowb);
+  u.ws = make_rsrc(WS, (uint32_t)(u.fp4 ? N : N / 32) * (G.K / 32));
+  u.wsoff = (uint32_t)u.col0 * rowb;
+  u.tstride = (uint32_t)16 * rowb;
+  u.wlane = (uint32_t)(j & 7) * rowb + (j < 8 ? 16 * g : 64 + 16 * g);
+  u.row8 = (uint32_t)8 * rowb;
+  if (u.fp4) {
+    u.ssoff = (uint32_t)u.col0 * (G.K / 32);       // the tile group's first row
+    u.sstride = (uint32_t)16 * (G.K / 32);         // per tile
+    u.slane = (uint32_t)j * (G.K / 32) + g;        // the lane's row, its K block
+  } else {
+    u.ssoff = (uint32_t)(u.col0 / 32) * (G.K / 32);  // the first tile pair's 32-row code block
+    u.sstride = (uint32_t)(G.K / 32);
+    u.slane = (uint32_t)g;  // the lane group's 32-column K block
+  }
   if (W13) {
     const int tok = j < u.c ? s_tok[u.row0 + j] : -1;
     u.a = make_rsrc(s.x8, (uint32_t)m * d.H);
@@ -159,6 +170,94 @@ __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, in
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// E2M1 weights: one 128-byte line of a row holds two K steps (64 bytes
+// each).  Lane (g, j) of load X reads row j & 7 of the tile at step st + (j
+// >= 8) bytes [16 g, +16), load Y the same for rows 8..15; the DPP row shifts
+// of lines_to_mfma give every lane its row's step st operand in `lo` and
+// step st + 1 in `hi`.
+template <int TT>
+struct Pair4 {
+  u32x4 x[TT], y[TT], alo[2], ahi[2];
+};
+
+// The segment's E8M0 codes, one word per lane and tile: byte s = the code of
+// step s of the segment for the lane's row and its lane group's K block.
+// Each lane loads the four codes of step g (blocks 4 g .. 4 g + 3 of its
+// row's 16 in the segment); a byte transpose across the lane groups turns
+// that into the four steps of its own block.
+template <int TT>
+struct Codes4 {
+  uint32_t b[TT], a;
+};
+
+template <int TT>
+__device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int seg, int g) {
+  const int st = seg * kSegSteps + g;  // the step whose codes this lane fetches
+  const bool ok = st < u.nsteps;
+  // slane = j * (K/32) + g: the row's code of block g; this load wants blocks
+  // 4 g .. 4 g + 3 of step seg * 4 + g, i.e. bytes 16 seg + 4 g .. + 4
+  const uint32_t bo = ok ? u.slane - g + 16 * seg + 4 * g : kNoRow;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) c.b[t] = __builtin_amdgcn_raw_buffer_load_b32(u.ws, (int)bo, (int)(u.ssoff + t * u.sstride), 0);
+  c.a = __builtin_amdgcn_raw_buffer_load_b32(u.as, (int)(ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow), 0, 0);
+}
+
+template <int TT>
+__device__ __forceinline__ void transpose_codes4(Codes4<TT>& c, int g) {
+#pragma unroll
+  for (int t = 0; t < TT; ++t) c.b[t] = transpose4_groups(c.b[t], g);
+  c.a = transpose4_groups(c.a, g);
+}
+
+template <int TT>
+__device__ __forceinline__ void load_pair4(Pair4<TT>& f, const UnitOps& u, int st, int j) {
+  const bool ok0 = st < u.nsteps, ok1 = st + 1 < u.nsteps;
+  const uint32_t wo = (j < 8 ? ok0 : ok1) ? u.wlane + (uint32_t)st * 64 : kNoRow;
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    f.x[t] = bload16_nt(u.w, wo, u.wsoff + t * u.tstride);
+    f.y[t] = bload16_nt(u.w, wo, u.wsoff + t * u.tstride + u.row8);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t ao = (q ? ok1 : ok0) ? u.alane + (uint32_t)(st + q) * 128 : kNoRow;
+    f.alo[q] = bload16(u.a, ao, 0);
+    f.ahi[q] = bload16(u.a, ao + 64, 0);
+  }
+}
+
+// Steps 2P and 2P + 1 of the segment (P: the pair's index in it).
+template <int TT, int P>
+__device__ __forceinline__ void mma_pair4(v4f (&acc)[TT], const Pair4<TT>& f, const Codes4<TT>& c) {
+  const v8i a0 = join(f.alo[0], f.ahi[0]), a1 = join(f.alo[1], f.ahi[1]);
+  const int sa0 = (int)((c.a >> (16 * P)) & 0xFF), sa1 = (int)((c.a >> (16 * P + 8)) & 0xFF);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    u32x4 lo, hi;
+    lines_to_mfma(f.x[t], f.y[t], lo, hi);
+    acc[t] = mfma_e4m3_e2m1_sel<2 * P>(a0, lo, acc[t], sa0, c.b[t]);
+    acc[t] = mfma_e4m3_e2m1_sel<2 * P + 1>(a1, hi, acc[t], sa1, c.b[t]);
+  }
+}
+
+// One segment's sums for E2M1 weights: both line pairs (2 K steps each) and
+// the codes loaded before the first MFMA; each tile's MFMAs run in K order.
+template <int TT>
+__device__ __forceinline__ void segment_sum_fp4(v4f (&acc)[TT], const UnitOps& u, int seg, int g, int j) {
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  Codes4<TT> c;
+  Pair4<TT> f0, f1;
+  load_codes4<TT>(c, u, seg, g);
+  load_pair4<TT>(f0, u, seg * kSegSteps, j);
+  load_pair4<TT>(f1, u, seg * kSegSteps + 2, j);
+  __builtin_amdgcn_sched_barrier(0);
+  transpose_codes4<TT>(c, g);
+  mma_pair4<TT, 0>(acc, f0, c);
+  mma_pair4<TT, 1>(acc, f1, c);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Units of one run, in order: the shared slots' units, then the routed ones;
@@ -257,14 +356,26 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
     unit_decode(um, u, v, tg, s0, s1);
     const UnitOps ops = unit_ops<W13, TT>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
     v4f tot[TT];
-    segment_sum<TT, BS>(tot, ops, s0);
-    for (int sg = s0 + 1; sg < s1; ++sg) {
-      v4f p[TT];
-      segment_sum<TT, BS>(p, ops, sg);
+    if (ops.fp4) {
+      segment_sum_fp4<TT>(tot, ops, s0, g, j);
+      for (int sg = s0 + 1; sg < s1; ++sg) {
+        v4f p[TT];
+        segment_sum_fp4<TT>(p, ops, sg, g, j);
 #pragma unroll
-      for (int t = 0; t < TT; ++t)
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+          for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+      }
+    } else {
+      segment_sum<TT, BS>(tot, ops, s0);
+      for (int sg = s0 + 1; sg < s1; ++sg) {
+        v4f p[TT];
+        segment_sum<TT, BS>(p, ops, sg);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+      }
     }
     // w13 sums go to the slot's rows; w2 sums to the rows' output rows
     float* dst = part + (size_t)(um.split ? s0 : 0) * plane + ops.col0 + j;

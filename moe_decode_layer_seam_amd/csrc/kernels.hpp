@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_ext.h>
+
+#include "moe_decode.h"
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +22,7 @@ constexpr int kThreads = 256;      // blocks of the small kernels
 struct LayerDims {
   int H, E, K, I, Is, Imax, Mx;
   float eps, routed_scale;
+  int rfmt;  // routed expert weights: MOE_DECODE_ROUTED_E4M3 or _MXFP4
 };
 
 // The plan's device scratch, laid out for Mx token rows.
@@ -141,5 +144,7 @@ int gemm_waves(bool w13);  // waves per block of the GEMM
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13);
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
                                hipStream_t st);
+// MXFP4 of ngroups consecutive 32-value groups (rows of 32 columns).
+hipError_t launch_quant_weight_fp4(const float* w, int64_t ngroups, uint8_t* q, uint8_t* sc, hipStream_t st);
 
 }  // namespace moe

@@ -38,7 +38,37 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
   }
 }
 
+// MXFP4: one row and 32 columns per 8 lanes, 4 columns per lane; codes
+// [rows, cols/32], elements E2M1 two per byte, column 2i in the low nibble
+// (page "vllm.models.deepseek_v41.amd.mono.runner", MonoLayerWeights.check:
+// routed w13 / w2 fp4x2 with one code per row and 32 columns).
+__global__ __launch_bounds__(256) void quant_weight_fp4_kernel(const float* __restrict__ w, int64_t ngroups,
+                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  const int64_t stride = (int64_t)gridDim.x * 32;  // groups of 32 columns per sweep
+  for (int64_t grp = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); grp < ngroups; grp += stride) {
+    const int sub = threadIdx.x & 7;
+    const float4 v = *reinterpret_cast<const float4*>(w + grp * 32 + 4 * sub);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = group_max(amax, 8);
+    const int code = fp4_code(amax);
+    const float mul = mx_mul(code);
+    const uint32_t n0 = e2m1_rne(v.x * mul), n1 = e2m1_rne(v.y * mul);
+    const uint32_t n2 = e2m1_rne(v.z * mul), n3 = e2m1_rne(v.w * mul);
+    *reinterpret_cast<uint16_t*>(q + grp * 16 + 2 * sub) = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
+    if (sub == 0) sc[grp] = (uint8_t)code;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant_weight_fp4(const float* w, int64_t ngroups, uint8_t* q, uint8_t* sc, hipStream_t st) {
+  // every lane of a 256-thread block stays in its 8-lane group for the loop,
+  // whose trip count is uniform across the group
+  const int64_t blocks = (ngroups + 31) / 32;
+  const int grid = (int)(blocks < 16384 ? blocks : 16384);
+  hipLaunchKernelGGL(quant_weight_fp4_kernel, dim3(grid), dim3(256), 0, st, w, ngroups, q, sc);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
                                hipStream_t st) {

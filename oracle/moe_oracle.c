@@ -87,12 +87,14 @@ double orc_e4m3_value(uint8_t b) {
  * quantisers and the dot products a call to ldexp per element. */
 static double E4M3[256];
 static double POW2[256];
+static double E2M1[16];
 
 __attribute__((constructor)) static void orc_tables(void) {
   for (int b = 0; b < 256; ++b) {
     E4M3[b] = orc_e4m3_value((uint8_t)b);
     POW2[b] = ldexp(1.0, b - 127);
   }
+  for (int n = 0; n < 16; ++n) E2M1[n] = orc_e2m1_value((uint8_t)n);
 }
 
 uint8_t orc_e4m3_rne(double v) {
@@ -149,7 +151,7 @@ uint8_t orc_e2m1_rne(double v) {
   int best = 0;
   double bd = a;  /* distance to code 0 (value 0) */
   for (int c = 1; c < 8; ++c) {
-    double dist = fabs(a - orc_e2m1_value((uint8_t)c));
+    double dist = fabs(a - E2M1[c]);
     if (dist < bd || (dist == bd && (c & 1) == 0)) {
       best = c;
       bd = dist;
@@ -268,7 +270,7 @@ static double weight_value(int32_t fmt, const uint8_t* w, const uint8_t* ws,
   if (fmt == ORC_FMT_MXFP4) {
     uint8_t byte = w[(size_t)n * (K / 2) + k / 2];
     uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
-    return orc_e2m1_value(nib) * POW2[ws[(size_t)n * (K / 32) + k / 32]];
+    return E2M1[nib] * POW2[ws[(size_t)n * (K / 32) + k / 32]];
   }
   return mx_value(w[(size_t)n * K + k], ws[(size_t)(n / 32) * (K / 32) + k / 32]);
 }

@@ -31,14 +31,15 @@ def test_every_declared_symbol_is_exported():
     dict(hidden=100), dict(hidden=0), dict(hidden=32768), dict(experts=0), dict(experts=2048),
     dict(topk=0), dict(topk=9, experts=8), dict(topk=33, experts=64), dict(inter=96),
     dict(shared_inter=0), dict(max_tokens=0), dict(max_tokens=49), dict(rms_eps=-1.0),
-    dict(rms_eps=float("nan")), dict(routed_scale=float("inf")),
+    dict(rms_eps=float("nan")), dict(routed_scale=float("inf")), dict(routed_format=2),
+    dict(routed_format=-1),
 ])
 def test_plan_rejects_invalid_dims(bad):
     d = dict(hidden=256, experts=8, topk=2, inter=128, shared_inter=128, max_tokens=4,
-             rms_eps=1e-6, routed_scale=1.0)
+             rms_eps=1e-6, routed_scale=1.0, routed_format=0)
     d.update(bad)
     dims = mdl.Dims(d["hidden"], d["experts"], d["topk"], d["inter"], d["shared_inter"],
-                    d["max_tokens"], d["rms_eps"], d["routed_scale"])
+                    d["max_tokens"], d["rms_eps"], d["routed_scale"], d["routed_format"])
     h = ctypes.c_void_p()
     assert mdl.lib().moe_decode_plan(ctypes.byref(dims), None, ctypes.byref(h)) == mdl.EINVAL
     assert h.value is None
@@ -51,5 +52,6 @@ def test_null_handles_are_rejected():
     assert L.moe_decode_inspect(None, 0, ctypes.byref(p), ctypes.byref(n)) == mdl.EINVAL
     assert L.moe_decode_timing(None, 1) == mdl.EINVAL
     assert L.moe_decode_quantize_weight(None, 1, 32, 32, None, None, None) == mdl.EINVAL
+    assert L.moe_decode_quantize_weight_fp4(None, 1, 32, 32, None, None, None) == mdl.EINVAL
     L.moe_decode_destroy(None)
     assert mdl.strerror(mdl.ECAPTURE) == "called during stream capture"

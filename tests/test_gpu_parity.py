@@ -44,7 +44,7 @@ SMALL = [
 def _plan_for(cfg, max_tokens=None):
     return mdl.plan(cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"],
                     cfg["shared_inter"], max_tokens or cfg["m"], cfg["rms_eps"],
-                    cfg["routed_scale"])
+                    cfg["routed_scale"], routed=data.routed_of(cfg))
 
 
 def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
@@ -89,7 +89,19 @@ def _bf16_f64(bits):
     return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c["name"])
+# MXFP4 (E2M1 pairs, 1 x 32 codes) routed experts: odd K step counts (H 640,
+# I 128) leave one half of a weight line pair empty
+SMALL_FP4 = [dict(c, routed="mxfp4", name=c["name"] + "_fp4") for c in (
+    synth.CONFIGS[0],
+    _cfg(5, 512, 64, 6, 256, 128),
+    _cfg(13, 640, 100, 8, 128, 256),
+    _cfg(33, 256, 8, 8, 128, 128),
+    _cfg(48, 512, 64, 4, 256, 256),
+    _cfg(7, 256, 1000, 32, 128, 128),
+)]
+
+
+@pytest.mark.parametrize("cfg", SMALL + SMALL_FP4, ids=lambda c: c["name"])
 def test_parity_small(cfg):
     inp, w = data.build_layer(7, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
@@ -108,7 +120,7 @@ def test_parity_small(cfg):
             for j in range(cfg["topk"]):
                 e = r["ids"][t, j]
                 ref = oracle.expert(o["x8"][t], o["x8s"][t], w["w13"][e], w["w13_s"][e],
-                                    w["w2"][e], w["w2_s"][e])["a8"]
+                                    w["w2"][e], w["w2_s"][e], fmt=data.routed_of(cfg))["a8"]
                 got = a8[row[t, j], :cfg["inter"]]
                 same += int((got == ref).sum())
                 tot += ref.size
@@ -269,6 +281,26 @@ def test_quantize_weight_matches_oracle():
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
 
+def test_quantize_weight_fp4_matches_oracle():
+    w = synth.normal(14, 78, (2, 96, 320), 0.0, 0.02)
+    w[0, 0, :32] = 0.0                        # all-zero group: code 0
+    w[0, 1, 32:64] *= 1e-30                   # tiny group
+    w[1, 5, 100] = 300.0                      # a spike
+    w[1, 6, 7] = -1e-41                       # a subnormal
+    w[1, 7, 64:96] = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)  # ties (code 127)
+    q_ref = np.empty((2, 96, 160), np.uint8)
+    s_ref = np.empty((2, 96, 10), np.uint8)
+    for i in range(2):
+        q_ref[i], s_ref[i] = oracle.quant_weight_fp4(w[i])
+    wd = torch.from_numpy(w).cuda()
+    q = torch.empty((2, 96, 160), dtype=torch.uint8, device="cuda")
+    s = torch.empty((2, 96, 10), dtype=torch.uint8, device="cuda")
+    mdl.quantize_weight_fp4(wd, q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
 def test_run_rejects_bad_arguments_without_launching():
     cfg = _cfg(4, 256, 8, 2, 128, 128)
     inp, w = data.build_layer(13, cfg)
@@ -328,6 +360,29 @@ def _full_layer(idx):
 
 
 SAMPLES = {1: [0], 2: [0, 9, 15], 3: [0, 29, 47], 4: [0, 23, 47]}
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_parity_full_size_mxfp4(idx):
+    cfg = dict(synth.CONFIGS[idx], routed="mxfp4")
+    base = dict(synth.CONFIGS[3], routed="mxfp4")
+    key = "dsv41_fp4"
+    if key not in _FULL:
+        inp, w = data.build_layer(0, base, experts="picked")
+        _FULL[key] = (base, inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
+    _, inp_all, w, dinp_all, dw = _FULL[key]
+    m = cfg["m"]
+    inp = dict(inp_all, x=inp_all["x"][:m])
+    dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
+    h = _plan_for(cfg, max_tokens=48)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        _check_layer(cfg, h, inp, w, out, rows_ref=SAMPLES[idx])
+    finally:
+        mdl.destroy(h)
+    if idx == 3:
+        _FULL.pop(key, None)
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
