@@ -72,6 +72,8 @@ def lib():
         L.orc_mx_quant_row.argtypes = [_I, _P, _P, _P]
         L.orc_quant_weight.argtypes = [_I, _I, _P, _P, _P]
         L.orc_quant_weight_fp4.argtypes = [_I, _I, _P, _P, _P]
+        L.orc_fp4_code_index.argtypes = [_I, _I, _I]
+        L.orc_fp4_code_index.restype = ctypes.c_size_t
         L.orc_expert_fmt.argtypes = [_I, _I, _I] + [_P] * 9
         L.orc_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
         L.orc_router.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
@@ -182,12 +184,22 @@ def quant_weight_into(w, q_out: np.ndarray, s_out: np.ndarray) -> None:
     lib().orc_quant_weight(rows, cols, _p(w), _p(q_out), _p(s_out))
 
 
+def fp4_codes_shape(rows: int, cols: int) -> tuple:
+    """Shape of an MXFP4 matrix's blocked code array."""
+    return (rows // 16, (cols + 511) // 512, 16, 16)
+
+
+def fp4_code_index(cols: int, r: int, b: int) -> int:
+    return lib().orc_fp4_code_index(cols, r, b)
+
+
 def quant_weight_fp4(w) -> tuple[np.ndarray, np.ndarray]:
-    """fp32 [rows, cols] -> (E2M1 pairs [rows, cols/2] u8, E8M0 [rows, cols/32] u8)."""
+    """fp32 [rows, cols] -> (E2M1 pairs [rows, cols/2] u8, blocked E8M0 codes
+    [rows/16, ceil(cols/512), 16, 16] u8)."""
     w = _c(w, np.float32)
     rows, cols = w.shape
     q = np.empty((rows, cols // 2), np.uint8)
-    s = np.empty((rows, cols // 32), np.uint8)
+    s = np.empty(fp4_codes_shape(rows, cols), np.uint8)
     lib().orc_quant_weight_fp4(rows, cols, _p(w), _p(q), _p(s))
     return q, s
 
@@ -196,7 +208,7 @@ def quant_weight_fp4_into(w, q_out: np.ndarray, s_out: np.ndarray) -> None:
     w = _c(w, np.float32)
     rows, cols = w.shape
     assert q_out.flags.c_contiguous and s_out.flags.c_contiguous
-    assert q_out.shape == (rows, cols // 2) and s_out.shape == (rows, cols // 32)
+    assert q_out.shape == (rows, cols // 2) and s_out.shape == fp4_codes_shape(rows, cols)
     lib().orc_quant_weight_fp4(rows, cols, _p(w), _p(q_out), _p(s_out))
 
 

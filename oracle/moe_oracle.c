@@ -232,14 +232,24 @@ void orc_quant_weight(int32_t rows, int32_t cols, const float* w, uint8_t* q,
   free(amax);
 }
 
+size_t orc_fp4_code_index(int32_t cols, int32_t r, int32_t b) {
+  /* Blocked order of the MXFP4 codes: [rows/16][ceil(cols/512)][16][16]; the
+   * 16 x 16 codes of a 16-row, 512-column tile are one contiguous 256-byte
+   * block, row-major inside (the pages keep these codes in a shuffled order
+   * of their own too: [runner] MonoLayerWeights, w13_s "shuffle_scale"). */
+  int32_t nsg = (cols + 511) / 512;
+  return ((size_t)(r / 16) * nsg + (size_t)(b / 16)) * 256 + (size_t)(r % 16) * 16 + (size_t)(b % 16);
+}
+
 void orc_quant_weight_fp4(int32_t rows, int32_t cols, const float* w, uint8_t* q,
                           uint8_t* scales) {
   /* MXFP4 of a [rows, cols] fp32 weight: one E8M0 code per row and 32
-   * consecutive columns (scales [rows, cols/32] row-major), elements
-   * E2M1(w * 2^(127 - code)), two per byte: column 2i in the low nibble,
-   * column 2i + 1 in the high one ([runner] MonoLayerWeights.check: w13
-   * [E, 2I, H/2] fp4x2 with [E 2I, H/32] codes, w2 [E, H, I/2]). */
+   * consecutive columns, elements E2M1(w * 2^(127 - code)), two per byte:
+   * column 2i in the low nibble, column 2i + 1 in the high one ([runner]
+   * MonoLayerWeights.check: w13 [E, 2I, H/2] fp4x2, w2 [E, H, I/2]).  Codes
+   * in the blocked order of orc_fp4_code_index; padding codes are 0. */
   int32_t cb = cols / 32;
+  memset(scales, 0, (size_t)(rows / 16) * ((cols + 511) / 512) * 256);
   for (int32_t r = 0; r < rows; ++r)
     for (int32_t b = 0; b < cb; ++b) {
       const float* src = w + (size_t)r * cols + (size_t)b * 32;
@@ -247,7 +257,7 @@ void orc_quant_weight_fp4(int32_t rows, int32_t cols, const float* w, uint8_t* q
       for (int i = 0; i < 32; ++i)
         if (fabs((double)src[i]) > amax) amax = fabs((double)src[i]);
       int32_t code = orc_fp4_code(amax);
-      scales[(size_t)r * cb + b] = (uint8_t)code;
+      scales[orc_fp4_code_index(cols, r, b)] = (uint8_t)code;
       uint8_t* dst = q + (size_t)r * (cols / 2) + (size_t)b * 16;
       for (int i = 0; i < 16; ++i) {
         uint8_t lo = orc_e2m1_rne((double)src[2 * i] * POW2[254 - code]);
@@ -264,13 +274,13 @@ static double mx_value(uint8_t q, uint8_t code) {
 
 /* Weight element (n, k) of an [N, K] expert matrix, dequantised, in either
  * routed format: E4M3 with 32 x 32 blocks (codes [N/32, K/32]) or MXFP4 with
- * 1 x 32 blocks (two elements per byte, codes [N, K/32]). */
+ * 1 x 32 blocks (two elements per byte, codes in blocked order). */
 static double weight_value(int32_t fmt, const uint8_t* w, const uint8_t* ws,
                            int32_t K, int32_t n, int32_t k) {
   if (fmt == ORC_FMT_MXFP4) {
     uint8_t byte = w[(size_t)n * (K / 2) + k / 2];
     uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
-    return E2M1[nib] * POW2[ws[(size_t)n * (K / 32) + k / 32]];
+    return E2M1[nib] * POW2[ws[orc_fp4_code_index(K, n, k / 32)]];
   }
   return mx_value(w[(size_t)n * K + k], ws[(size_t)(n / 32) * (K / 32) + k / 32]);
 }
@@ -468,9 +478,11 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   /* per-expert strides of the routed tensors in their format */
   int32_t fmt = d->routed_format;
   size_t w13_e = fmt == ORC_FMT_MXFP4 ? (size_t)2 * I * (H / 2) : (size_t)2 * I * H;
-  size_t w13s_e = fmt == ORC_FMT_MXFP4 ? (size_t)2 * I * (H / 32) : (size_t)(2 * I / 32) * (H / 32);
+  size_t w13s_e = fmt == ORC_FMT_MXFP4 ? (size_t)(2 * I / 16) * ((H + 511) / 512) * 256
+                                       : (size_t)(2 * I / 32) * (H / 32);
   size_t w2_e = fmt == ORC_FMT_MXFP4 ? (size_t)H * (I / 2) : (size_t)H * I;
-  size_t w2s_e = fmt == ORC_FMT_MXFP4 ? (size_t)H * (I / 32) : (size_t)(H / 32) * (I / 32);
+  size_t w2s_e = fmt == ORC_FMT_MXFP4 ? (size_t)(H / 16) * ((I + 511) / 512) * 256
+                                      : (size_t)(H / 32) * (I / 32);
   for (int32_t t = 0; t < m; ++t) {
     const uint8_t* xq = q + (size_t)t * H;
     const uint8_t* xc = qc + (size_t)t * (H / 32);

@@ -20,6 +20,7 @@
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -89,9 +90,13 @@ void orc_mx_quant_row(int32_t n, const double* v, uint8_t* q, uint8_t* codes);
  * [rows/32, cols/32].  [runner] MonoLayerWeights.check / AttnWeights.check. */
 void orc_quant_weight(int32_t rows, int32_t cols, const float* w, uint8_t* q,
                       uint8_t* scales);
-/* MXFP4 of a [rows, cols] fp32 weight: codes [rows, cols/32] (one per row and
- * 32 columns, orc_fp4_code of their amax), elements E2M1 two per byte, column
- * 2i in the low nibble.  [runner] MonoLayerWeights.check (w13, w2 fp4x2). */
+/* Position of the code of row r, 32-column block b of an MXFP4 [rows, cols]
+ * matrix in its blocked code array [rows/16][ceil(cols/512)][16][16]. */
+size_t orc_fp4_code_index(int32_t cols, int32_t r, int32_t b);
+/* MXFP4 of a [rows, cols] fp32 weight (rows % 16 == 0): one code per row and
+ * 32 columns (orc_fp4_code of their amax) in the blocked order above, padding
+ * codes 0; elements E2M1 two per byte, column 2i in the low nibble.
+ * [runner] MonoLayerWeights.check (w13, w2 fp4x2). */
 void orc_quant_weight_fp4(int32_t rows, int32_t cols, const float* w, uint8_t* q,
                           uint8_t* scales);
 

@@ -36,9 +36,9 @@ def alloc_weights(cfg: dict) -> dict:
     if routed_of(cfg) == "mxfp4":
         routed = {
             "w13": np.zeros((E, 2 * I, H // 2), np.uint8),
-            "w13_s": np.zeros((E, 2 * I, H // 32), np.uint8),
+            "w13_s": np.zeros((E,) + oracle.fp4_codes_shape(2 * I, H), np.uint8),
             "w2": np.zeros((E, H, I // 2), np.uint8),
-            "w2_s": np.zeros((E, H, I // 32), np.uint8),
+            "w2_s": np.zeros((E,) + oracle.fp4_codes_shape(H, I), np.uint8),
         }
     else:
         routed = {

@@ -78,8 +78,11 @@ def test_fp4_quantiser_layout_and_nearest_values():
     w = rng.normal(0.0, 0.02, (64, 96)).astype(np.float32)
     w[3, 32:64] = 0.0                                    # an all-zero block: code 0
     w[7, :32] = np.float32([0.5, 1, 1.5, 2, 3, 4, 6, -6] * 4)  # exact at code 127
-    q, s = oracle.quant_weight_fp4(w)
-    assert q.shape == (64, 48) and s.shape == (64, 3)
+    q, sb = oracle.quant_weight_fp4(w)
+    # blocked codes: [row tile of 16][512-column segment][row in tile][32-column block in segment]
+    assert q.shape == (64, 48) and sb.shape == (4, 1, 16, 16)
+    assert np.all(sb[:, :, :, 3:] == 0)                  # padding past the 3 real blocks
+    s = sb.transpose(0, 2, 1, 3).reshape(64, 16)[:, :3]  # back to [row, block]
     assert s[3, 1] == 0 and np.all(q[3, 16:32] == 0)
     assert s[7, 0] == 127
     assert list(q[7, :4]) == [0x21, 0x43, 0x65, 0xF7]    # column 2i in the low nibble
@@ -88,6 +91,7 @@ def test_fp4_quantiser_layout_and_nearest_values():
         for b in range(3):
             blk = w[r, 32 * b:32 * b + 32].astype(np.float64)
             code = int(s[r, b])
+            assert code == sb[r // 16, 0, r % 16, b]
             assert code == oracle.fp4_code(float(np.abs(blk).max()))
             scale = 2.0 ** (127 - code)
             for i in range(32):
@@ -96,6 +100,29 @@ def test_fp4_quantiser_layout_and_nearest_values():
                 assert nib == _nearest_even(blk[i] * scale), (r, b, i)
                 # dequantised value within half a spacing (at most 1 unit at 2^(code-127))
                 assert abs(table[nib] / scale - blk[i]) <= 1.0 / scale
+
+
+def test_fp4_blocked_code_order():
+    # cols 1056: two whole 512-column segments and one of 32 columns, so each
+    # row tile holds three 256-byte blocks, the last with 15 padding columns
+    rows, cols = 48, 1056
+    w = np.zeros((rows, cols), np.float32)
+    for r in range(rows):
+        for b in range(cols // 32):
+            w[r, 32 * b + (r + b) % 32] = 6.0 * 2.0 ** ((r * 7 + b * 3) % 40 - 20)
+    q, sb = oracle.quant_weight_fp4(w)
+    assert sb.shape == (3, 3, 16, 16)
+    flat = sb.reshape(-1)
+    seen = set()
+    for r in range(rows):
+        for b in range(cols // 32):
+            pos = ((r // 16) * 3 + b // 16) * 256 + (r % 16) * 16 + b % 16
+            assert oracle.fp4_code_index(cols, r, b) == pos
+            assert flat[pos] == 127 + (r * 7 + b * 3) % 40 - 20, (r, b)
+            seen.add(pos)
+    pad = np.ones(flat.size, bool)
+    pad[list(seen)] = False
+    assert pad.sum() == 3 * 15 * 16 and np.all(flat[pad] == 0)
 
 
 def test_fp4_unit_scale_round_trip_and_plain_matmul():
@@ -114,7 +141,8 @@ def test_fp4_unit_scale_round_trip_and_plain_matmul():
     w2f[:, 0] = 6.0
     q13, s13 = oracle.quant_weight_fp4(w13f.astype(np.float32))
     q2, s2 = oracle.quant_weight_fp4(w2f.astype(np.float32))
-    assert np.all(s13 == 127) and np.all(s2 == 127)
+    assert np.all(s13[..., :2] == 127) and np.all(s2[..., :1] == 127)  # the real blocks
+    assert np.all(s13[..., 2:] == 0) and np.all(s2[..., 1:] == 0)      # padding
     assert np.array_equal(torch_ref.fp4_dequant(q13, s13).numpy(), w13f)
     assert np.array_equal(torch_ref.fp4_dequant(q2, s2).numpy(), w2f)
     got = oracle.expert(x8, x8s, q13, s13, q2, s2, fmt="mxfp4")

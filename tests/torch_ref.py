@@ -72,12 +72,15 @@ def block_dequant(q, s) -> torch.Tensor:
 
 
 def fp4_dequant(q, s) -> torch.Tensor:
-    """[N, K/2] E2M1 pairs (column 2i in the low nibble) with [N, K/32] codes
-    -> float64 [N, K]."""
+    """[N, K/2] E2M1 pairs (column 2i in the low nibble) with blocked codes
+    [N/16, ceil(K/512), 16, 16] (tile of 16 rows, 512-column segment, row,
+    32-column block) -> float64 [N, K]."""
     b = torch.from_numpy(np.ascontiguousarray(q, np.uint8)).to(torch.int64)
     v = torch.stack([E2M1[b & 0xF], E2M1[b >> 4]], dim=-1).reshape(b.shape[0], -1)
-    sc = torch.from_numpy(np.ascontiguousarray(s, np.uint8)).to(F64).repeat_interleave(32, 1)
-    return v * torch.exp2(sc - 127)
+    N, K = v.shape
+    c = torch.from_numpy(np.ascontiguousarray(s, np.uint8)).to(F64)  # [N/16, nsg, 16, 16]
+    c = c.permute(0, 2, 1, 3).reshape(N, -1)[:, :K // 32]           # [N, K/32]
+    return v * torch.exp2(c.repeat_interleave(32, 1) - 127)
 
 
 def dequant(q, s, fmt: str) -> torch.Tensor:
