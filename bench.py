@@ -59,9 +59,9 @@ def make_weights(cfg: dict, seed: int, dev):
     if fp4:
         routed = {
             "w13": torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev),
-            "w13_s": torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=dev),
+            "w13_s": torch.empty((E,) + mdl.fp4_codes_shape(2 * I, H), dtype=torch.uint8, device=dev),
             "w2": torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev),
-            "w2_s": torch.empty((E, H, I // 32), dtype=torch.uint8, device=dev),
+            "w2_s": torch.empty((E,) + mdl.fp4_codes_shape(H, I), dtype=torch.uint8, device=dev),
         }
     else:
         routed = {

@@ -57,8 +57,11 @@ extern "C" {
  * 32 x 32 blocks). */
 #define MOE_DECODE_ROUTED_E4M3 0  /* E4M3 [N, K] with E8M0 codes [N/32, K/32] */
 #define MOE_DECODE_ROUTED_MXFP4 1 /* E2M1 pairs [N, K/2] (column 2i in the low
-                                     nibble) with E8M0 codes [N, K/32]: the
-                                     pages' A8W4 routed experts
+                                     nibble) with one E8M0 code per row and
+                                     32 columns, in the blocked order
+                                     [N/16][ceil(K/512)][16][16] (16-row tile,
+                                     512-column segment, row, 32-column block):
+                                     the pages' A8W4 routed experts
                                      (MonoLayerWeights.check, fp4x2) */
 
 /* Layer dimensions, fixed when the plan is made.
@@ -109,7 +112,8 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  *   d_w2      E4M3 [E, H, I]
  *   d_w2_s    E8M0 [E, H/32, I/32]
  *             (MXFP4 routed experts: w13 [E, 2I, H/2] with codes
- *             [E, 2I, H/32], w2 [E, H, I/2] with codes [E, H, I/32])
+ *             [E, 2I/16, H/512, 16, 16], w2 [E, H, I/2] with codes
+ *             [E, H/16, ceil(I/512), 16, 16], blocked as above)
  *   d_sgu     E4M3 [2Is, H]          shared expert gate/up
  *   d_sgu_s   E8M0 [2Is/32, H/32]
  *   d_sw2     E4M3 [H, Is]           shared expert down
@@ -213,10 +217,13 @@ int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows,
 
 /* Weight preparation for MXFP4 routed experts: quantise `count` back-to-back
  * fp32 [rows, cols] matrices to E2M1 pairs [rows, cols/2] (column 2i in the
- * low nibble) with one E8M0 code per row and 32 columns ([rows, cols/32]).
- * Code = the smallest c in [0, 254] with amax <= 6 * 2^(c-127); values
- * rounded to nearest, ties to the even mantissa bit, after scaling by
- * 2^(127 - code).  cols a multiple of 32; pointers 16-byte aligned. */
+ * low nibble) with one E8M0 code per row and 32 columns, stored in the
+ * blocked order [rows/16][ceil(cols/512)][16][16] per matrix (the codes of a
+ * 16-row, 512-column tile are one contiguous 256-byte block, row-major;
+ * padding codes of a ragged last segment are 0).  Code = the smallest c in
+ * [0, 254] with amax <= 6 * 2^(c-127); values rounded to nearest, ties to
+ * the even mantissa bit, after scaling by 2^(127 - code).  rows a multiple
+ * of 16, cols a multiple of 32; pointers 16-byte aligned. */
 int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows,
                                    int32_t cols, void* d_q, void* d_scales,
                                    void* stream);

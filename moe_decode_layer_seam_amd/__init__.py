@@ -172,9 +172,9 @@ def run(handle: int, dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s,
         _tensor(gate_w, "gate_w", (E, H), torch.bfloat16),
         _tensor(bias, "bias", (E,), torch.float32),
         *((_tensor(w13, "w13", (E, 2 * I, H // 2), torch.uint8),
-           _tensor(w13_s, "w13_s", (E, 2 * I, H // 32), torch.uint8),
+           _tensor(w13_s, "w13_s", (E,) + fp4_codes_shape(2 * I, H), torch.uint8),
            _tensor(w2, "w2", (E, H, I // 2), torch.uint8),
-           _tensor(w2_s, "w2_s", (E, H, I // 32), torch.uint8)) if fp4 else
+           _tensor(w2_s, "w2_s", (E,) + fp4_codes_shape(H, I), torch.uint8)) if fp4 else
           (q(w13, "w13", (E, 2 * I, H)), _tensor(w13_s, "w13_s", (E, 2 * I // 32, H // 32), torch.uint8),
            q(w2, "w2", (E, H, I)), _tensor(w2_s, "w2_s", (E, H // 32, I // 32), torch.uint8))),
         q(sgu, "sgu", (2 * Is, H)), _tensor(sgu_s, "sgu_s", (2 * Is // 32, H // 32), torch.uint8),
@@ -255,17 +255,26 @@ def destroy(handle: int) -> None:
     lib().moe_decode_destroy(handle)
 
 
+def fp4_codes_shape(rows: int, cols: int) -> tuple:
+    """Shape of the E8M0 code array of one MXFP4 [rows, cols] matrix: blocked
+    [rows/16, ceil(cols/512), 16, 16] (16-row tile, 512-column segment, row,
+    32-column block)."""
+    return (rows // 16, (cols + 511) // 512, 16, 16)
+
+
 def quantize_weight_fp4(w: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
     """moe_decode_quantize_weight_fp4: fp32 [..., rows, cols] -> E2M1 pairs q
-    (uint8 [..., rows, cols/2]) and E8M0 scales (uint8 [..., rows, cols/32])."""
+    (uint8 [..., rows, cols/2]) and blocked E8M0 codes (uint8 [...,
+    *fp4_codes_shape(rows, cols)])."""
     rows, cols = w.shape[-2], w.shape[-1]
     count = w.numel() // (rows * cols)
     if w.dtype != torch.float32 or not w.is_contiguous() or not w.is_cuda:
         raise ValueError("w: contiguous float32 on the GPU required")
     if tuple(q.shape) != tuple(w.shape[:-1]) + (cols // 2,) or q.dtype != torch.uint8 or not q.is_contiguous():
         raise ValueError("q: uint8 [..., rows, cols/2]")
-    if tuple(scales.shape) != tuple(w.shape[:-1]) + (cols // 32,) or scales.dtype != torch.uint8:
-        raise ValueError("scales: uint8 [..., rows, cols/32]")
+    if (tuple(scales.shape) != tuple(w.shape[:-2]) + fp4_codes_shape(rows, cols) or scales.dtype != torch.uint8
+            or not scales.is_contiguous()):
+        raise ValueError("scales: uint8 [..., rows/16, ceil(cols/512), 16, 16]")
     rc = lib().moe_decode_quantize_weight_fp4(w.data_ptr(), count, rows, cols, q.data_ptr(),
                                               scales.data_ptr(), _stream_ptr(stream))
     _check(rc, "moe_decode_quantize_weight_fp4")

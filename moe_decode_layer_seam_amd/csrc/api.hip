@@ -414,10 +414,9 @@ int moe_decode_quantize_weight(const float* d_w, int32_t count, int32_t rows, in
 
 int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows, int32_t cols, void* d_q,
                                    void* d_scales, void* stream) {
-  if (count < 1 || rows < 1 || cols < 32 || cols % 32) return MOE_DECODE_EINVAL;
+  if (count < 1 || rows < 16 || rows % 16 || cols < 32 || cols % 32) return MOE_DECODE_EINVAL;
   if (!aligned16(d_w) || !aligned16(d_q) || d_scales == nullptr) return MOE_DECODE_EINVAL;
-  const int64_t ngroups = (int64_t)count * rows * (cols / 32);
-  hipError_t e = launch_quant_weight_fp4(d_w, ngroups, static_cast<uint8_t*>(d_q),
+  hipError_t e = launch_quant_weight_fp4(d_w, count, rows, cols, static_cast<uint8_t*>(d_q),
                                          static_cast<uint8_t*>(d_scales), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "quantize launch");
   return MOE_DECODE_OK;

@@ -66,7 +66,7 @@ struct UnitOps {
   rsrc_t w, ws, a, as;
   uint32_t wsoff, wlane, row8, tstride, ssoff, sstride, slane, alane, aslane;
   int row0, c, col0, nsteps;
-  int fp4;  // weights as E2M1 pairs with per-row 32-column codes
+  int fp4;  // weights as E2M1 pairs with per-row 32-column codes, blocked
 };
 
 template <bool W13, int TT>
@@ -85,25 +85,29 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
   const uint32_t rowb = u.fp4 ? G.K / 2 : G.K;
   if (W13) {
     W = shared ? in.sgu : in.w13 + (size_t)ex * 2 * d.I * (d.H / (u.fp4 ? 2 : 1));
-    WS = shared ? in.sgu_s : in.w13_s + (size_t)ex * 2 * d.I * (d.H / 32) / (u.fp4 ? 1 : 32);
+    WS = shared ? in.sgu_s : in.w13_s + (size_t)ex * (u.fp4 ? (size_t)(2 * d.I / 16) * G.nseg * 256
+                                                          : (size_t)(2 * d.I / 32) * (d.H / 32));
   } else {
     W = shared ? in.sw2 : in.w2 + (size_t)ex * d.H * (d.I / (u.fp4 ? 2 : 1));
-    WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * d.H * (d.I / 32) / (u.fp4 ? 1 : 32);
+    WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * (u.fp4 ? (size_t)(d.H / 16) * G.nseg * 256
+                                                         : (size_t)(d.H / 32) * (d.I / 32));
   }
   u.row0 = slot.y;
   u.c = slot.z;
   u.col0 = 16 * TT * tgroup;
   u.nsteps = G.K / 128;
   u.w = make_rsrc(W, (uint32_t)N * rowb);
-  u.ws = make_rsrc(WS, (uint32_t)(u.fp4 ? N : N / 32) * (G.K / 32));
+  u.ws = make_rsrc(WS, u.fp4 ? (uint32_t)G.tiles * G.nseg * 256 : (uint32_t)(N / 32) * (G.K / 32));
   u.wsoff = (uint32_t)u.col0 * rowb;
   u.tstride = (uint32_t)16 * rowb;
   u.wlane = (uint32_t)(j & 7) * rowb + (j < 8 ? 16 * g : 64 + 16 * g);
   u.row8 = (uint32_t)8 * rowb;
   if (u.fp4) {
-    u.ssoff = (uint32_t)u.col0 * (G.K / 32);       // the tile group's first row
-    u.sstride = (uint32_t)16 * (G.K / 32);         // per tile
-    u.slane = (uint32_t)j * (G.K / 32) + g;        // the lane's row, its K block
+    // codes blocked [tile][segment][16 rows][16 blocks]: 256 bytes per tile
+    // and segment
+    u.ssoff = (uint32_t)(u.col0 / 16) * G.nseg * 256;  // the tile group's first tile
+    u.sstride = (uint32_t)G.nseg * 256;                // per tile
+    u.slane = (uint32_t)j * 16 + 4 * g;                // the lane's row, blocks 4 g .. 4 g + 3
   } else {
     u.ssoff = (uint32_t)(u.col0 / 32) * (G.K / 32);  // the first tile pair's 32-row code block
     u.sstride = (uint32_t)(G.K / 32);
@@ -196,9 +200,9 @@ template <int TT>
 __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int seg, int g) {
   const int st = seg * kSegSteps + g;  // the step whose codes this lane fetches
   const bool ok = st < u.nsteps;
-  // slane = j * (K/32) + g: the row's code of block g; this load wants blocks
-  // 4 g .. 4 g + 3 of step seg * 4 + g, i.e. bytes 16 seg + 4 g .. + 4
-  const uint32_t bo = ok ? u.slane - g + 16 * seg + 4 * g : kNoRow;
+  // the lane's row, blocks 4 g .. 4 g + 3 of the segment (step seg * 4 + g):
+  // the whole wave reads the segment's 256-byte code block of each tile
+  const uint32_t bo = ok ? u.slane + 256 * seg : kNoRow;
 #pragma unroll
   for (int t = 0; t < TT; ++t) c.b[t] = __builtin_amdgcn_raw_buffer_load_b32(u.ws, (int)bo, (int)(u.ssoff + t * u.sstride), 0);
   c.a = __builtin_amdgcn_raw_buffer_load_b32(u.as, (int)(ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow), 0, 0);

@@ -144,7 +144,9 @@ int gemm_waves(bool w13);  // waves per block of the GEMM
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13);
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
                                hipStream_t st);
-// MXFP4 of ngroups consecutive 32-value groups (rows of 32 columns).
-hipError_t launch_quant_weight_fp4(const float* w, int64_t ngroups, uint8_t* q, uint8_t* sc, hipStream_t st);
+// MXFP4 of count [rows, cols] matrices (rows % 16 == 0, cols % 32 == 0):
+// E2M1 pairs and blocked codes [rows/16][ceil(cols/512)][16][16] each.
+hipError_t launch_quant_weight_fp4(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
+                                   hipStream_t st);
 
 }  // namespace moe

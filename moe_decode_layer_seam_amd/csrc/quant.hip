@@ -41,9 +41,12 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
 // MXFP4: one row and 32 columns per 8 lanes, 4 columns per lane; codes
 // [rows, cols/32], elements E2M1 two per byte, column 2i in the low nibble
 // (page "vllm.models.deepseek_v41.amd.mono.runner", MonoLayerWeights.check:
-// routed w13 / w2 fp4x2 with one code per row and 32 columns).
+// routed w13 / w2 fp4x2 with one code per row and 32 columns; codes in a
+// blocked order, see the kernel).
 __global__ __launch_bounds__(256) void quant_weight_fp4_kernel(const float* __restrict__ w, int64_t ngroups,
-                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+                                                               int rows, int cols, uint8_t* __restrict__ q,
+                                                               uint8_t* __restrict__ sc) {
+  const int cb = cols / 32, nsg = (cols + 511) / 512;
   const int64_t stride = (int64_t)gridDim.x * 32;  // groups of 32 columns per sweep
   for (int64_t grp = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); grp < ngroups; grp += stride) {
     const int sub = threadIdx.x & 7;
@@ -55,18 +58,33 @@ __global__ __launch_bounds__(256) void quant_weight_fp4_kernel(const float* __re
     const uint32_t n0 = e2m1_rne(v.x * mul), n1 = e2m1_rne(v.y * mul);
     const uint32_t n2 = e2m1_rne(v.z * mul), n3 = e2m1_rne(v.w * mul);
     *reinterpret_cast<uint16_t*>(q + grp * 16 + 2 * sub) = (uint16_t)(n0 | (n1 << 4) | (n2 << 8) | (n3 << 12));
-    if (sub == 0) sc[grp] = (uint8_t)code;
+    if (sub == 0) {
+      // blocked code order [rows/16][nsg][16][16] per matrix: the codes of a
+      // 16-row tile's 512-column segment are one 256-byte block
+      const int64_t er = grp / cb;  // matrix * rows + row
+      const int b = (int)(grp - er * cb), r = (int)(er % rows);
+      const int64_t e = er / rows;
+      const int64_t at = ((e * (rows / 16) + r / 16) * nsg + b / 16) * 256 + (r % 16) * 16 + b % 16;
+      sc[at] = (uint8_t)code;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_quant_weight_fp4(const float* w, int64_t ngroups, uint8_t* q, uint8_t* sc, hipStream_t st) {
+hipError_t launch_quant_weight_fp4(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
+                                   hipStream_t st) {
+  if ((cols / 32) % 16) {  // a ragged last segment: its padding codes are 0
+    const size_t nbytes = (size_t)count * (rows / 16) * ((cols + 511) / 512) * 256;
+    const hipError_t e = hipMemsetAsync(sc, 0, nbytes, st);
+    if (e != hipSuccess) return e;
+  }
   // every lane of a 256-thread block stays in its 8-lane group for the loop,
   // whose trip count is uniform across the group
+  const int64_t ngroups = (int64_t)count * rows * (cols / 32);
   const int64_t blocks = (ngroups + 31) / 32;
   const int grid = (int)(blocks < 16384 ? blocks : 16384);
-  hipLaunchKernelGGL(quant_weight_fp4_kernel, dim3(grid), dim3(256), 0, st, w, ngroups, q, sc);
+  hipLaunchKernelGGL(quant_weight_fp4_kernel, dim3(grid), dim3(256), 0, st, w, ngroups, rows, cols, q, sc);
   return hipGetLastError();
 }
 

@@ -53,5 +53,6 @@ def test_null_handles_are_rejected():
     assert L.moe_decode_timing(None, 1) == mdl.EINVAL
     assert L.moe_decode_quantize_weight(None, 1, 32, 32, None, None, None) == mdl.EINVAL
     assert L.moe_decode_quantize_weight_fp4(None, 1, 32, 32, None, None, None) == mdl.EINVAL
+    assert L.moe_decode_quantize_weight_fp4(None, 1, 24, 32, None, None, None) == mdl.EINVAL  # rows % 16
     L.moe_decode_destroy(None)
     assert mdl.strerror(mdl.ECAPTURE) == "called during stream capture"

@@ -288,13 +288,14 @@ def test_quantize_weight_fp4_matches_oracle():
     w[1, 5, 100] = 300.0                      # a spike
     w[1, 6, 7] = -1e-41                       # a subnormal
     w[1, 7, 64:96] = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)  # ties (code 127)
+    # 320 columns: one ragged 512-column segment, so 6 of each row's 16 codes are padding
     q_ref = np.empty((2, 96, 160), np.uint8)
-    s_ref = np.empty((2, 96, 10), np.uint8)
+    s_ref = np.empty((2, 6, 1, 16, 16), np.uint8)
     for i in range(2):
         q_ref[i], s_ref[i] = oracle.quant_weight_fp4(w[i])
     wd = torch.from_numpy(w).cuda()
     q = torch.empty((2, 96, 160), dtype=torch.uint8, device="cuda")
-    s = torch.empty((2, 96, 10), dtype=torch.uint8, device="cuda")
+    s = torch.full((2, 6, 1, 16, 16), 0xAB, dtype=torch.uint8, device="cuda")  # padding must be cleared
     mdl.quantize_weight_fp4(wd, q, s)
     torch.cuda.synchronize()
     assert np.array_equal(s.cpu().numpy(), s_ref)
