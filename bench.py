@@ -145,11 +145,12 @@ def kernel_source_hash() -> str:
     return hsh.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per w13 launch from the counter summary under profiles/
-    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
-    when there is none for this workload or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"w13_{workload}_traffic.txt")
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the counter summary under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when there is none for this workload or the kernel
+    sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -189,6 +190,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--routed", choices=("e4m3", "mxfp4"), default="e4m3",
                     help="routed experts' weight format (the shared expert is E4M3)")
+    ap.add_argument("--schedule", choices=("launches", "fused"), default="launches",
+                    help="expert GEMMs as one fused launch or as w13, act and w2 launches")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -228,7 +231,9 @@ def main() -> int:
     outs = [torch.empty((m, H), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     print(f"[bench] weights ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    h = mdl.plan(H, E, K, I, Is, m, cfg["rms_eps"], cfg["routed_scale"], routed=args.routed)
+    h = mdl.plan(H, E, K, I, Is, m, cfg["rms_eps"], cfg["routed_scale"], routed=args.routed,
+                 schedule=args.schedule)
+    fused = args.schedule == "fused"
     stream = torch.cuda.current_stream()
 
     def step(c):
@@ -320,7 +325,7 @@ def main() -> int:
         step(i % copies)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("seam", "logits", "route", "w13", "act", "w2", "combine"):
+    for k in ("seam", "logits", "route") + (("experts",) if fused else ("w13", "act", "w2")) + ("combine",):
         tot, runs = mdl.timing_read(h, k)
         kern[k] = tot / max(1, runs)
     mdl.timing(h, False)
@@ -330,15 +335,22 @@ def main() -> int:
     tiles = int(sum(-(-int(c) // 16) for c in counts if c > 0)) + -(-m // 16)
     row_occupancy = (m * K + m) / (16 * tiles)
 
-    # algorithmic bytes of the dominant kernel (w13) per launch: every active
-    # expert's gate/up weights and codes (shared expert included) and the
-    # MXFP8 rows it multiplies them with
+    # algorithmic bytes per launch of the dominant kernel (the fused expert
+    # launch, else w13): every active expert's weights and codes (shared
+    # expert included) and the MXFP8 rows they are multiplied with
     steps_U = [U[i % copies] for i in range(args.steps)]
     avg_U = sum(steps_U) / len(steps_U)
     w13_bytes = avg_U * eb["w13"] + ebs["w13"] + m * (H + H // 32)
     expert_step_bytes = avg_U * (eb["w13"] + eb["w2"]) + ebs["w13"] + ebs["w2"]
-    achieved = w13_bytes / (kern["w13"] * 1e-3) / 1e9
     w2_bytes = avg_U * eb["w2"] + ebs["w2"] + (m * K + m) * (max(I, Is) + max(I, Is) // 32)
+    if fused:
+        dom, dom_bytes = "experts", w13_bytes + w2_bytes
+        kernel_gbs = {"experts": dom_bytes / (kern["experts"] * 1e-3) / 1e9}
+    else:
+        dom, dom_bytes = "w13", w13_bytes
+        kernel_gbs = {"w13": w13_bytes / (kern["w13"] * 1e-3) / 1e9,
+                      "w2": w2_bytes / (kern["w2"] * 1e-3) / 1e9}
+    achieved = kernel_gbs[dom]
 
     res = {
         "metric": METRIC,
@@ -356,7 +368,7 @@ def main() -> int:
         "config": {"workload": f"{cfg['name']}: M={m} token rows, hidden {H}, {E} routed experts top-{K}, "
                                f"intermediate {I}, shared expert {Is}, " + ("E4M3 weights with 32x32 E8M0 blocks" if args.routed == "e4m3" else
                                     "routed experts MXFP4 (E2M1, 1x32 E8M0), shared expert E4M3 32x32"),
-                   "tokens": m, "mode": args.mode, "weight_copies": copies},
+                   "tokens": m, "mode": args.mode, "weight_copies": copies, "schedule": args.schedule},
         "us_per_layer": ms_step * 1e3,
         "batch_us_per_layer": batch_us,
         "median_batch_us_per_layer": batch_us[len(batch_us) // 2],
@@ -366,12 +378,12 @@ def main() -> int:
         "expert_hbm_frac": expert_step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "active_experts_avg": avg_U,
         "kernel_us": {k: v * 1e3 for k, v in kern.items()},
-        "kernel_gbs": {"w13": achieved, "w2": w2_bytes / (kern["w2"] * 1e-3) / 1e9},
+        "kernel_gbs": kernel_gbs,
         "wall_s": wall,
-        "roofline": {"bound": "hbm", "kernel": "w13", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg["name"] + ("" if args.routed == "e4m3" else "_mxfp4")),
-                     "algorithmic_bytes": w13_bytes},
+                     "traffic": measured_traffic(dom, cfg["name"] + ("" if args.routed == "e4m3" else "_mxfp4")),
+                     "algorithmic_bytes": dom_bytes},
     }
     mdl.destroy(h)
     graphs.clear()

@@ -64,6 +64,20 @@ extern "C" {
                                      the pages' A8W4 routed experts
                                      (MonoLayerWeights.check, fp4x2) */
 
+/* How a run schedules the expert GEMMs.  LAUNCHES (the default): w13, the
+ * SiLU*up requantisation (act) and w2 as three launches.  FUSED: the three
+ * in one launch of one block per CU, each w2 work unit waiting on
+ * device-scope counters for its expert's a8 instead of on a launch boundary
+ * (the pages' persistent MoE launch with device counters: [layer] run_ffn,
+ * build_mono_ffn; [device] atomic_add_dev).  Both give the same output bits.
+ * FUSED assumes that all its blocks can be resident at once (no concurrent
+ * work holds CUs for its whole duration); a wait that runs past 100 ms flags
+ * the run (MOE_DECODE_TAP_STATUS) and goes on.  On MI355X it is the slower
+ * of the two: a hand-off between CUs through device memory waits behind the
+ * weight stream's queued reads, which costs more than a launch boundary. */
+#define MOE_DECODE_SCHEDULE_LAUNCHES 0
+#define MOE_DECODE_SCHEDULE_FUSED 1
+
 /* Layer dimensions, fixed when the plan is made.
  *   hidden        H, a multiple of 128 (the scaled MFMA's K step), <= 16384
  *   experts       E routed experts, 1..1024
@@ -73,7 +87,8 @@ extern "C" {
  *   max_tokens    largest m a run may pass, 1..48
  *   rms_eps       RMSNorm epsilon (added to mean(x^2) in double precision)
  *   routed_scale  factor applied to the renormalised routing weights
- *   routed_format MOE_DECODE_ROUTED_E4M3 or MOE_DECODE_ROUTED_MXFP4 */
+ *   routed_format MOE_DECODE_ROUTED_E4M3 or MOE_DECODE_ROUTED_MXFP4
+ *   schedule      MOE_DECODE_SCHEDULE_LAUNCHES or MOE_DECODE_SCHEDULE_FUSED */
 typedef struct moe_decode_dims {
   int32_t hidden;
   int32_t experts;
@@ -84,6 +99,7 @@ typedef struct moe_decode_dims {
   float rms_eps;
   float routed_scale;
   int32_t routed_format;
+  int32_t schedule;
 } moe_decode_dims;
 
 typedef struct moe_decode_plan_s* moe_decode_handle;
@@ -149,7 +165,10 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
  *                               ascending, then token ascending
  *   ROW_TOK   i32  [R]          token of each row
  *   A8        u8   [R, Imax]    E4M3 SiLU*up intermediate (Imax = max(I, Is))
- *   A8S       u8   [R, Imax/32] its E8M0 codes */
+ *   A8S       u8   [R, Imax/32] its E8M0 codes
+ *   STATUS    u32  [1]          0, or nonzero when a wait of the fused
+ *                               expert launch timed out (the output is then
+ *                               not valid) */
 enum moe_decode_tap {
   MOE_DECODE_TAP_NORMED = 0,
   MOE_DECODE_TAP_X8 = 1,
@@ -161,7 +180,8 @@ enum moe_decode_tap {
   MOE_DECODE_TAP_PAIR_ROW = 7,
   MOE_DECODE_TAP_ROW_TOK = 8,
   MOE_DECODE_TAP_A8 = 9,
-  MOE_DECODE_TAP_A8S = 10
+  MOE_DECODE_TAP_A8S = 10,
+  MOE_DECODE_TAP_STATUS = 11
 };
 int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
                        const void** d_ptr, size_t* bytes);
@@ -172,7 +192,8 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * moe_decode_timing(plan, 1) starts recording (and clears the totals), 0
  * stops.  While on, moe_decode_run must not be captured into a graph.
  * moe_decode_timing_read sums the elapsed milliseconds of kernel `kernel` (0
- * seam, 1 logits, 2 route, 3 w13, 4 act, 5 w2, 6 combine) over the recorded
+ * seam, 1 logits, 2 route, 3 w13, 4 act, 5 w2, 6 combine, 7 experts: the
+ * fused w13 + act + w2 launch) over the recorded
  * runs that launched it, and sets *runs to their number; it synchronises
  * with the recorded events.  (Steps of m <= 4 rows compute the logits inside
  * the seam launch and do not launch `logits`.) */
@@ -187,13 +208,13 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   logits: 0 start, 1 end
  *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
  *          4 plan written (3-4 only in the last block)
- *   w13, w2:      0 start, 3 + w: wave w of the block done
+ *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end
  *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
  * Unwritten points keep stale values.  moe_decode_timeline_read copies the
  * last run's records of kernel `kernel` (0 seam, 1 logits, 2 route, 3 w13,
- * 4 act, 5 w2, 6 combine) as
+ * 4 act, 5 w2, 6 combine, 7 experts) as
  * u64 [blocks][8] into h_out (n entries available), sets *blocks, and
  * synchronises the device. */
 int moe_decode_timeline(moe_decode_handle plan, int32_t on);

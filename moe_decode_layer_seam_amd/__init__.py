@@ -25,12 +25,15 @@ OK, EINVAL, ENOMEM, EHIP, ECAPTURE = 0, -1, -2, -3, -4
 MAX_TOKENS = 48
 
 TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
-        "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10}
-KERNELS = {"seam": 0, "logits": 1, "route": 2, "w13": 3, "act": 4, "w2": 5, "combine": 6}
+        "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10, "status": 11}
+KERNELS = {"seam": 0, "logits": 1, "route": 2, "w13": 3, "act": 4, "w2": 5, "combine": 6,
+           "experts": 7}
 
 
 # routed expert weight formats (moe_decode.h MOE_DECODE_ROUTED_*)
 ROUTED = {"e4m3": 0, "mxfp4": 1}
+# expert GEMM schedules (MOE_DECODE_SCHEDULE_*)
+SCHEDULES = {"launches": 0, "fused": 1}
 
 
 class Dims(ctypes.Structure):
@@ -39,7 +42,7 @@ class Dims(ctypes.Structure):
                 ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("routed_scale", ctypes.c_float),
-                ("routed_format", ctypes.c_int32)]
+                ("routed_format", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 class MoeDecodeError(RuntimeError):
@@ -128,11 +131,13 @@ def _check(rc: int, what: str, handle=None) -> None:
 
 def plan(hidden: int, experts: int, topk: int, inter: int, shared_inter: int,
          max_tokens: int = MAX_TOKENS, rms_eps: float = 1e-6,
-         routed_scale: float = 1.0, stream=None, routed: str = "e4m3") -> int:
+         routed_scale: float = 1.0, stream=None, routed: str = "e4m3",
+         schedule: str = "launches") -> int:
     """moe_decode_plan: returns an opaque handle (int).  routed: the routed
-    experts' weight format, "e4m3" or "mxfp4"."""
+    experts' weight format, "e4m3" or "mxfp4"; schedule: "launches" (w13,
+    act and w2 as three launches) or "fused" (one launch)."""
     d = Dims(hidden, experts, topk, inter, shared_inter, max_tokens, rms_eps, routed_scale,
-             ROUTED[routed])
+             ROUTED[routed], SCHEDULES[schedule])
     h = _P()
     _check(lib().moe_decode_plan(ctypes.byref(d), _stream_ptr(stream), ctypes.byref(h)),
            "moe_decode_plan")

@@ -50,7 +50,8 @@ struct moe_decode_plan_s {
   void* base = nullptr;
   Scratch s{};
   int last_m = 0;
-  int last_grid[kKernels] = {0, 0, 0, 0, 0, 0, 0};
+  int last_grid[kKernels] = {};
+  bool fused = false;  // MOE_DECODE_SCHEDULE_FUSED
   bool timeline = false;
   uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
   std::string err = "no error";
@@ -58,8 +59,8 @@ struct moe_decode_plan_s {
   bool timing = false;
   std::vector<TimingSet> ring;
   int ring_used = 0;
-  double total_ms[kKernels] = {0, 0, 0, 0, 0, 0, 0};
-  int runs[kKernels] = {0, 0, 0, 0, 0, 0, 0};
+  double total_ms[kKernels] = {};
+  int runs[kKernels] = {};
 };
 
 namespace {
@@ -84,6 +85,7 @@ bool valid_dims(const moe_decode_dims* d) {
   if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.0f) return false;
   if (!std::isfinite(d->routed_scale)) return false;
   if (d->routed_format != MOE_DECODE_ROUTED_E4M3 && d->routed_format != MOE_DECODE_ROUTED_MXFP4) return false;
+  if (d->schedule != MOE_DECODE_SCHEDULE_FUSED && d->schedule != MOE_DECODE_SCHEDULE_LAUNCHES) return false;
   return true;
 }
 
@@ -91,7 +93,8 @@ bool valid_dims(const moe_decode_dims* d) {
 void fold_timing(moe_decode_plan_s* p) {
   for (int i = 0; i < p->ring_used; ++i) {
     TimingSet& t = p->ring[i];
-    (void)hipEventSynchronize(t.ev[2 * kKernels - 1]);
+    for (int k = 0; k < kKernels; ++k)
+      if ((t.launched >> k) & 1u) (void)hipEventSynchronize(t.ev[2 * k + 1]);
     for (int k = 0; k < kKernels; ++k) {
       float ms = 0.0f;
       if (((t.launched >> k) & 1u) && hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]) == hipSuccess) {
@@ -142,6 +145,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   d.eps = dims->rms_eps;
   d.routed_scale = dims->routed_scale;
   d.rfmt = dims->routed_format;
+  p->fused = dims->schedule == MOE_DECODE_SCHEDULE_FUSED;
   p->max_vs = max_vslots(d.Mx, d.E, d.K);
   p->R = d.Mx * d.K + d.Mx;
 
@@ -157,7 +161,8 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   }
   // the expert GEMMs run one block per CU; every variant must fit once
   if (gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, p->max_vs, true)) < 1 ||
-      gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false)) < 1) {
+      gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false)) < 1 ||
+      (p->fused && experts_blocks_per_cu(experts_lds_bytes(d, d.Mx, p->max_vs)) < 1)) {
     p->err = g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
     delete p;
     return MOE_DECODE_EINVAL;
@@ -178,6 +183,11 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   const size_t o_rowout = take(R * 4);
   const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
   const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
+  // counters of the fused launch: status (padded to its own 256 bytes), the
+  // slots' ready words, the act groups' unit counts
+  const int act_stride = d.Imax / kActCols;
+  const size_t nsync = 64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride;
+  const size_t o_sync = take(nsync * 4);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
   // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
   // the step sizes that run in split mode
@@ -225,7 +235,13 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   p->tl_base = reinterpret_cast<uint64_t*>(b + o_tl);
   s.part13 = reinterpret_cast<float*>(b + o_part13);
   s.part2 = reinterpret_cast<float*>(b + o_part2);
-  s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = nullptr;
+  s.sync = reinterpret_cast<uint32_t*>(b + o_sync);
+  s.status = s.sync;
+  s.ready = s.sync + 64;
+  s.act_cnt = s.ready + p->max_vs;
+  s.nsync = (int)nsync;
+  s.act_stride = act_stride;
+  s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = s.tl_experts = nullptr;
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -290,6 +306,7 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     sc.tl_act = tl[4];
     sc.tl_w2 = tl[5];
     sc.tl_combine = tl[6];
+    sc.tl_experts = tl[7];
   }
   p->last_grid[0] = seam_blocks(d, m);
   p->last_grid[1] = logits_blocks(d, m);
@@ -298,6 +315,7 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   p->last_grid[4] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
   p->last_grid[5] = p->grid2;
   p->last_grid[6] = d.H / 64 * m;
+  p->last_grid[7] = p->grid13;
   hipError_t e;
   auto ev = [&](int k) {
     KernelEvents r;
@@ -311,11 +329,16 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
     return hip_fail(p, e, "logits launch");
   if ((e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
-  if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(3))) != hipSuccess)
-    return hip_fail(p, e, "w13 launch");
-  if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
-  if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)
-    return hip_fail(p, e, "w2 launch");
+  if (p->fused) {
+    if ((e = launch_experts(d, m, in, sc, p->grid13, p->max_vs, st, ev(7))) != hipSuccess)
+      return hip_fail(p, e, "experts launch");
+  } else {
+    if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(3))) != hipSuccess)
+      return hip_fail(p, e, "w13 launch");
+    if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
+    if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)
+      return hip_fail(p, e, "w2 launch");
+  }
   if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(6))) != hipSuccess)
     return hip_fail(p, e, "combine launch");
   p->last_m = m;
@@ -340,6 +363,7 @@ int moe_decode_inspect(moe_decode_handle p, int32_t tap, const void** d_ptr, siz
     case MOE_DECODE_TAP_ROW_TOK: *d_ptr = s.row_tok; *bytes = R * 4; break;
     case MOE_DECODE_TAP_A8: *d_ptr = s.a8; *bytes = R * d.Imax; break;
     case MOE_DECODE_TAP_A8S: *d_ptr = s.a8s; *bytes = R * d.Imax / 32; break;
+    case MOE_DECODE_TAP_STATUS: *d_ptr = s.status; *bytes = 4; break;
     default: return MOE_DECODE_EINVAL;
   }
   return MOE_DECODE_OK;

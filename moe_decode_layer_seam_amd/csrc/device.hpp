@@ -274,6 +274,50 @@ __device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t sof
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Data exchanged between the CUs of one launch.  The L2 of an XCD does not
+// see another XCD's writes, so such data is stored with the device-coherent
+// policy (sc1: written through) and loaded with it (served from beyond the
+// XCD's L2); AUX = kCoherent selects it on the buffer loads below, AUX = 0
+// the default policy.  A writer waits for its stores to complete
+// (wait_memory) before it counts them on a device-scope counter, and a
+// reader issues its loads only after it has seen the count.
+// ---------------------------------------------------------------------------
+constexpr int kCoherent = 16;  // sc1
+
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16a(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t bload8a(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t bload32a(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, AUX);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t count_arrival(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this wave issued has completed (vector
+// and scalar): stores with the coherent policy are then visible to every CU.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Timeline stamp (device page, memrealtime / stamp): thread 0 of the block
 // stores the 100 MHz device clock at record [block][point] (vector store).
 // tl == nullptr: no timeline.

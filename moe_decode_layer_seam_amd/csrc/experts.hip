@@ -129,8 +129,9 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
   return u;
 }
 
-// Loads of K step `st` (past the contraction: zeros, no traffic).
-template <int TT>
+// Loads of K step `st` (past the contraction: zeros, no traffic); AUX: the
+// cache policy of the activation loads.
+template <int TT, int AUX>
 __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st) {
   const bool ok = st < u.nsteps;
   const uint32_t kw = (uint32_t)st * 128;
@@ -144,15 +145,15 @@ __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st)
 #pragma unroll
   for (int p = 0; p < TT / 2; ++p) f.sb[p] = bload8(u.ws, so, u.ssoff + p * u.sstride);
   const uint32_t ao = ok ? u.alane + kw : kNoRow;
-  f.alo = bload16(u.a, ao, 0);
-  f.ahi = bload16(u.a, ao + 64, 0);
-  f.sa = bload8(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+  f.alo = bload16a<AUX>(u.a, ao, 0);
+  f.ahi = bload16a<AUX>(u.a, ao + 64, 0);
+  f.sa = bload8a<AUX>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
 }
 
 // One segment's sums for the TT tiles, in bursts of BS K steps: a burst's
 // loads are all issued before its first MFMA.  Each tile's MFMAs run in K
 // order whatever BS is.
-template <int TT, int BS>
+template <int TT, int BS, int AUX>
 __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, int seg) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -160,7 +161,7 @@ __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, in
   for (int b0 = 0; b0 < kSegSteps; b0 += BS) {
     Step<TT> f[BS];
 #pragma unroll
-    for (int q = 0; q < BS; ++q) load_step<TT>(f[q], u, seg * kSegSteps + b0 + q);
+    for (int q = 0; q < BS; ++q) load_step<TT, AUX>(f[q], u, seg * kSegSteps + b0 + q);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < BS; ++q) {
@@ -196,7 +197,7 @@ struct Codes4 {
   uint32_t b[TT], a;
 };
 
-template <int TT>
+template <int TT, int AUX>
 __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int seg, int g) {
   const int st = seg * kSegSteps + g;  // the step whose codes this lane fetches
   const bool ok = st < u.nsteps;
@@ -205,7 +206,7 @@ __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int
   const uint32_t bo = ok ? u.slane + 256 * seg : kNoRow;
 #pragma unroll
   for (int t = 0; t < TT; ++t) c.b[t] = __builtin_amdgcn_raw_buffer_load_b32(u.ws, (int)bo, (int)(u.ssoff + t * u.sstride), 0);
-  c.a = __builtin_amdgcn_raw_buffer_load_b32(u.as, (int)(ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow), 0, 0);
+  c.a = bload32a<AUX>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
 }
 
 template <int TT>
@@ -215,7 +216,7 @@ __device__ __forceinline__ void transpose_codes4(Codes4<TT>& c, int g) {
   c.a = transpose4_groups(c.a, g);
 }
 
-template <int TT>
+template <int TT, int AUX>
 __device__ __forceinline__ void load_pair4(Pair4<TT>& f, const UnitOps& u, int st, int j) {
   const bool ok0 = st < u.nsteps, ok1 = st + 1 < u.nsteps;
   const uint32_t wo = (j < 8 ? ok0 : ok1) ? u.wlane + (uint32_t)st * 64 : kNoRow;
@@ -227,8 +228,8 @@ __device__ __forceinline__ void load_pair4(Pair4<TT>& f, const UnitOps& u, int s
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint32_t ao = (q ? ok1 : ok0) ? u.alane + (uint32_t)(st + q) * 128 : kNoRow;
-    f.alo[q] = bload16(u.a, ao, 0);
-    f.ahi[q] = bload16(u.a, ao + 64, 0);
+    f.alo[q] = bload16a<AUX>(u.a, ao, 0);
+    f.ahi[q] = bload16a<AUX>(u.a, ao + 64, 0);
   }
 }
 
@@ -248,20 +249,48 @@ __device__ __forceinline__ void mma_pair4(v4f (&acc)[TT], const Pair4<TT>& f, co
 
 // One segment's sums for E2M1 weights: both line pairs (2 K steps each) and
 // the codes loaded before the first MFMA; each tile's MFMAs run in K order.
-template <int TT>
+template <int TT, int AUX>
 __device__ __forceinline__ void segment_sum_fp4(v4f (&acc)[TT], const UnitOps& u, int seg, int g, int j) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   Codes4<TT> c;
   Pair4<TT> f0, f1;
-  load_codes4<TT>(c, u, seg, g);
-  load_pair4<TT>(f0, u, seg * kSegSteps, j);
-  load_pair4<TT>(f1, u, seg * kSegSteps + 2, j);
+  load_codes4<TT, AUX>(c, u, seg, g);
+  load_pair4<TT, AUX>(f0, u, seg * kSegSteps, j);
+  load_pair4<TT, AUX>(f1, u, seg * kSegSteps + 2, j);
   __builtin_amdgcn_sched_barrier(0);
   transpose_codes4<TT>(c, g);
   mma_pair4<TT, 0>(acc, f0, c);
   mma_pair4<TT, 1>(acc, f1, c);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// The unit's sums over its segments [s0, s1), added in segment order; each
+// segment's sum starts from zero.
+template <int TT, int AUX>
+__device__ __forceinline__ void unit_sums(v4f (&tot)[TT], const UnitOps& ops, int s0, int s1, int g, int j) {
+  constexpr int BS = TT >= 8 ? 2 : kSegSteps;  // K steps per load burst
+  if (ops.fp4) {
+    segment_sum_fp4<TT, AUX>(tot, ops, s0, g, j);
+    for (int sg = s0 + 1; sg < s1; ++sg) {
+      v4f p[TT];
+      segment_sum_fp4<TT, AUX>(p, ops, sg, g, j);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+    }
+  } else {
+    segment_sum<TT, BS, AUX>(tot, ops, s0);
+    for (int sg = s0 + 1; sg < s1; ++sg) {
+      v4f p[TT];
+      segment_sum<TT, BS, AUX>(p, ops, sg);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+    }
+  }
 }
 
 // Units of one run, in order: the shared slots' units, then the routed ones;
@@ -325,7 +354,6 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
 template <bool W13, int TT, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
-  constexpr int BS = TT >= 8 ? 2 : kSegSteps;  // K steps per load burst
   extern __shared__ __align__(16) unsigned char lds_raw[];
   __shared__ uint32_t s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -360,27 +388,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
     unit_decode(um, u, v, tg, s0, s1);
     const UnitOps ops = unit_ops<W13, TT>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
     v4f tot[TT];
-    if (ops.fp4) {
-      segment_sum_fp4<TT>(tot, ops, s0, g, j);
-      for (int sg = s0 + 1; sg < s1; ++sg) {
-        v4f p[TT];
-        segment_sum_fp4<TT>(p, ops, sg, g, j);
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
-      }
-    } else {
-      segment_sum<TT, BS>(tot, ops, s0);
-      for (int sg = s0 + 1; sg < s1; ++sg) {
-        v4f p[TT];
-        segment_sum<TT, BS>(p, ops, sg);
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
-      }
-    }
+    unit_sums<TT, 0>(tot, ops, s0, s1, g, j);
     // w13 sums go to the slot's rows; w2 sums to the rows' output rows
     float* dst = part + (size_t)(um.split ? s0 : 0) * plane + ops.col0 + j;
 #pragma unroll
@@ -483,6 +491,234 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, I
   stamp(s.tl_combine, kTlPoints, 1);
 }
 
+// ===========================================================================
+// The fused expert launch: w13, act and w2 in one grid of one block per CU.
+//
+// Units are numbered w13 first, then w2, and dealt to the blocks as in the
+// separate GEMMs; a block's waves take its units in increasing order.  The
+// act of a slot is split into groups of 64 columns of a; the w13 unit that
+// completes a group (a device-scope count of its units) computes that
+// group's a8 and counts it on the slot's ready word, and a w2 unit waits
+// for the ready word of its slot before it loads a8.  No w13 unit waits, and
+// a wave holds at most w2 units while it waits, so with every block resident
+// the waits always end.  The w13 sums and a8 cross CUs with the coherent
+// policy; a unit's sums are counted when the wave's next unit is done (its
+// stores are complete by then, so counting them costs no wait), or before a
+// w2 unit.  Each tile, act group and output is computed with the same
+// arithmetic, in the same order, as by the separate launches.
+// ===========================================================================
+
+// Longest wait for a slot's a8 before the run is flagged (status) and the
+// wave goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
+constexpr uint64_t kWaitTicks = 10000000ull;
+
+// SiLU(gate) * up of act group q of a slot (columns [64 q, +64) of a, lane =
+// column) for its c rows from row0, from the w13 sums of nseg planes added in
+// plane order, then MXFP8 of each 32 columns: act_kernel's arithmetic.
+__device__ __forceinline__ void finish_row(const LayerDims& d, const Scratch& s, int r, int col, int lane,
+                                           float hg, float hu) {
+  const float a = hg / (1.0f + __expf(-hg)) * hu;
+  const float amax = group_max(fabsf(a), 32);
+  const int code = e8m0_code(amax);
+  const uint8_t byte = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
+  __hip_atomic_store(&s.a8[(size_t)r * d.Imax + col], byte, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((lane & 31) == 0)
+    __hip_atomic_store(&s.a8s[(size_t)r * (d.Imax / 32) + col / 32], (uint8_t)code, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ void finish_act(const LayerDims& d, const Scratch& s, int m, int row0, int c, int Kv, int q, int nseg,
+                           int lane) {
+  const size_t width = 2 * (size_t)d.Imax;
+  const size_t plane = (size_t)(m * d.K + m) * width;
+  const int col = kActCols * q + lane;
+  if (nseg == 1) {
+    // whole-mode sums: one plane; eight rows' loads in flight at once
+    for (int i0 = 0; i0 < c; i0 += 8) {
+      float vg[8], vu[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k < c ? i0 + k : c - 1;
+        const float* p = s.part13 + (size_t)(row0 + i) * width + col;
+        vg[k] = load_coherent(p);
+        vu[k] = load_coherent(p + Kv);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (i0 + k < c) finish_row(d, s, row0 + i0 + k, col, lane, vg[k], vu[k]);
+    }
+    return;
+  }
+  for (int i = 0; i < c; ++i) {
+    const float* p = s.part13 + (size_t)(row0 + i) * width + col;
+    float hg = 0.0f, hu = 0.0f;
+    for (int s0 = 0; s0 < nseg; s0 += 16) {
+      float vg[16], vu[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int sg = s0 + k < nseg ? s0 + k : nseg - 1;
+        vg[k] = load_coherent(p + (size_t)sg * plane);
+        vu[k] = load_coherent(p + (size_t)sg * plane + Kv);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (s0 + k < nseg) {
+          hg = s0 + k == 0 ? vg[k] : hg + vg[k];
+          hu = s0 + k == 0 ? vu[k] : hu + vu[k];
+        }
+      }
+    }
+    finish_row(d, s, row0 + i, col, lane, hg, hu);
+  }
+}
+
+// Counts w13 unit (slot v, tile group tg) on the act groups its rows belong
+// to; the unit that completes a group computes it and counts it on the
+// slot's ready word.  The unit's sums must be stored and complete.
+template <int TT13>
+__device__ __forceinline__ void arrive13(const LayerDims& d, const Scratch& s, int m, const int4& slot, int v, int tg,
+                                         uint32_t expect, int nseg, int lane) {
+  constexpr int G = TT13 * 16 / kActCols;  // act groups per tile group
+  const int Kv = slot.x < 0 ? d.Is : d.I;
+  int r0 = 16 * TT13 * tg;
+  if (r0 >= Kv) r0 -= Kv;  // up rows: the same columns of a as the gate rows
+  const int q0 = r0 / kActCols;
+  uint32_t old[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) old[k] = 0;
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) old[k] = count_arrival(&s.act_cnt[(size_t)v * s.act_stride + q0 + k]);
+  }
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    if ((uint32_t)__builtin_amdgcn_readlane((int)old[k], 0) + 1u == expect) {
+      finish_act(d, s, m, slot.y, slot.z, Kv, q0 + k, nseg, lane);
+      wait_memory();
+      if (lane == 0) (void)count_arrival(&s.ready[v]);
+    }
+  }
+}
+
+// Waits until slot v's ready word reaches want (seen: a value read earlier).
+__device__ __forceinline__ void wait_ready(const Scratch& s, int v, uint32_t want, uint32_t seen, int lane) {
+  if (seen >= want) return;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    const uint32_t now = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(&s.ready[v]));
+    if (now >= want) return;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      if (lane == 0) store_coherent(s.status, 1u);
+      return;
+    }
+  }
+}
+
+template <int TT13, int TT2, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int split2) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  __shared__ uint32_t s_next;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  stamp(s.tl_experts, kTlPoints, 0);
+  const UnitMap um13 = unit_map<true, TT13>(d, s, split13);
+  const UnitMap um2 = unit_map<false, TT2>(d, s, split2);
+  const int R = m * d.K + m;
+  int4* s_vs = reinterpret_cast<int4*>(lds_raw);
+  int* s_tok = reinterpret_cast<int*>(s_vs + um13.nvs);  // row -> token (w13's activation rows)
+  int* s_out = s_tok + R;                                 // row -> the row of its w2 sums
+  for (int i = tid; i < um13.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
+  for (int i = tid; i < R; i += NW * 64) {
+    s_tok[i] = s.row_tok[i];
+    s_out[i] = s.row_out[i];
+  }
+  if (tid == 0) s_next = 0;
+  __syncthreads();
+
+  const int nseg13 = split13 ? um13.nseg_r : 1;  // w13's K is H for every slot
+  const uint32_t expect = 2u * (uint32_t)nseg13;  // gate and up units per act group
+  const size_t width13 = 2 * (size_t)d.Imax, plane13 = (size_t)R * width13;
+  const size_t plane2 = (size_t)R * d.H;
+  const uint32_t n13 = um13.total, total = n13 + um2.total;
+  const uint32_t B = gridDim.x;
+  const uint32_t count = total > blockIdx.x ? (total - blockIdx.x + B - 1) / B : 0;
+  int pv = -1, ptg = 0;  // the w13 unit whose sums are stored but not yet counted
+  uint32_t seen = 0;     // the ready word of this unit's slot, read during the previous unit
+  uint32_t i = wave;
+  while (i < count) {
+    const uint32_t u = blockIdx.x + i * B;
+    uint32_t nx = 0;
+    if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t inext = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
+    // read the next unit's ready word now: it is in by the time that unit starts
+    uint32_t seen_next = 0;
+    {
+      const uint32_t un = blockIdx.x + inext * B;
+      if (inext < count && un >= n13) {
+        int vn, tgn, a0, a1;
+        unit_decode(um2, un - n13, vn, tgn, a0, a1);
+        seen_next = load_coherent(&s.ready[vn]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (u < n13) {
+      int v, tg, s0, s1;
+      unit_decode(um13, u, v, tg, s0, s1);
+      const UnitOps ops = unit_ops<true, TT13>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
+      v4f tot[TT13];
+      unit_sums<TT13, 0>(tot, ops, s0, s1, g, j);
+      if (pv >= 0) {
+        wait_memory();
+        arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
+      }
+      float* dst = s.part13 + (size_t)(split13 ? s0 : 0) * plane13 + ops.col0 + j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * g + q < ops.c) {
+          const size_t r = (size_t)(ops.row0 + 4 * g + q);
+#pragma unroll
+          for (int t = 0; t < TT13; ++t) store_coherent(&dst[r * width13 + 16 * t], tot[t][q]);
+        }
+      }
+      pv = v;
+      ptg = tg;
+    } else {
+      if (pv >= 0) {
+        wait_memory();
+        arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
+        pv = -1;
+      }
+      int v, tg, s0, s1;
+      unit_decode(um2, u - n13, v, tg, s0, s1);
+      const int4 slot = s_vs[v];
+      wait_ready(s, v, (uint32_t)((slot.x < 0 ? d.Is : d.I) / kActCols), seen, lane);
+      const UnitOps ops = unit_ops<false, TT2>(slot, tg, d, in, s, s_out, m, R, g, j);
+      v4f tot[TT2];
+      unit_sums<TT2, kCoherent>(tot, ops, s0, s1, g, j);
+      float* dst = s.part2 + (size_t)(split2 ? s0 : 0) * plane2 + ops.col0 + j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * g + q < ops.c) {
+          const size_t orow = (size_t)s_out[ops.row0 + 4 * g + q];
+#pragma unroll
+          for (int t = 0; t < TT2; ++t) dst[orow * d.H + 16 * t] = tot[t][q];
+        }
+      }
+    }
+    seen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen_next);
+    i = inext;
+  }
+  if (pv >= 0) {
+    wait_memory();
+    arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
+  }
+  stamp_wave(s.tl_experts, kTlPoints, 3 + (wave & 3));
+  __syncthreads();
+  stamp(s.tl_experts, kTlPoints, 1);
+}
+
 // Tiles per unit and waves per block (one block per CU) of each GEMM and
 // mode.  More tiles per unit share one activation fragment among more weight
 // tiles and keep more weight bytes in flight per wave; fewer tiles give more
@@ -572,6 +808,25 @@ hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scr
   return launch_kernel(combine_kernel<16>, grid, block, 0, st, ev, d, in, s, m, split);
 }
 
+size_t experts_lds(const LayerDims& d, int m, int max_vs) {
+  return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 8;
+}
+
+template <int TT13, int TT2>
+hipError_t launch_experts_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                            int split13, int split2, hipStream_t st, const KernelEvents& ev) {
+  return launch_kernel(experts_kernel<TT13, TT2, 8>, dim3(grid), dim3(8 * 64), (uint32_t)experts_lds(d, m, max_vs),
+                       st, ev, d, in, s, m, split13, split2);
+}
+
+template <int TT13, int TT2>
+int experts_occupancy_t(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, experts_kernel<TT13, TT2, 8>, 8 * 64, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+
 // Blocks per CU that every variant of the GEMM fits (one block per CU is
 // launched; 0 if a variant cannot run with this much LDS).
 int gemm_blocks_per_cu(bool w13, size_t lds) {
@@ -585,6 +840,28 @@ int gemm_blocks_per_cu(bool w13, size_t lds) {
   }
   return a < b ? a : b;
 }
+
+// The fused launch: split-mode GEMMs take 4 tiles per unit, whole-mode 8,
+// as in the separate launches.
+hipError_t launch_experts(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                          hipStream_t st, const KernelEvents& ev) {
+  const int waves = grid * 8;
+  const int sp13 = gemm_split(d, m, waves, true) ? 1 : 0, sp2 = gemm_split(d, m, waves, false) ? 1 : 0;
+  if (sp13 && sp2) return launch_experts_t<4, 4>(d, m, in, s, grid, max_vs, 1, 1, st, ev);
+  if (sp13) return launch_experts_t<4, 8>(d, m, in, s, grid, max_vs, 1, 0, st, ev);
+  if (sp2) return launch_experts_t<8, 4>(d, m, in, s, grid, max_vs, 0, 1, st, ev);
+  return launch_experts_t<8, 8>(d, m, in, s, grid, max_vs, 0, 0, st, ev);
+}
+
+int experts_blocks_per_cu(size_t lds) {
+  const int o[4] = {experts_occupancy_t<4, 4>(lds), experts_occupancy_t<4, 8>(lds), experts_occupancy_t<8, 4>(lds),
+                    experts_occupancy_t<8, 8>(lds)};
+  int n = o[0];
+  for (int k = 1; k < 4; ++k) n = o[k] < n ? o[k] : n;
+  return n;
+}
+
+size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs) { return experts_lds(d, m, max_vs); }
 
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {
   return w13 ? gemm_lds<true>(d, m, max_vs) : gemm_lds<false>(d, m, max_vs);

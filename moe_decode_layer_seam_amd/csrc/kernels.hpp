@@ -45,6 +45,16 @@ struct Scratch {
   uint8_t* a8s;       // [R, Imax/32] E8M0
   float* part13;       // [planes][R][2 Imax] fp32 w13 sums (per K segment in split mode)
   float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
+  // Counters of the fused expert launch, nsync words from `sync`, zeroed by
+  // the seam launch of every run: status (nonzero: a wait timed out), per
+  // virtual slot the act groups whose a8 is stored (ready), and per slot and
+  // 64-column act group the w13 units counted (act_cnt).
+  uint32_t* sync;
+  uint32_t* status;
+  uint32_t* ready;     // [max_vs]
+  uint32_t* act_cnt;   // [max_vs][act_stride]
+  int nsync;
+  int act_stride;      // Imax / 64
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
   uint64_t* tl_seam;
   uint64_t* tl_logits;
@@ -53,9 +63,11 @@ struct Scratch {
   uint64_t* tl_act;
   uint64_t* tl_w2;
   uint64_t* tl_combine;
+  uint64_t* tl_experts;
 };
 
-constexpr int kKernels = 7;      // seam, logits, route, w13, act, w2, combine
+constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, experts (fused)
+constexpr int kActCols = 64;     // columns of a per act group of the fused launch
 constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment
 
 constexpr int kTlPoints = 8;     // stamps per block and kernel
@@ -136,6 +148,13 @@ hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch&
                      hipStream_t st, const KernelEvents& ev);
 hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
                           hipStream_t st, const KernelEvents& ev);
+// w13, act and w2 in one launch of `grid` blocks (one per CU, all resident
+// at once): each w2 unit waits for its slot's a8, which the last w13 unit of
+// each act group computes.
+hipError_t launch_experts(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                          hipStream_t st, const KernelEvents& ev);
+int experts_blocks_per_cu(size_t lds);
+size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs);
 // Whether a step of m rows runs the GEMM (w13 or w2) in split mode on
 // `waves` waves, the occupancy of its kernel and its dynamic LDS bytes.
 bool gemm_split(const LayerDims& d, int m, int waves, bool w13);

@@ -43,6 +43,12 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
   const int H = d.H, E = d.E;
   const int e0 = es * EPB;
   stamp(s.tl_seam, kTlPoints, 0);
+  {
+    // the fused expert launch's counters start every run at zero
+    const uint32_t nthr = gridDim.x * gridDim.y * kThreads;
+    for (uint32_t w = (blockIdx.y * gridDim.x + blockIdx.x) * kThreads + tid; w < (uint32_t)s.nsync; w += nthr)
+      store_coherent(&s.sync[w], 0u);
+  }
 
   int col[CPT];
   bool live[CPT];

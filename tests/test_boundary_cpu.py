@@ -32,14 +32,15 @@ def test_every_declared_symbol_is_exported():
     dict(topk=0), dict(topk=9, experts=8), dict(topk=33, experts=64), dict(inter=96),
     dict(shared_inter=0), dict(max_tokens=0), dict(max_tokens=49), dict(rms_eps=-1.0),
     dict(rms_eps=float("nan")), dict(routed_scale=float("inf")), dict(routed_format=2),
-    dict(routed_format=-1),
+    dict(routed_format=-1), dict(schedule=2), dict(schedule=-1),
 ])
 def test_plan_rejects_invalid_dims(bad):
     d = dict(hidden=256, experts=8, topk=2, inter=128, shared_inter=128, max_tokens=4,
-             rms_eps=1e-6, routed_scale=1.0, routed_format=0)
+             rms_eps=1e-6, routed_scale=1.0, routed_format=0, schedule=0)
     d.update(bad)
     dims = mdl.Dims(d["hidden"], d["experts"], d["topk"], d["inter"], d["shared_inter"],
-                    d["max_tokens"], d["rms_eps"], d["routed_scale"], d["routed_format"])
+                    d["max_tokens"], d["rms_eps"], d["routed_scale"], d["routed_format"],
+                    d["schedule"])
     h = ctypes.c_void_p()
     assert mdl.lib().moe_decode_plan(ctypes.byref(dims), None, ctypes.byref(h)) == mdl.EINVAL
     assert h.value is None

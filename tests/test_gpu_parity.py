@@ -41,16 +41,17 @@ SMALL = [
 ]
 
 
-def _plan_for(cfg, max_tokens=None):
+def _plan_for(cfg, max_tokens=None, schedule="launches"):
     return mdl.plan(cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"],
                     cfg["shared_inter"], max_tokens or cfg["m"], cfg["rms_eps"],
-                    cfg["routed_scale"], routed=data.routed_of(cfg))
+                    cfg["routed_scale"], routed=data.routed_of(cfg), schedule=schedule)
 
 
 def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
     """Compare every intermediate of the last run with the oracle."""
     m, H, E, K = cfg["m"], cfg["hidden"], cfg["experts"], cfg["topk"]
     dims = data.dims_of(cfg)
+    assert gu.tap(handle, "status", torch.int32)[0] == 0, "a wait of the fused launch timed out"
     # norm, quant and router for every row (cheap on the CPU)
     y = oracle.rmsnorm(inp["x"], inp["norm_w"], cfg["rms_eps"])
     assert np.array_equal(gu.tap(handle, "normed", torch.int16).view(np.uint16).reshape(m, H), y)
@@ -208,11 +209,12 @@ def test_concentrated_routing_splits_slots():
         mdl.destroy(h)
 
 
-def test_runs_are_deterministic_and_plan_reusable_across_m():
+@pytest.mark.parametrize("schedule", ["launches", "fused"])
+def test_runs_are_deterministic_and_plan_reusable_across_m(schedule):
     cfg = _cfg(48, 512, 256, 8, 256, 256)
     inp, w = data.build_layer(10, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
-    h = _plan_for(cfg)
+    h = _plan_for(cfg, schedule=schedule)
     try:
         a = gu.run(h, cfg, dinp, dw).clone()
         b = gu.run(h, cfg, dinp, dw).clone()
@@ -226,15 +228,17 @@ def test_runs_are_deterministic_and_plan_reusable_across_m():
         assert torch.equal(c.view(torch.int16), a[:5].view(torch.int16))
         assert torch.equal(c3.view(torch.int16), a[:3].view(torch.int16))
         assert torch.equal(d.view(torch.int16), a.view(torch.int16))
+        assert gu.tap(h, "status", torch.int32)[0] == 0
     finally:
         mdl.destroy(h)
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("schedule", ["launches", "fused"])
+def test_graph_capture_replays_match_eager(schedule):
     cfg = _cfg(16, 512, 64, 6, 256, 128)
     inp, w = data.build_layer(11, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
-    h = _plan_for(cfg)
+    h = _plan_for(cfg, schedule=schedule)
     try:
         xs = [gu.bf16_dev(synth.to_bf16_bits(synth.normal(100 + i, 1, (16, 512)))) for i in range(4)]
         eager = []
@@ -257,9 +261,75 @@ def test_graph_capture_replays_match_eager():
                 g.replay()
                 torch.cuda.synchronize()
                 assert torch.equal(out.view(torch.int16), eager[i].view(torch.int16)), (rep, i)
+        assert gu.tap(h, "status", torch.int32)[0] == 0
         del g
     finally:
         mdl.destroy(h)
+
+
+def _gpu_weights(cfg, seed):
+    """N(0, 0.02) weights drawn on the GPU and quantised by the library."""
+    E, H, I, Is = cfg["experts"], cfg["hidden"], cfg["inter"], cfg["shared_inter"]
+    fp4 = data.routed_of(cfg) == "mxfp4"
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = {}
+
+    def make(name, shape, routed):
+        w = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * 0.02
+        rows, cols = shape[-2], shape[-1]
+        if routed and fp4:
+            q = torch.empty(shape[:-1] + (cols // 2,), dtype=torch.uint8, device="cuda")
+            sc = torch.empty(shape[:-2] + mdl.fp4_codes_shape(rows, cols), dtype=torch.uint8, device="cuda")
+            mdl.quantize_weight_fp4(w, q, sc)
+        else:
+            q = torch.empty(shape, dtype=torch.uint8, device="cuda")
+            sc = torch.empty(shape[:-2] + (rows // 32, cols // 32), dtype=torch.uint8, device="cuda")
+            mdl.quantize_weight(w, q, sc)
+        out[name], out[name + "_s"] = q, sc
+
+    make("w13", (E, 2 * I, H), True)
+    make("w2", (E, H, I), True)
+    make("sgu", (2 * Is, H), False)
+    make("sw2", (H, Is), False)
+    return out
+
+
+# (w13 mode, w2 mode) of the fused launch on 256 CUs: split/split at small
+# sizes and m <= 6 of the full layer, split/whole at m = 8, whole/whole at
+# m = 48, whole/split where I is much larger than H
+SCHEDULE_CASES = [
+    _cfg(13, 640, 100, 8, 128, 256),
+    dict(synth.CONFIGS[1], m=8, name="dsv41_m8"),
+    synth.CONFIGS[3],
+    _cfg(40, 256, 64, 4, 8192, 128),
+    dict(synth.CONFIGS[1], routed="mxfp4", name="dsv41_m1_fp4"),
+    dict(synth.CONFIGS[3], routed="mxfp4", name="dsv41_m48_fp4"),
+]
+
+
+@pytest.mark.parametrize("cfg", SCHEDULE_CASES, ids=lambda c: c["name"])
+def test_fused_launch_matches_separate_launches_bit_for_bit(cfg):
+    """The fused expert launch runs the separate launches' arithmetic in the
+    same order: output and intermediate bytes are identical."""
+    m, H, E = cfg["m"], cfg["hidden"], cfg["experts"]
+    dw = _gpu_weights(cfg, 31)
+    inp = synth.small_inputs(5, m, H, E)
+    dinp = gu.inputs_dev(inp)
+    got = {}
+    for schedule in ("launches", "fused"):
+        h = _plan_for(cfg, max_tokens=48, schedule=schedule)
+        try:
+            outs = [gu.run(h, cfg, dinp, dw).clone() for _ in range(2)]
+            torch.cuda.synchronize()
+            assert gu.tap(h, "status", torch.int32)[0] == 0
+            got[schedule] = (outs, gu.tap(h, "a8"), gu.tap(h, "a8s"))
+        finally:
+            mdl.destroy(h)
+    (o_l, a8_l, a8s_l), (o_f, a8_f, a8s_f) = got["launches"], got["fused"]
+    assert np.array_equal(a8_l, a8_f) and np.array_equal(a8s_l, a8s_f)
+    for a, b in zip(o_l + o_f[1:], o_f):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_quantize_weight_matches_oracle():
