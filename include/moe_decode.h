@@ -206,8 +206,9 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  * kernel stores the 100 MHz device clock (s_memrealtime) at fixed points:
  *   seam:  0 start, 1 squares summed, 2 logits (or rows) stored
  *   logits: 0 start, 1 end
- *   route: 0 start, 1 groups sorted, 2 picks stored, 3 last block admitted,
- *          4 plan written (3-4 only in the last block)
+ *   route: 0 start, 5 scores computed, 1 groups sorted, 6 lists merged,
+ *          2 picks stored, 3 last block admitted, 4 plan written (3-4 only
+ *          in the last block)
  *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end
  *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the

@@ -21,7 +21,8 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------------------
 // Lane exchange: value of lane (lane ^ mask).  Masks 1 and 2 are DPP quad
 // permutations, 4 and 8 a pair of DPP row shifts with bank masks, 16 and 32
-// permlane swaps across rows (device page, xshfl); others ds_bpermute.
+// permlane swaps across rows (device page, xshfl), 15 the DPP row mirror
+// (31 and 63: the mirror, then the row swaps); others ds_bpermute.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int xor_lane(int v, int mask) {
   switch (mask) {
@@ -48,6 +49,22 @@ __device__ __forceinline__ int xor_lane(int v, int mask) {
       // with the lower 32 of the second
       const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
       return (int)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+    }
+    case 15:
+      return __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    case 31: {
+      // row mirror, then the 16-lane rows swapped in pairs
+      const int y = __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false);
+      const auto r = __builtin_amdgcn_permlane16_swap((unsigned)y, (unsigned)y, false, false);
+      return (int)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+    }
+    case 63: {
+      // row mirror, then rows swapped in pairs, then the halves swapped
+      const int y = __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false);
+      const auto r = __builtin_amdgcn_permlane16_swap((unsigned)y, (unsigned)y, false, false);
+      const unsigned z = ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+      const auto q = __builtin_amdgcn_permlane32_swap(z, z, false, false);
+      return (int)(((threadIdx.x >> 5) & 1) ? q[0] : q[1]);
     }
     default:
       return __shfl_xor(v, mask, kWave);

@@ -343,8 +343,18 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
   }
 }
 
-// The GEMM, one block of NW waves per CU.  Block b of B takes units b,
-// b + B, b + 2B, ... of the T units, so every CU streams the same bytes and
+// The unit of a block's turn i: the units are dealt in rows of B, one per
+// block, the order of the blocks reversed every other row.  Consecutive
+// units are consecutive K segments of a tile group, so without the reversal
+// a block (and an XCD, which runs every eighth block) would only ever see
+// one parity of segment: the XCDs that read the odd 512-byte segments of
+// the rows took 12% longer.
+__device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) {
+  return i * B + ((i & 1u) ? B - 1u - blockIdx.x : blockIdx.x);
+}
+
+// The GEMM, one block of NW waves per CU.  Block b of B takes one unit of
+// every row of B units (unit_turn), so every CU streams the same bytes and
 // gets its part of every slot; its waves take the block's units from a
 // counter in LDS, so a slow wave does not hold the CU back.  Lane (g, j) of a unit ends with rows
 // 4g..4g+3 of the slot and weight rows col0 + 16 t + j; rows past the slot's
@@ -373,15 +383,15 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
   const int width = W13 ? 2 * d.Imax : d.H;
   float* part = W13 ? s.part13 : s.part2;
   const size_t plane = (size_t)R * width;
-  // the block's units are blockIdx.x + i B, i < count: units of one slot
-  // (costlier for slots with more rows) spread over every CU
-  const uint32_t B = gridDim.x;
-  const uint32_t count = um.total > blockIdx.x ? (um.total - blockIdx.x + B - 1) / B : 0;
+  // the block's turns i take unit unit_turn(i): units of one slot (costlier
+  // for slots with more rows) spread over every CU
+  const uint32_t B = gridDim.x, turns = (um.total + B - 1) / B;
   // first unit by wave index, the rest from the block's counter; the next
   // index is fetched while the current unit streams
   uint32_t i = wave;
-  while (i < count) {
-    const uint32_t u = blockIdx.x + i * B;
+  while (i < turns) {
+    const uint32_t u = unit_turn(i, B);
+    if (u >= um.total) break;  // the last turn has no unit for this block
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int v, tg, s0, s1;
@@ -642,21 +652,21 @@ void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int s
   const size_t width13 = 2 * (size_t)d.Imax, plane13 = (size_t)R * width13;
   const size_t plane2 = (size_t)R * d.H;
   const uint32_t n13 = um13.total, total = n13 + um2.total;
-  const uint32_t B = gridDim.x;
-  const uint32_t count = total > blockIdx.x ? (total - blockIdx.x + B - 1) / B : 0;
+  const uint32_t B = gridDim.x, turns = (total + B - 1) / B;
   int pv = -1, ptg = 0;  // the w13 unit whose sums are stored but not yet counted
   uint32_t seen = 0;     // the ready word of this unit's slot, read during the previous unit
   uint32_t i = wave;
-  while (i < count) {
-    const uint32_t u = blockIdx.x + i * B;
+  while (i < turns) {
+    const uint32_t u = unit_turn(i, B);
+    if (u >= total) break;  // the last turn has no unit for this block
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t inext = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
     // read the next unit's ready word now: it is in by the time that unit starts
     uint32_t seen_next = 0;
     {
-      const uint32_t un = blockIdx.x + inext * B;
-      if (inext < count && un >= n13) {
+      const uint32_t un = unit_turn(inext, B);
+      if (inext < turns && un < total && un >= n13) {
         int vn, tgn, a0, a1;
         unit_decode(um2, un - n13, vn, tgn, a0, a1);
         seen_next = load_coherent(&s.ready[vn]);

@@ -1,10 +1,10 @@
 // seam.hip -- the FFN seam and the router, two launches:
 //   seam:  RMSNorm -> bf16 normed rows -> MXFP8 (x8, x8s); router logits in
 //          double precision.  Blocks tile (experts) x (token rows).
-//   route: per token, sigmoid + bias -> top-k by bitonic sort networks over
-//          expert groups of 64 (the four waves of a block sort groups in
-//          parallel, then merge) -> routing weights; the last block to
-//          finish writes the token->expert plan.
+//   route: per token, sigmoid + bias -> top-k by bitonic sort networks on
+//          64-bit selection keys over expert groups of 64 (the four waves of
+//          a block sort groups in parallel, then merge) -> routing weights;
+//          the last block to finish writes the token->expert plan.
 //
 // Pages: "vllm.models.deepseek_v41.amd.mono.layer" run_ffn (the seam's norm,
 // then the MoE), store_normed (the normed row, bf16), store_x8 (MXFP8 of 8
@@ -57,6 +57,14 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
     col[q] = 8 * tid + 2048 * q;
     live[q] = col[q] < H;
   }
+  // the token rows first: loads complete in issue order, so the sum of
+  // squares need not wait for the gate rows
+  u32x4 xv[TB][CPT];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      if (tt < nt && live[q]) xv[tt][q] = ld16(reinterpret_cast<const uint8_t*>(in.x + (size_t)(t0 + tt) * H + col[q]));
   u32x4 wv[PRE ? CPT : 1], gv[PRE ? EPB : 1][PRE ? CPT : 1];
   if constexpr (PRE) {
 #pragma unroll
@@ -69,12 +77,6 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
       }
     }
   }
-  u32x4 xv[TB][CPT];
-#pragma unroll
-  for (int tt = 0; tt < TB; ++tt)
-#pragma unroll
-    for (int q = 0; q < CPT; ++q)
-      if (tt < nt && live[q]) xv[tt][q] = ld16(reinterpret_cast<const uint8_t*>(in.x + (size_t)(t0 + tt) * H + col[q]));
 
   // sum of squares in double: each square of a bf16 is exact; lanes, then
   // waves, are added in a fixed order
@@ -311,58 +313,6 @@ hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Sc
 // route: top-k per token, weights, plan
 // ===========================================================================
 
-// Strict total order of the router: larger biased score first, the lower
-// expert index on equal scores.
-__device__ __forceinline__ bool ranks_before(double b1, int e1, double b2, int e2) {
-  return b1 > b2 || (b1 == b2 && e1 < e2);
-}
-
-// Bitonic sorting network over the 64 lanes, descending in the router order,
-// run on G independent groups at once.
-template <int G>
-__device__ __forceinline__ void sort64(double (&b)[G], int (&e)[G], int lane) {
-#pragma unroll
-  for (int k2 = 2; k2 <= 64; k2 <<= 1) {
-#pragma unroll
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      const bool up = (lane & k2) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool keep_first = (lower == up);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const double pb = xor_lane(b[g], j);
-        const int pe = xor_lane(e[g], j);
-        if (ranks_before(b[g], e[g], pb, pe) != keep_first) {
-          b[g] = pb;
-          e[g] = pe;
-        }
-      }
-    }
-  }
-}
-
-// a, c: sorted descending across the lanes.  Leaves the 64 first of a and c
-// in a, sorted: the lane-wise better of a[i] and c[63 - i] is a bitonic
-// sequence holding them, which a half-cleaner cascade sorts.
-__device__ __forceinline__ void merge64(double& ab, int& ae, double cb, int ce, int lane) {
-  const double rb = xor_lane(cb, 63);
-  const int re = xor_lane(ce, 63);
-  if (ranks_before(rb, re, ab, ae)) {
-    ab = rb;
-    ae = re;
-  }
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const double pb = xor_lane(ab, j);
-    const int pe = xor_lane(ae, j);
-    const bool lower = (lane & j) == 0;
-    if (ranks_before(ab, ae, pb, pe) != lower) {
-      ab = pb;
-      ae = pe;
-    }
-  }
-}
-
 // Exclusive prefix sum of arr[0, n) (n <= 4 * kThreads) in place; returns
 // the total.  Called by all kThreads threads.
 __device__ int block_scan(int* arr, int n, int* tmp4) {
@@ -397,9 +347,8 @@ __device__ int block_scan(int* arr, int n, int* tmp4) {
 }
 
 struct RouteLds {
-  double cb[4][64];  // each wave's sorted candidates
-  int ce[4][64];
-  double sig[kMaxExperts];  // this token's sigmoid scores
+  uint64_t cand[4][64];      // each wave's sorted selection keys
+  double sig[kMaxExperts];   // this token's sigmoid scores
   int ids[kMaxTokens * kMaxTopk];
   float w[kMaxTokens * kMaxTopk];
   uint32_t mlo[kMaxExperts], mhi[kMaxExperts];  // tokens 0-31 / 32-47 per expert
@@ -409,17 +358,85 @@ struct RouteLds {
   int last;
 };
 
+// The plan of a step of at most 64 pairs and 16 tokens, by wave 0 alone:
+// lane p takes pair p, a bitonic sort of the keys expert * 64 + token puts
+// row r's pair in lane r, and every expert has one virtual slot (its rows
+// are at most the 16 tokens).  Same plan as build_plan's general path.
+__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane) {
+  const int E = d.E, K = d.K, P = m * K;
+  // key: expert, token, pair (10 + 4 + 6 bits), unique; sorted ascending over
+  // the smallest power-of-two number of lanes that holds the pairs
+  int key = 0x7FFFFFFF;
+  if (lane < P) key = (L.ids[lane] << 10) | ((lane / K) << 6) | lane;
+  const int width = P <= 8 ? 8 : (P <= 16 ? 16 : (P <= 32 ? 32 : 64));
+  // (every stage unrolled, so each exchange is a fixed DPP or permlane
+  // pattern; a level is skipped as a whole when it is wider than needed)
+#pragma unroll
+  for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+    if (k2 <= width) {
+#pragma unroll
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        const int pk = xor_lane(key, j);
+        // ascending: the lower lane of a pair keeps the smaller key when up
+        const bool keep_min = ((lane & j) == 0) == ((lane & k2) == 0);
+        key = keep_min ? min(key, pk) : max(key, pk);
+      }
+    }
+  }
+  const int r = lane;
+  const bool valid = r < P;
+  const int e = key >> 10, t = (key >> 6) & 15, p = key & 63;
+  const int eprev = __shfl_up(e, 1, 64);
+  const bool first = valid && (r == 0 || eprev != e);
+  const uint64_t fm = __ballot(first);
+  const uint64_t above = r == 63 ? 0ull : fm & ~((2ull << r) - 1ull);
+  const int cnt = (above ? __ffsll((unsigned long long)above) - 1 : P) - r;
+  const int nR = __popcll(fm), nS = 1;
+  if (valid) {
+    s.row_tok[r] = t;
+    s.row_w[r] = L.w[p];
+    s.pair_row[p] = r;
+    s.row_out[r] = p;
+  }
+  if (first) s.vslots[nS + __popcll(fm & ((1ull << r) - 1ull))] = make_int4(e, r, cnt, 0);
+  // tokens per expert: a table in LDS (one wave: its LDS accesses are in
+  // order), then copied out whole
+  for (int x = lane; x < E; x += 64) L.base[x] = 0;
+  if (first) L.base[e] = cnt;
+  for (int x = lane; x < E; x += 64) s.counts[x] = L.base[x];
+  if (lane < m) {
+    s.row_tok[P + lane] = lane;
+    s.row_w[P + lane] = 1.0f;
+    s.row_out[P + lane] = P + lane;
+  }
+  if (lane == 0) {
+    s.vslots[0] = make_int4(-1, P, m, 0);
+    s.header[0] = nS + nR;
+    s.header[1] = nS;
+    s.header[2] = nR;
+    s.header[3] = m;
+    __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // The plan, from every token's picks: rows listed by expert ascending, then
 // token ascending; an expert's rows split into virtual slots of at most
 // kTokTile rows; the shared expert's m rows last, its slots first.  With at
 // most 48 tokens, the tokens of an expert form one 64-bit mask and a pair's
 // rank within its expert is the count of lower tokens in the mask.
-__device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds& L) {
+// own: the token whose picks this block holds in LDS already.
+__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L) {
   const int tid = threadIdx.x;
   const int E = d.E, K = d.K, P = m * K;
   for (int p = tid; p < P; p += kThreads) {
+    if (p / K == own) continue;
     L.ids[p] = __hip_atomic_load(&s.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     L.w[p] = __hip_atomic_load(&s.wts[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (P <= 64 && m <= kTokTile) {
+    __syncthreads();
+    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x);
+    return;
   }
   for (int e = tid; e < E; e += kThreads) L.mlo[e] = L.mhi[e] = 0u;
   __syncthreads();
@@ -474,8 +491,54 @@ __device__ void build_plan(const LayerDims& d, int m, const Scratch& s, RouteLds
   }
 }
 
-// Block t: token t.  Wave w sorts groups w, w + 4, ... (GPW of them) and
-// merges them; wave 0 merges the four waves' lists and writes the picks.
+// Selection key of expert e with biased score b: the fp64 order of b
+// (larger first) in the upper 54 bits, then the lower index first.  Scores
+// closer than 2^-42 relative (below the 10 low bits) fall to the index.
+__device__ __forceinline__ uint64_t select_key(double b, int e) {
+  const uint64_t u = (uint64_t)__double_as_longlong(b + 0.0);  // -0 -> +0
+  const uint64_t mono = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (mono & ~0x3FFull) | (uint64_t)(1023 - e);
+}
+
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int mask) {
+  const int lo = xor_lane((int)(uint32_t)v, mask), hi = xor_lane((int)(uint32_t)(v >> 32), mask);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Bitonic sorting network over the 64 lanes, descending, on G independent
+// lists at once.
+template <int G>
+__device__ __forceinline__ void sort64(uint64_t (&k)[G], int lane) {
+#pragma unroll
+  for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      const bool keep_max = ((lane & j) == 0) == ((lane & k2) == 0);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint64_t p = xor_lane64(k[g], j);
+        k[g] = keep_max ? (p > k[g] ? p : k[g]) : (p < k[g] ? p : k[g]);
+      }
+    }
+  }
+}
+
+// a, c: sorted descending across the lanes.  Leaves the 64 largest of both
+// in a, sorted: the lane-wise larger of a[i] and c[63 - i] is a bitonic
+// sequence holding them, which a half-cleaner cascade sorts.
+__device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
+  const uint64_t r = xor_lane64(c, 63);
+  a = r > a ? r : a;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t p = xor_lane64(a, j);
+    a = ((lane & j) == 0) ? (p > a ? p : a) : (p < a ? p : a);
+  }
+}
+
+// Block t: token t.  Wave w sorts the selection keys of expert groups w,
+// w + 4, ... (GPW groups of 64) and merges them; wave 0 merges the four
+// waves' lists, and its lanes [0, k) hold the picks in selection order.
 template <int GPW>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, const float* __restrict__ bias,
                                                          Scratch s) {
@@ -486,63 +549,85 @@ __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, con
   const int groups = (E + 63) / 64;
   stamp(s.tl_route, kTlPoints, 0);
 
-  double b[GPW];
-  int e[GPW];
+  uint64_t k[GPW];
 #pragma unroll
   for (int i = 0; i < GPW; ++i) {
     const int ex = 64 * (wave + 4 * i) + lane;
+    k[i] = 0;  // below every real expert's key
     if (ex < E) {
       const double sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex]));
-      L.sig[ex] = sg;
       const double bb = sg + (double)bias[ex];
-      // a NaN score ranks last among the real experts, never below the
-      // padding, so the picks are always real experts
-      b[i] = (bb == bb) ? bb : -INFINITY;
-      e[i] = ex;
-    } else {
-      b[i] = -INFINITY;
-      e[i] = ex;  // distinct, above every real expert
+      L.sig[ex] = sg;
+      k[i] = select_key((bb == bb) ? bb : -INFINITY, ex);  // a NaN score ranks last
     }
   }
+  stamp(s.tl_route, kTlPoints, 5);
   if (wave < groups) {
-    sort64<GPW>(b, e, lane);
+    sort64<GPW>(k, lane);
 #pragma unroll
     for (int width = GPW / 2; width >= 1; width >>= 1) {
 #pragma unroll
-      for (int i = 0; i < width; ++i) merge64(b[i], e[i], b[i + width], e[i + width], lane);
+      for (int i = 0; i < width; ++i) merge64(k[i], k[i + width], lane);
     }
   }
-  L.cb[wave][lane] = b[0];
-  L.ce[wave][lane] = e[0];
+  L.cand[wave][lane] = k[0];
   __syncthreads();
   stamp(s.tl_route, kTlPoints, 1);
   if (wave == 0) {
     const int nw = groups < 4 ? groups : 4;
-    for (int w = 1; w < nw; ++w) merge64(b[0], e[0], L.cb[w][lane], L.ce[w][lane], lane);
-    // lanes [0, K) hold the picks in selection order
-    double sg = 0.0;
-    if (lane < K) sg = L.sig[e[0]];
+    if (K <= 16) {
+      // the four lists' top 16 side by side (lanes [16 w, +16)), merged by
+      // two bitonic merges: pairs of 16 into 32, then 32 into 64
+      k[0] = (lane >> 4) < nw ? L.cand[lane >> 4][lane & 15] : 0ull;
+      uint64_t p = xor_lane64(k[0], 31);
+      k[0] = (lane & 16) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+#pragma unroll
+      for (int j = 8; j > 0; j >>= 1) {
+        p = xor_lane64(k[0], j);
+        k[0] = (lane & j) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+      }
+      p = xor_lane64(k[0], 63);
+      k[0] = (lane & 32) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+#pragma unroll
+      for (int j = 16; j > 0; j >>= 1) {
+        p = xor_lane64(k[0], j);
+        k[0] = (lane & j) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+      }
+    } else {
+      for (int w = 1; w < nw; ++w) merge64(k[0], L.cand[w][lane], lane);
+    }
+    stamp(s.tl_route, kTlPoints, 6);
+    const int e = 1023 - (int)(k[0] & 0x3FF);
+    const double sg = lane < K ? L.sig[e] : 0.0;
     const double ssum = wave_sum(sg);
     if (lane < K) {
       const float w = (float)((double)d.routed_scale * sg / ssum);
+      L.ids[t * K + lane] = e;
+      L.w[t * K + lane] = w;
       // read by another block of this launch: stored device-coherent
-      __hip_atomic_store(&s.ids[t * K + lane], e[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&s.ids[t * K + lane], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&s.wts[t * K + lane], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   stamp(s.tl_route, kTlPoints, 2);
 
-  // Arrival: wait until this block's coherent stores completed, count the
-  // block, and let the last one through to the plan.  Nothing spins.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (tid == 0)
-    L.last = (__hip_atomic_fetch_add(s.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              (uint32_t)(gridDim.x - 1));
-  __syncthreads();
-  if (!L.last) return;
+  if (gridDim.x > 1) {
+    // Arrival: wait until this block's coherent stores completed, count the
+    // block, and let the last one through to the plan.  Nothing spins.  (A
+    // workgroup-scope fence would not wait for the stores: only the explicit
+    // wait orders them before the count.)
+    wait_memory();
+    __syncthreads();
+    if (tid == 0)
+      L.last = (__hip_atomic_fetch_add(s.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(gridDim.x - 1));
+    __syncthreads();
+    if (!L.last) return;
+  } else {
+    __syncthreads();
+  }
   stamp(s.tl_route, kTlPoints, 3);
-  build_plan(d, m, s, L);
+  build_plan(d, m, t, s, L);
   stamp(s.tl_route, kTlPoints, 4);
 }
 
