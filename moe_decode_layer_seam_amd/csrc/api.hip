@@ -328,12 +328,13 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   if ((e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
   if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
     return hip_fail(p, e, "logits launch");
-  if ((e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
+  const bool route13 = !p->fused && route_in_w13(d, m);
+  if (!route13 && (e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
   if (p->fused) {
     if ((e = launch_experts(d, m, in, sc, p->grid13, p->max_vs, st, ev(7))) != hipSuccess)
       return hip_fail(p, e, "experts launch");
   } else {
-    if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, st, ev(3))) != hipSuccess)
+    if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, route13, st, ev(3))) != hipSuccess)
       return hip_fail(p, e, "w13 launch");
     if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
     if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)

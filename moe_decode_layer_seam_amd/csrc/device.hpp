@@ -95,24 +95,23 @@ __device__ __forceinline__ double wave_sum(double v) {
 // lane carries (it keeps one half, adds its partner's copy of that half and
 // hands over the other); the rest are plain butterfly steps.  On return v[0]
 // of lane l holds the sum of value l >> (6 - log2(NV)).
-template <int NV>
+template <int NV, int M = kWave / 2, int H = NV / 2>
 __device__ __forceinline__ void reduce_scatter(double (&v)[NV], int lane) {
-  int h = NV / 2;
+  // one butterfly step per template level, so every index is a constant and
+  // the values stay in registers
+  if constexpr (M >= 1) {
+    if constexpr (H >= 1) {
+      const bool up = (lane & M) != 0;
 #pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) {
-    if (h >= 1) {
-      const bool up = (lane & m) != 0;
-#pragma unroll
-      for (int i = 0; i < NV / 2; ++i) {
-        if (i < h) {
-          const double keep = up ? v[h + i] : v[i];
-          const double give = up ? v[i] : v[h + i];
-          v[i] = keep + xor_lane(give, m);
-        }
+      for (int i = 0; i < H; ++i) {
+        const double keep = up ? v[H + i] : v[i];
+        const double give = up ? v[i] : v[H + i];
+        v[i] = keep + xor_lane(give, M);
       }
-      h >>= 1;
+      reduce_scatter<NV, M / 2, H / 2>(v, lane);
     } else {
-      v[0] += xor_lane(v[0], m);
+      v[0] += xor_lane(v[0], M);
+      reduce_scatter<NV, M / 2, 0>(v, lane);
     }
   }
 }

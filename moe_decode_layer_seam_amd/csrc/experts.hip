@@ -30,6 +30,7 @@
 // inside a CU, fast waves take more of them.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "route.hpp"
 
 namespace moe {
 namespace {
@@ -303,10 +304,10 @@ struct UnitMap {
 };
 
 template <bool W13, int TT>
-__device__ __forceinline__ UnitMap unit_map(const LayerDims& d, const Scratch& s, int split) {
+__device__ __forceinline__ UnitMap unit_map_n(const LayerDims& d, int nvs, int nS, int split) {
   UnitMap um;
-  um.nvs = s.header[0];
-  um.nS = s.header[1];
+  um.nvs = nvs;
+  um.nS = nS;
   um.split = split;
   const Geo gs = geo<W13>(d, true), gr = geo<W13>(d, false);
   um.nseg_s = gs.nseg;
@@ -315,6 +316,11 @@ __device__ __forceinline__ UnitMap unit_map(const LayerDims& d, const Scratch& s
   um.per_r = gr.tiles / TT * (split ? gr.nseg : 1);
   um.total = (uint32_t)(um.nS * um.per_s + (um.nvs - um.nS) * um.per_r);
   return um;
+}
+
+template <bool W13, int TT>
+__device__ __forceinline__ UnitMap unit_map(const LayerDims& d, const Scratch& s, int split) {
+  return unit_map_n<W13, TT>(d, s.header[0], s.header[1], split);
 }
 
 // unit -> (slot, tile group, first segment, end segment)
@@ -349,8 +355,52 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
 // a block (and an XCD, which runs every eighth block) would only ever see
 // one parity of segment: the XCDs that read the odd 512-byte segments of
 // the rows took 12% longer.
-__device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) {
-  return i * B + ((i & 1u) ? B - 1u - blockIdx.x : blockIdx.x);
+__device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B, uint32_t b) {
+  return i * B + ((i & 1u) ? B - 1u - b : b);
+}
+__device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) { return unit_turn(i, B, blockIdx.x); }
+
+// Longest wait for the plan before the run is flagged (status) and the wave
+// goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
+constexpr uint64_t kPlanWaitTicks = 10000000ull;
+
+// The plan of a w13 launch that routes in its first blocks, copied into the
+// block's LDS by the first wave that needs it (the others wait for that
+// wave): the slots, every row's token and the slot count.  The plan's
+// builder wrote it back from its L2 before it raised the flag; it is read
+// with the coherent policy.
+__device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int R, int* s_plan, int* s_nvs, int lane) {
+  int st = 0;
+  if (lane == 0) st = atomicCAS(s_plan, 0, 1);
+  st = __builtin_amdgcn_readfirstlane(st);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  if (st == 0) {
+    while ((uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(s.sync + kPlanFlag)) == 0u) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
+        if (lane == 0) store_coherent(s.status, 2u);
+        break;
+      }
+    }
+    const int nvs = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.header));
+    for (int k = lane; k < nvs; k += 64) {
+      const uint32_t* v = reinterpret_cast<const uint32_t*>(s.vslots + k);
+      s_vs[k] = make_int4((int)load_coherent(v), (int)load_coherent(v + 1), (int)load_coherent(v + 2),
+                          (int)load_coherent(v + 3));
+    }
+    for (int k = lane; k < R; k += 64) s_tok[k] = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.row_tok + k));
+    if (lane == 0) *s_nvs = nvs;
+    wait_memory();
+    if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * kPlanWaitTicks) {
+        if (lane == 0) store_coherent(s.status, 2u);
+        break;
+      }
+    }
+  }
 }
 
 // The GEMM, one block of NW waves per CU.  Block b of B takes one unit of
@@ -361,22 +411,54 @@ __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) {
 // c are not stored.  Split units store their segment sums in plane s0 of
 // `part`, whole units the tiles' totals in plane 0.  Part planes are
 // [R][width] fp32, R = m (k + 1).
-template <bool W13, int TT, int NW>
+template <bool W13, int TT, int NW, bool ROUTE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
-void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
+void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   __shared__ uint32_t s_next;
+  __shared__ int s_plan, s_nvs;  // ROUTE: the plan's staging state (0, 1, 2) and slot count
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
   uint64_t* tl = W13 ? s.tl_w13 : s.tl_w2;
   stamp(tl, kTlPoints, 0);
-  const UnitMap um = unit_map<W13, TT>(d, s, split);
+  if constexpr (ROUTE) {
+    // blocks [0, m) route the m tokens; the last of them builds the plan,
+    // writes it back from its L2 and raises the plan flag
+    if ((int)blockIdx.x < m) {
+      __shared__ RouteLds L;
+      if (route_block<1>(d, m, blockIdx.x, m, in.bias, s, L)) {
+        wait_memory();
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          store_coherent(s.sync + kPlanFlag, 1u);
+        }
+      }
+      return;
+    }
+  }
   const int R = m * d.K + m;
+  const int P = m * d.K;
   int4* s_vs = reinterpret_cast<int4*>(lds_raw);
-  int* s_tok = reinterpret_cast<int*>(s_vs + um.nvs);  // w13: token of a row; w2: its output row
-  const int* row_map = W13 ? s.row_tok : s.row_out;
-  for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
-  for (int i = tid; i < R; i += NW * 64) s_tok[i] = row_map[i];
+  int* s_tok = reinterpret_cast<int*>(s_vs + vs_cap);  // w13: token of a row; w2: its output row
+  UnitMap um;
+  if constexpr (ROUTE) {
+    // until the plan is in: the shared expert's slots and rows, which do not
+    // depend on the routing
+    const int nS = (m + kTokTile - 1) / kTokTile;
+    um = unit_map_n<W13, TT>(d, nS, nS, split);
+    for (int v = tid; v < nS; v += NW * 64) {
+      const int rows = m - v * kTokTile;
+      s_vs[v] = make_int4(-1, P + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+    }
+    for (int t = tid; t < m; t += NW * 64) s_tok[P + t] = t;
+    if (tid == 0) s_plan = 0;
+  } else {
+    um = unit_map<W13, TT>(d, s, split);
+    const int* row_map = W13 ? s.row_tok : s.row_out;
+    for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
+    for (int i = tid; i < R; i += NW * 64) s_tok[i] = row_map[i];
+  }
   if (tid == 0) s_next = 0;
   __syncthreads();
 
@@ -384,14 +466,24 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split) {
   float* part = W13 ? s.part13 : s.part2;
   const size_t plane = (size_t)R * width;
   // the block's turns i take unit unit_turn(i): units of one slot (costlier
-  // for slots with more rows) spread over every CU
-  const uint32_t B = gridDim.x, turns = (um.total + B - 1) / B;
+  // for slots with more rows) spread over every CU (the routing blocks take
+  // none)
+  const uint32_t nroute = ROUTE ? (uint32_t)m : 0u;
+  const uint32_t B = gridDim.x - nroute, b = blockIdx.x - nroute;
+  bool planned = !ROUTE;
   // first unit by wave index, the rest from the block's counter; the next
   // index is fetched while the current unit streams
   uint32_t i = wave;
-  while (i < turns) {
-    const uint32_t u = unit_turn(i, B);
-    if (u >= um.total) break;  // the last turn has no unit for this block
+  while (true) {
+    const uint32_t u = unit_turn(i, B, b);
+    if (u >= um.total) {
+      // past the shared expert's units: the routed ones need the plan
+      if (planned) break;
+      stage_plan(s, s_vs, s_tok, R, &s_plan, &s_nvs, lane);
+      um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
+      planned = true;
+      if (u >= um.total) break;  // the last turn has no unit for this block
+    }
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int v, tg, s0, s1;
@@ -752,17 +844,17 @@ size_t gemm_lds(const LayerDims& d, int m, int max_vs) {
   return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4;
 }
 
-template <bool W13, int TT, int NW>
+template <bool W13, int TT, int NW, bool ROUTE = false>
 hipError_t launch_gemm_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                          int split, hipStream_t st, const KernelEvents& ev) {
-  return launch_kernel(gemm_kernel<W13, TT, NW>, dim3(grid), dim3(NW * 64), (uint32_t)gemm_lds<W13>(d, m, max_vs),
-                       st, ev, d, in, s, m, split);
+  return launch_kernel(gemm_kernel<W13, TT, NW, ROUTE>, dim3(grid), dim3(NW * 64),
+                       (uint32_t)gemm_lds<W13>(d, m, max_vs), st, ev, d, in, s, m, split, max_vs);
 }
 
-template <bool W13, int TT, int NW>
+template <bool W13, int TT, int NW, bool ROUTE = false>
 int occupancy_t(size_t lds) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<W13, TT, NW>, NW * 64, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<W13, TT, NW, ROUTE>, NW * 64, lds) != hipSuccess)
     return 0;
   return n;
 }
@@ -783,9 +875,13 @@ bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
 }
 
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
-                      hipStream_t st, const KernelEvents& ev) {
-  if (gemm_split(d, m, grid * gemm_waves(true), true))
-    return launch_gemm_t<true, MOE_W13_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
+                      bool route, hipStream_t st, const KernelEvents& ev) {
+  const bool split = gemm_split(d, m, grid * gemm_waves(true), true);
+  if (route) {
+    if (split) return launch_gemm_t<true, MOE_W13_SPLIT, true>(d, m, in, s, grid, max_vs, 1, st, ev);
+    return launch_gemm_t<true, MOE_W13_WHOLE, true>(d, m, in, s, grid, max_vs, 0, st, ev);
+  }
+  if (split) return launch_gemm_t<true, MOE_W13_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
   return launch_gemm_t<true, MOE_W13_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
 
@@ -844,6 +940,9 @@ int gemm_blocks_per_cu(bool w13, size_t lds) {
   if (w13) {
     a = occupancy_t<true, MOE_W13_WHOLE>(lds);
     b = occupancy_t<true, MOE_W13_SPLIT>(lds);
+    const int c = occupancy_t<true, MOE_W13_WHOLE, true>(lds), e = occupancy_t<true, MOE_W13_SPLIT, true>(lds);
+    a = c < a ? c : a;
+    b = e < b ? e : b;
   } else {
     a = occupancy_t<false, MOE_W2_WHOLE>(lds);
     b = occupancy_t<false, MOE_W2_SPLIT>(lds);

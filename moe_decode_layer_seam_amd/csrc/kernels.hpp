@@ -110,6 +110,12 @@ inline int seam_blocks(const LayerDims& d, int m) {
   const int tiles = (m + seam_tb(d.H) - 1) / seam_tb(d.H);
   return seam_fused(m) ? (d.E + epb - 1) / epb * tiles : m;
 }
+// Steps of at most 4 tokens route in the w13 launch's first blocks (one per
+// token) instead of a launch of their own, while the other blocks start on
+// the shared expert: when the router's expert groups fit its four waves
+// and the plan fits one wave (at most 64 pairs).
+inline bool route_in_w13(const LayerDims& d, int m) { return m <= 4 && m * d.K <= 64 && d.E <= 256; }
+constexpr int kPlanFlag = 1;  // word of Scratch::sync raised when the plan is written
 inline int logits_blocks(const LayerDims& d, int m) {
   const int cpt = (d.H + 2047) / 2048;
   const int tb = cpt <= 3 ? 8 : 4, epb = cpt <= 3 ? 4 : 2;
@@ -140,8 +146,10 @@ hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scra
                          const KernelEvents& ev);
 hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                         const KernelEvents& ev);
+// route: the launch also routes (route_in_w13): its first m blocks run the
+// router while the others stream the shared expert's units.
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
-                      hipStream_t st, const KernelEvents& ev);
+                      bool route, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
                       const KernelEvents& ev);
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,

@@ -1,0 +1,341 @@
+// route.hpp -- the router as block-level device code: per token, sigmoid +
+// bias -> top-k -> routing weights, and the token -> expert plan built by the
+// last block to finish.  Used by the route launch (seam.hip) and, for steps
+// of a few tokens, by the first blocks of the w13 launch (experts.hip).
+//
+// Pages: "vllm.models.deepseek_v41.amd.mono.runner" MonoLayerWeights (gate_w,
+// bias: the e_score_correction_bias), build_mono_ffn (expert groups of 64 for
+// the routing sort networks); "vllm.models.deepseek_v41.amd.mono.attention.
+// device" atomic_add_dev (relaxed device-scope counters).
+#pragma once
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+// Exclusive prefix sum of arr[0, n) (n <= 4 * kThreads) in place; returns
+// the total.  Called by all kThreads threads.
+__device__ int block_scan(int* arr, int n, int* tmp4) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int v[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = tid * 4 + q;
+    v[q] = i < n ? arr[i] : 0;
+    sum += v[q];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) tmp4[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += tmp4[w];
+  const int total = tmp4[0] + tmp4[1] + tmp4[2] + tmp4[3];
+  int run = base + inc - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = tid * 4 + q;
+    if (i < n) arr[i] = run;
+    run += v[q];
+  }
+  __syncthreads();
+  return total;
+}
+
+struct RouteLds {
+  uint64_t cand[4][64];      // each wave's sorted selection keys
+  double sig[kMaxExperts];   // this token's sigmoid scores
+  int ids[kMaxTokens * kMaxTopk];
+  float w[kMaxTokens * kMaxTopk];
+  uint32_t mlo[kMaxExperts], mhi[kMaxExperts];  // tokens 0-31 / 32-47 per expert
+  int base[kMaxExperts];
+  int vsb[kMaxExperts];
+  int tmp4[4];
+  int last;
+};
+
+// The plan of a step of at most 64 pairs and 16 tokens, by wave 0 alone:
+// lane p takes pair p, a bitonic sort of the keys expert * 64 + token puts
+// row r's pair in lane r, and every expert has one virtual slot (its rows
+// are at most the 16 tokens).  Same plan as build_plan's general path.
+__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane) {
+  const int E = d.E, K = d.K, P = m * K;
+  // key: expert, token, pair (10 + 4 + 6 bits), unique; sorted ascending over
+  // the smallest power-of-two number of lanes that holds the pairs
+  int key = 0x7FFFFFFF;
+  if (lane < P) key = (L.ids[lane] << 10) | ((lane / K) << 6) | lane;
+  const int width = P <= 8 ? 8 : (P <= 16 ? 16 : (P <= 32 ? 32 : 64));
+  // (every stage unrolled, so each exchange is a fixed DPP or permlane
+  // pattern; a level is skipped as a whole when it is wider than needed)
+#pragma unroll
+  for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+    if (k2 <= width) {
+#pragma unroll
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        const int pk = xor_lane(key, j);
+        // ascending: the lower lane of a pair keeps the smaller key when up
+        const bool keep_min = ((lane & j) == 0) == ((lane & k2) == 0);
+        key = keep_min ? min(key, pk) : max(key, pk);
+      }
+    }
+  }
+  const int r = lane;
+  const bool valid = r < P;
+  const int e = key >> 10, t = (key >> 6) & 15, p = key & 63;
+  const int eprev = __shfl_up(e, 1, 64);
+  const bool first = valid && (r == 0 || eprev != e);
+  const uint64_t fm = __ballot(first);
+  const uint64_t above = r == 63 ? 0ull : fm & ~((2ull << r) - 1ull);
+  const int cnt = (above ? __ffsll((unsigned long long)above) - 1 : P) - r;
+  const int nR = __popcll(fm), nS = 1;
+  if (valid) {
+    s.row_tok[r] = t;
+    s.row_w[r] = L.w[p];
+    s.pair_row[p] = r;
+    s.row_out[r] = p;
+  }
+  if (first) s.vslots[nS + __popcll(fm & ((1ull << r) - 1ull))] = make_int4(e, r, cnt, 0);
+  // tokens per expert: a table in LDS (one wave: its LDS accesses are in
+  // order), then copied out whole
+  for (int x = lane; x < E; x += 64) L.base[x] = 0;
+  if (first) L.base[e] = cnt;
+  for (int x = lane; x < E; x += 64) s.counts[x] = L.base[x];
+  if (lane < m) {
+    s.row_tok[P + lane] = lane;
+    s.row_w[P + lane] = 1.0f;
+    s.row_out[P + lane] = P + lane;
+  }
+  if (lane == 0) {
+    s.vslots[0] = make_int4(-1, P, m, 0);
+    s.header[0] = nS + nR;
+    s.header[1] = nS;
+    s.header[2] = nR;
+    s.header[3] = m;
+    __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The plan, from every token's picks: rows listed by expert ascending, then
+// token ascending; an expert's rows split into virtual slots of at most
+// kTokTile rows; the shared expert's m rows last, its slots first.  With at
+// most 48 tokens, the tokens of an expert form one 64-bit mask and a pair's
+// rank within its expert is the count of lower tokens in the mask.
+// own: the token whose picks this block holds in LDS already.
+__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L) {
+  const int tid = threadIdx.x;
+  const int E = d.E, K = d.K, P = m * K;
+  for (int p = tid; p < P; p += kThreads) {
+    if (p / K == own) continue;
+    L.ids[p] = __hip_atomic_load(&s.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.w[p] = __hip_atomic_load(&s.wts[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (P <= 64 && m <= kTokTile) {
+    __syncthreads();
+    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x);
+    return;
+  }
+  for (int e = tid; e < E; e += kThreads) L.mlo[e] = L.mhi[e] = 0u;
+  __syncthreads();
+  for (int p = tid; p < P; p += kThreads) {
+    const int t = p / K, e = L.ids[p];
+    if (t < 32) atomicOr(&L.mlo[e], 1u << t);
+    else atomicOr(&L.mhi[e], 1u << (t - 32));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    const int c = __popc(L.mlo[e]) + __popc(L.mhi[e]);
+    L.base[e] = c;
+    L.vsb[e] = (c + kTokTile - 1) / kTokTile;
+    s.counts[e] = c;
+  }
+  __syncthreads();
+  block_scan(L.base, E, L.tmp4);
+  const int nR = block_scan(L.vsb, E, L.tmp4);
+  const int nS = (m + kTokTile - 1) / kTokTile;
+  for (int p = tid; p < P; p += kThreads) {
+    const int t = p / K, e = L.ids[p];
+    const int rank = t < 32 ? __popc(L.mlo[e] & ((1u << t) - 1u))
+                            : __popc(L.mlo[e]) + __popc(L.mhi[e] & ((1u << (t - 32)) - 1u));
+    const int r = L.base[e] + rank;
+    s.row_tok[r] = t;
+    s.row_w[r] = L.w[p];
+    s.pair_row[p] = r;
+    s.row_out[r] = p;
+  }
+  for (int e = tid; e < E; e += kThreads) {
+    const int c = __popc(L.mlo[e]) + __popc(L.mhi[e]);
+    for (int v = 0; v * kTokTile < c; ++v) {
+      const int rows = c - v * kTokTile;
+      s.vslots[nS + L.vsb[e] + v] = make_int4(e, L.base[e] + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+    }
+  }
+  for (int t = tid; t < m; t += kThreads) {
+    s.row_tok[P + t] = t;
+    s.row_w[P + t] = 1.0f;
+    s.row_out[P + t] = P + t;
+  }
+  for (int v = tid; v < nS; v += kThreads) {
+    const int rows = m - v * kTokTile;
+    s.vslots[v] = make_int4(-1, P + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+  }
+  if (tid == 0) {
+    s.header[0] = nS + nR;
+    s.header[1] = nS;
+    s.header[2] = nR;
+    s.header[3] = m;
+    __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Selection key of expert e with biased score b: the fp64 order of b
+// (larger first) in the upper 54 bits, then the lower index first.  Scores
+// closer than 2^-42 relative (below the 10 low bits) fall to the index.
+__device__ __forceinline__ uint64_t select_key(double b, int e) {
+  const uint64_t u = (uint64_t)__double_as_longlong(b + 0.0);  // -0 -> +0
+  const uint64_t mono = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (mono & ~0x3FFull) | (uint64_t)(1023 - e);
+}
+
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int mask) {
+  const int lo = xor_lane((int)(uint32_t)v, mask), hi = xor_lane((int)(uint32_t)(v >> 32), mask);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Bitonic sorting network over the 64 lanes, descending, on G independent
+// lists at once.
+template <int G>
+__device__ __forceinline__ void sort64(uint64_t (&k)[G], int lane) {
+#pragma unroll
+  for (int k2 = 2; k2 <= 64; k2 <<= 1) {
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      const bool keep_max = ((lane & j) == 0) == ((lane & k2) == 0);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint64_t p = xor_lane64(k[g], j);
+        k[g] = keep_max ? (p > k[g] ? p : k[g]) : (p < k[g] ? p : k[g]);
+      }
+    }
+  }
+}
+
+// a, c: sorted descending across the lanes.  Leaves the 64 largest of both
+// in a, sorted: the lane-wise larger of a[i] and c[63 - i] is a bitonic
+// sequence holding them, which a half-cleaner cascade sorts.
+__device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
+  const uint64_t r = xor_lane64(c, 63);
+  a = r > a ? r : a;
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t p = xor_lane64(a, j);
+    a = ((lane & j) == 0) ? (p > a ? p : a) : (p < a ? p : a);
+  }
+}
+
+// Block code of the router for token t, run by the first kThreads threads
+// of a block of at least kThreads (the others only take part in its
+// barriers); nblocks route blocks run in the launch (one per token).
+// Returns true in the block that built the plan.  Wave w sorts the selection
+// keys of expert groups w, w + 4, ... (GPW groups of 64) and merges them;
+// wave 0 merges the four waves' lists, and its lanes [0, k) hold the picks
+// in selection order.
+template <int GPW>
+__device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
+                            const Scratch& s, RouteLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = d.E, K = d.K;
+  const int groups = (E + 63) / 64;
+  stamp(s.tl_route, kTlPoints, 0);
+
+  uint64_t k[GPW];
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int ex = 64 * (wave + 4 * i) + lane;
+    k[i] = 0;  // below every real expert's key
+    if (wave < 4 && ex < E) {
+      const double sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex]));
+      const double bb = sg + (double)bias[ex];
+      L.sig[ex] = sg;
+      k[i] = select_key((bb == bb) ? bb : -INFINITY, ex);  // a NaN score ranks last
+    }
+  }
+  stamp(s.tl_route, kTlPoints, 5);
+  if (wave < groups && wave < 4) {
+    sort64<GPW>(k, lane);
+#pragma unroll
+    for (int width = GPW / 2; width >= 1; width >>= 1) {
+#pragma unroll
+      for (int i = 0; i < width; ++i) merge64(k[i], k[i + width], lane);
+    }
+  }
+  if (wave < 4) L.cand[wave][lane] = k[0];
+  __syncthreads();
+  stamp(s.tl_route, kTlPoints, 1);
+  if (wave == 0) {
+    const int nw = groups < 4 ? groups : 4;
+    if (K <= 16) {
+      // the four lists' top 16 side by side (lanes [16 w, +16)), merged by
+      // two bitonic merges: pairs of 16 into 32, then 32 into 64
+      k[0] = (lane >> 4) < nw ? L.cand[lane >> 4][lane & 15] : 0ull;
+      uint64_t p = xor_lane64(k[0], 31);
+      k[0] = (lane & 16) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+#pragma unroll
+      for (int j = 8; j > 0; j >>= 1) {
+        p = xor_lane64(k[0], j);
+        k[0] = (lane & j) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+      }
+      p = xor_lane64(k[0], 63);
+      k[0] = (lane & 32) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+#pragma unroll
+      for (int j = 16; j > 0; j >>= 1) {
+        p = xor_lane64(k[0], j);
+        k[0] = (lane & j) == 0 ? (p > k[0] ? p : k[0]) : (p < k[0] ? p : k[0]);
+      }
+    } else {
+      for (int w = 1; w < nw; ++w) merge64(k[0], L.cand[w][lane], lane);
+    }
+    stamp(s.tl_route, kTlPoints, 6);
+    const int e = 1023 - (int)(k[0] & 0x3FF);
+    const double sg = lane < K ? L.sig[e] : 0.0;
+    const double ssum = wave_sum(sg);
+    if (lane < K) {
+      const float w = (float)((double)d.routed_scale * sg / ssum);
+      L.ids[t * K + lane] = e;
+      L.w[t * K + lane] = w;
+      // read by another block of this launch: stored device-coherent
+      __hip_atomic_store(&s.ids[t * K + lane], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&s.wts[t * K + lane], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  stamp(s.tl_route, kTlPoints, 2);
+
+  if (nblocks > 1) {
+    // Arrival: wait until this block's coherent stores completed, count the
+    // block, and let the last one through to the plan.  Nothing spins.  (A
+    // workgroup-scope fence would not wait for the stores: only the explicit
+    // wait orders them before the count.)
+    wait_memory();
+    __syncthreads();
+    if (tid == 0)
+      L.last = (__hip_atomic_fetch_add(s.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(nblocks - 1));
+    __syncthreads();
+    if (!L.last) return false;
+  } else {
+    __syncthreads();
+  }
+  stamp(s.tl_route, kTlPoints, 3);
+  build_plan(d, m, t, s, L);
+  stamp(s.tl_route, kTlPoints, 4);
+  return true;
+}
+
+
+}  // namespace
+}  // namespace moe
