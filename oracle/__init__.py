@@ -76,6 +76,10 @@ def lib():
         L.orc_fp4_code_index.restype = ctypes.c_size_t
         L.orc_expert_fmt.argtypes = [_I, _I, _I] + [_P] * 9
         L.orc_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
+        L.orc_hc_fold.argtypes = [_I, _I] + [_P] * 7
+        L.orc_vllm_mx_code.argtypes = [ctypes.c_double]
+        L.orc_vllm_mx_code.restype = _I
+        L.orc_attn_x8.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P, _P]
         L.orc_router.argtypes = [_I, _I, _I, _I, _P, _P, _P, ctypes.c_float,
                                  _P, _P, _P, _P]
         L.orc_plan.argtypes = [_I, _I, _I, _P, _P, _P]
@@ -83,7 +87,8 @@ def lib():
         L.orc_layer.argtypes = [ctypes.POINTER(Dims), _I] + [_P] * 20
         L.orc_layer.restype = _I
         for f in ("orc_mx_quant_row", "orc_quant_weight", "orc_quant_weight_fp4",
-                  "orc_rmsnorm", "orc_router", "orc_plan", "orc_expert", "orc_expert_fmt"):
+                  "orc_rmsnorm", "orc_router", "orc_plan", "orc_expert", "orc_expert_fmt",
+                  "orc_hc_fold", "orc_attn_x8"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -213,6 +218,37 @@ def quant_weight_fp4_into(w, q_out: np.ndarray, s_out: np.ndarray) -> None:
 
 
 # ---- layer steps ---------------------------------------------------------
+
+def hc_fold(part, residual, post, res, pre) -> tuple[np.ndarray, np.ndarray]:
+    """The hyper-connection residual fold: part bf16 bits [m, H], residual
+    [m, 4, H], post [m, 4], res [m, 4, 4], pre [m, 4] -> (residual_out
+    [m, 4, H], x [m, H]) bf16 bits."""
+    part = _c(part, np.uint16)
+    residual = _c(residual, np.uint16)
+    post, res, pre = _c(post, np.float32), _c(res, np.float32), _c(pre, np.float32)
+    m, h = part.shape
+    assert residual.shape == (m, 4, h) and post.shape == (m, 4) and res.shape == (m, 4, 4) and pre.shape == (m, 4)
+    ro = np.empty((m, 4, h), np.uint16)
+    x = np.empty((m, h), np.uint16)
+    lib().orc_hc_fold(m, h, _p(part), _p(residual), _p(post), _p(res), _p(pre), _p(ro), _p(x))
+    return ro, x
+
+
+def vllm_mx_code(amax: float) -> int:
+    return lib().orc_vllm_mx_code(amax)
+
+
+def attn_x8(x, w, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """The attention seam's norm + MXFP8: x bf16 bits [m, H], w [H] ->
+    (x8 [m, H], x8s [m, H/32])."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    m, h = x.shape
+    x8 = np.empty((m, h), np.uint8)
+    x8s = np.empty((m, h // 32), np.uint8)
+    lib().orc_attn_x8(m, h, _p(x), _p(w), eps, _p(x8), _p(x8s))
+    return x8, x8s
+
 
 def rmsnorm(x, w, eps: float) -> np.ndarray:
     x = _c(x, np.uint16)

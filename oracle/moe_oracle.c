@@ -515,3 +515,95 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   free(acc);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* The seam around the MoE: the hyper-connection residual fold and the      */
+/* attention seam's MXFP8 ([layer] run_ffn, store_x8; [runner] ffn)          */
+/* ------------------------------------------------------------------------ */
+
+void orc_hc_fold(int32_t m, int32_t h, const uint16_t* part, const uint16_t* residual,
+                 const float* post, const float* res, const float* pre,
+                 uint16_t* residual_out, uint16_t* x) {
+  /* [layer] run_ffn: the attention's output (part, TP-summed) is folded into
+   * the four-stream residual [m, 4, H] with the attention seam's mixes
+   * ([runner] ffn: post_mix [m, 4, 1], res_mix [m, 4, 4]); the FFN's input
+   * row combines the streams with pre_mix [m, 4].  The pages give the shapes,
+   * not the arithmetic; the reading taken: stream i of the new residual is
+   * bf16(sum_j res[i][j] r_j + post[i] part), the input row
+   * bf16(sum_i pre[i] r'_i) over the stored (bf16) new streams, each sum in
+   * double in the order written, one rounding. */
+  for (int32_t t = 0; t < m; ++t) {
+    const uint16_t* r = residual + (size_t)t * 4 * h;
+    uint16_t* ro = residual_out + (size_t)t * 4 * h;
+    const float* po = post + (size_t)t * 4;
+    const float* rm = res + (size_t)t * 16;
+    const float* pr = pre + (size_t)t * 4;
+    for (int32_t c = 0; c < h; ++c) {
+      double rv[4];
+      for (int j = 0; j < 4; ++j) rv[j] = orc_bf16_value(r[(size_t)j * h + c]);
+      const double pv = orc_bf16_value(part[(size_t)t * h + c]);
+      double xs = 0.0;
+      for (int i = 0; i < 4; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < 4; ++j) acc += (double)rm[i * 4 + j] * rv[j];
+        acc += (double)po[i] * pv;
+        const uint16_t b = orc_bf16_rne(acc);
+        ro[(size_t)i * h + c] = b;
+        xs += (double)pr[i] * orc_bf16_value(b);
+      }
+      x[(size_t)t * h + c] = orc_bf16_rne(xs);
+    }
+  }
+}
+
+int32_t orc_vllm_mx_code(double amax) {
+  /* [layer] store_x8 quantises with vLLM's MXFP8 code (vllm_mx_code, not
+   * printed), then clamps the scaled values to the E4M3 range (clamp_fp8).
+   * The reading taken: the OCP MX rule, code = floor(log2(amax)) - 8 + 127
+   * (8: the exponent of E4M3's largest power of two), clamped to [0, 254]
+   * (0 for amax = 0); the clamp is what keeps the scaled values, which can
+   * reach 2^9, inside +-448. */
+  if (!(amax > 0.0)) return 0;
+  int e;
+  (void)frexp(amax, &e); /* amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  int32_t c = (e - 1) - 8 + 127;
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+void orc_attn_x8(int32_t m, int32_t h, const uint16_t* x, const uint16_t* w, float eps,
+                 uint8_t* x8, uint8_t* x8s) {
+  /* [layer] store_x8: the attention seam's norm output (the RMSNorm chain of
+   * orc_rmsnorm up to its fp32 product, not rounded to bf16) -> per 32
+   * columns vllm_mx_code of the amax, the values scaled by 2^(127 - code),
+   * clamped to +-448 and rounded to E4M3. */
+  float* y = (float*)malloc(sizeof(float) * (size_t)h);
+  if (!y) return;
+  for (int32_t t = 0; t < m; ++t) {
+    const uint16_t* xr = x + (size_t)t * h;
+    double ss = 0.0;
+    for (int32_t i = 0; i < h; ++i) {
+      double v = orc_bf16_value(xr[i]);
+      ss += v * v;
+    }
+    float r = round_f32(1.0 / sqrt(ss / (double)h + (double)eps));
+    for (int32_t i = 0; i < h; ++i) {
+      float xr_ = round_f32(orc_bf16_value(xr[i]) * (double)r);
+      y[i] = round_f32((double)xr_ * orc_bf16_value(w[i]));
+    }
+    for (int32_t g = 0; g < h / 32; ++g) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs((double)y[g * 32 + i]) > amax) amax = fabs((double)y[g * 32 + i]);
+      int32_t c = orc_vllm_mx_code(amax);
+      x8s[(size_t)t * (h / 32) + g] = (uint8_t)c;
+      for (int i = 0; i < 32; ++i) {
+        double v = ldexp((double)y[g * 32 + i], 127 - c);
+        if (v > 448.0) v = 448.0;
+        if (v < -448.0) v = -448.0;
+        x8[(size_t)t * h + g * 32 + i] = orc_e4m3_rne(v);
+      }
+    }
+  }
+  free(y);
+}
+

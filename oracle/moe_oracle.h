@@ -140,6 +140,21 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
                   uint8_t* x8s, double* logits, int32_t* ids, double* wts,
                   double* out_f64, uint16_t* out);
 
+/* The hyper-connection residual fold around the FFN seam: residual and
+ * residual_out bf16 [m, 4, H], part bf16 [m, H], post [m, 4], res [m, 4, 4]
+ * (res[i][j]: output stream i, input stream j), pre [m, 4]; x bf16 [m, H]
+ * the FFN's input row. */
+void orc_hc_fold(int32_t m, int32_t h, const uint16_t* part, const uint16_t* residual,
+                 const float* post, const float* res, const float* pre,
+                 uint16_t* residual_out, uint16_t* x);
+/* The attention seam's MXFP8 scale code of a 32-group's amax (vLLM's rule as
+ * read here: floor(log2(amax)) - 8 + 127, clamped to [0, 254]). */
+int32_t orc_vllm_mx_code(double amax);
+/* The attention seam's norm + MXFP8 (store_x8): x bf16 [m, H], w bf16 [H]
+ * -> x8 [m, H] E4M3, x8s [m, H/32]. */
+void orc_attn_x8(int32_t m, int32_t h, const uint16_t* x, const uint16_t* w, float eps,
+                 uint8_t* x8, uint8_t* x8s);
+
 #ifdef __cplusplus
 }
 #endif
