@@ -162,6 +162,56 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def seam_timing(m: int, H: int, reps: int = 50) -> dict:
+    """Device time of the seam upstream of the MoE at m rows of H columns:
+    the hyper-connection residual fold and the attention seam's MXFP8, each
+    replayed from a graph of `reps` launches on synthetic inputs resident in
+    HBM.  Bytes are the algorithmic ones (every input read once, every output
+    written once)."""
+    import torch
+    import moe_decode_layer_seam_amd as mdl
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    part = torch.randn((m, H), generator=g, device="cuda").to(torch.bfloat16)
+    resid = torch.randn((m, 4, H), generator=g, device="cuda").to(torch.bfloat16)
+    post = torch.rand((m, 4), generator=g, device="cuda") * 2
+    res = torch.rand((m, 4, 4), generator=g, device="cuda")
+    pre = torch.rand((m, 4), generator=g, device="cuda")
+    rout, x = torch.empty_like(resid), torch.empty_like(part)
+    norm_w = (1 + 0.1 * torch.randn((H,), generator=g, device="cuda")).to(torch.bfloat16)
+    x8 = torch.empty((m, H), dtype=torch.uint8, device="cuda")
+    x8s = torch.empty((m, H // 32), dtype=torch.uint8, device="cuda")
+    calls = {
+        "hc_fold": (lambda: mdl.hc_fold(part, resid, post, res, pre, rout, x),
+                    20 * m * H + m * 24 * 4),
+        "attn_x8": (lambda: mdl.attn_x8(part, norm_w, 1e-6, x8, x8s),
+                    2 * m * H + 2 * H + m * H + m * H // 32),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(gr, stream=s):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.current_stream().wait_stream(s)
+        gr.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (5 * reps)
+        out[name] = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+        del gr
+    return out
+
+
 def copy_probe(mib: int, reps: int = 5) -> int:
     """A plain device copy of known size (for calibrating the HBM byte
     counters): dst = ~src over mib MiB of int32, reps times."""
@@ -385,6 +435,8 @@ def main() -> int:
                      "traffic": measured_traffic(dom, cfg["name"] + ("" if args.routed == "e4m3" else "_mxfp4")),
                      "algorithmic_bytes": dom_bytes},
     }
+    # the seam upstream of the MoE (reported beside the step, not part of it)
+    res["upstream_seam"] = seam_timing(m, H)
     mdl.destroy(h)
     graphs.clear()
     del wsets

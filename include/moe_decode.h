@@ -250,6 +250,47 @@ int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows
                                    int32_t cols, void* d_q, void* d_scales,
                                    void* stream);
 
+/* The seam upstream of the MoE ([layer] run_ffn: the attention's partials
+ * summed and folded into the four-stream hyper-connection residual, whose
+ * streams then give the FFN's input row; [runner] DSV41MonoLayer.ffn for
+ * the shapes).  For each of m tokens (1 <= m <= 48) and column c < hidden:
+ *   residual_out[t][i][c] = bf16(sum_j res[t][i][j] residual[t][j][c]
+ *                                + post[t][i] part[t][c])       (i, j < 4)
+ *   x[t][c] = bf16(sum_i pre[t][i] residual_out[t][i][c])
+ * each sum in double precision in the order written, one rounding to nearest
+ * even.  The pages give the tensors, not this arithmetic (the reading taken
+ * here); the mixes of the FFN seam itself (its gate) are not computed: pre
+ * is an input.
+ *   d_part          bf16 [m, H]     attention output (TP-summed)
+ *   d_residual      bf16 [m, 4, H]
+ *   d_post          f32  [m, 4]     (the pages' [m, 4, 1])
+ *   d_res           f32  [m, 4, 4]  res[t][i][j]: output stream i, input j
+ *   d_pre           f32  [m, 4]
+ *   d_residual_out  bf16 [m, 4, H]  may be d_residual itself (in place),
+ *                                   else must not overlap it
+ *   d_x             bf16 [m, H]     must not overlap any other argument
+ * hidden a multiple of 128, <= 16384; pointers 16-byte aligned.  EINVAL on
+ * bad arguments (nothing enqueued), EHIP on a failed launch. */
+int moe_decode_hc_fold(int32_t m, int32_t hidden, const void* d_part,
+                       const void* d_residual, const float* d_post,
+                       const float* d_res, const float* d_pre,
+                       void* d_residual_out, void* d_x, void* stream);
+
+/* The attention seam's input quantisation ([layer] store_x8): the RMSNorm of
+ * each row x [m, H] bf16 with weight d_norm_w bf16 [H] (the seam's chain:
+ * sum of squares in double, r = 1/sqrt(ss/H + eps) rounded once to fp32,
+ * two fp32 products; no bf16 rounding), then per 32 columns vLLM's MXFP8
+ * code of the amax, read as the OCP MX rule code = floor(log2(amax)) - 8 +
+ * 127 clamped to [0, 254], the values scaled by 2^(127 - code), clamped to
+ * +-448 (clamp_fp8) and rounded to nearest even E4M3.
+ *   d_x8   u8 [m, H]     E4M3
+ *   d_x8s  u8 [m, H/32]  E8M0 codes
+ * 1 <= m <= 48, hidden a multiple of 128, <= 16384, rms_eps finite >= 0;
+ * pointers 16-byte aligned.  EINVAL / EHIP as above. */
+int moe_decode_attn_x8(int32_t m, int32_t hidden, const void* d_x,
+                       const void* d_norm_w, float rms_eps, void* d_x8,
+                       void* d_x8s, void* stream);
+
 /* Text of an error code. */
 const char* moe_decode_strerror(int code);
 /* The last HIP error a plan (or, with NULL, the library) saw, as text. */

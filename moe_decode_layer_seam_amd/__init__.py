@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_quantize_weight_fp4.argtypes = [_P, ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, _P, _P, _P]
         L.moe_decode_quantize_weight_fp4.restype = ctypes.c_int
+        L.moe_decode_hc_fold.argtypes = [ctypes.c_int32, ctypes.c_int32] + [_P] * 8
+        L.moe_decode_hc_fold.restype = ctypes.c_int
+        L.moe_decode_attn_x8.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P, _P]
+        L.moe_decode_attn_x8.restype = ctypes.c_int
         L.moe_decode_strerror.argtypes = [ctypes.c_int]
         L.moe_decode_strerror.restype = ctypes.c_char_p
         L.moe_decode_last_hip_error.argtypes = [_P]
@@ -103,8 +107,8 @@ EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
            "moe_decode_inspect", "moe_decode_timing", "moe_decode_timing_read",
            "moe_decode_timeline", "moe_decode_timeline_read",
            "moe_decode_destroy", "moe_decode_quantize_weight",
-           "moe_decode_quantize_weight_fp4", "moe_decode_strerror",
-           "moe_decode_last_hip_error")
+           "moe_decode_quantize_weight_fp4", "moe_decode_hc_fold", "moe_decode_attn_x8",
+           "moe_decode_strerror", "moe_decode_last_hip_error")
 
 
 def strerror(code: int) -> str:
@@ -258,6 +262,44 @@ def timeline_read(handle: int, kernel: str):
 
 def destroy(handle: int) -> None:
     lib().moe_decode_destroy(handle)
+
+
+def hc_fold(part: torch.Tensor, residual: torch.Tensor, post: torch.Tensor, res: torch.Tensor,
+            pre: torch.Tensor, residual_out: torch.Tensor = None, x: torch.Tensor = None, stream=None):
+    """moe_decode_hc_fold: part bf16 [m, H], residual bf16 [m, 4, H], post f32
+    [m, 4] (or [m, 4, 1]), res f32 [m, 4, 4], pre f32 [m, 4] -> (residual_out
+    [m, 4, H], x [m, H]) bf16.  residual_out may be residual (in place)."""
+    m, H = part.shape
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if x is None:
+        x = torch.empty_like(part)
+    ptrs = [_tensor(part, "part", (m, H), torch.bfloat16),
+            _tensor(residual, "residual", (m, 4, H), torch.bfloat16),
+            _tensor(post.reshape(m, 4) if post.dim() == 3 else post, "post", (m, 4), torch.float32),
+            _tensor(res, "res", (m, 4, 4), torch.float32),
+            _tensor(pre, "pre", (m, 4), torch.float32),
+            _tensor(residual_out, "residual_out", (m, 4, H), torch.bfloat16),
+            _tensor(x, "x", (m, H), torch.bfloat16)]
+    _check(lib().moe_decode_hc_fold(m, H, *ptrs, _stream_ptr(stream)), "moe_decode_hc_fold")
+    return residual_out, x
+
+
+def attn_x8(x: torch.Tensor, norm_w: torch.Tensor, rms_eps: float = 1e-6, x8: torch.Tensor = None,
+            x8s: torch.Tensor = None, stream=None):
+    """moe_decode_attn_x8: x bf16 [m, H], norm_w bf16 [H] -> (x8 uint8 [m, H]
+    E4M3, x8s uint8 [m, H/32] E8M0)."""
+    m, H = x.shape
+    if x8 is None:
+        x8 = torch.empty((m, H), dtype=torch.uint8, device=x.device)
+    if x8s is None:
+        x8s = torch.empty((m, H // 32), dtype=torch.uint8, device=x.device)
+    ptrs = [_tensor(x, "x", (m, H), torch.bfloat16), _tensor(norm_w, "norm_w", (H,), torch.bfloat16)]
+    _check(lib().moe_decode_attn_x8(m, H, *ptrs, rms_eps,
+                                    _tensor(x8, "x8", (m, H), torch.uint8),
+                                    _tensor(x8s, "x8s", (m, H // 32), torch.uint8), _stream_ptr(stream)),
+           "moe_decode_attn_x8")
+    return x8, x8s
 
 
 def fp4_codes_shape(rows: int, cols: int) -> tuple:

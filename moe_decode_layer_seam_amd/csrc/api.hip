@@ -447,6 +447,42 @@ int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows
   return MOE_DECODE_OK;
 }
 
+int moe_decode_hc_fold(int32_t m, int32_t hidden, const void* d_part, const void* d_residual, const float* d_post,
+                       const float* d_res, const float* d_pre, void* d_residual_out, void* d_x, void* stream) {
+  if (m < 1 || m > kMaxTokens || hidden < 128 || hidden > kMaxHidden || hidden % 128) return MOE_DECODE_EINVAL;
+  const void* ptrs[] = {d_part, d_residual, d_post, d_res, d_pre, d_residual_out, d_x};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MOE_DECODE_EINVAL;
+  // the new residual may replace the old one in place, or lie apart from it;
+  // x lies apart from every input
+  const uintptr_t ri = reinterpret_cast<uintptr_t>(d_residual), ro = reinterpret_cast<uintptr_t>(d_residual_out);
+  const uintptr_t rn = (uintptr_t)m * 4 * hidden * 2, xn = (uintptr_t)m * hidden * 2;
+  if (ri != ro && ri < ro + rn && ro < ri + rn) return MOE_DECODE_EINVAL;
+  const uintptr_t xo = reinterpret_cast<uintptr_t>(d_x), po = reinterpret_cast<uintptr_t>(d_part);
+  if ((xo < ri + rn && ri < xo + xn) || (xo < ro + rn && ro < xo + xn) || (xo < po + xn && po < xo + xn))
+    return MOE_DECODE_EINVAL;
+  hipError_t e = launch_hc_fold(m, hidden, static_cast<const uint16_t*>(d_part),
+                                static_cast<const uint16_t*>(d_residual), d_post, d_res, d_pre,
+                                static_cast<uint16_t*>(d_residual_out), static_cast<uint16_t*>(d_x),
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hc_fold launch");
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_attn_x8(int32_t m, int32_t hidden, const void* d_x, const void* d_norm_w, float rms_eps, void* d_x8,
+                       void* d_x8s, void* stream) {
+  if (m < 1 || m > kMaxTokens || hidden < 128 || hidden > kMaxHidden || hidden % 128) return MOE_DECODE_EINVAL;
+  if (!std::isfinite(rms_eps) || rms_eps < 0.0f) return MOE_DECODE_EINVAL;
+  const void* ptrs[] = {d_x, d_norm_w, d_x8, d_x8s};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MOE_DECODE_EINVAL;
+  hipError_t e = launch_attn_x8(m, hidden, static_cast<const uint16_t*>(d_x), static_cast<const uint16_t*>(d_norm_w),
+                                rms_eps, static_cast<uint8_t*>(d_x8), static_cast<uint8_t*>(d_x8s),
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "attn_x8 launch");
+  return MOE_DECODE_OK;
+}
+
 const char* moe_decode_strerror(int code) {
   switch (code) {
     case MOE_DECODE_OK: return "success";

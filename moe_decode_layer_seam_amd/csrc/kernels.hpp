@@ -171,6 +171,12 @@ int gemm_waves(bool w13);  // waves per block of the GEMM
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13);
 hipError_t launch_quant_weight(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,
                                hipStream_t st);
+// The seam upstream of the MoE (hc.hip): the hyper-connection residual fold
+// and the attention seam's MXFP8.
+hipError_t launch_hc_fold(int m, int H, const uint16_t* part, const uint16_t* residual, const float* post,
+                          const float* res, const float* pre, uint16_t* residual_out, uint16_t* x, hipStream_t st);
+hipError_t launch_attn_x8(int m, int H, const uint16_t* x, const uint16_t* w, float eps, uint8_t* x8, uint8_t* x8s,
+                          hipStream_t st);
 // MXFP4 of count [rows, cols] matrices (rows % 16 == 0, cols % 32 == 0):
 // E2M1 pairs and blocked codes [rows/16][ceil(cols/512)][16][16] each.
 hipError_t launch_quant_weight_fp4(const float* w, int count, int rows, int cols, uint8_t* q, uint8_t* sc,

@@ -57,3 +57,24 @@ def test_null_handles_are_rejected():
     assert L.moe_decode_quantize_weight_fp4(None, 1, 24, 32, None, None, None) == mdl.EINVAL  # rows % 16
     L.moe_decode_destroy(None)
     assert mdl.strerror(mdl.ECAPTURE) == "called during stream capture"
+
+
+def test_seam_entry_points_reject_bad_arguments_without_a_gpu():
+    L = mdl.lib()
+    ok = ctypes.c_void_p(256)  # aligned, never dereferenced: argument checks come first
+    args7 = [ok] * 7
+    assert L.moe_decode_hc_fold(0, 256, *args7, None) == mdl.EINVAL      # m
+    assert L.moe_decode_hc_fold(49, 256, *args7, None) == mdl.EINVAL
+    assert L.moe_decode_hc_fold(1, 200, *args7, None) == mdl.EINVAL      # hidden % 128
+    assert L.moe_decode_hc_fold(1, 256, *([None] + [ok] * 6), None) == mdl.EINVAL
+    # x overlapping the residual
+    assert L.moe_decode_hc_fold(1, 256, ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ok, ok, ok,
+                                ctypes.c_void_p(3 << 20), ctypes.c_void_p((2 << 20) + 512), None) == mdl.EINVAL
+    # partial overlap of residual_out and residual
+    assert L.moe_decode_hc_fold(1, 256, ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ok, ok, ok,
+                                ctypes.c_void_p((2 << 20) + 256), ctypes.c_void_p(4 << 20), None) == mdl.EINVAL
+    assert L.moe_decode_attn_x8(0, 256, ok, ok, ctypes.c_float(1e-6), ok, ok, None) == mdl.EINVAL
+    assert L.moe_decode_attn_x8(1, 96, ok, ok, ctypes.c_float(1e-6), ok, ok, None) == mdl.EINVAL
+    assert L.moe_decode_attn_x8(1, 256, ok, ok, ctypes.c_float(-1.0), ok, ok, None) == mdl.EINVAL
+    assert L.moe_decode_attn_x8(1, 256, ok, None, ctypes.c_float(1e-6), ok, ok, None) == mdl.EINVAL
+
