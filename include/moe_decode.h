@@ -142,7 +142,12 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  * smaller than its shape above is read past its end (the pages check shapes
  * on the host for the same reason, _check_tensors).  The caller keeps every
  * buffer alive until the enqueued work completes.  A plan serves one stream
- * at a time: two runs of one plan must not overlap (they share its scratch). */
+ * at a time: two runs of one plan must not overlap (they share its scratch).
+ * For m <= 4 (at most 64 pairs, E <= 256) the router runs in the first m
+ * blocks of the w13 launch, whose other blocks wait for its plan; the launch
+ * has one block per CU, so with all its blocks resident the wait always
+ * ends.  A wait that runs past 100 ms (another workload holding CUs for that
+ * long) flags the run in MOE_DECODE_TAP_STATUS and goes on. */
 int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
                    const void* d_norm_w, const void* d_gate_w,
                    const float* d_bias, const void* d_w13,
@@ -166,9 +171,10 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
  *   ROW_TOK   i32  [R]          token of each row
  *   A8        u8   [R, Imax]    E4M3 SiLU*up intermediate (Imax = max(I, Is))
  *   A8S       u8   [R, Imax/32] its E8M0 codes
- *   STATUS    u32  [1]          0, or nonzero when a wait of the fused
- *                               expert launch timed out (the output is then
- *                               not valid) */
+ *   STATUS    u32  [1]          0, or nonzero when a wait timed out and the
+ *                               output is not valid: 1 the fused expert
+ *                               launch's wait for a slot's a8, 2 the w13
+ *                               launch's wait for the plan (m <= 4) */
 enum moe_decode_tap {
   MOE_DECODE_TAP_NORMED = 0,
   MOE_DECODE_TAP_X8 = 1,
