@@ -326,6 +326,16 @@ __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
 __device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(int4* p, int4 v) {
+  int* q = reinterpret_cast<int*>(p);
+  store_coherent(q, v.x);
+  store_coherent(q + 1, v.y);
+  store_coherent(q + 2, v.z);
+  store_coherent(q + 3, v.w);
+}
 __device__ __forceinline__ uint32_t count_arrival(uint32_t* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

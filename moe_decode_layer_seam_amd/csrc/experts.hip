@@ -366,10 +366,11 @@ constexpr uint64_t kPlanWaitTicks = 10000000ull;
 
 // The plan of a w13 launch that routes in its first blocks, copied into the
 // block's LDS by the first wave that needs it (the others wait for that
-// wave): the slots, every row's token and the slot count.  The plan's
-// builder wrote it back from its L2 before it raised the flag; it is read
-// with the coherent policy.
-__device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int R, int* s_plan, int* s_nvs, int lane) {
+// wave): the routed slots, their rows' tokens and the slot count.  The plan's
+// builder stored them device-coherent before it raised the flag; they are
+// read with the coherent policy.
+__device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap, int* s_plan, int* s_nvs,
+                           int lane) {
   int st = 0;
   if (lane == 0) st = atomicCAS(s_plan, 0, 1);
   st = __builtin_amdgcn_readfirstlane(st);
@@ -382,13 +383,17 @@ __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int R, int*
         break;
       }
     }
+    // one round trip: the slot count, the routed slots [nS, nS + P) (at most
+    // that many; those past the count are not used) and the routed rows'
+    // tokens; the shared slots and rows are in LDS already
     const int nvs = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.header));
-    for (int k = lane; k < nvs; k += 64) {
+    const int vend = min(nS + P, vs_cap);
+    for (int k = nS + lane; k < vend; k += 64) {
       const uint32_t* v = reinterpret_cast<const uint32_t*>(s.vslots + k);
       s_vs[k] = make_int4((int)load_coherent(v), (int)load_coherent(v + 1), (int)load_coherent(v + 2),
                           (int)load_coherent(v + 3));
     }
-    for (int k = lane; k < R; k += 64) s_tok[k] = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.row_tok + k));
+    for (int k = lane; k < P; k += 64) s_tok[k] = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.row_tok + k));
     if (lane == 0) *s_nvs = nvs;
     wait_memory();
     if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -422,18 +427,11 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   uint64_t* tl = W13 ? s.tl_w13 : s.tl_w2;
   stamp(tl, kTlPoints, 0);
   if constexpr (ROUTE) {
-    // blocks [0, m) route the m tokens; the last of them builds the plan,
-    // writes it back from its L2 and raises the plan flag
+    // blocks [0, m) route the m tokens; the last of them builds the plan and
+    // raises the plan flag as soon as what this launch reads of it is stored
     if ((int)blockIdx.x < m) {
       __shared__ RouteLds L;
-      if (route_block<1>(d, m, blockIdx.x, m, in.bias, s, L)) {
-        wait_memory();
-        __syncthreads();
-        if (tid == 0) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          store_coherent(s.sync + kPlanFlag, 1u);
-        }
-      }
+      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.sync + kPlanFlag);
       return;
     }
   }
@@ -479,7 +477,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     if (u >= um.total) {
       // past the shared expert's units: the routed ones need the plan
       if (planned) break;
-      stage_plan(s, s_vs, s_tok, R, &s_plan, &s_nvs, lane);
+      stage_plan(s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
       um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
       planned = true;
       if (u >= um.total) break;  // the last turn has no unit for this block
