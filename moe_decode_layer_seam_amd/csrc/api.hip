@@ -186,7 +186,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   // counters of the fused launch: status (padded to its own 256 bytes), the
   // slots' ready words, the act groups' unit counts
   const int act_stride = d.Imax / kActCols;
-  const size_t nsync = 64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride;
+  const size_t nsync = 64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPlanBox;
   const size_t o_sync = take(nsync * 4);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
   // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
@@ -239,6 +239,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.status = s.sync;
   s.ready = s.sync + 64;
   s.act_cnt = s.ready + p->max_vs;
+  s.plan_box = s.act_cnt + (size_t)p->max_vs * act_stride;
   s.nsync = (int)nsync;
   s.act_stride = act_stride;
   s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = s.tl_experts = nullptr;

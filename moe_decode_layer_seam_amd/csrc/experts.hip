@@ -364,11 +364,11 @@ __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) { return u
 // goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
 constexpr uint64_t kPlanWaitTicks = 10000000ull;
 
-// The plan of a w13 launch that routes in its first blocks, copied into the
-// block's LDS by the first wave that needs it (the others wait for that
-// wave): the routed slots, their rows' tokens and the slot count.  The plan's
-// builder stored them device-coherent before it raised the flag; they are
-// read with the coherent policy.
+// The routed slots of a w13 launch that routes in its first blocks, copied
+// into the block's LDS by the first wave that needs them (the others wait
+// for that wave): the wave reads the plan box until the count and every slot
+// it counts carry the tag, then expands each slot's token mask into its rows.
+// On a timeout the status word is set and no routed slot is staged.
 __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap, int* s_plan, int* s_nvs,
                            int lane) {
   int st = 0;
@@ -376,25 +376,32 @@ __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int
   st = __builtin_amdgcn_readfirstlane(st);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   if (st == 0) {
-    while ((uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(s.sync + kPlanFlag)) == 0u) {
-      __builtin_amdgcn_s_sleep(1);
+    int nR = 0;
+    uint32_t sv = 0;
+    while (true) {
+      const uint32_t hv = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(s.plan_box));
+      sv = lane < P ? load_coherent(s.plan_box + 1 + lane) : kBoxTag;
+      const int n = min((int)(hv & 0xFFFFu), min(P, vs_cap - nS));
+      if ((hv & kBoxTag) && __ballot(lane < n && !(sv & kBoxTag)) == 0ull) {
+        nR = n;
+        break;
+      }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
         if (lane == 0) store_coherent(s.status, 2u);
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    // one round trip: the slot count, the routed slots [nS, nS + P) (at most
-    // that many; those past the count are not used) and the routed rows'
-    // tokens; the shared slots and rows are in LDS already
-    const int nvs = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.header));
-    const int vend = min(nS + P, vs_cap);
-    for (int k = nS + lane; k < vend; k += 64) {
-      const uint32_t* v = reinterpret_cast<const uint32_t*>(s.vslots + k);
-      s_vs[k] = make_int4((int)load_coherent(v), (int)load_coherent(v + 1), (int)load_coherent(v + 2),
-                          (int)load_coherent(v + 3));
+    if (lane < nR) {
+      const int e = (int)(sv & 0xFFu), r = (int)((sv >> 8) & 63u);
+      const uint32_t mask = (sv >> 16) & 15u;
+      s_vs[nS + lane] = make_int4(e, r, __popc(mask), 0);
+      int i = r;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (((mask >> t) & 1u) && i < P) s_tok[i++] = t;
     }
-    for (int k = lane; k < P; k += 64) s_tok[k] = (int)load_coherent(reinterpret_cast<const uint32_t*>(s.row_tok + k));
-    if (lane == 0) *s_nvs = nvs;
+    if (lane == 0) *s_nvs = nS + nR;
     wait_memory();
     if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
@@ -428,10 +435,10 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   stamp(tl, kTlPoints, 0);
   if constexpr (ROUTE) {
     // blocks [0, m) route the m tokens; the last of them builds the plan and
-    // raises the plan flag as soon as what this launch reads of it is stored
+    // stores the routed slots in the plan box first
     if ((int)blockIdx.x < m) {
       __shared__ RouteLds L;
-      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.sync + kPlanFlag);
+      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.plan_box);
       return;
     }
   }

@@ -53,6 +53,7 @@ struct Scratch {
   uint32_t* status;
   uint32_t* ready;     // [max_vs]
   uint32_t* act_cnt;   // [max_vs][act_stride]
+  uint32_t* plan_box;  // [kPlanBox] the routed slots of a w13 launch that routes (tagged words)
   int nsync;
   int act_stride;      // Imax / 64
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
@@ -115,7 +116,13 @@ inline int seam_blocks(const LayerDims& d, int m) {
 // the shared expert: when the router's expert groups fit its four waves
 // and the plan fits one wave (at most 64 pairs).
 inline bool route_in_w13(const LayerDims& d, int m) { return m <= 4 && m * d.K <= 64 && d.E <= 256; }
-constexpr int kPlanFlag = 1;  // word of Scratch::sync raised when the plan is written
+// The plan as the w13 launch that routes reads it: word 0 the routed slot
+// count, word 1 + k routed slot k as expert (bits 0-7), first row (8-13) and
+// its rows' tokens as a bit mask (16-19; a slot's rows are its tokens in
+// ascending order).  Every word has bit 31 set, and the box is zeroed before
+// each step, so a reader knows a word is in from the word alone.
+constexpr int kPlanBox = 65;
+constexpr uint32_t kBoxTag = 0x80000000u;
 inline int logits_blocks(const LayerDims& d, int m) {
   const int cpt = (d.H + 2047) / 2048;
   const int tb = cpt <= 3 ? 8 : 4, epb = cpt <= 3 ? 4 : 2;

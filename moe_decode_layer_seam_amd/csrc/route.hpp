@@ -64,11 +64,9 @@ struct RouteLds {
 // lane p takes pair p, a bitonic sort of the keys expert * 64 + token puts
 // row r's pair in lane r, and every expert has one virtual slot (its rows
 // are at most the 16 tokens).  Same plan as build_plan's general path.
-// publish (may be nullptr): a flag raised as soon as the slots, the rows'
-// tokens and the header are stored, for a launch whose other blocks wait
-// for the plan; those are stored device-coherent, the rest plainly after
-// the flag (the later launches read it).
-__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane, uint32_t* publish) {
+// box (may be nullptr; m <= 4 and E <= 256 then): the routed slots stored
+// first as tagged words, for the other blocks of a launch that routes.
+__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane, uint32_t* box) {
   const int K = d.K, P = m * K;
   // key: expert, token, pair (10 + 4 + 6 bits), unique; sorted ascending over
   // the smallest power-of-two number of lanes that holds the pairs
@@ -98,31 +96,38 @@ __device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds
   const uint64_t above = r == 63 ? 0ull : fm & ~((2ull << r) - 1ull);
   const int cnt = (above ? __ffsll((unsigned long long)above) - 1 : P) - r;
   const int nR = __popcll(fm), nS = 1;
-  // what the w13 launch needs first: rows' tokens, slots, header
-  if (valid) store_coherent(&s.row_tok[r], t);
-  if (lane < m) store_coherent(&s.row_tok[P + lane], lane);
-  if (first) store_coherent(&s.vslots[nS + __popcll(fm & ((1ull << r) - 1ull))], make_int4(e, r, cnt, 0));
-  if (lane == 0) {
-    store_coherent(&s.vslots[0], make_int4(-1, P, m, 0));
-    store_coherent(&s.header[0], nS + nR);
-    store_coherent(&s.header[1], nS);
-    store_coherent(&s.header[2], nR);
-    store_coherent(&s.header[3], m);
-  }
-  if (publish) {
-    wait_memory();
-    if (lane == 0) store_coherent(publish, 1u);
+  const int slot = nS + __popcll(fm & ((1ull << r) - 1ull));
+  if (box) {
+    // a slot's rows are the next cnt <= m <= 4 lanes
+    uint32_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ti = __shfl_down(t, i, 64);
+      if (i < cnt) mask |= 1u << ti;
+    }
+    if (first) store_coherent(box + slot, kBoxTag | (mask << 16) | ((uint32_t)r << 8) | (uint32_t)e);
+    if (lane == 0) store_coherent(box, kBoxTag | (uint32_t)nR);
   }
   if (valid) {
+    s.row_tok[r] = t;
     s.row_w[r] = L.w[p];
     s.pair_row[p] = r;
     s.row_out[r] = p;
   }
+  if (first) s.vslots[slot] = make_int4(e, r, cnt, 0);
   if (lane < m) {
+    s.row_tok[P + lane] = lane;
     s.row_w[P + lane] = 1.0f;
     s.row_out[P + lane] = P + lane;
   }
-  if (lane == 0) __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) {
+    s.vslots[0] = make_int4(-1, P, m, 0);
+    s.header[0] = nS + nR;
+    s.header[1] = nS;
+    s.header[2] = nR;
+    s.header[3] = m;
+    __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Tokens per expert of a plan of P picks in L.ids (the second wave, beside
@@ -140,9 +145,9 @@ __device__ void plan_counts(const LayerDims& d, int P, const Scratch& s, const R
 // kTokTile rows; the shared expert's m rows last, its slots first.  With at
 // most 48 tokens, the tokens of an expert form one 64-bit mask and a pair's
 // rank within its expert is the count of lower tokens in the mask.
-// own: the token whose picks this block holds in LDS already; publish: see
-// plan_small (the general path raises it at its end).
-__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L, uint32_t* publish) {
+// own: the token whose picks this block holds in LDS already; box: see
+// plan_small (only that path fills it).
+__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L, uint32_t* box) {
   const int tid = threadIdx.x;
   const int E = d.E, K = d.K, P = m * K;
   for (int p = tid; p < P; p += kThreads) {
@@ -152,7 +157,7 @@ __device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s,
   }
   if (P <= 64 && m <= kTokTile) {
     __syncthreads();
-    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x, publish);
+    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x, box);
     else if (threadIdx.x < 128) plan_counts(d, P, s, L, threadIdx.x - 64);
     return;
   }
@@ -207,15 +212,6 @@ __device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s,
     s.header[3] = m;
     __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (publish) {
-    // every wave's plain stores complete, the L2 written back, then the flag
-    wait_memory();
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      store_coherent(publish, 1u);
-    }
-  }
 }
 
 // Selection key of expert e with biased score b: the fp64 order of b
@@ -266,14 +262,14 @@ __device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
 // Block code of the router for token t, run by the first kThreads threads
 // of a block of at least kThreads (the others only take part in its
 // barriers); nblocks route blocks run in the launch (one per token).
-// Returns true in the block that built the plan, which raises `publish` (if
-// given) once the plan can be read by other blocks of the launch.  Wave w sorts the selection
+// Returns true in the block that built the plan, which fills `box` (if
+// given; see plan_small).  Wave w sorts the selection
 // keys of expert groups w, w + 4, ... (GPW groups of 64) and merges them;
 // wave 0 merges the four waves' lists, and its lanes [0, k) hold the picks
 // in selection order.
 template <int GPW>
 __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
-                            const Scratch& s, RouteLds& L, uint32_t* publish = nullptr) {
+                            const Scratch& s, RouteLds& L, uint32_t* box = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = d.E, K = d.K;
   const int groups = (E + 63) / 64;
@@ -357,7 +353,7 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     __syncthreads();
   }
   stamp(s.tl_route, kTlPoints, 3);
-  build_plan(d, m, t, s, L, publish);
+  build_plan(d, m, t, s, L, box);
   stamp(s.tl_route, kTlPoints, 4);
   return true;
 }
