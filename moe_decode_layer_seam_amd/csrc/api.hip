@@ -51,6 +51,7 @@ struct moe_decode_plan_s {
   Scratch s{};
   int last_m = 0;
   int last_grid[kKernels] = {};
+  bool boxes_dirty = false;  // a w13 launch that routes ran without the act launch after it
   bool fused = false;  // MOE_DECODE_SCHEDULE_FUSED
   bool timeline = false;
   uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
@@ -186,7 +187,10 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   // counters of the fused launch: status (padded to its own 256 bytes), the
   // slots' ready words, the act groups' unit counts
   const int act_stride = d.Imax / kActCols;
-  const size_t nsync = 64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPlanBox;
+  // ... and the boxes of the w13 launch that routes: the plan box, then
+  // (from an even word) the logit box
+  const size_t o_lbox = (64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPlanBox + 1) & ~(size_t)1;
+  const size_t nsync = o_lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   const size_t o_sync = take(nsync * 4);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
   // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
@@ -240,6 +244,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.ready = s.sync + 64;
   s.act_cnt = s.ready + p->max_vs;
   s.plan_box = s.act_cnt + (size_t)p->max_vs * act_stride;
+  s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + o_lbox) : nullptr;
   s.nsync = (int)nsync;
   s.act_stride = act_stride;
   s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = s.tl_experts = nullptr;
@@ -309,7 +314,12 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     sc.tl_combine = tl[6];
     sc.tl_experts = tl[7];
   }
-  p->last_grid[0] = seam_blocks(d, m);
+  // the w13 launch that routes runs the seam itself; the seam launch runs
+  // then only to zero the boxes after a run that stopped between the w13
+  // and act launches (act zeroes them for the next run)
+  const bool route13 = !p->fused && route_in_w13(d, m, p->grid13);
+  const bool seam = !route13 || p->boxes_dirty;
+  p->last_grid[0] = seam ? seam_blocks(d, m) : 0;
   p->last_grid[1] = logits_blocks(d, m);
   p->last_grid[2] = m;
   p->last_grid[3] = p->grid13;
@@ -326,18 +336,19 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     }
     return r;
   };
-  if ((e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
+  if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
   if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
     return hip_fail(p, e, "logits launch");
-  const bool route13 = !p->fused && route_in_w13(d, m);
   if (!route13 && (e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
   if (p->fused) {
     if ((e = launch_experts(d, m, in, sc, p->grid13, p->max_vs, st, ev(7))) != hipSuccess)
       return hip_fail(p, e, "experts launch");
   } else {
+    if (route13) p->boxes_dirty = true;
     if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, route13, st, ev(3))) != hipSuccess)
       return hip_fail(p, e, "w13 launch");
     if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
+    p->boxes_dirty = false;
     if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)
       return hip_fail(p, e, "w2 launch");
   }

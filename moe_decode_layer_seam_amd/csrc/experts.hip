@@ -52,6 +52,12 @@ __device__ __forceinline__ Geo geo(const LayerDims& d, bool shared) {
   return g;
 }
 
+// The dynamic LDS of the GEMM launches (slots, row map, and in the launch
+// that routes the MXFP8 rows), addressed by byte offset.
+extern __shared__ __align__(16) unsigned char dyn_lds[];
+__device__ __forceinline__ u32x4 lds16(uint32_t o) { return *reinterpret_cast<const u32x4*>(dyn_lds + o); }
+__device__ __forceinline__ uint32_t lds32(uint32_t o) { return *reinterpret_cast<const uint32_t*>(dyn_lds + o); }
+
 // One K step of a lane for TT weight tiles: each tile's lines (x: rows 0-7,
 // y: rows 8-15), the activation fragment they share, and the E8M0 codes of
 // the lane group's K block (one weight code per pair of tiles).
@@ -70,9 +76,13 @@ struct UnitOps {
   int fp4;  // weights as E2M1 pairs with per-row 32-column codes, blocked
 };
 
-template <bool W13, int TT>
+// ALDS (w13 of the launch that routes): the activation rows are the MXFP8
+// in the block's LDS, values at byte x8o, codes at xso; alane and aslane are
+// then LDS offsets.
+template <bool W13, int TT, bool ALDS = false>
 __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const LayerDims& d, const Inputs& in,
-                                            const Scratch& s, const int* s_tok, int m, int R, int g, int j) {
+                                            const Scratch& s, const int* s_tok, int m, int R, int g, int j,
+                                            uint32_t x8o = 0, uint32_t xso = 0) {
   const int ex = slot.x;
   const bool shared = ex < 0;
   const Geo G = geo<W13>(d, shared);
@@ -118,8 +128,8 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
     const int tok = j < u.c ? s_tok[u.row0 + j] : -1;
     u.a = make_rsrc(s.x8, (uint32_t)m * d.H);
     u.as = make_rsrc(s.x8s, (uint32_t)m * (d.H / 32));
-    u.alane = tok >= 0 ? (uint32_t)tok * d.H + 16 * g : kNoRow;
-    u.aslane = tok >= 0 ? (uint32_t)tok * (d.H / 32) + g : kNoRow;
+    u.alane = tok >= 0 ? (ALDS ? x8o : 0u) + (uint32_t)tok * d.H + 16 * g : kNoRow;
+    u.aslane = tok >= 0 ? (ALDS ? xso : 0u) + (uint32_t)tok * (d.H / 32) + g : kNoRow;
   } else {
     const uint32_t r = (uint32_t)(u.row0 + j);
     u.a = make_rsrc(s.a8, (uint32_t)R * d.Imax);
@@ -132,7 +142,7 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
 
 // Loads of K step `st` (past the contraction: zeros, no traffic); AUX: the
 // cache policy of the activation loads.
-template <int TT, int AUX>
+template <int TT, int AUX, bool ALDS>
 __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st) {
   const bool ok = st < u.nsteps;
   const uint32_t kw = (uint32_t)st * 128;
@@ -145,16 +155,23 @@ __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st)
   const uint32_t so = ok ? u.slane + 4 * st : kNoRow;
 #pragma unroll
   for (int p = 0; p < TT / 2; ++p) f.sb[p] = bload8(u.ws, so, u.ssoff + p * u.sstride);
-  const uint32_t ao = ok ? u.alane + kw : kNoRow;
-  f.alo = bload16a<AUX>(u.a, ao, 0);
-  f.ahi = bload16a<AUX>(u.a, ao + 64, 0);
-  f.sa = bload8a<AUX>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+  if constexpr (ALDS) {
+    const bool ar = ok && u.alane != kNoRow;
+    f.alo = ar ? lds16(u.alane + kw) : u32x4{0u, 0u, 0u, 0u};
+    f.ahi = ar ? lds16(u.alane + kw + 64) : u32x4{0u, 0u, 0u, 0u};
+    f.sa = ar ? (int)dyn_lds[u.aslane + 4 * st] : 0;
+  } else {
+    const uint32_t ao = ok ? u.alane + kw : kNoRow;
+    f.alo = bload16a<AUX>(u.a, ao, 0);
+    f.ahi = bload16a<AUX>(u.a, ao + 64, 0);
+    f.sa = bload8a<AUX>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+  }
 }
 
 // One segment's sums for the TT tiles, in bursts of BS K steps: a burst's
 // loads are all issued before its first MFMA.  Each tile's MFMAs run in K
 // order whatever BS is.
-template <int TT, int BS, int AUX>
+template <int TT, int BS, int AUX, bool ALDS>
 __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, int seg) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -162,7 +179,7 @@ __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, in
   for (int b0 = 0; b0 < kSegSteps; b0 += BS) {
     Step<TT> f[BS];
 #pragma unroll
-    for (int q = 0; q < BS; ++q) load_step<TT, AUX>(f[q], u, seg * kSegSteps + b0 + q);
+    for (int q = 0; q < BS; ++q) load_step<TT, AUX, ALDS>(f[q], u, seg * kSegSteps + b0 + q);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < BS; ++q) {
@@ -198,7 +215,7 @@ struct Codes4 {
   uint32_t b[TT], a;
 };
 
-template <int TT, int AUX>
+template <int TT, int AUX, bool ALDS>
 __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int seg, int g) {
   const int st = seg * kSegSteps + g;  // the step whose codes this lane fetches
   const bool ok = st < u.nsteps;
@@ -207,7 +224,10 @@ __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int
   const uint32_t bo = ok ? u.slane + 256 * seg : kNoRow;
 #pragma unroll
   for (int t = 0; t < TT; ++t) c.b[t] = __builtin_amdgcn_raw_buffer_load_b32(u.ws, (int)bo, (int)(u.ssoff + t * u.sstride), 0);
-  c.a = bload32a<AUX>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
+  if constexpr (ALDS)
+    c.a = ok && u.aslane != kNoRow ? lds32(u.aslane - g + 16 * seg + 4 * g) : 0u;
+  else
+    c.a = bload32a<AUX>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
 }
 
 template <int TT>
@@ -217,7 +237,7 @@ __device__ __forceinline__ void transpose_codes4(Codes4<TT>& c, int g) {
   c.a = transpose4_groups(c.a, g);
 }
 
-template <int TT, int AUX>
+template <int TT, int AUX, bool ALDS>
 __device__ __forceinline__ void load_pair4(Pair4<TT>& f, const UnitOps& u, int st, int j) {
   const bool ok0 = st < u.nsteps, ok1 = st + 1 < u.nsteps;
   const uint32_t wo = (j < 8 ? ok0 : ok1) ? u.wlane + (uint32_t)st * 64 : kNoRow;
@@ -228,9 +248,16 @@ __device__ __forceinline__ void load_pair4(Pair4<TT>& f, const UnitOps& u, int s
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const uint32_t ao = (q ? ok1 : ok0) ? u.alane + (uint32_t)(st + q) * 128 : kNoRow;
-    f.alo[q] = bload16a<AUX>(u.a, ao, 0);
-    f.ahi[q] = bload16a<AUX>(u.a, ao + 64, 0);
+    if constexpr (ALDS) {
+      const bool ar = (q ? ok1 : ok0) && u.alane != kNoRow;
+      const uint32_t ao = u.alane + (uint32_t)(st + q) * 128;
+      f.alo[q] = ar ? lds16(ao) : u32x4{0u, 0u, 0u, 0u};
+      f.ahi[q] = ar ? lds16(ao + 64) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const uint32_t ao = (q ? ok1 : ok0) ? u.alane + (uint32_t)(st + q) * 128 : kNoRow;
+      f.alo[q] = bload16a<AUX>(u.a, ao, 0);
+      f.ahi[q] = bload16a<AUX>(u.a, ao + 64, 0);
+    }
   }
 }
 
@@ -250,15 +277,15 @@ __device__ __forceinline__ void mma_pair4(v4f (&acc)[TT], const Pair4<TT>& f, co
 
 // One segment's sums for E2M1 weights: both line pairs (2 K steps each) and
 // the codes loaded before the first MFMA; each tile's MFMAs run in K order.
-template <int TT, int AUX>
+template <int TT, int AUX, bool ALDS>
 __device__ __forceinline__ void segment_sum_fp4(v4f (&acc)[TT], const UnitOps& u, int seg, int g, int j) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   Codes4<TT> c;
   Pair4<TT> f0, f1;
-  load_codes4<TT, AUX>(c, u, seg, g);
-  load_pair4<TT, AUX>(f0, u, seg * kSegSteps, j);
-  load_pair4<TT, AUX>(f1, u, seg * kSegSteps + 2, j);
+  load_codes4<TT, AUX, ALDS>(c, u, seg, g);
+  load_pair4<TT, AUX, ALDS>(f0, u, seg * kSegSteps, j);
+  load_pair4<TT, AUX, ALDS>(f1, u, seg * kSegSteps + 2, j);
   __builtin_amdgcn_sched_barrier(0);
   transpose_codes4<TT>(c, g);
   mma_pair4<TT, 0>(acc, f0, c);
@@ -268,24 +295,24 @@ __device__ __forceinline__ void segment_sum_fp4(v4f (&acc)[TT], const UnitOps& u
 
 // The unit's sums over its segments [s0, s1), added in segment order; each
 // segment's sum starts from zero.
-template <int TT, int AUX>
+template <int TT, int AUX, bool ALDS = false>
 __device__ __forceinline__ void unit_sums(v4f (&tot)[TT], const UnitOps& ops, int s0, int s1, int g, int j) {
   constexpr int BS = TT >= 8 ? 2 : kSegSteps;  // K steps per load burst
   if (ops.fp4) {
-    segment_sum_fp4<TT, AUX>(tot, ops, s0, g, j);
+    segment_sum_fp4<TT, AUX, ALDS>(tot, ops, s0, g, j);
     for (int sg = s0 + 1; sg < s1; ++sg) {
       v4f p[TT];
-      segment_sum_fp4<TT, AUX>(p, ops, sg, g, j);
+      segment_sum_fp4<TT, AUX, ALDS>(p, ops, sg, g, j);
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
     }
   } else {
-    segment_sum<TT, BS, AUX>(tot, ops, s0);
+    segment_sum<TT, BS, AUX, ALDS>(tot, ops, s0);
     for (int sg = s0 + 1; sg < s1; ++sg) {
       v4f p[TT];
-      segment_sum<TT, BS, AUX>(p, ops, sg);
+      segment_sum<TT, BS, AUX, ALDS>(p, ops, sg);
 #pragma unroll
       for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -415,6 +442,144 @@ __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int
   }
 }
 
+// The seam of the w13 launch that routes (m <= kRouteRows rows, H <= 8192),
+// run by the block's first four waves with the seam launch's thread mapping
+// (8 columns a thread, chunks of 2048) and order of every sum, so its bits
+// are that launch's:
+//   - the rows' RMSNorm and MXFP8 into the block's LDS (values at x8o, codes
+//     at xso): the A operand of the block's w13 units;
+//   - the router logits of experts b and b + G for every row (b: the block,
+//     G: the blocks of the launch), stored tagged into the logit box;
+//   - block 0 also stores the normed rows and the MXFP8 (s.normed, s.x8,
+//     s.x8s) for inspection.
+// Every thread of the block calls it; the LDS rows are complete when the
+// barrier inside has passed.
+__device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scratch& s, uint32_t x8o,
+                          uint32_t xso) {
+  constexpr int CPT = 4, EB = 2;
+  __shared__ double red_ss[kRouteRows][4];
+  __shared__ double red_lg[kRouteRows][EB][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool seam = tid < kThreads;
+  const int H = d.H, E = d.E, G = gridDim.x, b = blockIdx.x;
+  const bool taps = b == 0;
+  int col[CPT];
+  bool live[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    col[q] = 8 * tid + 2048 * q;
+    live[q] = seam && col[q] < H;
+  }
+  // every load at once: the rows, the norm weight, the block's gate rows
+  u32x4 xv[kRouteRows][CPT], wv[CPT], gv[EB][CPT];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < kRouteRows; ++t)
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      xv[t][q] = (t < m && live[q]) ? ld16(reinterpret_cast<const uint8_t*>(in.x + (size_t)t * H + col[q])) : zero;
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) wv[q] = live[q] ? ld16(reinterpret_cast<const uint8_t*>(in.norm_w + col[q])) : zero;
+#pragma unroll
+  for (int k = 0; k < EB; ++k) {
+    const int e = b + k * G;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      gv[k][q] = (e < E && live[q]) ? ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)e * H + col[q])) : zero;
+  }
+  // sums of squares in double, lanes then waves in a fixed order
+#pragma unroll
+  for (int t = 0; t < kRouteRows; ++t) {
+    if (t >= m) break;
+    double ss = 0.0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      if (live[q]) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const double lo = bf16_to_f32(xv[t][q][z] & 0xFFFFu), hi = bf16_to_f32(xv[t][q][z] >> 16);
+          ss += lo * lo;
+          ss += hi * hi;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (seam && lane == 0) red_ss[t][wave] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kRouteRows; ++t) {
+    if (t >= m) break;
+    const double sst = red_ss[t][0] + red_ss[t][1] + red_ss[t][2] + red_ss[t][3];
+    const float r = (float)(1.0 / sqrt(sst / (double)H + (double)d.eps));
+    double acc[EB];
+#pragma unroll
+    for (int k = 0; k < EB; ++k) acc[k] = 0.0;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      float y[8];
+      uint32_t yb[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        const uint32_t xb = (z & 1) ? (xv[t][q][z >> 1] >> 16) : (xv[t][q][z >> 1] & 0xFFFFu);
+        const uint32_t wb = (z & 1) ? (wv[q][z >> 1] >> 16) : (wv[q][z >> 1] & 0xFFFFu);
+        const float xr = bf16_to_f32(xb) * r;   // fp32 product, rounded
+        const float yw = xr * bf16_to_f32(wb);  // fp32 product, rounded
+        yb[z] = live[q] ? f32_to_bf16(yw) : 0u;
+        y[z] = bf16_to_f32(yb[z]);
+      }
+      if (live[q]) {
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          if (b + k * G < E) {
+#pragma unroll
+            for (int z = 0; z < 8; ++z) {
+              const uint32_t gb = (z & 1) ? (gv[k][q][z >> 1] >> 16) : (gv[k][q][z >> 1] & 0xFFFFu);
+              acc[k] += (double)y[z] * (double)bf16_to_f32(gb);  // exact products
+            }
+          }
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
+      amax = group_max(amax, 4);
+      const int code = e8m0_code(amax);
+      const float mul = mx_mul(code);
+      if (live[q]) {
+        u32x2 qv;
+        qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
+        qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
+        *reinterpret_cast<u32x2*>(dyn_lds + x8o + (uint32_t)(t * H + col[q])) = qv;
+        if ((lane & 3) == 0) dyn_lds[xso + (uint32_t)(t * (H / 32) + col[q] / 32)] = (uint8_t)code;
+        if (taps) {
+          u32x4 nv;
+#pragma unroll
+          for (int z = 0; z < 4; ++z) nv[z] = yb[2 * z] | (yb[2 * z + 1] << 16);
+          *reinterpret_cast<u32x4*>(s.normed + (size_t)t * H + col[q]) = nv;
+          *reinterpret_cast<u32x2*>(s.x8 + (size_t)t * H + col[q]) = qv;
+          if ((lane & 3) == 0) s.x8s[(size_t)t * (H / 32) + col[q] / 32] = (uint8_t)code;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+      const double tot = wave_sum(acc[k]);
+      if (seam && lane == 0) red_lg[t][k][wave] = tot;
+    }
+  }
+  __syncthreads();
+  if (tid < m * EB) {
+    const int t = tid / EB, k = tid % EB, e = b + k * G;
+    if (e < E) {
+      const double v = red_lg[t][k][0] + red_lg[t][k][1] + red_lg[t][k][2] + red_lg[t][k][3];
+      uint64_t w = (uint64_t)__double_as_longlong(v) ^ kLogitTag;
+      if (w == 0ull) w = kLogitTag;  // (-0 is not a sum from +0; kept as +0 all the same)
+      __hip_atomic_store(&s.logit_box[(size_t)t * E + e], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // The GEMM, one block of NW waves per CU.  Block b of B takes one unit of
 // every row of B units (unit_turn), so every CU streams the same bytes and
 // gets its part of every slot; its waves take the block's units from a
@@ -426,24 +591,32 @@ __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int
 template <bool W13, int TT, int NW, bool ROUTE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap) {
-  extern __shared__ __align__(16) unsigned char lds_raw[];
+  unsigned char* lds_raw = dyn_lds;
   __shared__ uint32_t s_next;
   __shared__ int s_plan, s_nvs;  // ROUTE: the plan's staging state (0, 1, 2) and slot count
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
   uint64_t* tl = W13 ? s.tl_w13 : s.tl_w2;
   stamp(tl, kTlPoints, 0);
+  const int R = m * d.K + m;
+  const int P = m * d.K;
+  // ROUTE: the MXFP8 rows after the slots and the row map
+  const uint32_t x8o = ((uint32_t)vs_cap * 16 + (uint32_t)R * 4 + 15u) & ~15u;
+  const uint32_t xso = x8o + (uint32_t)(m * d.H);
   if constexpr (ROUTE) {
-    // blocks [0, m) route the m tokens; the last of them builds the plan and
-    // stores the routed slots in the plan box first
+    // no seam launch ran: block 0 clears the status word (a wait gives up
+    // only after 100 ms)
+    if (blockIdx.x == 0 && tid == 0) store_coherent(s.status, 0u);
+    seam_rows(d, m, in, s, x8o, xso);
+    stamp(tl, kTlPoints, 2);
+    // blocks [0, m) route the m tokens from the logit box; the last of them
+    // builds the plan and stores the routed slots in the plan box first
     if ((int)blockIdx.x < m) {
       __shared__ RouteLds L;
-      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.plan_box);
+      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.plan_box, s.logit_box);
       return;
     }
   }
-  const int R = m * d.K + m;
-  const int P = m * d.K;
   int4* s_vs = reinterpret_cast<int4*>(lds_raw);
   int* s_tok = reinterpret_cast<int*>(s_vs + vs_cap);  // w13: token of a row; w2: its output row
   UnitMap um;
@@ -493,9 +666,9 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int v, tg, s0, s1;
     unit_decode(um, u, v, tg, s0, s1);
-    const UnitOps ops = unit_ops<W13, TT>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
+    const UnitOps ops = unit_ops<W13, TT, ROUTE>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j, x8o, xso);
     v4f tot[TT];
-    unit_sums<TT, 0>(tot, ops, s0, s1, g, j);
+    unit_sums<TT, 0, ROUTE>(tot, ops, s0, s1, g, j);
     // w13 sums go to the slot's rows; w2 sums to the rows' output rows
     float* dst = part + (size_t)(um.split ? s0 : 0) * plane + ops.col0 + j;
 #pragma unroll
@@ -524,6 +697,12 @@ __global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, i
   const int P = m * d.K;
   const int Kv = r < P ? d.I : d.Is;
   stamp(s.tl_act, kTlPoints, 0);
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    // the boxes of a w13 launch that routes start the next run at zero
+    for (int w = threadIdx.x; w < kPlanBox; w += kThreads) s.plan_box[w] = 0u;
+    if (s.logit_box)
+      for (int w = threadIdx.x; w < kRouteRows * d.E; w += kThreads) s.logit_box[w] = 0ull;
+  }
   if (c >= Kv) return;  // whole groups of 32 (Kv is a multiple of 128)
   const int nseg = split ? (d.H / 128 + kSegSteps - 1) / kSegSteps : 1;
   const size_t plane = (size_t)(m * d.K + m) * 2 * d.Imax;
@@ -725,7 +904,7 @@ __device__ __forceinline__ void wait_ready(const Scratch& s, int v, uint32_t wan
 template <int TT13, int TT2, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int split2) {
-  extern __shared__ __align__(16) unsigned char lds_raw[];
+  unsigned char* lds_raw = dyn_lds;
   __shared__ uint32_t s_next;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
@@ -844,16 +1023,19 @@ void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int s
 #define MOE_W2_SPLIT 4, 8
 #endif
 
+// ROUTE: and the MXFP8 rows of at most kRouteRows tokens
 template <bool W13>
-size_t gemm_lds(const LayerDims& d, int m, int max_vs) {
-  return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4;
+size_t gemm_lds(const LayerDims& d, int m, int max_vs, bool route = false) {
+  const size_t base = ((size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4 + 15) & ~(size_t)15;
+  const size_t mr = m < kRouteRows ? m : kRouteRows;
+  return route ? base + mr * d.H + mr * (d.H / 32) : base;
 }
 
 template <bool W13, int TT, int NW, bool ROUTE = false>
 hipError_t launch_gemm_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                          int split, hipStream_t st, const KernelEvents& ev) {
   return launch_kernel(gemm_kernel<W13, TT, NW, ROUTE>, dim3(grid), dim3(NW * 64),
-                       (uint32_t)gemm_lds<W13>(d, m, max_vs), st, ev, d, in, s, m, split, max_vs);
+                       (uint32_t)gemm_lds<W13>(d, m, max_vs, ROUTE), st, ev, d, in, s, m, split, max_vs);
 }
 
 template <bool W13, int TT, int NW, bool ROUTE = false>
@@ -882,10 +1064,9 @@ bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                       bool route, hipStream_t st, const KernelEvents& ev) {
   const bool split = gemm_split(d, m, grid * gemm_waves(true), true);
-  if (route) {
-    if (split) return launch_gemm_t<true, MOE_W13_SPLIT, true>(d, m, in, s, grid, max_vs, 1, st, ev);
-    return launch_gemm_t<true, MOE_W13_WHOLE, true>(d, m, in, s, grid, max_vs, 0, st, ev);
-  }
+  // the launch that routes: 4 tiles per unit in either mode (registers for
+  // its seam)
+  if (route) return launch_gemm_t<true, 4, 8, true>(d, m, in, s, grid, max_vs, split ? 1 : 0, st, ev);
   if (split) return launch_gemm_t<true, MOE_W13_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
   return launch_gemm_t<true, MOE_W13_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
@@ -945,9 +1126,8 @@ int gemm_blocks_per_cu(bool w13, size_t lds) {
   if (w13) {
     a = occupancy_t<true, MOE_W13_WHOLE>(lds);
     b = occupancy_t<true, MOE_W13_SPLIT>(lds);
-    const int c = occupancy_t<true, MOE_W13_WHOLE, true>(lds), e = occupancy_t<true, MOE_W13_SPLIT, true>(lds);
+    const int c = occupancy_t<true, 4, 8, true>(lds);
     a = c < a ? c : a;
-    b = e < b ? e : b;
   } else {
     a = occupancy_t<false, MOE_W2_WHOLE>(lds);
     b = occupancy_t<false, MOE_W2_SPLIT>(lds);
@@ -978,7 +1158,7 @@ int experts_blocks_per_cu(size_t lds) {
 size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs) { return experts_lds(d, m, max_vs); }
 
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {
-  return w13 ? gemm_lds<true>(d, m, max_vs) : gemm_lds<false>(d, m, max_vs);
+  return w13 ? gemm_lds<true>(d, m, max_vs, true) : gemm_lds<false>(d, m, max_vs);
 }
 
 }  // namespace moe

@@ -54,6 +54,7 @@ struct Scratch {
   uint32_t* ready;     // [max_vs]
   uint32_t* act_cnt;   // [max_vs][act_stride]
   uint32_t* plan_box;  // [kPlanBox] the routed slots of a w13 launch that routes (tagged words)
+  uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
   int nsync;
   int act_stride;      // Imax / 64
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
@@ -111,11 +112,17 @@ inline int seam_blocks(const LayerDims& d, int m) {
   const int tiles = (m + seam_tb(d.H) - 1) / seam_tb(d.H);
   return seam_fused(m) ? (d.E + epb - 1) / epb * tiles : m;
 }
-// Steps of at most 4 tokens route in the w13 launch's first blocks (one per
-// token) instead of a launch of their own, while the other blocks start on
-// the shared expert: when the router's expert groups fit its four waves
-// and the plan fits one wave (at most 64 pairs).
-inline bool route_in_w13(const LayerDims& d, int m) { return m <= 4 && m * d.K <= 64 && d.E <= 256; }
+// Steps of at most 4 tokens run the seam and the router inside the w13
+// launch instead of launches of their own: every block normalises and
+// quantises the rows into its LDS and sums the logits of one or two experts,
+// the first m blocks route (one per token), and the others start on the
+// shared expert.  When the router's expert groups fit its four waves, the
+// plan fits one wave (at most 64 pairs), a row fits four 2048-column chunks
+// of the seam's thread mapping, and two experts per block cover E.
+constexpr int kRouteRows = 4;
+inline bool route_in_w13(const LayerDims& d, int m, int grid) {
+  return m <= kRouteRows && m * d.K <= 64 && d.E <= 256 && d.H <= 8192 && d.E <= 2 * grid && grid > m;
+}
 // The plan as the w13 launch that routes reads it: word 0 the routed slot
 // count, word 1 + k routed slot k as expert (bits 0-7), first row (8-13) and
 // its rows' tokens as a bit mask (16-19; a slot's rows are its tokens in
@@ -123,6 +130,10 @@ inline bool route_in_w13(const LayerDims& d, int m) { return m <= 4 && m * d.K <
 // each step, so a reader knows a word is in from the word alone.
 constexpr int kPlanBox = 65;
 constexpr uint32_t kBoxTag = 0x80000000u;
+// A logit in the logit box: its bits with the sign bit flipped.  A logit is
+// a sum that starts from +0, so it is never -0 and its word never 0 (the
+// zeroed box's value).
+constexpr uint64_t kLogitTag = 0x8000000000000000ull;
 inline int logits_blocks(const LayerDims& d, int m) {
   const int cpt = (d.H + 2047) / 2048;
   const int tb = cpt <= 3 ? 8 : 4, epb = cpt <= 3 ? 4 : 2;
@@ -153,8 +164,8 @@ hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scra
                          const KernelEvents& ev);
 hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                         const KernelEvents& ev);
-// route: the launch also routes (route_in_w13): its first m blocks run the
-// router while the others stream the shared expert's units.
+// route: the launch also runs the seam and routes (route_in_w13): its first
+// m blocks run the router while the others stream the shared expert's units.
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                       bool route, hipStream_t st, const KernelEvents& ev);
 hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,

@@ -263,25 +263,53 @@ __device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
 // of a block of at least kThreads (the others only take part in its
 // barriers); nblocks route blocks run in the launch (one per token).
 // Returns true in the block that built the plan, which fills `box` (if
-// given; see plan_small).  Wave w sorts the selection
+// given; see plan_small).  The logits come from s.logits, or with lbox from
+// the logit box as the blocks of the launch store them (then also copied to
+// s.logits).  Wave w sorts the selection
 // keys of expert groups w, w + 4, ... (GPW groups of 64) and merges them;
 // wave 0 merges the four waves' lists, and its lanes [0, k) hold the picks
 // in selection order.
+// Longest wait for a logit of the logit box before the run is flagged
+// (status 2) and the logit taken as 0: 100 ms of the 100 MHz device clock.
+constexpr uint64_t kLogitWaitTicks = 10000000ull;
+
+// The logit at w of the logit box, once it is in.
+__device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s, uint64_t t0) {
+  uint64_t v;
+  while ((v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0ull) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kLogitWaitTicks) {
+      store_coherent(s.status, 2u);
+      return 0.0;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return __longlong_as_double((long long)(v ^ kLogitTag));
+}
+
 template <int GPW>
 __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
-                            const Scratch& s, RouteLds& L, uint32_t* box = nullptr) {
+                            const Scratch& s, RouteLds& L, uint32_t* box = nullptr,
+                            const uint64_t* lbox = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = d.E, K = d.K;
   const int groups = (E + 63) / 64;
   stamp(s.tl_route, kTlPoints, 0);
 
   uint64_t k[GPW];
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
   for (int i = 0; i < GPW; ++i) {
     const int ex = 64 * (wave + 4 * i) + lane;
     k[i] = 0;  // below every real expert's key
     if (wave < 4 && ex < E) {
-      const double sg = 1.0 / (1.0 + exp(-s.logits[(size_t)t * E + ex]));
+      double lg;
+      if (lbox) {
+        lg = take_logit(lbox + (size_t)t * E + ex, s, t0);
+        s.logits[(size_t)t * E + ex] = lg;
+      } else {
+        lg = s.logits[(size_t)t * E + ex];
+      }
+      const double sg = 1.0 / (1.0 + exp(-lg));
       const double bb = sg + (double)bias[ex];
       L.sig[ex] = sg;
       k[i] = select_key((bb == bb) ? bb : -INFINITY, ex);  // a NaN score ranks last
