@@ -45,6 +45,17 @@ def expert_bytes(H: int, I: int, fmt: str = "e4m3") -> dict:
     return {"w13": w13, "w2": w2}
 
 
+def w13_input_bytes(m: int, H: int, E: int, K: int, schedule: str = "launches") -> int:
+    """Algorithmic bytes the w13 launch reads besides the expert weights.
+    Steps of up to 4 tokens (the launches schedule, E <= 256, H <= 8192, at
+    most 64 pairs) run the seam and the router in that launch: it reads the
+    bf16 rows, the norm weight, the router's gate rows and bias.  Otherwise
+    it reads the MXFP8 rows and their codes."""
+    if schedule == "launches" and m <= 4 and m * K <= 64 and E <= 256 and H <= 8192:
+        return 2 * m * H + 2 * H + 2 * E * H + 4 * E
+    return m * (H + H // 32)
+
+
 def make_weights(cfg: dict, seed: int, dev):
     """One device copy of the expert weights: N(0, 0.02) fp32 drawn on the GPU,
     quantised by the library's weight quantisers (E4M3 with 32 x 32 E8M0
@@ -387,10 +398,12 @@ def main() -> int:
 
     # algorithmic bytes per launch of the dominant kernel (the fused expert
     # launch, else w13): every active expert's weights and codes (shared
-    # expert included) and the MXFP8 rows they are multiplied with
+    # expert included) and the rows they are multiplied with (MXFP8, or at
+    # m <= 4 the bf16 rows, norm weight and router weights the launch's own
+    # seam and router read)
     steps_U = [U[i % copies] for i in range(args.steps)]
     avg_U = sum(steps_U) / len(steps_U)
-    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + m * (H + H // 32)
+    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + w13_input_bytes(m, H, E, K, args.schedule)
     expert_step_bytes = avg_U * (eb["w13"] + eb["w2"]) + ebs["w13"] + ebs["w2"]
     w2_bytes = avg_U * eb["w2"] + ebs["w2"] + (m * K + m) * (max(I, Is) + max(I, Is) // 32)
     if fused:

@@ -143,11 +143,17 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  * on the host for the same reason, _check_tensors).  The caller keeps every
  * buffer alive until the enqueued work completes.  A plan serves one stream
  * at a time: two runs of one plan must not overlap (they share its scratch).
- * For m <= 4 (at most 64 pairs, E <= 256) the router runs in the first m
- * blocks of the w13 launch, whose other blocks wait for its plan; the launch
- * has one block per CU, so with all its blocks resident the wait always
- * ends.  A wait that runs past 100 ms (another workload holding CUs for that
- * long) flags the run in MOE_DECODE_TAP_STATUS and goes on. */
+ * For m <= 4 (at most 64 pairs, E <= 256, H <= 8192, E at most twice the
+ * CUs; the launches schedule) no seam launch runs: every block of the w13
+ * launch normalises and quantises the rows into its LDS and sums the logits
+ * of one or two experts; its first m blocks wait for those logits and route,
+ * and the other blocks wait for their plan once the shared expert's units
+ * are done.  The launch has one block per CU, so with all its blocks
+ * resident every wait ends.  A wait that runs past 100 ms (another workload
+ * holding CUs for that long) flags the run in MOE_DECODE_TAP_STATUS and goes
+ * on.  The act launch clears the hand-off words for the next run; after a
+ * run that returned an error between the w13 and act launches, the next run
+ * launches the seam to clear them. */
 int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
                    const void* d_norm_w, const void* d_gate_w,
                    const float* d_bias, const void* d_w13,
@@ -174,7 +180,8 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
  *   STATUS    u32  [1]          0, or nonzero when a wait timed out and the
  *                               output is not valid: 1 the fused expert
  *                               launch's wait for a slot's a8, 2 the w13
- *                               launch's wait for the plan (m <= 4) */
+ *                               launch's wait for the logits or the plan
+ *                               (m <= 4) */
 enum moe_decode_tap {
   MOE_DECODE_TAP_NORMED = 0,
   MOE_DECODE_TAP_X8 = 1,
@@ -202,7 +209,8 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * fused w13 + act + w2 launch) over the recorded
  * runs that launched it, and sets *runs to their number; it synchronises
  * with the recorded events.  (Steps of m <= 4 rows compute the logits inside
- * the seam launch and do not launch `logits`.) */
+ * the seam launch and do not launch `logits`; with the launches schedule they
+ * run the seam and the router inside w13 and launch neither.) */
 int moe_decode_timing(moe_decode_handle plan, int32_t on);
 int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
                            double* total_ms, int32_t* runs);
@@ -215,7 +223,9 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   route: 0 start, 5 scores computed, 1 groups sorted, 6 lists merged,
  *          2 picks stored, 3 last block admitted, 4 plan written (3-4 only
  *          in the last block)
- *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end
+ *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end;
+ *          w13 that routes also 2: its seam done (the route block's
+ *          route points are stored as route's, block = token)
  *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.

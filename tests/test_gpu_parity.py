@@ -224,23 +224,33 @@ def test_runs_are_deterministic_and_plan_reusable_across_m(schedule):
         c = gu.run(h, cfg, dinp, dw, x=dinp["x"][:5].contiguous()).clone()
         c3 = gu.run(h, cfg, dinp, dw, x=dinp["x"][:3].contiguous()).clone()
         d = gu.run(h, cfg, dinp, dw)
+        # steps of up to 4 tokens route inside the w13 launch: twice in a row,
+        # after a larger step, and with another token count
+        e3 = gu.run(h, cfg, dinp, dw, x=dinp["x"][:3].contiguous()).clone()
+        e3b = gu.run(h, cfg, dinp, dw, x=dinp["x"][:3].contiguous()).clone()
+        e1 = gu.run(h, cfg, dinp, dw, x=dinp["x"][:1].contiguous()).clone()
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.int16), a[:5].view(torch.int16))
         assert torch.equal(c3.view(torch.int16), a[:3].view(torch.int16))
         assert torch.equal(d.view(torch.int16), a.view(torch.int16))
+        assert torch.equal(e3.view(torch.int16), a[:3].view(torch.int16))
+        assert torch.equal(e3b.view(torch.int16), a[:3].view(torch.int16))
+        assert torch.equal(e1.view(torch.int16), a[:1].view(torch.int16))
         assert gu.tap(h, "status", torch.int32)[0] == 0
     finally:
         mdl.destroy(h)
 
 
-@pytest.mark.parametrize("schedule", ["launches", "fused"])
-def test_graph_capture_replays_match_eager(schedule):
-    cfg = _cfg(16, 512, 64, 6, 256, 128)
+# m = 3: the launches schedule runs the seam and the router inside the w13
+# launch, whose hand-off boxes the act launch clears for the next replay
+@pytest.mark.parametrize("schedule,m", [("launches", 16), ("fused", 16), ("launches", 3)])
+def test_graph_capture_replays_match_eager(schedule, m):
+    cfg = _cfg(m, 512, 64, 6, 256, 128)
     inp, w = data.build_layer(11, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
     h = _plan_for(cfg, schedule=schedule)
     try:
-        xs = [gu.bf16_dev(synth.to_bf16_bits(synth.normal(100 + i, 1, (16, 512)))) for i in range(4)]
+        xs = [gu.bf16_dev(synth.to_bf16_bits(synth.normal(100 + i, 1, (m, 512)))) for i in range(4)]
         eager = []
         for x in xs:
             eager.append(gu.run(h, cfg, dinp, dw, x=x).clone())
