@@ -38,6 +38,12 @@ SMALL = [
     _cfg(48, 512, 64, 4, 256, 256),
     _cfg(48, 256, 512, 16, 128, 128),       # 8 sort groups, k = 16
     _cfg(7, 256, 1000, 32, 128, 128),       # 16 sort groups, k = 32
+    # m <= 4: the seam and router inside the w13 launch (ragged H, E), and the
+    # cases that keep their own launches (E > 256, m k > 64, H > 8192)
+    _cfg(4, 640, 100, 8, 128, 256),
+    _cfg(2, 256, 300, 8, 128, 128),
+    _cfg(4, 256, 64, 20, 128, 128),
+    _cfg(2, 8320, 16, 2, 128, 128),
 ]
 
 
@@ -94,6 +100,7 @@ def _bf16_f64(bits):
 # I 128) leave one half of a weight line pair empty
 SMALL_FP4 = [dict(c, routed="mxfp4", name=c["name"] + "_fp4") for c in (
     synth.CONFIGS[0],
+    _cfg(4, 640, 100, 8, 128, 256),
     _cfg(5, 512, 64, 6, 256, 128),
     _cfg(13, 640, 100, 8, 128, 256),
     _cfg(33, 256, 8, 8, 128, 128),
