@@ -222,7 +222,7 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   logits: 0 start, 1 end
  *   route: 0 start, 5 scores computed, 1 groups sorted, 6 lists merged,
  *          2 picks stored, 3 last block admitted, 4 plan written (3-4 only
- *          in the last block)
+ *          in the last block; 3 not with one token)
  *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end;
  *          w13 that routes also 2: its seam done (the route block's
  *          route points are stored as route's, block = token)

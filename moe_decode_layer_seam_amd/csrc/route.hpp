@@ -130,14 +130,13 @@ __device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds
   }
 }
 
-// Tokens per expert of a plan of P picks in L.ids (the second wave, beside
-// plan_small): each lane counts its experts' picks.
-__device__ void plan_counts(const LayerDims& d, int P, const Scratch& s, const RouteLds& L, int lane) {
-  for (int x = lane; x < d.E; x += 64) {
-    int c = 0;
-    for (int p = 0; p < P; ++p) c += L.ids[p] == x ? 1 : 0;
-    s.counts[x] = c;
-  }
+// Tokens per expert of a plan of P <= 64 picks in L.ids, by one wave: a
+// table in LDS (L.base) zeroed, counted into and copied out.  One wave's LDS
+// operations run in order, so no barrier is needed.
+__device__ void plan_counts(const LayerDims& d, int P, const Scratch& s, RouteLds& L, int lane) {
+  for (int x = lane; x < d.E; x += 64) L.base[x] = 0;
+  if (lane < P) atomicAdd(&L.base[L.ids[lane]], 1);
+  for (int x = lane; x < d.E; x += 64) s.counts[x] = L.base[x];
 }
 
 // The plan, from every token's picks: rows listed by expert ascending, then
@@ -364,6 +363,16 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     }
   }
   stamp(s.tl_route, kTlPoints, 2);
+  if (nblocks == 1 && K <= 64) {
+    // one token: wave 0 holds every pick and builds the plan from them
+    // straight away (its own LDS writes, in order; no barrier)
+    if (wave == 0) {
+      plan_small(d, 1, s, L, lane, box);
+      plan_counts(d, K, s, L, lane);
+    }
+    stamp(s.tl_route, kTlPoints, 4);
+    return true;
+  }
 
   if (nblocks > 1) {
     // Arrival: wait until this block's coherent stores completed, count the
