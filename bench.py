@@ -150,7 +150,7 @@ def kernel_source_hash() -> str:
     figures measured with hardware counters hold only for this code."""
     import hashlib
     hsh = hashlib.sha256()
-    for f in ("experts.hip", "device.hpp", "kernels.hpp"):
+    for f in ("experts.hip", "route.hpp", "device.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "moe_decode_layer_seam_amd", "csrc", f), "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()
