@@ -187,9 +187,9 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   // counters of the fused launch: status (padded to its own 256 bytes), the
   // slots' ready words, the act groups' unit counts
   const int act_stride = d.Imax / kActCols;
-  // ... and the boxes of the w13 launch that routes: the plan box, then
+  // ... and the boxes of the w13 launch that routes: the pick box, then
   // (from an even word) the logit box
-  const size_t o_lbox = (64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPlanBox + 1) & ~(size_t)1;
+  const size_t o_lbox = (64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPickBox + 1) & ~(size_t)1;
   const size_t nsync = o_lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   const size_t o_sync = take(nsync * 4);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
@@ -243,7 +243,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.status = s.sync;
   s.ready = s.sync + 64;
   s.act_cnt = s.ready + p->max_vs;
-  s.plan_box = s.act_cnt + (size_t)p->max_vs * act_stride;
+  s.pick_box = s.act_cnt + (size_t)p->max_vs * act_stride;
   s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + o_lbox) : nullptr;
   s.nsync = (int)nsync;
   s.act_stride = act_stride;

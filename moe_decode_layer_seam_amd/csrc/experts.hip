@@ -391,26 +391,25 @@ __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) { return u
 // goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
 constexpr uint64_t kPlanWaitTicks = 10000000ull;
 
-// The routed slots of a w13 launch that routes in its first blocks, copied
-// into the block's LDS by the first wave that needs them (the others wait
-// for that wave): the wave reads the plan box until the count and every slot
-// it counts carry the tag, then expands each slot's token mask into its rows.
-// On a timeout the status word is set and no routed slot is staged.
-__device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap, int* s_plan, int* s_nvs,
-                           int lane) {
+// The routed slots of a w13 launch that routes in its first blocks, built in
+// the block's LDS by the first wave that needs them (the others wait for
+// that wave): the wave reads the pick box until every pick of the step
+// carries the tag, then sorts the picks into the plan's rows (small_rows:
+// the same rows and slots as the router's plan).  On a timeout the status
+// word is set and no routed slot is staged.
+__device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap,
+                           int* s_plan, int* s_nvs, int lane) {
   int st = 0;
   if (lane == 0) st = atomicCAS(s_plan, 0, 1);
   st = __builtin_amdgcn_readfirstlane(st);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   if (st == 0) {
-    int nR = 0;
-    uint32_t sv = 0;
+    uint32_t w = 0;
+    bool in = false;
     while (true) {
-      const uint32_t hv = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(s.plan_box));
-      sv = lane < P ? load_coherent(s.plan_box + 1 + lane) : kBoxTag;
-      const int n = min((int)(hv & 0xFFFFu), min(P, vs_cap - nS));
-      if ((hv & kBoxTag) && __ballot(lane < n && !(sv & kBoxTag)) == 0ull) {
-        nR = n;
+      w = lane < P ? load_coherent(s.pick_box + lane) : kBoxTag;
+      if (__ballot(!(w & kBoxTag)) == 0ull) {
+        in = true;
         break;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
@@ -419,17 +418,13 @@ __device__ void stage_plan(const Scratch& s, int4* s_vs, int* s_tok, int nS, int
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (lane < nR) {
-      const int e = (int)(sv & 0xFFu), r = (int)((sv >> 8) & 63u);
-      const uint32_t mask = (sv >> 16) & 15u;
-      s_vs[nS + lane] = make_int4(e, r, __popc(mask), 0);
-      int i = r;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (((mask >> t) & 1u) && i < P) s_tok[i++] = t;
-    }
+    const int n = in ? P : 0;
+    const SmallRows q = small_rows((int)(w & 0x3FFu), n, d.K, lane);
+    const int nR = min(q.nR, vs_cap - nS);
+    if (q.valid) s_tok[lane] = q.t;
+    if (q.first && q.ri < nR) s_vs[nS + q.ri] = make_int4(q.e, lane, q.cnt, 0);
     if (lane == 0) *s_nvs = nS + nR;
-    wait_memory();
+    wait_memory();  // the LDS writes are done
     if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
@@ -609,11 +604,12 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     if (blockIdx.x == 0 && tid == 0) store_coherent(s.status, 0u);
     seam_rows(d, m, in, s, x8o, xso);
     stamp(tl, kTlPoints, 2);
-    // blocks [0, m) route the m tokens from the logit box; the last of them
-    // builds the plan and stores the routed slots in the plan box first
+    // blocks [0, m) route the m tokens from the logit box and store their
+    // picks in the pick box; the last of them builds the plan for the
+    // launches after this one
     if ((int)blockIdx.x < m) {
       __shared__ RouteLds L;
-      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.plan_box, s.logit_box);
+      (void)route_block<1>(d, m, blockIdx.x, m, in.bias, s, L, s.pick_box, s.logit_box);
       return;
     }
   }
@@ -657,7 +653,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     if (u >= um.total) {
       // past the shared expert's units: the routed ones need the plan
       if (planned) break;
-      stage_plan(s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
+      stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
       um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
       planned = true;
       if (u >= um.total) break;  // the last turn has no unit for this block
@@ -699,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, i
   stamp(s.tl_act, kTlPoints, 0);
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     // the boxes of a w13 launch that routes start the next run at zero
-    for (int w = threadIdx.x; w < kPlanBox; w += kThreads) s.plan_box[w] = 0u;
+    for (int w = threadIdx.x; w < kPickBox; w += kThreads) s.pick_box[w] = 0u;
     if (s.logit_box)
       for (int w = threadIdx.x; w < kRouteRows * d.E; w += kThreads) s.logit_box[w] = 0ull;
   }

@@ -53,7 +53,7 @@ struct Scratch {
   uint32_t* status;
   uint32_t* ready;     // [max_vs]
   uint32_t* act_cnt;   // [max_vs][act_stride]
-  uint32_t* plan_box;  // [kPlanBox] the routed slots of a w13 launch that routes (tagged words)
+  uint32_t* pick_box;  // [kPickBox] the picks, for the w13 launch that routes (tagged words)
   uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
   int nsync;
   int act_stride;      // Imax / 64
@@ -123,12 +123,10 @@ constexpr int kRouteRows = 4;
 inline bool route_in_w13(const LayerDims& d, int m, int grid) {
   return m <= kRouteRows && m * d.K <= 64 && d.E <= 256 && d.H <= 8192 && d.E <= 2 * grid && grid > m;
 }
-// The plan as the w13 launch that routes reads it: word 0 the routed slot
-// count, word 1 + k routed slot k as expert (bits 0-7), first row (8-13) and
-// its rows' tokens as a bit mask (16-19; a slot's rows are its tokens in
-// ascending order).  Every word has bit 31 set, and the box is zeroed before
-// each step, so a reader knows a word is in from the word alone.
-constexpr int kPlanBox = 65;
+// The picks as the w13 launch that routes reads them: word t k + j holds the
+// expert of token t's pick j with bit 31 set.  The box is zeroed before each
+// step, so a reader knows a word is in from the word alone.
+constexpr int kPickBox = 64;
 constexpr uint32_t kBoxTag = 0x80000000u;
 // A logit in the logit box: its bits with the sign bit flipped.  A logit is
 // a sum that starts from +0, so it is never -0 and its word never 0 (the

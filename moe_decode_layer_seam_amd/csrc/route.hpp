@@ -60,21 +60,26 @@ struct RouteLds {
   int last;
 };
 
-// The plan of a step of at most 64 pairs and 16 tokens, by wave 0 alone:
-// lane p takes pair p, a bitonic sort of the keys expert * 64 + token puts
-// row r's pair in lane r, and every expert has one virtual slot (its rows
-// are at most the 16 tokens).  Same plan as build_plan's general path.
-// box (may be nullptr; m <= 4 and E <= 256 then): the routed slots stored
-// first as tagged words, for the other blocks of a launch that routes.
-__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane, uint32_t* box) {
-  const int K = d.K, P = m * K;
-  // key: expert, token, pair (10 + 4 + 6 bits), unique; sorted ascending over
-  // the smallest power-of-two number of lanes that holds the pairs
+// The rows of a plan of P <= 64 pairs and at most 16 tokens, by one wave:
+// lane p brings pair p's expert (token t's pairs are t k .. t k + k - 1),
+// and a bitonic sort of the unique keys expert * 1024 + token * 64 + pair
+// leaves row r's pair in lane r.  Every expert has one virtual slot (its rows
+// are at most the 16 tokens); `ri` numbers the routed slots from 0.  The same
+// rows as build_plan's general path.
+struct SmallRows {
+  int e, t, p;    // row r = lane: its expert, token and pair
+  int cnt, ri;    // where a slot starts: its rows and routed slot index
+  int nR;         // routed slots
+  bool valid, first;
+};
+
+__device__ __forceinline__ SmallRows small_rows(int ex, int P, int K, int lane) {
   int key = 0x7FFFFFFF;
-  if (lane < P) key = (L.ids[lane] << 10) | ((lane / K) << 6) | lane;
+  if (lane < P) key = (ex << 10) | ((lane / K) << 6) | lane;
+  // sorted ascending over the smallest power-of-two number of lanes that
+  // holds the pairs; every stage unrolled, so each exchange is a fixed DPP
+  // or permlane pattern, and a level wider than needed is skipped as a whole
   const int width = P <= 8 ? 8 : (P <= 16 ? 16 : (P <= 32 ? 32 : 64));
-  // (every stage unrolled, so each exchange is a fixed DPP or permlane
-  // pattern; a level is skipped as a whole when it is wider than needed)
 #pragma unroll
   for (int k2 = 2; k2 <= 64; k2 <<= 1) {
     if (k2 <= width) {
@@ -87,34 +92,36 @@ __device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds
       }
     }
   }
+  SmallRows q;
   const int r = lane;
-  const bool valid = r < P;
-  const int e = key >> 10, t = (key >> 6) & 15, p = key & 63;
-  const int eprev = __shfl_up(e, 1, 64);
-  const bool first = valid && (r == 0 || eprev != e);
-  const uint64_t fm = __ballot(first);
+  q.valid = r < P;
+  q.e = key >> 10;
+  q.t = (key >> 6) & 15;
+  q.p = key & 63;
+  const int eprev = __shfl_up(q.e, 1, 64);
+  q.first = q.valid && (r == 0 || eprev != q.e);
+  const uint64_t fm = __ballot(q.first);
   const uint64_t above = r == 63 ? 0ull : fm & ~((2ull << r) - 1ull);
-  const int cnt = (above ? __ffsll((unsigned long long)above) - 1 : P) - r;
-  const int nR = __popcll(fm), nS = 1;
-  const int slot = nS + __popcll(fm & ((1ull << r) - 1ull));
-  if (box) {
-    // a slot's rows are the next cnt <= m <= 4 lanes
-    uint32_t mask = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ti = __shfl_down(t, i, 64);
-      if (i < cnt) mask |= 1u << ti;
-    }
-    if (first) store_coherent(box + slot, kBoxTag | (mask << 16) | ((uint32_t)r << 8) | (uint32_t)e);
-    if (lane == 0) store_coherent(box, kBoxTag | (uint32_t)nR);
+  q.cnt = (above ? __ffsll((unsigned long long)above) - 1 : P) - r;
+  q.nR = __popcll(fm);
+  q.ri = __popcll(fm & ((1ull << r) - 1ull));
+  return q;
+}
+
+// The plan of a step of at most 64 pairs and 16 tokens, by wave 0 alone,
+// from the picks in L.ids and L.w (small_rows; slot 0 is the shared
+// expert's).
+__device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds& L, int lane) {
+  const int K = d.K, P = m * K, nS = 1;
+  const SmallRows q = small_rows(lane < P ? L.ids[lane] : 0, P, K, lane);
+  const int r = lane;
+  if (q.valid) {
+    s.row_tok[r] = q.t;
+    s.row_w[r] = L.w[q.p];
+    s.pair_row[q.p] = r;
+    s.row_out[r] = q.p;
   }
-  if (valid) {
-    s.row_tok[r] = t;
-    s.row_w[r] = L.w[p];
-    s.pair_row[p] = r;
-    s.row_out[r] = p;
-  }
-  if (first) s.vslots[slot] = make_int4(e, r, cnt, 0);
+  if (q.first) s.vslots[nS + q.ri] = make_int4(q.e, r, q.cnt, 0);
   if (lane < m) {
     s.row_tok[P + lane] = lane;
     s.row_w[P + lane] = 1.0f;
@@ -122,9 +129,9 @@ __device__ void plan_small(const LayerDims& d, int m, const Scratch& s, RouteLds
   }
   if (lane == 0) {
     s.vslots[0] = make_int4(-1, P, m, 0);
-    s.header[0] = nS + nR;
+    s.header[0] = nS + q.nR;
     s.header[1] = nS;
-    s.header[2] = nR;
+    s.header[2] = q.nR;
     s.header[3] = m;
     __hip_atomic_store(s.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -144,9 +151,8 @@ __device__ void plan_counts(const LayerDims& d, int P, const Scratch& s, RouteLd
 // kTokTile rows; the shared expert's m rows last, its slots first.  With at
 // most 48 tokens, the tokens of an expert form one 64-bit mask and a pair's
 // rank within its expert is the count of lower tokens in the mask.
-// own: the token whose picks this block holds in LDS already; box: see
-// plan_small (only that path fills it).
-__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L, uint32_t* box) {
+// own: the token whose picks this block holds in LDS already.
+__device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L) {
   const int tid = threadIdx.x;
   const int E = d.E, K = d.K, P = m * K;
   for (int p = tid; p < P; p += kThreads) {
@@ -156,7 +162,7 @@ __device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s,
   }
   if (P <= 64 && m <= kTokTile) {
     __syncthreads();
-    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x, box);
+    if (threadIdx.x < 64) plan_small(d, m, s, L, threadIdx.x);
     else if (threadIdx.x < 128) plan_counts(d, P, s, L, threadIdx.x - 64);
     return;
   }
@@ -261,8 +267,9 @@ __device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
 // Block code of the router for token t, run by the first kThreads threads
 // of a block of at least kThreads (the others only take part in its
 // barriers); nblocks route blocks run in the launch (one per token).
-// Returns true in the block that built the plan, which fills `box` (if
-// given; see plan_small).  The logits come from s.logits, or with lbox from
+// Returns true in the block that built the plan.  With pbox, each pick is
+// also stored there as soon as it is known (kPickBox).  The logits come from
+// s.logits, or with lbox from
 // the logit box as the blocks of the launch store them (then also copied to
 // s.logits).  Wave w sorts the selection
 // keys of expert groups w, w + 4, ... (GPW groups of 64) and merges them;
@@ -287,7 +294,7 @@ __device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s
 
 template <int GPW>
 __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
-                            const Scratch& s, RouteLds& L, uint32_t* box = nullptr,
+                            const Scratch& s, RouteLds& L, uint32_t* pbox = nullptr,
                             const uint64_t* lbox = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = d.E, K = d.K;
@@ -353,6 +360,7 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     const int e = 1023 - (int)(k[0] & 0x3FF);
     const double sg = lane < K ? L.sig[e] : 0.0;
     const double ssum = wave_sum(sg);
+    if (pbox && lane < K) store_coherent(pbox + t * K + lane, kBoxTag | (uint32_t)e);
     if (lane < K) {
       const float w = (float)((double)d.routed_scale * sg / ssum);
       L.ids[t * K + lane] = e;
@@ -367,7 +375,7 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     // one token: wave 0 holds every pick and builds the plan from them
     // straight away (its own LDS writes, in order; no barrier)
     if (wave == 0) {
-      plan_small(d, 1, s, L, lane, box);
+      plan_small(d, 1, s, L, lane);
       plan_counts(d, K, s, L, lane);
     }
     stamp(s.tl_route, kTlPoints, 4);
@@ -390,7 +398,7 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     __syncthreads();
   }
   stamp(s.tl_route, kTlPoints, 3);
-  build_plan(d, m, t, s, L, box);
+  build_plan(d, m, t, s, L);
   stamp(s.tl_route, kTlPoints, 4);
   return true;
 }
