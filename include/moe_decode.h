@@ -147,7 +147,7 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  * CUs; the launches schedule) no seam launch runs: every block of the w13
  * launch normalises and quantises the rows into its LDS and sums the logits
  * of one or two experts; its first m blocks wait for those logits and route,
- * and the other blocks wait for their plan once the shared expert's units
+ * and the other blocks wait for the picks once the shared expert's units
  * are done.  The launch has one block per CU, so with all its blocks
  * resident every wait ends.  A wait that runs past 100 ms (another workload
  * holding CUs for that long) flags the run in MOE_DECODE_TAP_STATUS and goes
@@ -180,7 +180,7 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
  *   STATUS    u32  [1]          0, or nonzero when a wait timed out and the
  *                               output is not valid: 1 the fused expert
  *                               launch's wait for a slot's a8, 2 the w13
- *                               launch's wait for the logits or the plan
+ *                               launch's wait for the logits or the picks
  *                               (m <= 4) */
 enum moe_decode_tap {
   MOE_DECODE_TAP_NORMED = 0,
