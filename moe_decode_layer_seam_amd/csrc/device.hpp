@@ -190,6 +190,62 @@ __device__ __forceinline__ uint32_t fp8x2(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
+// The FFN seam on one lane's 8 columns ([layer] store_normed / store_x8),
+// shared by every kernel that runs it so that they give the same bits.
+// ---------------------------------------------------------------------------
+
+// ss plus the squares of 8 bf16 (4 words), in double and column order (each
+// square of a bf16 is exact in double).
+__device__ __forceinline__ double add_squares8(double ss, const u32x4& x) {
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    const double lo = bf16_to_f32(x[z] & 0xFFFFu), hi = bf16_to_f32(x[z] >> 16);
+    ss += lo * lo;
+    ss += hi * hi;
+  }
+  return ss;
+}
+
+// The normed values of 8 columns: (x r) w, each product rounded to fp32,
+// then rounded to bf16 (yb) and read back (y).
+__device__ __forceinline__ void norm8(const u32x4& x, const u32x4& w, float r, float (&y)[8], uint32_t (&yb)[8]) {
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    const uint32_t xb = (z & 1) ? (x[z >> 1] >> 16) : (x[z >> 1] & 0xFFFFu);
+    const uint32_t wb = (z & 1) ? (w[z >> 1] >> 16) : (w[z >> 1] & 0xFFFFu);
+    const float xr = bf16_to_f32(xb) * r;   // fp32 product, rounded
+    const float yw = xr * bf16_to_f32(wb);  // fp32 product, rounded
+    yb[z] = f32_to_bf16(yw);
+    y[z] = bf16_to_f32(yb[z]);
+  }
+}
+
+// acc plus the router logit's terms of 8 columns: y times the bf16 gate
+// weights, in double (exact products) and column order.
+__device__ __forceinline__ double add_logit8(double acc, const float (&y)[8], const u32x4& g) {
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    const uint32_t gb = (z & 1) ? (g[z >> 1] >> 16) : (g[z >> 1] & 0xFFFFu);
+    acc += (double)y[z] * (double)bf16_to_f32(gb);
+  }
+  return acc;
+}
+
+// MXFP8 of 8 values of a 32-group held by 4 consecutive lanes (all four
+// call it): the group's E8M0 code, and the 8 E4M3 bytes in qv.
+__device__ __forceinline__ int mx8(const float (&y)[8], u32x2& qv) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
+  amax = group_max(amax, 4);
+  const int code = e8m0_code(amax);
+  const float mul = mx_mul(code);
+  qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
+  qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
+  return code;
+}
+
+// ---------------------------------------------------------------------------
 // Scaled MFMA 16x16x128, E4M3 x E4M3 -> fp32 (device page, mfma_scaled).
 //
 // Operand layout, for one 128-byte K window starting at byte kw of a row:

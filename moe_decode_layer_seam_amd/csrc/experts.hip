@@ -488,16 +488,8 @@ __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scr
     if (t >= m) break;
     double ss = 0.0;
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      if (live[q]) {
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          const double lo = bf16_to_f32(xv[t][q][z] & 0xFFFFu), hi = bf16_to_f32(xv[t][q][z] >> 16);
-          ss += lo * lo;
-          ss += hi * hi;
-        }
-      }
-    }
+    for (int q = 0; q < CPT; ++q)
+      if (live[q]) ss = add_squares8(ss, xv[t][q]);
     ss = wave_sum(ss);
     if (seam && lane == 0) red_ss[t][wave] = ss;
   }
@@ -514,37 +506,21 @@ __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scr
     for (int q = 0; q < CPT; ++q) {
       float y[8];
       uint32_t yb[8];
-#pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        const uint32_t xb = (z & 1) ? (xv[t][q][z >> 1] >> 16) : (xv[t][q][z >> 1] & 0xFFFFu);
-        const uint32_t wb = (z & 1) ? (wv[q][z >> 1] >> 16) : (wv[q][z >> 1] & 0xFFFFu);
-        const float xr = bf16_to_f32(xb) * r;   // fp32 product, rounded
-        const float yw = xr * bf16_to_f32(wb);  // fp32 product, rounded
-        yb[z] = live[q] ? f32_to_bf16(yw) : 0u;
-        y[z] = bf16_to_f32(yb[z]);
-      }
       if (live[q]) {
+        norm8(xv[t][q], wv[q], r, y, yb);
 #pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          if (b + k * G < E) {
+        for (int k = 0; k < EB; ++k)
+          if (b + k * G < E) acc[k] = add_logit8(acc[k], y, gv[k][q]);
+      } else {
 #pragma unroll
-            for (int z = 0; z < 8; ++z) {
-              const uint32_t gb = (z & 1) ? (gv[k][q][z >> 1] >> 16) : (gv[k][q][z >> 1] & 0xFFFFu);
-              acc[k] += (double)y[z] * (double)bf16_to_f32(gb);  // exact products
-            }
-          }
+        for (int z = 0; z < 8; ++z) {
+          y[z] = 0.0f;
+          yb[z] = 0u;
         }
       }
-      float amax = 0.0f;
-#pragma unroll
-      for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
-      amax = group_max(amax, 4);
-      const int code = e8m0_code(amax);
-      const float mul = mx_mul(code);
+      u32x2 qv;
+      const int code = mx8(y, qv);
       if (live[q]) {
-        u32x2 qv;
-        qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
-        qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
         *reinterpret_cast<u32x2*>(dyn_lds + x8o + (uint32_t)(t * H + col[q])) = qv;
         if ((lane & 3) == 0) dyn_lds[xso + (uint32_t)(t * (H / 32) + col[q] / 32)] = (uint8_t)code;
         if (taps) {

@@ -114,13 +114,7 @@ __global__ __launch_bounds__(kThreads) void attn_x8_kernel(int H, const uint16_t
     wv[q] = live[q] ? *reinterpret_cast<const u32x4*>(w + col[q]) : u32x4{0u, 0u, 0u, 0u};
   double ss = 0.0;
 #pragma unroll
-  for (int q = 0; q < CPT; ++q)
-#pragma unroll
-    for (int z = 0; z < 4; ++z) {
-      const double lo = bf16_to_f32(xv[q][z] & 0xFFFFu), hi = bf16_to_f32(xv[q][z] >> 16);
-      ss += lo * lo;
-      ss += hi * hi;
-    }
+  for (int q = 0; q < CPT; ++q) ss = add_squares8(ss, xv[q]);
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();

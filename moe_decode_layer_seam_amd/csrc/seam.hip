@@ -85,16 +85,8 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
   for (int tt = 0; tt < TB; ++tt) {
     double ss = 0.0;
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      if (tt < nt && live[q]) {
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          const double lo = bf16_to_f32(xv[tt][q][z] & 0xFFFFu), hi = bf16_to_f32(xv[tt][q][z] >> 16);
-          ss += lo * lo;
-          ss += hi * hi;
-        }
-      }
-    }
+    for (int q = 0; q < CPT; ++q)
+      if (tt < nt && live[q]) ss = add_squares8(ss, xv[tt][q]);
     ss = wave_sum(ss);
     if (lane == 0) red_ss[tt][wave] = ss;
   }
@@ -119,26 +111,14 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
         u32x4 w;
         if constexpr (PRE) w = wv[q];
         else w = ld16(reinterpret_cast<const uint8_t*>(in.norm_w + col[q]));
-#pragma unroll
-        for (int z = 0; z < 8; ++z) {
-          const uint32_t xb = (z & 1) ? (xv[tt][q][z >> 1] >> 16) : (xv[tt][q][z >> 1] & 0xFFFFu);
-          const uint32_t wb = (z & 1) ? (w[z >> 1] >> 16) : (w[z >> 1] & 0xFFFFu);
-          const float xr = bf16_to_f32(xb) * r;   // fp32 product, rounded
-          const float yw = xr * bf16_to_f32(wb);  // fp32 product, rounded
-          yb[z] = f32_to_bf16(yw);
-          y[z] = bf16_to_f32(yb[z]);
-        }
+        norm8(xv[tt][q], w, r, y, yb);
 #pragma unroll
         for (int e = 0; e < EPB; ++e) {
           if (LOGITS && e0 + e < E) {
             u32x4 g;
             if constexpr (PRE) g = gv[e][q];
             else g = ld16(reinterpret_cast<const uint8_t*>(in.gate_w + (size_t)(e0 + e) * H + col[q]));
-#pragma unroll
-            for (int z = 0; z < 8; ++z) {
-              const uint32_t gb = (z & 1) ? (g[z >> 1] >> 16) : (g[z >> 1] & 0xFFFFu);
-              acc[e] += (double)y[z] * (double)bf16_to_f32(gb);  // exact products
-            }
+            acc[e] = add_logit8(acc[e], y, g);
           }
         }
       } else {
@@ -151,20 +131,13 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
       if (owner) {
         // store_normed: the bf16 row; store_x8: MXFP8 of each 32 columns,
         // held by 4 consecutive lanes
-        float amax = 0.0f;
-#pragma unroll
-        for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
-        amax = group_max(amax, 4);
-        const int code = e8m0_code(amax);
-        const float mul = mx_mul(code);
+        u32x2 qv;
+        const int code = mx8(y, qv);
         if (live[q]) {
           u32x4 nv;
 #pragma unroll
           for (int z = 0; z < 4; ++z) nv[z] = yb[2 * z] | (yb[2 * z + 1] << 16);
           *reinterpret_cast<u32x4*>(s.normed + (size_t)t * H + col[q]) = nv;
-          u32x2 qv;
-          qv[0] = fp8x4(y[0] * mul, y[1] * mul, y[2] * mul, y[3] * mul);
-          qv[1] = fp8x4(y[4] * mul, y[5] * mul, y[6] * mul, y[7] * mul);
           *reinterpret_cast<u32x2*>(s.x8 + (size_t)t * H + col[q]) = qv;
           if ((lane & 3) == 0) s.x8s[(size_t)t * (H / 32) + col[q] / 32] = (uint8_t)code;
         }
