@@ -593,8 +593,8 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   int* s_tok = reinterpret_cast<int*>(s_vs + vs_cap);  // w13: token of a row; w2: its output row
   UnitMap um;
   if constexpr (ROUTE) {
-    // until the plan is in: the shared expert's slots and rows, which do not
-    // depend on the routing
+    // until the picks are in: the shared expert's slots and rows, which do
+    // not depend on the routing
     const int nS = (m + kTokTile - 1) / kTokTile;
     um = unit_map_n<W13, TT>(d, nS, nS, split);
     for (int v = tid; v < nS; v += NW * 64) {
@@ -627,7 +627,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   while (true) {
     const uint32_t u = unit_turn(i, B, b);
     if (u >= um.total) {
-      // past the shared expert's units: the routed ones need the plan
+      // past the shared expert's units: the routed ones need the picks
       if (planned) break;
       stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
       um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);

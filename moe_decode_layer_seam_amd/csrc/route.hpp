@@ -302,6 +302,12 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
   stamp(s.tl_route, kTlPoints, 0);
 
   uint64_t k[GPW];
+  float bx[GPW];  // the biases, loaded before the logits are waited for
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    const int ex = 64 * (wave + 4 * i) + lane;
+    bx[i] = (wave < 4 && ex < E) ? bias[ex] : 0.0f;
+  }
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
   for (int i = 0; i < GPW; ++i) {
@@ -316,7 +322,7 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
         lg = s.logits[(size_t)t * E + ex];
       }
       const double sg = 1.0 / (1.0 + exp(-lg));
-      const double bb = sg + (double)bias[ex];
+      const double bb = sg + (double)bx[i];
       L.sig[ex] = sg;
       k[i] = select_key((bb == bb) ? bb : -INFINITY, ex);  // a NaN score ranks last
     }
@@ -358,9 +364,10 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     }
     stamp(s.tl_route, kTlPoints, 6);
     const int e = 1023 - (int)(k[0] & 0x3FF);
+    // the w13 launch's blocks wait for the picks alone: stored first
+    if (pbox && lane < K) store_coherent(pbox + t * K + lane, kBoxTag | (uint32_t)e);
     const double sg = lane < K ? L.sig[e] : 0.0;
     const double ssum = wave_sum(sg);
-    if (pbox && lane < K) store_coherent(pbox + t * K + lane, kBoxTag | (uint32_t)e);
     if (lane < K) {
       const float w = (float)((double)d.routed_scale * sg / ssum);
       L.ids[t * K + lane] = e;
