@@ -56,6 +56,36 @@ def w13_input_bytes(m: int, H: int, E: int, K: int, schedule: str = "launches") 
     return m * (H + H // 32)
 
 
+def read_peak(gib: float = 4.0, reps: int = 5) -> dict:
+    """Measured HBM read rate of a plain stream over gib GiB: the library's
+    read probe (128-bit non-temporal loads, every byte once), timed with
+    events on the current stream; best and median of reps launches after one
+    untimed launch."""
+    import torch
+    import moe_decode_layer_seam_amd as mdl
+
+    n = int(gib * 2**30) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(mdl.PROBE_BLOCKS, dtype=torch.int32, device="cuda")
+    mdl.read_probe(buf, sink)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mdl.read_probe(buf, sink)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    del buf
+    torch.cuda.empty_cache()
+    ts.sort()
+    return {"bytes": n, "reps": reps, "gbs_best": n / (ts[0] * 1e-3) / 1e9,
+            "gbs_median": n / (ts[len(ts) // 2] * 1e-3) / 1e9,
+            "kernel": f"moe_decode_read_probe: 128-bit non-temporal loads, {mdl.PROBE_BLOCKS} blocks x 256 "
+                      "threads, 16 loads in flight per thread, a contiguous range per block"}
+
+
 def make_weights(cfg: dict, seed: int, dev):
     """One device copy of the expert weights: N(0, 0.02) fp32 drawn on the GPU,
     quantised by the library's weight quantisers (E4M3 with 32 x 32 E8M0
@@ -454,6 +484,10 @@ def main() -> int:
     graphs.clear()
     del wsets
     torch.cuda.empty_cache()
+    # the measured streaming-read peak beside the published one
+    res["hbm_read_probe"] = read_peak()
+    res["expert_hbm_frac_of_measured"] = (expert_step_bytes / (ms_step * 1e-3)
+                                          / (res["hbm_read_probe"]["gbs_best"] * 1e9))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)

@@ -307,6 +307,21 @@ int moe_decode_attn_x8(int32_t m, int32_t hidden, const void* d_x,
                        const void* d_norm_w, float rms_eps, void* d_x8,
                        void* d_x8s, void* stream);
 
+/* Measurement aid (not part of a decode step): the HBM read rate a plain
+ * stream reaches on this device.  Reads the `bytes` bytes at d_buf once, in
+ * 128-bit non-temporal loads (the width and cache policy of the expert
+ * GEMMs' weight loads) from MOE_DECODE_PROBE_BLOCKS blocks of 256 threads,
+ * sixteen loads in flight per thread, each block one contiguous range; time
+ * it with events on `stream`.  Block b stores the XOR of the 32-bit words it
+ * read at d_sink[b], so the XOR of all of d_sink is the XOR of every word of
+ * the buffer.
+ *   d_buf   16-byte aligned, bytes a multiple of 16 (>= 16)
+ *   d_sink  u32 [MOE_DECODE_PROBE_BLOCKS], 4-byte aligned, fully overwritten
+ * EINVAL on bad arguments (nothing enqueued), EHIP on a failed launch. */
+#define MOE_DECODE_PROBE_BLOCKS 4096
+int moe_decode_read_probe(const void* d_buf, size_t bytes, uint32_t* d_sink,
+                          void* stream);
+
 /* Text of an error code. */
 const char* moe_decode_strerror(int code);
 /* The last HIP error a plan (or, with NULL, the library) saw, as text. */

@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_hc_fold.restype = ctypes.c_int
         L.moe_decode_attn_x8.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_float, _P, _P, _P]
         L.moe_decode_attn_x8.restype = ctypes.c_int
+        L.moe_decode_read_probe.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.moe_decode_read_probe.restype = ctypes.c_int
         L.moe_decode_strerror.argtypes = [ctypes.c_int]
         L.moe_decode_strerror.restype = ctypes.c_char_p
         L.moe_decode_last_hip_error.argtypes = [_P]
@@ -108,7 +110,9 @@ EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
            "moe_decode_timeline", "moe_decode_timeline_read",
            "moe_decode_destroy", "moe_decode_quantize_weight",
            "moe_decode_quantize_weight_fp4", "moe_decode_hc_fold", "moe_decode_attn_x8",
-           "moe_decode_strerror", "moe_decode_last_hip_error")
+           "moe_decode_read_probe", "moe_decode_strerror", "moe_decode_last_hip_error")
+
+PROBE_BLOCKS = 4096  # MOE_DECODE_PROBE_BLOCKS
 
 
 def strerror(code: int) -> str:
@@ -300,6 +304,19 @@ def attn_x8(x: torch.Tensor, norm_w: torch.Tensor, rms_eps: float = 1e-6, x8: to
                                     _tensor(x8s, "x8s", (m, H // 32), torch.uint8), _stream_ptr(stream)),
            "moe_decode_attn_x8")
     return x8, x8s
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """moe_decode_read_probe: one streaming read of the bytes of buf (uint8,
+    contiguous, a multiple of 16 bytes).  Returns sink, int32 [PROBE_BLOCKS]:
+    the XOR of the 32-bit words each block read."""
+    if sink is None:
+        sink = torch.empty(PROBE_BLOCKS, dtype=torch.int32, device=buf.device)
+    n = buf.numel()
+    _check(lib().moe_decode_read_probe(_tensor(buf, "buf", (n,), torch.uint8), n,
+                                       _tensor(sink, "sink", (PROBE_BLOCKS,), torch.int32),
+                                       _stream_ptr(stream)), "moe_decode_read_probe")
+    return sink
 
 
 def fp4_codes_shape(rows: int, cols: int) -> tuple:

@@ -117,6 +117,13 @@ void free_timing(moe_decode_plan_s* p) {
 
 }  // namespace
 
+namespace moe {
+// probe.hip: the streaming read of `bytes` (a multiple of 16) from buf by
+// MOE_DECODE_PROBE_BLOCKS blocks, each storing the XOR of the words it read
+// at sink[block].
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+}  // namespace moe
+
 extern "C" {
 
 int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle* out) {
@@ -456,6 +463,15 @@ int moe_decode_quantize_weight_fp4(const float* d_w, int32_t count, int32_t rows
   hipError_t e = launch_quant_weight_fp4(d_w, count, rows, cols, static_cast<uint8_t*>(d_q),
                                          static_cast<uint8_t*>(d_scales), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(nullptr, e, "quantize launch");
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_read_probe(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (bytes < 16 || bytes % 16 || !aligned16(d_buf) || d_sink == nullptr ||
+      reinterpret_cast<uintptr_t>(d_sink) % 4)
+    return MOE_DECODE_EINVAL;
+  hipError_t e = launch_read_probe(d_buf, bytes, d_sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(nullptr, e, "read probe launch");
   return MOE_DECODE_OK;
 }
 
