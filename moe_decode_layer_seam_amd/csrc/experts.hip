@@ -981,9 +981,11 @@ void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int s
 // mode.  More tiles per unit share one activation fragment among more weight
 // tiles and keep more weight bytes in flight per wave; fewer tiles give more
 // units to balance at small m.  Each tile's sums are the same whichever
-// variant runs it.
+// variant runs it.  Whole-mode w13 units take 4 tiles: a block's 25-26
+// units of 8 tiles (655 KB each at H = 5120) left one wave streaming the
+// last unit alone for up to 40 us after its block's other waves ended.
 #ifndef MOE_W13_WHOLE
-#define MOE_W13_WHOLE 8, 8
+#define MOE_W13_WHOLE 4, 8
 #endif
 #ifndef MOE_W13_SPLIT
 #define MOE_W13_SPLIT 4, 8
