@@ -134,7 +134,7 @@ constexpr uint32_t kBoxTag = 0x80000000u;
 constexpr uint64_t kLogitTag = 0x8000000000000000ull;
 inline int logits_blocks(const LayerDims& d, int m) {
   const int cpt = (d.H + 2047) / 2048;
-  const int tb = cpt <= 3 ? 8 : 4, epb = cpt <= 3 ? 4 : 2;
+  const int tb = 4, epb = cpt <= 3 ? 4 : 2;
   return seam_fused(m) ? 0 : (d.E + epb - 1) / epb * ((m + tb - 1) / tb);
 }
 

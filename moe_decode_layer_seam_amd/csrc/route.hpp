@@ -155,10 +155,28 @@ __device__ void plan_counts(const LayerDims& d, int P, const Scratch& s, RouteLd
 __device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s, RouteLds& L) {
   const int tid = threadIdx.x;
   const int E = d.E, K = d.K, P = m * K;
-  for (int p = tid; p < P; p += kThreads) {
-    if (p / K == own) continue;
-    L.ids[p] = __hip_atomic_load(&s.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    L.w[p] = __hip_atomic_load(&s.wts[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    // the other blocks' picks: every load issued before the first is used
+    // (one round trip instead of one per kThreads picks)
+    constexpr int NL = (kMaxTokens * kMaxTopk + kThreads - 1) / kThreads;
+    int idr[NL];
+    float wr[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int p = tid + k * kThreads;
+      if (p < P && p / K != own) {
+        idr[k] = __hip_atomic_load(&s.ids[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wr[k] = __hip_atomic_load(&s.wts[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int p = tid + k * kThreads;
+      if (p < P && p / K != own) {
+        L.ids[p] = idr[k];
+        L.w[p] = wr[k];
+      }
+    }
   }
   if (P <= 64 && m <= kTokTile) {
     __syncthreads();
