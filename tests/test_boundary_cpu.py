@@ -78,3 +78,15 @@ def test_seam_entry_points_reject_bad_arguments_without_a_gpu():
     assert L.moe_decode_attn_x8(1, 256, ok, ok, ctypes.c_float(-1.0), ok, ok, None) == mdl.EINVAL
     assert L.moe_decode_attn_x8(1, 256, ok, None, ctypes.c_float(1e-6), ok, ok, None) == mdl.EINVAL
 
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message, before
+    touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
