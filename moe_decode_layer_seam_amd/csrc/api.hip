@@ -346,7 +346,10 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
   if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
     return hip_fail(p, e, "logits launch");
-  if (!route13 && (e = launch_route(d, m, in, sc, st, ev(2))) != hipSuccess) return hip_fail(p, e, "route launch");
+  // the fused launch reads the route launch's plan; the w13 launch of the
+  // launches schedule builds its own from the stored picks
+  if (!route13 && (e = launch_route(d, m, in, sc, p->fused, st, ev(2))) != hipSuccess)
+    return hip_fail(p, e, "route launch");
   if (p->fused) {
     if ((e = launch_experts(d, m, in, sc, p->grid13, p->max_vs, st, ev(7))) != hipSuccess)
       return hip_fail(p, e, "experts launch");

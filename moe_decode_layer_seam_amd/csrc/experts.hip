@@ -571,7 +571,8 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   stamp(tl, kTlPoints, 0);
   const int R = m * d.K + m;
   const int P = m * d.K;
-  // ROUTE: the MXFP8 rows after the slots and the row map
+  // after the slots and the row map: ROUTE, the MXFP8 rows; other w13
+  // launches, the LDS of the plan they build
   const uint32_t x8o = ((uint32_t)vs_cap * 16 + (uint32_t)R * 4 + 15u) & ~15u;
   const uint32_t xso = x8o + (uint32_t)(m * d.H);
   if constexpr (ROUTE) {
@@ -603,11 +604,16 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     }
     for (int t = tid; t < m; t += NW * 64) s_tok[P + t] = t;
     if (tid == 0) s_plan = 0;
+  } else if constexpr (W13) {
+    // the plan, from the picks the route launch stored (after the slots and
+    // the row map in the LDS); block 0 also stores it for the w2 launch and
+    // the taps
+    const int nvs = plan_block<NW>(d, m, s, s_vs, s_tok, reinterpret_cast<uint32_t*>(lds_raw + x8o), blockIdx.x == 0);
+    um = unit_map_n<W13, TT>(d, nvs, (m + kTokTile - 1) / kTokTile, split);
   } else {
     um = unit_map<W13, TT>(d, s, split);
-    const int* row_map = W13 ? s.row_tok : s.row_out;
     for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
-    for (int i = tid; i < R; i += NW * 64) s_tok[i] = row_map[i];
+    for (int i = tid; i < R; i += NW * 64) s_tok[i] = s.row_out[i];
   }
   if (tid == 0) s_next = 0;
   __syncthreads();
@@ -1002,7 +1008,8 @@ template <bool W13>
 size_t gemm_lds(const LayerDims& d, int m, int max_vs, bool route = false) {
   const size_t base = ((size_t)max_vs * 16 + (size_t)(m * d.K + m) * 4 + 15) & ~(size_t)15;
   const size_t mr = m < kRouteRows ? m : kRouteRows;
-  return route ? base + mr * d.H + mr * (d.H / 32) : base;
+  if (route) return base + mr * d.H + mr * (d.H / 32);
+  return W13 ? base + plan_block_words(d.E) * 4 : base;
 }
 
 template <bool W13, int TT, int NW, bool ROUTE = false>
@@ -1132,7 +1139,9 @@ int experts_blocks_per_cu(size_t lds) {
 size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs) { return experts_lds(d, m, max_vs); }
 
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {
-  return w13 ? gemm_lds<true>(d, m, max_vs, true) : gemm_lds<false>(d, m, max_vs);
+  if (!w13) return gemm_lds<false>(d, m, max_vs);
+  const size_t a = gemm_lds<true>(d, m, max_vs, true), b = gemm_lds<true>(d, m, max_vs, false);
+  return a > b ? a : b;
 }
 
 }  // namespace moe

@@ -160,7 +160,9 @@ hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratc
                        const KernelEvents& ev);
 hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                          const KernelEvents& ev);
-hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+// plan: the route launch also builds the plan (last block to finish); else
+// the w13 launch builds it from the stored picks.
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, bool plan, hipStream_t st,
                         const KernelEvents& ev);
 // route: the launch also runs the seam and routes (route_in_w13): its first
 // m blocks run the router while the others stream the shared expert's units.

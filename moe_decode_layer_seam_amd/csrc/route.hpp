@@ -237,6 +237,127 @@ __device__ void build_plan(const LayerDims& d, int m, int own, const Scratch& s,
   }
 }
 
+// Exclusive prefix sum of arr[0, n) (n <= 2 * NW * 64) in place by the NW
+// waves of a block; returns the total.  tmp: NW ints.
+template <int NW>
+__device__ int block_scan_w(int* arr, int n, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int v[2], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid * 2 + q;
+    v[q] = i < n ? arr[i] : 0;
+    sum += v[q];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wave ? tmp[w] : 0;
+    total += tmp[w];
+  }
+  int run = base + inc - sum;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid * 2 + q;
+    if (i < n) arr[i] = run;
+    run += v[q];
+  }
+  __syncthreads();
+  return total;
+}
+
+// LDS words plan_block needs beyond the slots and the row map.
+inline size_t plan_block_words(int E) { return 4 * (size_t)E + 16; }
+
+// The plan of a step of m tokens from the picks the route launch stored
+// (s.ids, s.wts), built by every thread of a block of NW waves with
+// build_plan's rows and slots: the slots into s_vs, the token of each row
+// into s_tok (both LDS).  With mem, also the plan's arrays in the scratch
+// (for the later launches and the taps).  pl: plan_block_words(E) LDS words.
+// Returns the number of virtual slots; the LDS is complete on return.
+template <int NW>
+__device__ int plan_block(const LayerDims& d, int m, const Scratch& s, int4* s_vs, int* s_tok, uint32_t* pl,
+                          bool mem) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x;
+  const int E = d.E, K = d.K, P = m * K;
+  uint32_t* mlo = pl;  // tokens 0-31 / 32-47 of each expert
+  uint32_t* mhi = pl + E;
+  int* base = reinterpret_cast<int*>(pl + 2 * E);
+  int* vsb = reinterpret_cast<int*>(pl + 3 * E);
+  int* tmp = reinterpret_cast<int*>(pl + 4 * E);
+  for (int e = tid; e < E; e += NT) mlo[e] = mhi[e] = 0u;
+  __syncthreads();
+  for (int p = tid; p < P; p += NT) {
+    const int t = p / K, e = s.ids[p];
+    if (t < 32) atomicOr(&mlo[e], 1u << t);
+    else atomicOr(&mhi[e], 1u << (t - 32));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    const int c = __popc(mlo[e]) + __popc(mhi[e]);
+    base[e] = c;
+    vsb[e] = (c + kTokTile - 1) / kTokTile;
+    if (mem) s.counts[e] = c;
+  }
+  __syncthreads();
+  block_scan_w<NW>(base, E, tmp);
+  const int nR = block_scan_w<NW>(vsb, E, tmp + NW);
+  const int nS = (m + kTokTile - 1) / kTokTile;
+  for (int p = tid; p < P; p += NT) {
+    const int t = p / K, e = s.ids[p];
+    const int rank = t < 32 ? __popc(mlo[e] & ((1u << t) - 1u))
+                            : __popc(mlo[e]) + __popc(mhi[e] & ((1u << (t - 32)) - 1u));
+    const int r = base[e] + rank;
+    s_tok[r] = t;
+    if (mem) {
+      s.row_tok[r] = t;
+      s.row_w[r] = s.wts[p];
+      s.pair_row[p] = r;
+      s.row_out[r] = p;
+    }
+  }
+  for (int e = tid; e < E; e += NT) {
+    const int c = __popc(mlo[e]) + __popc(mhi[e]);
+    for (int v = 0; v * kTokTile < c; ++v) {
+      const int rows = c - v * kTokTile;
+      const int4 sl = make_int4(e, base[e] + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+      s_vs[nS + vsb[e] + v] = sl;
+      if (mem) s.vslots[nS + vsb[e] + v] = sl;
+    }
+  }
+  for (int t = tid; t < m; t += NT) {
+    s_tok[P + t] = t;
+    if (mem) {
+      s.row_tok[P + t] = t;
+      s.row_w[P + t] = 1.0f;
+      s.row_out[P + t] = P + t;
+    }
+  }
+  for (int v = tid; v < nS; v += NT) {
+    const int rows = m - v * kTokTile;
+    const int4 sl = make_int4(-1, P + v * kTokTile, rows < kTokTile ? rows : kTokTile, 0);
+    s_vs[v] = sl;
+    if (mem) s.vslots[v] = sl;
+  }
+  if (mem && tid == 0) {
+    s.header[0] = nS + nR;
+    s.header[1] = nS;
+    s.header[2] = nR;
+    s.header[3] = m;
+  }
+  __syncthreads();
+  return nS + nR;
+}
+
 // Selection key of expert e with biased score b: the fp64 order of b
 // (larger first) in the upper 54 bits, then the lower index first.  Scores
 // closer than 2^-42 relative (below the 10 low bits) fall to the index.
@@ -313,7 +434,7 @@ __device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s
 template <int GPW>
 __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
                             const Scratch& s, RouteLds& L, uint32_t* pbox = nullptr,
-                            const uint64_t* lbox = nullptr) {
+                            const uint64_t* lbox = nullptr, bool plan = true) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = d.E, K = d.K;
   const int groups = (E + 63) / 64;
@@ -396,6 +517,8 @@ __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const
     }
   }
   stamp(s.tl_route, kTlPoints, 2);
+  // without plan, the launch after this one builds it from the stored picks
+  if (!plan) return false;
   if (nblocks == 1 && K <= 64) {
     // one token: wave 0 holds every pick and builds the plan from them
     // straight away (its own LDS writes, in order; no barrier)

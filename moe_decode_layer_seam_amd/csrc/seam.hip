@@ -292,9 +292,9 @@ hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Sc
 
 template <int GPW>
 __global__ __launch_bounds__(kThreads) void route_kernel(LayerDims d, int m, const float* __restrict__ bias,
-                                                         Scratch s) {
+                                                         Scratch s, int plan) {
   __shared__ RouteLds L;
-  (void)route_block<GPW>(d, m, blockIdx.x, gridDim.x, bias, s, L);
+  (void)route_block<GPW>(d, m, blockIdx.x, gridDim.x, bias, s, L, nullptr, nullptr, plan != 0);
 }
 
 }  // namespace
@@ -323,13 +323,14 @@ hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scra
   }
 }
 
-hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+hipError_t launch_route(const LayerDims& d, int m, const Inputs& in, const Scratch& s, bool plan, hipStream_t st,
                         const KernelEvents& ev) {
   const int groups = (d.E + 63) / 64;  // sort groups; wave w takes w, w+4, ...
   const int gpw = (groups + 3) / 4;
-  if (gpw <= 1) return launch_kernel(route_kernel<1>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
-  if (gpw <= 2) return launch_kernel(route_kernel<2>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
-  return launch_kernel(route_kernel<4>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s);
+  const int pl = plan ? 1 : 0;
+  if (gpw <= 1) return launch_kernel(route_kernel<1>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s, pl);
+  if (gpw <= 2) return launch_kernel(route_kernel<2>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s, pl);
+  return launch_kernel(route_kernel<4>, dim3(m), dim3(kThreads), 0, st, ev, d, m, in.bias, s, pl);
 }
 
 }  // namespace moe
