@@ -305,7 +305,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    cfg = dict(synth.CONFIGS[args.config], routed=args.routed)
+    cfg = dict(synth.WORKLOADS[args.config], routed=args.routed)
     m, H, E, K, I, Is = cfg["m"], cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"], cfg["shared_inter"]
     eb = expert_bytes(H, I, args.routed)
     ebs = expert_bytes(H, Is)

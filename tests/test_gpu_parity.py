@@ -28,7 +28,7 @@ def _cfg(m, H, E, K, I, Is, **kw):
 
 
 SMALL = [
-    synth.CONFIGS[0],
+    synth.WORKLOADS[0],
     _cfg(1, 256, 64, 6, 128, 128),
     _cfg(5, 512, 64, 6, 256, 128),          # I != Is
     _cfg(13, 640, 100, 8, 128, 256),        # H % 512 != 0, E not a multiple of 64
@@ -99,7 +99,7 @@ def _bf16_f64(bits):
 # MXFP4 (E2M1 pairs, 1 x 32 codes) routed experts: odd K step counts (H 640,
 # I 128) leave one half of a weight line pair empty
 SMALL_FP4 = [dict(c, routed="mxfp4", name=c["name"] + "_fp4") for c in (
-    synth.CONFIGS[0],
+    synth.WORKLOADS[0],
     _cfg(4, 640, 100, 8, 128, 256),
     _cfg(5, 512, 64, 6, 256, 128),
     _cfg(13, 640, 100, 8, 128, 256),
@@ -317,11 +317,11 @@ def _gpu_weights(cfg, seed):
 # m = 48, whole/split where I is much larger than H
 SCHEDULE_CASES = [
     _cfg(13, 640, 100, 8, 128, 256),
-    dict(synth.CONFIGS[1], m=8, name="dsv41_m8"),
-    synth.CONFIGS[3],
+    dict(synth.WORKLOADS[1], m=8, name="dsv41_m8"),
+    synth.WORKLOADS[3],
     _cfg(40, 256, 64, 4, 8192, 128),
-    dict(synth.CONFIGS[1], routed="mxfp4", name="dsv41_m1_fp4"),
-    dict(synth.CONFIGS[3], routed="mxfp4", name="dsv41_m48_fp4"),
+    dict(synth.WORKLOADS[1], routed="mxfp4", name="dsv41_m1_fp4"),
+    dict(synth.WORKLOADS[3], routed="mxfp4", name="dsv41_m48_fp4"),
 ]
 
 
@@ -441,7 +441,7 @@ def _full_layer(idx):
     configs 1 and 2, whose rows are its first rows); config 4 has its own."""
     key = "dsv41" if idx in (1, 2, 3) else "draft"
     if key not in _FULL:
-        base = synth.CONFIGS[3] if key == "dsv41" else synth.CONFIGS[4]
+        base = synth.WORKLOADS[3] if key == "dsv41" else synth.WORKLOADS[4]
         inp, w = data.build_layer(0, base, experts="picked")
         _FULL[key] = (base, inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
     return _FULL[key]
@@ -452,8 +452,8 @@ SAMPLES = {1: [0], 2: [0, 9, 15], 3: [0, 29, 47], 4: [0, 23, 47]}
 
 @pytest.mark.parametrize("idx", [1, 3])
 def test_parity_full_size_mxfp4(idx):
-    cfg = dict(synth.CONFIGS[idx], routed="mxfp4")
-    base = dict(synth.CONFIGS[3], routed="mxfp4")
+    cfg = dict(synth.WORKLOADS[idx], routed="mxfp4")
+    base = dict(synth.WORKLOADS[3], routed="mxfp4")
     key = "dsv41_fp4"
     if key not in _FULL:
         inp, w = data.build_layer(0, base, experts="picked")
@@ -475,7 +475,7 @@ def test_parity_full_size_mxfp4(idx):
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_parity_full_size(idx):
-    cfg = synth.CONFIGS[idx]
+    cfg = synth.WORKLOADS[idx]
     base, inp_all, w, dinp_all, dw = _full_layer(idx)
     m = cfg["m"]
     inp = dict(inp_all, x=inp_all["x"][:m])

@@ -170,7 +170,7 @@ def test_fp4_expert_matches_torch_reference():
 
 @pytest.mark.parametrize("m", [1, 3])
 def test_fp4_layer_matches_torch_reference(m):
-    cfg = dict(synth.CONFIGS[0], routed="mxfp4", m=m)
+    cfg = dict(synth.WORKLOADS[0], routed="mxfp4", m=m)
     inp, w = data.build_layer(4, cfg)
     dims = data.dims_of(cfg)
     o = oracle.layer(dims, inp, w)

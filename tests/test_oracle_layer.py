@@ -193,7 +193,7 @@ def test_weight_quantiser_block_layout_and_error_bound():
 
 # ------------------------------------------------------- Whole layer ----
 
-@pytest.mark.parametrize("cfg", [synth.CONFIGS[0], _small_cfg(),
+@pytest.mark.parametrize("cfg", [synth.WORKLOADS[0], _small_cfg(),
                                  _small_cfg(m=3, experts=8, topk=8, routed_scale=2.5)])
 def test_layer_matches_torch_reference_on_tiny_shapes(cfg):
     inp, w = data.build_layer(51, cfg)
