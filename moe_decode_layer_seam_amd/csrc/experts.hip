@@ -438,9 +438,9 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
 }
 
 // The seam of the w13 launch that routes (m <= kRouteRows rows, H <= 8192),
-// run by the block's first four waves with the seam launch's thread mapping
-// (8 columns a thread, chunks of 2048) and order of every sum, so its bits
-// are that launch's:
+// run by all eight waves of the block with the seam launch's thread mapping
+// (8 columns a thread, chunks of kSeamChunk) and order of every sum, so its
+// bits are that launch's:
 //   - the rows' RMSNorm and MXFP8 into the block's LDS (values at x8o, codes
 //     at xso): the A operand of the block's w13 units;
 //   - the router logits of experts b and b + G for every row (b: the block,
@@ -451,18 +451,18 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
 // barrier inside has passed.
 __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scratch& s, uint32_t x8o,
                           uint32_t xso) {
-  constexpr int CPT = 4, EB = 2;
-  __shared__ double red_ss[kRouteRows][4];
-  __shared__ double red_lg[kRouteRows][EB][4];
+  constexpr int CPT = 2, EB = 2;  // H <= 2 kSeamChunk
+  __shared__ double red_ss[kRouteRows][kSeamWaves];
+  __shared__ double red_lg[kRouteRows][EB][kSeamWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool seam = tid < kThreads;
+  const bool seam = tid < kSeamThreads;
   const int H = d.H, E = d.E, G = gridDim.x, b = blockIdx.x;
   const bool taps = b == 0;
   int col[CPT];
   bool live[CPT];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
-    col[q] = 8 * tid + 2048 * q;
+    col[q] = 8 * tid + kSeamChunk * q;
     live[q] = seam && col[q] < H;
   }
   // every load at once: the rows, the norm weight, the block's gate rows
@@ -497,7 +497,9 @@ __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scr
 #pragma unroll
   for (int t = 0; t < kRouteRows; ++t) {
     if (t >= m) break;
-    const double sst = red_ss[t][0] + red_ss[t][1] + red_ss[t][2] + red_ss[t][3];
+    double sst = red_ss[t][0];
+#pragma unroll
+    for (int w = 1; w < kSeamWaves; ++w) sst += red_ss[t][w];
     const float r = (float)(1.0 / sqrt(sst / (double)H + (double)d.eps));
     double acc[EB];
 #pragma unroll
@@ -543,7 +545,9 @@ __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scr
   if (tid < m * EB) {
     const int t = tid / EB, k = tid % EB, e = b + k * G;
     if (e < E) {
-      const double v = red_lg[t][k][0] + red_lg[t][k][1] + red_lg[t][k][2] + red_lg[t][k][3];
+      double v = red_lg[t][k][0];
+#pragma unroll
+      for (int w = 1; w < kSeamWaves; ++w) v += red_lg[t][k][w];
       uint64_t w = (uint64_t)__double_as_longlong(v) ^ kLogitTag;
       if (w == 0ull) w = kLogitTag;  // (-0 is not a sum from +0; kept as +0 all the same)
       __hip_atomic_store(&s.logit_box[(size_t)t * E + e], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -576,6 +580,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   const uint32_t x8o = ((uint32_t)vs_cap * 16 + (uint32_t)R * 4 + 15u) & ~15u;
   const uint32_t xso = x8o + (uint32_t)(m * d.H);
   if constexpr (ROUTE) {
+    static_assert(NW * 64 == kSeamThreads, "the seam's thread mapping takes the whole block");
     // no seam launch ran: block 0 clears the status word (a wait gives up
     // only after 100 ms)
     if (blockIdx.x == 0 && tid == 0) store_coherent(s.status, 0u);

@@ -92,8 +92,17 @@ inline int max_vslots(int m, int E, int K) {
   return routed + (m + kTokTile - 1) / kTokTile;
 }
 
+// The seam's thread mapping, shared bit for bit by every kernel that sums a
+// row's squares or a router logit (the seam launch, the logits launch and
+// the seam inside the w13 launch that routes): 8 columns a thread in chunks
+// of kSeamChunk columns, a thread's chunks in order, then the lanes'
+// butterfly (32 apart first), then the kSeamWaves waves in order.
+constexpr int kSeamThreads = 512;
+constexpr int kSeamWaves = kSeamThreads / 64;
+constexpr int kSeamChunk = 8 * kSeamThreads;
+inline int seam_cpt(int H) { return (H + kSeamChunk - 1) / kSeamChunk; }
 // Token rows per block of the seam launch (rows held in registers).
-inline int seam_tb(int H) { return (H + 2047) / 2048 <= 4 ? 8 : 4; }
+inline int seam_tb(int H) { return seam_cpt(H) <= 2 ? 8 : 4; }
 // Experts per block of the seam launch: every block recomputes the norm of
 // its rows, so blocks take as many experts as keeps about 256 blocks (and at
 // most 256 expert slices).
@@ -117,8 +126,8 @@ inline int seam_blocks(const LayerDims& d, int m) {
 // quantises the rows into its LDS and sums the logits of one or two experts,
 // the first m blocks route (one per token), and the others start on the
 // shared expert.  When the router's expert groups fit its four waves, the
-// plan fits one wave (at most 64 pairs), a row fits four 2048-column chunks
-// of the seam's thread mapping, and two experts per block cover E.
+// plan fits one wave (at most 64 pairs), a row fits two chunks of the seam's
+// thread mapping, and two experts per block cover E.
 constexpr int kRouteRows = 4;
 inline bool route_in_w13(const LayerDims& d, int m, int grid) {
   return m <= kRouteRows && m * d.K <= 64 && d.E <= 256 && d.H <= 8192 && d.E <= 2 * grid && grid > m;
@@ -133,8 +142,7 @@ constexpr uint32_t kBoxTag = 0x80000000u;
 // zeroed box's value).
 constexpr uint64_t kLogitTag = 0x8000000000000000ull;
 inline int logits_blocks(const LayerDims& d, int m) {
-  const int cpt = (d.H + 2047) / 2048;
-  const int tb = 4, epb = cpt <= 3 ? 4 : 2;
+  const int tb = 4, epb = seam_cpt(d.H) <= 2 ? 4 : 2;
   return seam_fused(m) ? 0 : (d.E + epb - 1) / epb * ((m + tb - 1) / tb);
 }
 

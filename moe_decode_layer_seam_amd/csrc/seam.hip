@@ -26,16 +26,16 @@ namespace {
 // ===========================================================================
 
 // Block (es, ts): experts [EPB es, +EPB) and token rows [TB ts, +TB).  Every
-// thread covers CPT chunks of 8 columns, the block 2048 consecutive columns
-// per chunk.  The norm weight and the gate rows are loaded once, up front,
+// thread covers CPT chunks of 8 columns, the block kSeamChunk consecutive
+// columns per chunk.  The norm weight and the gate rows are loaded once, up front,
 // when they fit in registers (PRE); the token rows are held in registers
 // between the sum of squares and the normed row.
 // LOGITS false: the norm and MXFP8 only (one block column owns every row;
 // logits_kernel computes the logits from the stored rows).
 template <int EPB, int CPT, int TB, bool LOGITS>
-__global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inputs in, Scratch s) {
-  __shared__ double red_ss[TB][4];
-  __shared__ double red_lg[TB][EPB][4];
+__global__ __launch_bounds__(kSeamThreads) void seam_kernel(LayerDims d, int m, Inputs in, Scratch s) {
+  __shared__ double red_ss[TB][kSeamWaves];
+  __shared__ double red_lg[TB][EPB][kSeamWaves];
   constexpr bool PRE = LOGITS && EPB * CPT <= 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int es = blockIdx.x, nES = gridDim.x;
@@ -46,8 +46,8 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
   stamp(s.tl_seam, kTlPoints, 0);
   {
     // the fused expert launch's counters start every run at zero
-    const uint32_t nthr = gridDim.x * gridDim.y * kThreads;
-    for (uint32_t w = (blockIdx.y * gridDim.x + blockIdx.x) * kThreads + tid; w < (uint32_t)s.nsync; w += nthr)
+    const uint32_t nthr = gridDim.x * gridDim.y * kSeamThreads;
+    for (uint32_t w = (blockIdx.y * gridDim.x + blockIdx.x) * kSeamThreads + tid; w < (uint32_t)s.nsync; w += nthr)
       store_coherent(&s.sync[w], 0u);
   }
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
   bool live[CPT];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
-    col[q] = 8 * tid + 2048 * q;
+    col[q] = 8 * tid + kSeamChunk * q;
     live[q] = col[q] < H;
   }
   // the token rows first: loads complete in issue order, so the sum of
@@ -97,7 +97,9 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
   for (int tt = 0; tt < TB; ++tt) {
     if (tt >= nt) break;
     const int t = t0 + tt;
-    const double ss = red_ss[tt][0] + red_ss[tt][1] + red_ss[tt][2] + red_ss[tt][3];
+    double ss = red_ss[tt][0];
+#pragma unroll
+    for (int w = 1; w < kSeamWaves; ++w) ss += red_ss[tt][w];
     const float r = (float)(1.0 / sqrt(ss / (double)H + (double)d.eps));
     const bool owner = (t % nES) == es;
     double acc[EPB];
@@ -156,10 +158,14 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
     return;
   }
   __syncthreads();
-  for (int i = tid; i < nt * EPB; i += kThreads) {
+  for (int i = tid; i < nt * EPB; i += kSeamThreads) {
     const int tt = i / EPB, e = i % EPB;
-    if (e0 + e < E)
-      s.logits[(size_t)(t0 + tt) * E + e0 + e] = red_lg[tt][e][0] + red_lg[tt][e][1] + red_lg[tt][e][2] + red_lg[tt][e][3];
+    if (e0 + e < E) {
+      double v = red_lg[tt][e][0];
+#pragma unroll
+      for (int w = 1; w < kSeamWaves; ++w) v += red_lg[tt][e][w];
+      s.logits[(size_t)(t0 + tt) * E + e0 + e] = v;
+    }
   }
   stamp(s.tl_seam, kTlPoints, 2);
 }
@@ -167,16 +173,16 @@ __global__ __launch_bounds__(kThreads) void seam_kernel(LayerDims d, int m, Inpu
 // Rows per block: a block holds TB rows of CPT chunks in registers.
 template <int CPT>
 constexpr int seam_tb() {
-  return CPT <= 4 ? 8 : 4;
+  return CPT <= 2 ? 8 : 4;
 }
 
 // Router logits from the stored bf16 rows: block (es, ts) takes experts
 // [EPB es, +EPB) and rows [TB ts, +TB).  Every logit is summed exactly as in
 // seam_kernel (a thread's columns in the same order, the same wave sum, the
-// four waves in order), so both paths give the same bits.
+// waves in order), so both paths give the same bits.
 template <int EPB, int CPT, int TB>
-__global__ __launch_bounds__(kThreads) void logits_kernel(LayerDims d, int m, Inputs in, Scratch s) {
-  __shared__ double red_lg[TB][EPB][4];
+__global__ __launch_bounds__(kSeamThreads) void logits_kernel(LayerDims d, int m, Inputs in, Scratch s) {
+  __shared__ double red_lg[TB][EPB][kSeamWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.y * TB;
   const int nt = m - t0 < TB ? m - t0 : TB;
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LayerDims d, int m, In
   bool live[CPT];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
-    col[q] = 8 * tid + 2048 * q;
+    col[q] = 8 * tid + kSeamChunk * q;
     live[q] = col[q] < H;
   }
   u32x4 yv[TB][CPT], gv[EPB][CPT];
@@ -242,10 +248,14 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(LayerDims d, int m, In
     red_lg[i / EPB][i % EPB][wave] = v[0];
   }
   __syncthreads();
-  for (int i = tid; i < nt * EPB; i += kThreads) {
+  for (int i = tid; i < nt * EPB; i += kSeamThreads) {
     const int tt = i / EPB, e = i % EPB;
-    if (e0 + e < E)
-      s.logits[(size_t)(t0 + tt) * E + e0 + e] = red_lg[tt][e][0] + red_lg[tt][e][1] + red_lg[tt][e][2] + red_lg[tt][e][3];
+    if (e0 + e < E) {
+      double v = red_lg[tt][e][0];
+#pragma unroll
+      for (int w = 1; w < kSeamWaves; ++w) v += red_lg[tt][e][w];
+      s.logits[(size_t)(t0 + tt) * E + e0 + e] = v;
+    }
   }
   stamp(s.tl_logits, kTlPoints, 1);
 }
@@ -255,35 +265,31 @@ hipError_t launch_seam_t(const LayerDims& d, int m, const Inputs& in, const Scra
                          const KernelEvents& ev) {
   constexpr int TB = LOGITS ? seam_tb<CPT>() : 1;
   const dim3 grid(LOGITS ? (d.E + EPB - 1) / EPB : 1, (m + TB - 1) / TB);
-  return launch_kernel(seam_kernel<EPB, CPT, TB, LOGITS>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
+  return launch_kernel(seam_kernel<EPB, CPT, TB, LOGITS>, grid, dim3(kSeamThreads), 0, st, ev, d, m, in, s);
 }
 
 template <int EPB, bool LOGITS>
 hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                            const KernelEvents& ev) {
-  switch ((d.H + 2047) / 2048) {
+  switch (seam_cpt(d.H)) {
     case 1: return launch_seam_t<EPB, 1, LOGITS>(d, m, in, s, st, ev);
     case 2: return launch_seam_t<EPB, 2, LOGITS>(d, m, in, s, st, ev);
     case 3: return launch_seam_t<EPB, 3, LOGITS>(d, m, in, s, st, ev);
-    case 4: return launch_seam_t<EPB, 4, LOGITS>(d, m, in, s, st, ev);
-    case 5: return launch_seam_t<EPB, 5, LOGITS>(d, m, in, s, st, ev);
-    case 6: return launch_seam_t<EPB, 6, LOGITS>(d, m, in, s, st, ev);
-    case 7: return launch_seam_t<EPB, 7, LOGITS>(d, m, in, s, st, ev);
-    default: return launch_seam_t<EPB, 8, LOGITS>(d, m, in, s, st, ev);
+    default: return launch_seam_t<EPB, 4, LOGITS>(d, m, in, s, st, ev);
   }
 }
 
 // Logits tiles: 4 rows x 4 experts when a thread's chunks of the row number
-// at most 3 (registers), else 4 rows x 2 experts.  Against 8 rows x 4
-// experts, the smaller tiles halve each block's chain of double FMAs and
-// double the blocks: 9.7 -> 8.1 us at m = 48 and 6.0 -> 4.4 us at m = 16
-// (H = 5120, E = 256).  A logit is summed in the same tree whatever the tile.
+// at most 2 (registers), else 4 rows x 2 experts.  At H = 5120, E = 256 this
+// takes 9.5 us at m = 48 and 4.5 us at m = 16; tiles of 8 x 4, 4 x 8 or
+// 8 x 2 took 12 and 4.7-6.3 us.  A logit is summed in the same tree
+// whatever the tile.
 template <int CPT>
 hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                            const KernelEvents& ev) {
-  constexpr int TB = 4, EPB = CPT <= 3 ? 4 : 2;
+  constexpr int TB = 4, EPB = CPT <= 2 ? 4 : 2;
   const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
-  return launch_kernel(logits_kernel<EPB, CPT, TB>, grid, dim3(kThreads), 0, st, ev, d, m, in, s);
+  return launch_kernel(logits_kernel<EPB, CPT, TB>, grid, dim3(kSeamThreads), 0, st, ev, d, m, in, s);
 }
 
 // ===========================================================================
@@ -311,15 +317,11 @@ hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratc
 
 hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                          const KernelEvents& ev) {
-  switch ((d.H + 2047) / 2048) {
+  switch (seam_cpt(d.H)) {
     case 1: return launch_logits_t<1>(d, m, in, s, st, ev);
     case 2: return launch_logits_t<2>(d, m, in, s, st, ev);
     case 3: return launch_logits_t<3>(d, m, in, s, st, ev);
-    case 4: return launch_logits_t<4>(d, m, in, s, st, ev);
-    case 5: return launch_logits_t<5>(d, m, in, s, st, ev);
-    case 6: return launch_logits_t<6>(d, m, in, s, st, ev);
-    case 7: return launch_logits_t<7>(d, m, in, s, st, ev);
-    default: return launch_logits_t<8>(d, m, in, s, st, ev);
+    default: return launch_logits_t<4>(d, m, in, s, st, ev);
   }
 }
 
