@@ -274,7 +274,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index 1-4 (0 = tiny)")
+    ap.add_argument("--config", type=int, default=1, help="workload index 1-6 (0 = tiny; 5-6 the eight-way tensor-parallel share)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: auto)")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,7 +310,7 @@ def main() -> int:
     eb = expert_bytes(H, I, args.routed)
     ebs = expert_bytes(H, Is)
     per_step_expected = (min(E, m * K) + 1) * (eb["w13"] + eb["w2"])
-    copies = args.copies or max(2, min(8, -(-2 * 512 * 2**20 // per_step_expected)))
+    copies = args.copies or max(2, min(32, -(-2 * 512 * 2**20 // per_step_expected)))
 
     print(f"[bench] {cfg['name']}: building {copies} weight copies", file=sys.stderr, flush=True)
     t0 = time.time()
@@ -343,14 +343,17 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # graphs of G consecutive steps (whole laps over the weight copies), as a
-    # decode graph holds many layers; a second graph takes K mod G steps
+    # decode graph holds many layers; another takes the rest of each batch
     G = copies * max(1, -(-8 // copies))
+    # the timed region: K steps in 5 batches (events between batches)
+    nb = 5 if args.steps >= 5 * G else 1
+    sizes = [args.steps // nb + (1 if b < args.steps % nb else 0) for b in range(nb)]
     graphs = {}
     if args.mode == "graph":
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for n in sorted({G, args.steps % G} - {0}):
+            for n in sorted(({G} | {sz % G for sz in sizes}) - {0}):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
                     for i in range(n):
@@ -371,9 +374,7 @@ def main() -> int:
             for i in range(n):
                 step(i % copies)
 
-    # ---- timed region: K steps in 5 batches (events between batches)
-    nb = 5 if args.steps >= 5 * G else 1
-    sizes = [args.steps // nb + (1 if b < args.steps % nb else 0) for b in range(nb)]
+    # ---- timed region
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()

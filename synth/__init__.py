@@ -98,15 +98,19 @@ def expert_f32(seed: int, name: str, expert: int, rows: int, cols: int,
     return normal(seed, STREAM[name], (rows, cols), 0.0, std, start=expert * n)
 
 
-# The five workloads (shapes only).  Index 0 is the tiny layer the oracle
-# finishes in well under a second; 1-3 are one DeepSeek-V4.1-style layer at
-# 1, 16 and 48 token rows; 4 is the 64-expert draft layer at 48 rows.
+# The workloads (shapes only).  Index 0 is the tiny layer the oracle finishes
+# in well under a second; 1-3 are one DeepSeek-V4.1-style layer at 1, 16 and
+# 48 token rows; 4 is the 64-expert draft layer at 48 rows; 5-6 are one GPU's
+# share of layers 1 and 3 under eight-way tensor parallelism (the routed and
+# shared intermediate split eight ways, hidden and router whole).
 WORKLOADS = {
     0: dict(name="tiny", m=1, hidden=256, experts=8, topk=2, inter=128, shared_inter=128),
     1: dict(name="dsv41_m1", m=1, hidden=5120, experts=256, topk=8, inter=2048, shared_inter=2048),
     2: dict(name="dsv41_m16", m=16, hidden=5120, experts=256, topk=8, inter=2048, shared_inter=2048),
     3: dict(name="dsv41_m48", m=48, hidden=5120, experts=256, topk=8, inter=2048, shared_inter=2048),
     4: dict(name="draft_m48", m=48, hidden=5120, experts=64, topk=4, inter=1024, shared_inter=1024),
+    5: dict(name="dsv41_tp8_m1", m=1, hidden=5120, experts=256, topk=8, inter=256, shared_inter=256),
+    6: dict(name="dsv41_tp8_m48", m=48, hidden=5120, experts=256, topk=8, inter=256, shared_inter=256),
 }
 for _c in WORKLOADS.values():
     _c.setdefault("rms_eps", 1e-6)

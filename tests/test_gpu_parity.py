@@ -451,6 +451,23 @@ def _full_layer(idx):
 SAMPLES = {1: [0], 2: [0, 9, 15], 3: [0, 29, 47], 4: [0, 23, 47]}
 
 
+@pytest.mark.parametrize("idx", [5, 6])
+def test_parity_tensor_parallel_share(idx):
+    """One GPU's share of the layer under eight-way tensor parallelism (I = Is
+    = 256 at the full hidden size and router): every output row."""
+    cfg = synth.WORKLOADS[idx]
+    inp, w = data.build_layer(0, cfg, experts="picked")
+    dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
+    h = _plan_for(cfg, max_tokens=48)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        print(f"[{cfg['name']}] ran; checking every row", flush=True)
+        _check_layer(cfg, h, inp, w, out)
+    finally:
+        mdl.destroy(h)
+
+
 @pytest.mark.parametrize("idx", [1, 3])
 def test_parity_full_size_mxfp4(idx):
     cfg = dict(synth.WORKLOADS[idx], routed="mxfp4")
