@@ -28,6 +28,8 @@
 // are few (at small m: then the segment sums are stored and the next kernel
 // adds them, in the same order).  Each CU takes an equal share of the units;
 // inside a CU, fast waves take more of them.
+#include <cmath>
+
 #include "device.hpp"
 #include "kernels.hpp"
 #include "route.hpp"
@@ -1037,14 +1039,33 @@ int occupancy_t(size_t lds) {
 // Nominal waves per block of each GEMM, for the split decision.
 int gemm_waves(bool w13) { return w13 ? 8 : 8; }
 
-// Weight tiles of the larger expert kind times the slots a step of m rows
-// can have (distinct experts, plus the shared expert's slots); split mode
-// when whole-tile units would number under about four per wave.
+template <int TT, int NW>
+constexpr int unit_tiles() { return TT; }
+
+// Split mode when whole units would leave waves without one.  w13: the
+// expected slots of a step under uniform routing (E (1 - (1 - K/E)^m)
+// distinct experts, plus the shared expert's slots) times the whole units
+// of a slot, against 0.9 units per wave (the cases below bracket the cut
+// between 0.8 and 1.0).  At H = 5120 on 256 CUs: 64 slots of the
+// draft layer (E = 64, k = 4, m = 48) fill 2,048 waves with one unit each
+// and run w13 in 112 us whole against 131 us split; a step of 8 rows of the
+// 256-expert layer (1.8 units per wave) takes 199 against 206 us; 48 rows at
+// I = 256 (0.8 per wave) take 96 whole against 93 us split.  Steps that route
+// inside the w13 launch (m <= 4) stay split: there the shared expert's units
+// start first, and whole ones (one per wave at m = 4) ended later than the
+// split ones (118 against 115 us).  w2: the slot bound min(m k, E) plus the
+// shared slots, split under one whole 8-tile unit per wave.
 bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
+  const long shared = (m + kTokTile - 1) / kTokTile;
+  if (w13) {
+    if (m <= kRouteRows) return true;
+    const double distinct = d.E * (1.0 - std::pow(1.0 - (double)d.K / d.E, m));
+    const double units = (distinct + shared) * (2.0 * d.Imax / 16 / unit_tiles<MOE_W13_WHOLE>());
+    return units < 0.9 * waves;
+  }
   const int pairs = m * d.K;
-  const long slots = (long)(pairs < d.E ? pairs : d.E) + (m + kTokTile - 1) / kTokTile;
-  const long tiles = w13 ? 2L * d.Imax / 16 : d.H / 16;
-  return slots * tiles < (w13 ? 16L : 8L) * waves;
+  const long slots = (long)(pairs < d.E ? pairs : d.E) + shared;
+  return slots * (d.H / 16) < 8L * waves;
 }
 
 hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,

@@ -314,12 +314,14 @@ def _gpu_weights(cfg, seed):
 
 
 # (w13 mode, w2 mode) of the fused launch on 256 CUs: split/split at small
-# sizes and m <= 6 of the full layer, split/whole at m = 8, whole/whole at
-# m = 48, whole/split where I is much larger than H
+# sizes and m <= 4 of the full layer, whole/whole at m = 8 and 48,
+# split/whole for 48 rows at I = 256, whole/split where I is much larger
+# than H
 SCHEDULE_CASES = [
     _cfg(13, 640, 100, 8, 128, 256),
     dict(synth.WORKLOADS[1], m=8, name="dsv41_m8"),
     synth.WORKLOADS[3],
+    synth.WORKLOADS[6],
     _cfg(40, 256, 64, 4, 8192, 128),
     dict(synth.WORKLOADS[1], routed="mxfp4", name="dsv41_m1_fp4"),
     dict(synth.WORKLOADS[3], routed="mxfp4", name="dsv41_m48_fp4"),
