@@ -249,6 +249,27 @@ def test_runs_are_deterministic_and_plan_reusable_across_m(schedule):
         mdl.destroy(h)
 
 
+def test_whole_and_split_units_give_the_same_bits():
+    """Batch invariance across the GEMM modes: on the draft layer's shape (H
+    5120, 64 experts top-4, I = Is = 1024) 48 rows run w13 and w2 in whole
+    units, 8 and 5 rows in split units, and 1 row routes inside the w13
+    launch; a token's output bits are the same in each."""
+    cfg = dict(synth.WORKLOADS[4], name="draft_modes")
+    dw = _gpu_weights(cfg, 41)
+    inp = synth.small_inputs(9, 48, cfg["hidden"], cfg["experts"])
+    dinp = gu.inputs_dev(inp)
+    h = _plan_for(cfg)
+    try:
+        full = gu.run(h, cfg, dinp, dw).clone()
+        parts = {n: gu.run(h, cfg, dinp, dw, x=dinp["x"][:n].contiguous()).clone() for n in (8, 5, 1)}
+        torch.cuda.synchronize()
+        assert gu.tap(h, "status", torch.int32)[0] == 0
+        for n, o in parts.items():
+            assert torch.equal(o.view(torch.int16), full[:n].view(torch.int16)), f"{n} rows"
+    finally:
+        mdl.destroy(h)
+
+
 # m = 3: the launches schedule runs the seam and the router inside the w13
 # launch, whose hand-off boxes the act launch clears for the next replay
 @pytest.mark.parametrize("schedule,m", [("launches", 16), ("fused", 16), ("launches", 3)])
