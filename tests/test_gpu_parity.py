@@ -39,6 +39,7 @@ SMALL = [
     _cfg(48, 256, 512, 16, 128, 128),       # 8 sort groups, k = 16
     _cfg(7, 256, 1000, 32, 128, 128),       # 16 sort groups, k = 32
     _cfg(48, 256, 1024, 32, 128, 128),      # the largest plan: 1536 picks over 1024 experts
+    _cfg(48, 640, 100, 8, 1024, 512),       # w13 in whole units over a ragged last K segment
     # m <= 4: the seam and router inside the w13 launch (ragged H, E), and the
     # cases that keep their own launches (E > 256, m k > 64, H > 8192)
     _cfg(4, 640, 100, 8, 128, 256),
@@ -107,6 +108,7 @@ SMALL_FP4 = [dict(c, routed="mxfp4", name=c["name"] + "_fp4") for c in (
     _cfg(33, 256, 8, 8, 128, 128),
     _cfg(48, 512, 64, 4, 256, 256),
     _cfg(7, 256, 1000, 32, 128, 128),
+    _cfg(48, 640, 100, 8, 1024, 512),
 )]
 
 
