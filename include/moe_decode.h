@@ -295,10 +295,11 @@ int moe_decode_hc_fold(int32_t m, int32_t hidden, const void* d_part,
 /* The attention seam's input quantisation ([layer] store_x8): the RMSNorm of
  * each row x [m, H] bf16 with weight d_norm_w bf16 [H] (the seam's chain:
  * sum of squares in double, r = 1/sqrt(ss/H + eps) rounded once to fp32,
- * two fp32 products; no bf16 rounding), then per 32 columns vLLM's MXFP8
- * code of the amax, read as the OCP MX rule code = floor(log2(amax)) - 8 +
- * 127 clamped to [0, 254], the values scaled by 2^(127 - code), clamped to
- * +-448 (clamp_fp8) and rounded to nearest even E4M3.
+ * two fp32 products; no bf16 rounding), then per 32 columns vLLM's ROCm
+ * MXFP8 code of the amax ([device] mx_code: clamp(ceil(log2(amax / 448)) +
+ * 127, 0, 254), amax floored at FLT_MIN), the values scaled by
+ * 2^(127 - code), clamped to +-448 (clamp_fp8) and rounded to nearest even
+ * E4M3.
  *   d_x8   u8 [m, H]     E4M3
  *   d_x8s  u8 [m, H/32]  E8M0 codes
  * 1 <= m <= 48, hidden a multiple of 128, <= 16384, rms_eps finite >= 0;

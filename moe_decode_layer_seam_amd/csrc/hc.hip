@@ -3,7 +3,8 @@
 //            hyper-connection residual with the attention seam's mixes, and
 //            the FFN's input row combined from the new streams;
 //   attn_x8: the attention seam's norm output quantised with vLLM's MXFP8
-//            code and clamped to the E4M3 range (the attention's input).
+//            code (the device page's mx_code) and clamped to the E4M3 range
+//            (the attention's input).
 //
 // Pages: "vllm.models.deepseek_v41.amd.mono.layer" run_ffn (the attention's
 // partials summed and folded into the residual), store_x8 (amax over 32
@@ -81,18 +82,12 @@ __global__ __launch_bounds__(kThreads) void hc_fold_kernel(int H, const uint16_t
   *reinterpret_cast<uint32_t*>(x + row) = xo;
 }
 
-// vLLM's MXFP8 code of a 32-group's amax, read as the OCP MX rule:
-// floor(log2(amax)) - 8 + 127 = (amax's biased exponent) - 8, at least 0
-// (zero and subnormal amax give 0); at most 246 for a finite fp32.
-__device__ __forceinline__ int vllm_mx_code(float amax) {
-  const int e = (int)(__float_as_uint(amax) >> 23);
-  return e > 8 ? e - 8 : 0;
-}
-
 // Token t = blockIdx.x: the RMSNorm chain of the seam (double sum of
 // squares, r rounded once to fp32, two fp32 products) without the bf16 step,
-// then per 32 columns (4 lanes of 8) the code of the amax, the values scaled
-// by 2^(127 - code), clamped to +-448 and rounded to E4M3.
+// then per 32 columns (4 lanes of 8) vLLM's MXFP8 code of the amax (the
+// device page's mx_code: the smallest code whose range 448 * 2^(code - 127)
+// holds the amax, e8m0_code), the values scaled by 2^(127 - code), clamped to
+// +-448 as clamp_fp8 does, and rounded to E4M3.
 template <int CPT>
 __global__ __launch_bounds__(kThreads) void attn_x8_kernel(int H, const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w, float eps,
@@ -134,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void attn_x8_kernel(int H, const uint16_t
 #pragma unroll
     for (int z = 0; z < 8; ++z) amax = fmaxf(amax, fabsf(y[z]));
     amax = group_max(amax, 4);
-    const int code = vllm_mx_code(amax);
+    const int code = e8m0_code(amax);
     const float mul = mx_mul(code);
     float v[8];
 #pragma unroll

@@ -557,17 +557,16 @@ void orc_hc_fold(int32_t m, int32_t h, const uint16_t* part, const uint16_t* res
 }
 
 int32_t orc_vllm_mx_code(double amax) {
-  /* [layer] store_x8 quantises with vLLM's MXFP8 code (vllm_mx_code, not
-   * printed), then clamps the scaled values to the E4M3 range (clamp_fp8).
-   * The reading taken: the OCP MX rule, code = floor(log2(amax)) - 8 + 127
-   * (8: the exponent of E4M3's largest power of two), clamped to [0, 254]
-   * (0 for amax = 0); the clamp is what keeps the scaled values, which can
-   * reach 2^9, inside +-448. */
-  if (!(amax > 0.0)) return 0;
-  int e;
-  (void)frexp(amax, &e); /* amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
-  int32_t c = (e - 1) - 8 + 127;
-  return c < 0 ? 0 : (c > 254 ? 254 : c);
+  /* [layer] store_x8 quantises with vLLM's MXFP8 code of the group's amax;
+   * [device] mx_code is that code, named there as vLLM's ROCm MXFP8 scale
+   * code: clamp(ceil(log2(amax / 448)) + 127, 0, 254), amax floored at
+   * FLT_MIN.  Read as the smallest integer c in [0, 254] with
+   * amax <= 448 * 2^(c - 127) (exact power-of-two scalings in double); the
+   * floor at FLT_MIN only keeps the logarithm finite and yields 0 for every
+   * amax below 448 * 2^-127, the all-zero group included. */
+  for (int32_t c = 0; c < 254; ++c)
+    if (amax <= ldexp(448.0, c - 127)) return c;
+  return 254;
 }
 
 void orc_attn_x8(int32_t m, int32_t h, const uint16_t* x, const uint16_t* w, float eps,
@@ -575,7 +574,8 @@ void orc_attn_x8(int32_t m, int32_t h, const uint16_t* x, const uint16_t* w, flo
   /* [layer] store_x8: the attention seam's norm output (the RMSNorm chain of
    * orc_rmsnorm up to its fp32 product, not rounded to bf16) -> per 32
    * columns vllm_mx_code of the amax, the values scaled by 2^(127 - code),
-   * clamped to +-448 and rounded to E4M3. */
+   * clamped to +-448 (clamp_fp8; the code's bracket keeps every finite scaled
+   * value inside it) and rounded to E4M3. */
   float* y = (float*)malloc(sizeof(float) * (size_t)h);
   if (!y) return;
   for (int32_t t = 0; t < m; ++t) {

@@ -147,8 +147,9 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
 void orc_hc_fold(int32_t m, int32_t h, const uint16_t* part, const uint16_t* residual,
                  const float* post, const float* res, const float* pre,
                  uint16_t* residual_out, uint16_t* x);
-/* The attention seam's MXFP8 scale code of a 32-group's amax (vLLM's rule as
- * read here: floor(log2(amax)) - 8 + 127, clamped to [0, 254]). */
+/* The attention seam's MXFP8 scale code of a 32-group's amax: vLLM's ROCm
+ * MXFP8 code, clamp(ceil(log2(amax / 448)) + 127, 0, 254) with amax floored
+ * at FLT_MIN (the same rule as orc_mx_code). */
 int32_t orc_vllm_mx_code(double amax);
 /* The attention seam's norm + MXFP8 (store_x8): x bf16 [m, H], w bf16 [H]
  * -> x8 [m, H] E4M3, x8s [m, H/32]. */

@@ -3,7 +3,7 @@ residual fold and the attention seam's MXFP8 (page "vllm.models.deepseek_v41.
 amd.mono.layer", sections run_ffn and store_x8; page "vllm.models.deepseek_v41.
 amd.mono.runner", section DSV41MonoLayer.ffn for the shapes).  Each check
 compares the oracle with something other than itself: a hand table of the
-scale code, the relation between the two scale rules, exact cases where the
+scale code, its equality with the MoE's code, exact cases where the
 norm output is known in closed form (decoded through torch's float8_e4m3fn),
 and mixes whose results are exact (identity, permutations, powers of two).
 """
@@ -38,22 +38,28 @@ def test_vllm_mx_code_hand_table():
             line = line.split("#", 1)[0].strip()
             if line:
                 expr, code = line.rsplit(None, 1)
-                rows.append((eval(expr), int(code)))
+                rows.append((eval(expr, {"math": math}), int(code)))
     assert len(rows) >= 15
     for amax, code in rows:
         assert oracle.vllm_mx_code(amax) == code, (amax, code)
 
 
-def test_vllm_code_is_the_mx_code_less_one_exactly_above_1_75():
-    # for a normal amax = f 2^e (f in [1, 2)): the floor rule gives e - 8 + 127
-    # and the MoE's ceil rule the same, plus one when f > 1.75 (448 = 1.75 2^8)
+def test_vllm_code_equals_the_mx_code_and_brackets_amax():
+    # the device page names mx_code as vLLM's ROCm MXFP8 scale code, so the
+    # attention seam's code is the MoE's; either way the code is the smallest
+    # c with amax <= 448 * 2^(c - 127): 448 * 2^(c - 128) < amax for c > 0
     rng = np.random.default_rng(4)
-    for amax in np.exp2(rng.uniform(-100, 100, 4000)):
-        f = amax / 2.0 ** math.floor(math.log2(amax))
-        v, c = oracle.vllm_mx_code(float(amax)), oracle.mx_code(float(amax))
-        assert c == v + (1 if f > 1.75 else 0), amax
-        if 0 < v < 254:
-            assert 2.0 ** (v - 119) <= amax < 2.0 ** (v - 118)
+    amaxes = list(np.exp2(rng.uniform(-140, 128, 4000)))
+    amaxes += [1.75 * 2.0 ** j * f for j in range(-130, 120, 7)
+               for f in (1.0, 1.0 + 2.0 ** -30, 1.0 - 2.0 ** -30)]
+    for amax in amaxes:
+        amax = float(amax)
+        v = oracle.vllm_mx_code(amax)
+        assert v == oracle.mx_code(amax), amax
+        if v < 254:
+            assert amax <= math.ldexp(448.0, v - 127), amax
+        if v > 0:
+            assert amax > math.ldexp(448.0, v - 128), amax
 
 
 # ------------------------------------------------- attention seam MXFP8 ----
@@ -63,20 +69,20 @@ def _e4m3_values(q) -> np.ndarray:
     return t.to(torch.float64).numpy()
 
 
-def test_attn_x8_exact_norm_and_clamp():
+def test_attn_x8_exact_norm_and_codes():
     # x = 1 everywhere and eps = 0: r = 1 exactly, so the norm output is the
     # weight row itself, chosen exactly representable
     H = 128
     w = np.ones(H, np.float32)
-    w[0:32] = [500.0, -3.0, 1.0] + [0.25] * 29        # amax 500: code 127, 500 -> 448
+    w[0:32] = [500.0, -3.0, 1.0] + [0.25] * 29        # amax 500: code 128, scale 2^-1
     w[32:64] = [2.0, -1.5, 0.0] + [0.5] * 29          # amax 2: code 120, scale 2^7
     w[64:96] = 0.0                                    # zero group: code 0, zero bytes
     w[96:128] = [-448.0] + [7.0] * 31                 # amax 448: code 127, exact
     x8, x8s = oracle.attn_x8(_bf16(np.ones((1, H), np.float32)), _bf16(w), 0.0)
-    assert list(x8s[0]) == [127, 120, 0, 127]
+    assert list(x8s[0]) == [128, 120, 0, 127]
     got = _e4m3_values(x8[0])
     want = np.concatenate([
-        [448.0, -3.0, 1.0] + [0.25] * 29,
+        [256.0, -1.5, 0.5] + [0.125] * 29,            # 250 rounds to 256 (240 | 256)
         np.array([2.0, -1.5, 0.0] + [0.5] * 29) * 128.0,
         np.zeros(32),
         [-448.0] + [7.0] * 31,
@@ -90,7 +96,7 @@ def test_attn_x8_codes_values_and_error_bound():
     w = synth.to_bf16_bits(synth.normal(3, 2, (H,), 1.0, 0.1))
     x8, x8s = oracle.attn_x8(x, w, 1e-6)
     # the FFN seam's norm of the same rows is the attention norm rounded to
-    # bf16; the attention codes follow the floor rule on the groups' amax
+    # bf16; the attention codes follow mx_code's rule on the groups' amax
     y = _val(oracle.rmsnorm(x, w, 1e-6))
     for t in range(m):
         for g in range(H // 32):
@@ -100,11 +106,12 @@ def test_attn_x8_codes_values_and_error_bound():
             # rounding to bf16 moves amax by at most 2^-8 relative
             assert oracle.vllm_mx_code(amax_bf * (1 - 2 ** -8)) <= c <= oracle.vllm_mx_code(amax_bf * (1 + 2 ** -8))
             dq = _e4m3_values(x8[t, 32 * g:32 * g + 32]) * 2.0 ** (c - 127)
-            # within E4M3's half-ulp (2^-4 relative) of the value, or the clamp
-            # (at most 512/448 - 1 relative for the top of the range), plus
-            # the bf16 rounding of the comparison row
+            # within E4M3's half-ulp (2^-4 relative) of the value or half its
+            # smallest step, plus the bf16 rounding of the comparison row;
+            # the code keeps every scaled value within +-448, so the clamp
+            # never bites
             err = np.abs(dq - grp)
-            assert np.all(err <= np.abs(grp) * (2 ** -4 + 2 ** -8) + 2.0 ** (c - 127 - 9) + 0.15 * amax_bf)
+            assert np.all(err <= np.abs(grp) * (2 ** -4 + 2 ** -8) + 2.0 ** (c - 127 - 10))
 
 
 # ------------------------------------------------ hyper-connection fold ----
