@@ -72,7 +72,7 @@ extern "C" {
  * build_mono_ffn; [device] atomic_add_dev).  Both give the same output bits.
  * FUSED assumes that all its blocks can be resident at once (no concurrent
  * work holds CUs for its whole duration); a wait that runs past 100 ms flags
- * the run (MOE_DECODE_TAP_STATUS) and goes on.  On MI355X it is the slower
+ * the run (moe_decode_status) and goes on.  On MI355X it is the slower
  * of the two: a hand-off between CUs through device memory waits behind the
  * weight stream's queued reads, which costs more than a launch boundary. */
 #define MOE_DECODE_SCHEDULE_LAUNCHES 0
@@ -150,8 +150,8 @@ size_t moe_decode_scratch_bytes(moe_decode_handle plan);
  * and the other blocks wait for the picks once the shared expert's units
  * are done.  The launch has one block per CU, so with all its blocks
  * resident every wait ends.  A wait that runs past 100 ms (another workload
- * holding CUs for that long) flags the run in MOE_DECODE_TAP_STATUS and goes
- * on.  The act launch clears the hand-off words for the next run; after a
+ * holding CUs for that long) sets a bit of the status word
+ * (moe_decode_status) and goes on.  The act launch clears the hand-off words for the next run; after a
  * run that returned an error between the w13 and act launches, the next run
  * launches the seam to clear them. */
 int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
@@ -177,11 +177,7 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
  *   ROW_TOK   i32  [R]          token of each row
  *   A8        u8   [R, Imax]    E4M3 SiLU*up intermediate (Imax = max(I, Is))
  *   A8S       u8   [R, Imax/32] its E8M0 codes
- *   STATUS    u32  [1]          0, or nonzero when a wait timed out and the
- *                               output is not valid: 1 the fused expert
- *                               launch's wait for a slot's a8, 2 the w13
- *                               launch's wait for the logits or the picks
- *                               (m <= 4) */
+ *   STATUS    u32  [1]          the status word (see moe_decode_status) */
 enum moe_decode_tap {
   MOE_DECODE_TAP_NORMED = 0,
   MOE_DECODE_TAP_X8 = 1,
@@ -198,6 +194,21 @@ enum moe_decode_tap {
 };
 int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
                        const void** d_ptr, size_t* bytes);
+
+/* The plan's status word: 0 while every run since the last clear was valid.
+ * A kernel that waits on other blocks of its launch (the hand-offs of the
+ * pages' persistent launch through device-scope words, [device]
+ * atomic_add_dev; [layer] run_ffn) gives up after 100 ms and sets a bit; the
+ * run's output is then not valid.  Bits: 1 a wait of the fused expert launch
+ * for a slot's a8; 2 a wait of the w13 launch that routes (m <= 4) for the
+ * logits or the picks.  The bits are sticky: no kernel clears them, so a
+ * check after many runs (a graph replayed many times) covers all of them.
+ * moe_decode_status synchronises `stream`, copies the word to *h_status and,
+ * when `clear` is nonzero, zeroes it.  Not during stream capture
+ * (MOE_DECODE_ECAPTURE); EINVAL for a NULL plan or h_status; EHIP on a
+ * runtime error. */
+int moe_decode_status(moe_decode_handle plan, void* stream, uint32_t* h_status,
+                      int32_t clear);
 
 /* Per-kernel timing of runs: each kernel is launched with a start and a stop
  * HIP event that its dispatch itself records (hipExtLaunchKernelGGL), so an

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_inspect.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(_P),
                                          ctypes.POINTER(ctypes.c_size_t)]
         L.moe_decode_inspect.restype = ctypes.c_int
+        L.moe_decode_status.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]
+        L.moe_decode_status.restype = ctypes.c_int
         L.moe_decode_timing.argtypes = [_P, ctypes.c_int32]
         L.moe_decode_timing.restype = ctypes.c_int
         L.moe_decode_timing_read.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
@@ -106,7 +108,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
-           "moe_decode_inspect", "moe_decode_timing", "moe_decode_timing_read",
+           "moe_decode_inspect", "moe_decode_status", "moe_decode_timing", "moe_decode_timing_read",
            "moe_decode_timeline", "moe_decode_timeline_read",
            "moe_decode_destroy", "moe_decode_quantize_weight",
            "moe_decode_quantize_weight_fp4", "moe_decode_hc_fold", "moe_decode_attn_x8",
@@ -211,6 +213,16 @@ def inspect(handle: int, tap: str):
     _check(lib().moe_decode_inspect(handle, TAPS[tap], ctypes.byref(p), ctypes.byref(n)),
            "moe_decode_inspect", handle)
     return p.value, n.value
+
+
+def status(handle: int, clear: bool = True, stream=None) -> int:
+    """moe_decode_status: the plan's sticky status word (0: every run since
+    the last clear was valid); synchronises the stream, and by default
+    clears the word."""
+    v = ctypes.c_uint32()
+    _check(lib().moe_decode_status(handle, _stream_ptr(stream), ctypes.byref(v), 1 if clear else 0),
+           "moe_decode_status", handle)
+    return v.value
 
 
 def inspect_tensor(handle: int, tap: str, dtype=torch.uint8) -> torch.Tensor:

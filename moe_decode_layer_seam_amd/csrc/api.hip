@@ -191,14 +191,15 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   const size_t o_rowout = take(R * 4);
   const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
   const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
-  // counters of the fused launch: status (padded to its own 256 bytes), the
-  // slots' ready words, the act groups' unit counts
+  // counters of the fused launch (from word 64): the slots' ready words,
+  // the act groups' unit counts
   const int act_stride = d.Imax / kActCols;
   // ... and the boxes of the w13 launch that routes: the pick box, then
   // (from an even word) the logit box
   const size_t o_lbox = (64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPickBox + 1) & ~(size_t)1;
   const size_t nsync = o_lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   const size_t o_sync = take(nsync * 4);
+  const size_t o_status = take(4);
   const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
   // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
   // the step sizes that run in split mode
@@ -247,7 +248,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   s.part13 = reinterpret_cast<float*>(b + o_part13);
   s.part2 = reinterpret_cast<float*>(b + o_part2);
   s.sync = reinterpret_cast<uint32_t*>(b + o_sync);
-  s.status = s.sync;
+  s.status = reinterpret_cast<uint32_t*>(b + o_status);
   s.ready = s.sync + 64;
   s.act_cnt = s.ready + p->max_vs;
   s.pick_box = s.act_cnt + (size_t)p->max_vs * act_stride;
@@ -365,6 +366,28 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
   if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(6))) != hipSuccess)
     return hip_fail(p, e, "combine launch");
   p->last_m = m;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_status(moe_decode_handle p, void* stream, uint32_t* h_status, int32_t clear) {
+  if (!p || !h_status) return MOE_DECODE_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(st, &cap);
+  if (e != hipSuccess) return hip_fail(p, e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) {
+    p->err = "moe_decode_status called during stream capture";
+    return MOE_DECODE_ECAPTURE;
+  }
+  uint32_t v = 0;
+  if ((e = hipMemcpyAsync(&v, p->s.status, 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+      (e = hipStreamSynchronize(st)) != hipSuccess)
+    return hip_fail(p, e, "status read");
+  if (clear && v != 0u) {
+    if ((e = hipMemsetAsync(p->s.status, 0, 4, st)) != hipSuccess || (e = hipStreamSynchronize(st)) != hipSuccess)
+      return hip_fail(p, e, "status clear");
+  }
+  *h_status = v;
   return MOE_DECODE_OK;
 }
 

@@ -396,6 +396,12 @@ __device__ __forceinline__ uint32_t count_arrival(uint32_t* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Sets status bits of the run (bits are only ever added: the word is
+// cleared by the host, moe_decode_status, never by a kernel).
+__device__ __forceinline__ void flag_status(uint32_t* p, uint32_t bits) {
+  (void)__hip_atomic_fetch_or(p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait until every memory operation this wave issued has completed (vector
 // and scalar): stores with the coherent policy are then visible to every CU.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }

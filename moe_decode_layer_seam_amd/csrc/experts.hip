@@ -415,7 +415,7 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
         break;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
-        if (lane == 0) store_coherent(s.status, 2u);
+        if (lane == 0) flag_status(s.status, kStatusRouteWait);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -432,7 +432,7 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
     while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
       __builtin_amdgcn_s_sleep(1);
       if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * kPlanWaitTicks) {
-        if (lane == 0) store_coherent(s.status, 2u);
+        if (lane == 0) flag_status(s.status, kStatusRouteWait);
         break;
       }
     }
@@ -583,9 +583,6 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   const uint32_t xso = x8o + (uint32_t)(m * d.H);
   if constexpr (ROUTE) {
     static_assert(NW * 64 == kSeamThreads, "the seam's thread mapping takes the whole block");
-    // no seam launch ran: block 0 clears the status word (a wait gives up
-    // only after 100 ms)
-    if (blockIdx.x == 0 && tid == 0) store_coherent(s.status, 0u);
     seam_rows(d, m, in, s, x8o, xso);
     stamp(tl, kTlPoints, 2);
     // blocks [0, m) route the m tokens from the logit box and store their
@@ -880,7 +877,7 @@ __device__ __forceinline__ void wait_ready(const Scratch& s, int v, uint32_t wan
     const uint32_t now = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(&s.ready[v]));
     if (now >= want) return;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-      if (lane == 0) store_coherent(s.status, 1u);
+      if (lane == 0) flag_status(s.status, kStatusA8Wait);
       return;
     }
   }

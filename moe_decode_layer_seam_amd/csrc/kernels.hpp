@@ -46,10 +46,12 @@ struct Scratch {
   float* part13;       // [planes][R][2 Imax] fp32 w13 sums (per K segment in split mode)
   float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
   // Counters of the fused expert launch, nsync words from `sync`, zeroed by
-  // the seam launch of every run: status (nonzero: a wait timed out), per
-  // virtual slot the act groups whose a8 is stored (ready), and per slot and
-  // 64-column act group the w13 units counted (act_cnt).
+  // the seam launch of every run: per virtual slot the act groups whose a8
+  // is stored (ready), and per slot and 64-column act group the w13 units
+  // counted (act_cnt).
   uint32_t* sync;
+  // The run's status word, in its own 256 bytes: bits set by a wait that
+  // timed out (kStatus*); sticky across runs until the host clears it.
   uint32_t* status;
   uint32_t* ready;     // [max_vs]
   uint32_t* act_cnt;   // [max_vs][act_stride]
@@ -67,6 +69,11 @@ struct Scratch {
   uint64_t* tl_combine;
   uint64_t* tl_experts;
 };
+
+// Status bits: a wait of the fused expert launch for a slot's a8; a wait of
+// the w13 launch that routes for the logits or the picks.
+constexpr uint32_t kStatusA8Wait = 1u;
+constexpr uint32_t kStatusRouteWait = 2u;
 
 constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, experts (fused)
 constexpr int kActCols = 64;     // columns of a per act group of the fused launch

@@ -423,7 +423,7 @@ __device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s
   uint64_t v;
   while ((v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0ull) {
     if (__builtin_amdgcn_s_memrealtime() - t0 > kLogitWaitTicks) {
-      store_coherent(s.status, 2u);
+      flag_status(s.status, kStatusRouteWait);
       return 0.0;
     }
     __builtin_amdgcn_s_sleep(1);

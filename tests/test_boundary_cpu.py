@@ -90,3 +90,40 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+# ---- the near-tie rule of the parity tests (host logic) ------------------
+
+def test_near_tie_rule_accepts_ties_and_rejects_real_differences():
+    import numpy as np
+    from tests import routing_check as rc
+
+    # scores chosen through the logits: b = sigmoid(l) + bias
+    E, k = 8, 3
+    bias = np.zeros(E)
+    logits = np.array([[3.0, 2.0, 1.0, 0.5, 0.0, -1.0, -2.0, -3.0]])
+    ref = np.array([[0, 1, 2]])
+    assert rc.check_picks(ref, ref, logits, bias) == []
+    # a real difference: expert 3 instead of 2 (b lower by ~0.09)
+    with pytest.raises(AssertionError):
+        rc.check_picks(np.array([[0, 1, 3]]), ref, logits, bias)
+    # the order of picks matters beyond the margin
+    with pytest.raises(AssertionError):
+        rc.check_picks(np.array([[1, 0, 2]]), ref, logits, bias)
+    # a boundary near-tie: experts 2 and 3 within 1e-9 of each other
+    bias2 = bias.copy()
+    s = 1.0 / (1.0 + np.exp(-logits[0]))
+    bias2[3] = s[2] - s[3] - 1e-9
+    assert rc.check_picks(np.array([[0, 1, 3]]), ref, logits, bias2) == [0]
+    # a near-tie between two picks: their order may swap
+    bias3 = bias.copy()
+    bias3[1] = s[0] - s[1] - 1e-10
+    assert rc.check_picks(np.array([[1, 0, 2]]), np.array([[0, 1, 2]]), logits, bias3) == [0]
+    # repeated or out-of-range picks never pass
+    with pytest.raises(AssertionError):
+        rc.check_picks(np.array([[0, 0, 1]]), ref, logits, bias2)
+    with pytest.raises(AssertionError):
+        rc.check_picks(np.array([[0, 1, 8]]), ref, logits, bias2)
+    # weights of given picks: renormalised sigmoid scores
+    w = rc.weights_of(np.array([[0, 1, 3]]), logits, 2.0)
+    assert np.allclose(w.sum(), 2.0) and np.allclose(w[0, 0] / w[0, 1], s[0] / s[1])

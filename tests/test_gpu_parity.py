@@ -14,6 +14,7 @@ import oracle
 import synth
 from tests import data
 from tests import gpu_util as gu
+from tests import routing_check
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +60,7 @@ def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
     """Compare every intermediate of the last run with the oracle."""
     m, H, E, K = cfg["m"], cfg["hidden"], cfg["experts"], cfg["topk"]
     dims = data.dims_of(cfg)
-    assert gu.tap(handle, "status", torch.int32)[0] == 0, "a wait of the fused launch timed out"
+    assert mdl.status(handle) == 0, "a wait inside a launch timed out"
     # norm, quant and router for every row (cheap on the CPU)
     y = oracle.rmsnorm(inp["x"], inp["norm_w"], cfg["rms_eps"])
     assert np.array_equal(gu.tap(handle, "normed", torch.int16).view(np.uint16).reshape(m, H), y)
@@ -73,10 +74,20 @@ def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
     logits = gu.tap(handle, "logits", torch.float64).reshape(m, E)
     assert np.allclose(logits, r["logits"], rtol=1e-12, atol=1e-12)
     ids = gu.tap(handle, "topk_ids", torch.int32).reshape(m, K)
-    assert np.array_equal(ids, r["ids"]), f"ids differ; oracle margins {r['margin']}"
+    # ids bit-exact, except near-ties at the top-k boundary (or between picks)
+    # that leave a valid top-k of the oracle's biased scores
+    ties = routing_check.check_picks(ids, r["ids"], r["logits"], inp["bias"])
+    if ties:
+        print(f"[{cfg['name']}] near-tie picks at tokens {ties}; oracle margins "
+              f"{r['margin'][ties]}", flush=True)
+    assert len(ties) <= max(1, m // 16), f"too many near-ties to be chance: {ties}"
     wts = gu.tap(handle, "topk_w", torch.float32).reshape(m, K)
-    assert np.allclose(wts, r["wts"], rtol=1e-6, atol=0)
-    counts, row = oracle.plan(r["ids"], E)
+    want_w = r["wts"].copy()
+    if ties:
+        want_w[ties] = routing_check.weights_of(ids[ties], r["logits"][ties], cfg["routed_scale"])
+    assert np.allclose(wts, want_w, rtol=1e-6, atol=0)
+    # the plan of the picks the run made
+    counts, row = oracle.plan(ids, E)
     assert np.array_equal(gu.tap(handle, "counts", torch.int32), counts)
     assert np.array_equal(gu.tap(handle, "pair_row", torch.int32).reshape(m, K), row)
     row_tok = gu.tap(handle, "row_tok", torch.int32)
@@ -84,12 +95,14 @@ def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
     want_tok[row.ravel()] = np.repeat(np.arange(m), K)
     want_tok[m * K:] = np.arange(m)
     assert np.array_equal(row_tok, want_tok)
-    # output rows (all, or a sample at full size)
+    # output rows (all, or a sample), less the near-tie tokens: their output
+    # follows other picks than the oracle's
     rows = list(range(m)) if rows_ref is None else list(rows_ref)
     if o is None:
         o = oracle.layer_parallel(dims, inp, w, rows, workers=data.WORKERS)
-    got = gu.out_f64(out)[rows]
-    gu.assert_out_close(got, o["out_f64"], what=cfg["name"])
+    keep = [i for i, t in enumerate(rows) if t not in ties]
+    got = gu.out_f64(out)[rows][keep]
+    gu.assert_out_close(got, o["out_f64"][keep], what=cfg["name"])
     return r, o
 
 
@@ -246,7 +259,7 @@ def test_runs_are_deterministic_and_plan_reusable_across_m(schedule):
         assert torch.equal(e3.view(torch.int16), a[:3].view(torch.int16))
         assert torch.equal(e3b.view(torch.int16), a[:3].view(torch.int16))
         assert torch.equal(e1.view(torch.int16), a[:1].view(torch.int16))
-        assert gu.tap(h, "status", torch.int32)[0] == 0
+        assert mdl.status(h) == 0
     finally:
         mdl.destroy(h)
 
@@ -265,7 +278,7 @@ def test_whole_and_split_units_give_the_same_bits():
         full = gu.run(h, cfg, dinp, dw).clone()
         parts = {n: gu.run(h, cfg, dinp, dw, x=dinp["x"][:n].contiguous()).clone() for n in (8, 5, 1)}
         torch.cuda.synchronize()
-        assert gu.tap(h, "status", torch.int32)[0] == 0
+        assert mdl.status(h) == 0
         for n, o in parts.items():
             assert torch.equal(o.view(torch.int16), full[:n].view(torch.int16)), f"{n} rows"
     finally:
@@ -302,7 +315,7 @@ def test_graph_capture_replays_match_eager(schedule, m):
                 g.replay()
                 torch.cuda.synchronize()
                 assert torch.equal(out.view(torch.int16), eager[i].view(torch.int16)), (rep, i)
-        assert gu.tap(h, "status", torch.int32)[0] == 0
+        assert mdl.status(h) == 0
         del g
     finally:
         mdl.destroy(h)
@@ -365,7 +378,7 @@ def test_fused_launch_matches_separate_launches_bit_for_bit(cfg):
         try:
             outs = [gu.run(h, cfg, dinp, dw).clone() for _ in range(2)]
             torch.cuda.synchronize()
-            assert gu.tap(h, "status", torch.int32)[0] == 0
+            assert mdl.status(h) == 0
             got[schedule] = (outs, gu.tap(h, "a8"), gu.tap(h, "a8s"))
         finally:
             mdl.destroy(h)
@@ -462,18 +475,37 @@ def test_plan_refuses_during_capture():
 _FULL = {}
 
 
-def _full_layer(idx):
-    """Configs 1-3 share one weight set (the picks of config 3's 48 rows cover
-    configs 1 and 2, whose rows are its first rows); config 4 has its own."""
-    key = "dsv41" if idx in (1, 2, 3) else "draft"
-    if key not in _FULL:
-        base = synth.WORKLOADS[3] if key == "dsv41" else synth.WORKLOADS[4]
-        inp, w = data.build_layer(0, base, experts="picked")
-        _FULL[key] = (base, inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
-    return _FULL[key]
+def _full_layer(key, seed=0):
+    """The full-size layers' seeded inputs for 48 rows and the weights of the
+    experts the oracle picks for them (configs 1 and 2 use the first 1 and 16
+    of those rows: their picks are among the 48 rows' picks).  One weight set
+    is held at a time (8 GB of host memory at H = 5120, E = 256)."""
+    want = (key, seed)
+    if want not in _FULL:
+        _FULL.clear()
+        base = {"dsv41": synth.WORKLOADS[3], "draft": synth.WORKLOADS[4],
+                "dsv41_fp4": dict(synth.WORKLOADS[3], routed="mxfp4")}[key]
+        inp, w = data.build_layer(seed, base, experts="picked")
+        _FULL[want] = (inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
+    return _FULL[want]
 
 
-SAMPLES = {1: [0], 2: [0, 9, 15], 3: [0, 29, 47], 4: [0, 23, 47]}
+def _run_full(cfg, key, seed=0, rows_ref=None):
+    """One step at full size planned exactly as bench.py plans it (max_tokens
+    = m), every output row (or rows_ref) checked against the oracle."""
+    inp_all, w, dinp_all, dw = _full_layer(key, seed)
+    m = cfg["m"]
+    inp = dict(inp_all, x=inp_all["x"][:m])
+    dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
+    h = _plan_for(cfg, max_tokens=m)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        print(f"[{cfg['name']} seed {seed}] ran; checking "
+              f"{'every row' if rows_ref is None else rows_ref}", flush=True)
+        _check_layer(cfg, h, inp, w, out, rows_ref=rows_ref)
+    finally:
+        mdl.destroy(h)
 
 
 @pytest.mark.parametrize("idx", [5, 6])
@@ -483,7 +515,7 @@ def test_parity_tensor_parallel_share(idx):
     cfg = synth.WORKLOADS[idx]
     inp, w = data.build_layer(0, cfg, experts="picked")
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
-    h = _plan_for(cfg, max_tokens=48)
+    h = _plan_for(cfg, max_tokens=cfg["m"])
     try:
         out = gu.run(h, cfg, dinp, dw)
         torch.cuda.synchronize()
@@ -493,41 +525,40 @@ def test_parity_tensor_parallel_share(idx):
         mdl.destroy(h)
 
 
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_parity_full_size(idx):
+    _run_full(synth.WORKLOADS[idx], "dsv41")
+
+
+def test_parity_full_size_m1_on_a_48_row_plan():
+    """The M = 1 step on a plan made for 48 rows (a serving plan reused for
+    every decode width): a sample row, as the plan changes only the layout."""
+    cfg = synth.WORKLOADS[1]
+    inp_all, w, dinp_all, dw = _full_layer("dsv41")
+    inp = dict(inp_all, x=inp_all["x"][:1])
+    dinp = dict(dinp_all, x=dinp_all["x"][:1].contiguous())
+    h = _plan_for(cfg, max_tokens=48)
+    try:
+        out = gu.run(h, cfg, dinp, dw)
+        torch.cuda.synchronize()
+        _check_layer(cfg, h, inp, w, out)
+    finally:
+        mdl.destroy(h)
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_parity_full_size_more_seeds(idx, seed):
+    _run_full(synth.WORKLOADS[idx], "dsv41", seed=seed)
+
+
+def test_parity_full_size_draft():
+    _run_full(synth.WORKLOADS[4], "draft")
+
+
 @pytest.mark.parametrize("idx", [1, 3])
 def test_parity_full_size_mxfp4(idx):
-    cfg = dict(synth.WORKLOADS[idx], routed="mxfp4")
-    base = dict(synth.WORKLOADS[3], routed="mxfp4")
-    key = "dsv41_fp4"
-    if key not in _FULL:
-        inp, w = data.build_layer(0, base, experts="picked")
-        _FULL[key] = (base, inp, w, gu.inputs_dev(inp), gu.weights_dev(w))
-    _, inp_all, w, dinp_all, dw = _FULL[key]
-    m = cfg["m"]
-    inp = dict(inp_all, x=inp_all["x"][:m])
-    dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
-    h = _plan_for(cfg, max_tokens=48)
-    try:
-        out = gu.run(h, cfg, dinp, dw)
-        torch.cuda.synchronize()
-        _check_layer(cfg, h, inp, w, out, rows_ref=SAMPLES[idx])
-    finally:
-        mdl.destroy(h)
+    cfg = dict(synth.WORKLOADS[idx], routed="mxfp4", name=synth.WORKLOADS[idx]["name"] + "_fp4")
+    _run_full(cfg, "dsv41_fp4")
     if idx == 3:
-        _FULL.pop(key, None)
-
-
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
-def test_parity_full_size(idx):
-    cfg = synth.WORKLOADS[idx]
-    base, inp_all, w, dinp_all, dw = _full_layer(idx)
-    m = cfg["m"]
-    inp = dict(inp_all, x=inp_all["x"][:m])
-    dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
-    h = _plan_for(cfg, max_tokens=48)
-    try:
-        out = gu.run(h, cfg, dinp, dw)
-        torch.cuda.synchronize()
-        print(f"[{cfg['name']}] ran; checking rows {SAMPLES[idx]}", flush=True)
-        _check_layer(cfg, h, inp, w, out, rows_ref=SAMPLES[idx])
-    finally:
-        mdl.destroy(h)
+        _FULL.clear()
