@@ -75,6 +75,9 @@ def lib():
         L.orc_fp4_code_index.argtypes = [_I, _I, _I]
         L.orc_fp4_code_index.restype = ctypes.c_size_t
         L.orc_expert_fmt.argtypes = [_I, _I, _I] + [_P] * 9
+        L.orc_expert_up.argtypes = [_I, _I, _I] + [_P] * 9
+        L.orc_expert_down.argtypes = [_I, _I, _I] + [_P] * 5
+        L.orc_combine.argtypes = [_I, _I] + [_P] * 5
         L.orc_rmsnorm.argtypes = [_I, _I, _P, _P, ctypes.c_float, _P]
         L.orc_hc_fold.argtypes = [_I, _I] + [_P] * 7
         L.orc_vllm_mx_code.argtypes = [ctypes.c_double]
@@ -88,6 +91,7 @@ def lib():
         L.orc_layer.restype = _I
         for f in ("orc_mx_quant_row", "orc_quant_weight", "orc_quant_weight_fp4",
                   "orc_rmsnorm", "orc_router", "orc_plan", "orc_expert", "orc_expert_fmt",
+                  "orc_expert_up", "orc_expert_down", "orc_combine",
                   "orc_hc_fold", "orc_attn_x8"):
             getattr(L, f).restype = None
         _lib = L
@@ -300,6 +304,51 @@ def expert(x8, x8s, w13, w13_s, w2, w2_s, fmt: str = "e4m3") -> dict:
     lib().orc_expert_fmt(h, inter, FORMATS[fmt], _p(x8), _p(x8s), _p(w13), _p(w13_s),
                          _p(w2), _p(w2_s), _p(y), _p(a8), _p(a8s))
     return {"y": y, "a8": a8, "a8s": a8s}
+
+
+def expert_up(x8, x8s, w13, w13_s, fmt: str = "e4m3") -> dict:
+    """The up half of one expert for one token: h [2I] (double), habs [2I]
+    (sums of |x_k w_nk|), a [I] (fp32 SiLU(g) u, as double), a8 [I], a8s
+    [I/32]."""
+    x8 = _c(x8, np.uint8).ravel()
+    x8s = _c(x8s, np.uint8).ravel()
+    w13 = _c(w13, np.uint8)
+    w13_s = _c(w13_s, np.uint8)
+    h = x8.size
+    inter = w13.shape[0] // 2
+    hv = np.empty(2 * inter, np.float64)
+    habs = np.empty(2 * inter, np.float64)
+    av = np.empty(inter, np.float64)
+    a8 = np.empty(inter, np.uint8)
+    a8s = np.empty(inter // 32, np.uint8)
+    lib().orc_expert_up(h, inter, FORMATS[fmt], _p(x8), _p(x8s), _p(w13), _p(w13_s),
+                        _p(hv), _p(habs), _p(av), _p(a8), _p(a8s))
+    return {"h": hv, "habs": habs, "a": av, "a8": a8, "a8s": a8s}
+
+
+def expert_down(a8, a8s, w2, w2_s, fmt: str = "e4m3") -> np.ndarray:
+    """The down half: y [H] = a8 . W2^T in double."""
+    a8 = _c(a8, np.uint8).ravel()
+    a8s = _c(a8s, np.uint8).ravel()
+    w2 = _c(w2, np.uint8)
+    w2_s = _c(w2_s, np.uint8)
+    inter = a8.size
+    h = w2.shape[0]
+    y = np.empty(h, np.float64)
+    lib().orc_expert_down(h, inter, FORMATS[fmt], _p(a8), _p(a8s), _p(w2), _p(w2_s), _p(y))
+    return y
+
+
+def combine(wts, y_routed, y_shared) -> np.ndarray:
+    """One token's output sum in double: wts [k], y_routed [k, H], y_shared
+    [H] -> out_f64 [H]."""
+    wts = _c(wts, np.float64).ravel()
+    y_routed = _c(y_routed, np.float64)
+    y_shared = _c(y_shared, np.float64).ravel()
+    k, h = y_routed.shape
+    out = np.empty(h, np.float64)
+    lib().orc_combine(k, h, _p(wts), _p(y_routed), _p(y_shared), _p(out), None)
+    return out
 
 
 def layer(dims: dict, inp: dict, w: dict, rows=None) -> dict:

@@ -392,41 +392,60 @@ void orc_plan(int32_t m, int32_t e, int32_t k, const int32_t* ids,
 /* Experts and the combine                                                  */
 /* ------------------------------------------------------------------------ */
 
-void orc_expert_fmt(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
-                    const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
-                    const uint8_t* w2, const uint8_t* w2_s, double* y,
-                    uint8_t* a8, uint8_t* a8s) {
-  /* w13 [2I, H]: rows [0, I) the gate, rows [I, 2I) the up projection;
-   * w2 [H, I]; both in the weight format fmt (see weight_value). */
-  int32_t ib = inter / 32;
+void orc_expert_up(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
+                   const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                   double* hv, double* habs, double* av, uint8_t* a8, uint8_t* a8s) {
+  /* w13 [2I, H]: rows [0, I) the gate, rows [I, 2I) the up projection, in
+   * the weight format fmt (see weight_value).  h = x . W13^T with both
+   * operands dequantised; habs (if given) = sum over the contraction of
+   * |x_k w_nk|, the magnitude the sum is taken over. */
   double* xd = (double*)malloc(sizeof(double) * (size_t)h);
-  double* hv = (double*)malloc(sizeof(double) * 2 * (size_t)inter);
-  double* av = (double*)malloc(sizeof(double) * (size_t)inter);
-  uint8_t* q = (uint8_t*)malloc((size_t)inter);
-  uint8_t* qc = (uint8_t*)malloc((size_t)ib);
-  /* h = x . W13^T, both operands dequantised. */
   for (int32_t i = 0; i < h; ++i) xd[i] = mx_value(x8[i], x8s[i / 32]);
   for (int32_t n = 0; n < 2 * inter; ++n) {
-    double acc = 0.0;
-    for (int32_t i = 0; i < h; ++i) acc += xd[i] * weight_value(fmt, w13, w13_s, h, n, i);
+    double acc = 0.0, mag = 0.0;
+    for (int32_t i = 0; i < h; ++i) {
+      double p = xd[i] * weight_value(fmt, w13, w13_s, h, n, i);
+      acc += p;
+      mag += fabs(p);
+    }
     hv[n] = acc;
+    if (habs) habs[n] = mag;
   }
   /* a = SiLU(gate) * up, held as fp32, then MXFP8 along the intermediate. */
   for (int32_t i = 0; i < inter; ++i) {
     double g = hv[i], u = hv[inter + i];
     av[i] = (double)round_f32(g * sigmoid(g) * u);
   }
-  orc_mx_quant_row(inter, av, q, qc);
-  /* y = a . W2^T. */
+  orc_mx_quant_row(inter, av, a8, a8s);
+  free(xd);
+}
+
+void orc_expert_down(int32_t h, int32_t inter, int32_t fmt, const uint8_t* a8,
+                     const uint8_t* a8s, const uint8_t* w2, const uint8_t* w2_s,
+                     double* y) {
+  /* y = a . W2^T with a the dequantised MXFP8 intermediate; w2 [H, I]. */
   for (int32_t n = 0; n < h; ++n) {
     double acc = 0.0;
     for (int32_t i = 0; i < inter; ++i)
-      acc += mx_value(q[i], qc[i / 32]) * weight_value(fmt, w2, w2_s, inter, n, i);
+      acc += mx_value(a8[i], a8s[i / 32]) * weight_value(fmt, w2, w2_s, inter, n, i);
     y[n] = acc;
   }
+}
+
+void orc_expert_fmt(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
+                    const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                    const uint8_t* w2, const uint8_t* w2_s, double* y,
+                    uint8_t* a8, uint8_t* a8s) {
+  /* One token through one expert: the up projection with SiLU * up and
+   * its MXFP8, then the down projection. */
+  double* hv = (double*)malloc(sizeof(double) * 2 * (size_t)inter);
+  double* av = (double*)malloc(sizeof(double) * (size_t)inter);
+  uint8_t* q = (uint8_t*)malloc((size_t)inter);
+  uint8_t* qc = (uint8_t*)malloc((size_t)inter / 32);
+  orc_expert_up(h, inter, fmt, x8, x8s, w13, w13_s, hv, NULL, av, q, qc);
+  orc_expert_down(h, inter, fmt, q, qc, w2, w2_s, y);
   if (a8) memcpy(a8, q, (size_t)inter);
-  if (a8s) memcpy(a8s, qc, (size_t)ib);
-  free(xd);
+  if (a8s) memcpy(a8s, qc, (size_t)inter / 32);
   free(hv);
   free(av);
   free(q);
@@ -438,6 +457,20 @@ void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
                 const uint8_t* w2, const uint8_t* w2_s, double* y, uint8_t* a8,
                 uint8_t* a8s) {
   orc_expert_fmt(h, inter, ORC_FMT_E4M3, x8, x8s, w13, w13_s, w2, w2_s, y, a8, a8s);
+}
+
+void orc_combine(int32_t k, int32_t h, const double* wts, const double* y_routed,
+                 const double* y_shared, double* out_f64, uint16_t* out) {
+  /* One token's output: the picked experts' outputs weighted in selection
+   * order, then the shared expert's, summed in double; one rounding to bf16
+   * ([layer] run_ffn: the MoE's output row). */
+  for (int32_t n = 0; n < h; ++n) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < k; ++j) acc += wts[j] * y_routed[(size_t)j * h + n];
+    acc += y_shared[n];
+    if (out_f64) out_f64[n] = acc;
+    if (out) out[n] = orc_bf16_rne(acc);
+  }
 }
 
 int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
@@ -461,9 +494,9 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   double* yv = (double*)malloc(sizeof(double) * (size_t)H);
   int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)m * K);
   double* w = (double*)malloc(sizeof(double) * (size_t)m * K);
-  double* ye = (double*)malloc(sizeof(double) * (size_t)H);
-  double* acc = (double*)malloc(sizeof(double) * (size_t)H);
-  if (!y || !q || !qc || !yv || !sel || !w || !ye || !acc) return -1;
+  double* ye = (double*)malloc(sizeof(double) * (size_t)K * H);
+  double* ysh = (double*)malloc(sizeof(double) * (size_t)H);
+  if (!y || !q || !qc || !yv || !sel || !w || !ye || !ysh) return -1;
 
   /* 1. norm -> bf16 rows; 2. MXFP8 of each bf16 row. */
   orc_rmsnorm(m, H, x, norm_w, d->rms_eps, y);
@@ -486,19 +519,14 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   for (int32_t t = 0; t < m; ++t) {
     const uint8_t* xq = q + (size_t)t * H;
     const uint8_t* xc = qc + (size_t)t * (H / 32);
-    for (int32_t n = 0; n < H; ++n) acc[n] = 0.0;
     for (int32_t j = 0; j < K; ++j) {
       size_t ex = (size_t)sel[(size_t)t * K + j];
       orc_expert_fmt(H, I, fmt, xq, xc, w13 + ex * w13_e, w13_s + ex * w13s_e,
-                     w2 + ex * w2_e, w2_s + ex * w2s_e, ye, NULL, NULL);
-      for (int32_t n = 0; n < H; ++n) acc[n] += w[(size_t)t * K + j] * ye[n];
+                     w2 + ex * w2_e, w2_s + ex * w2s_e, ye + (size_t)j * H, NULL, NULL);
     }
-    orc_expert(H, Is, xq, xc, sgu, sgu_s, sw2, sw2_s, ye, NULL, NULL);
-    for (int32_t n = 0; n < H; ++n) {
-      acc[n] += ye[n];
-      if (out_f64) out_f64[(size_t)t * H + n] = acc[n];
-      if (out) out[(size_t)t * H + n] = orc_bf16_rne(acc[n]);
-    }
+    orc_expert(H, Is, xq, xc, sgu, sgu_s, sw2, sw2_s, ysh, NULL, NULL);
+    orc_combine(K, H, w + (size_t)t * K, ye, ysh, out_f64 ? out_f64 + (size_t)t * H : NULL,
+                out ? out + (size_t)t * H : NULL);
   }
   if (normed) memcpy(normed, y, sizeof(uint16_t) * mh);
   if (x8) memcpy(x8, q, mh);
@@ -512,7 +540,7 @@ int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
   free(sel);
   free(w);
   free(ye);
-  free(acc);
+  free(ysh);
   return 0;
 }
 

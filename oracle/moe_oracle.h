@@ -116,6 +116,16 @@ void orc_router(int32_t m, int32_t h, int32_t e, int32_t k, const uint16_t* y,
  * when the m*k pairs are listed by expert ascending, then token ascending. */
 void orc_plan(int32_t m, int32_t e, int32_t k, const int32_t* ids,
               int32_t* counts, int32_t* row);
+/* The two halves of one expert for one token (orc_expert_fmt is the two in
+ * turn).  up: hv [2I] = x . W13^T in double, habs [2I] (may be NULL) the
+ * sums of |x_k w_nk| over the contraction, av [I] = fp32(SiLU(g) u) held in
+ * double, a8 [I] / a8s [I/32] its MXFP8.  down: y [H] = a8 . W2^T. */
+void orc_expert_up(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
+                   const uint8_t* x8s, const uint8_t* w13, const uint8_t* w13_s,
+                   double* hv, double* habs, double* av, uint8_t* a8, uint8_t* a8s);
+void orc_expert_down(int32_t h, int32_t inter, int32_t fmt, const uint8_t* a8,
+                     const uint8_t* a8s, const uint8_t* w2, const uint8_t* w2_s,
+                     double* y);
 /* One expert on one token: x8/x8s (H bytes, H/32 codes) -> y[H] (double);
  * a8/a8s (may be NULL) receive the quantised SiLU*up intermediate. */
 void orc_expert(int32_t h, int32_t inter, const uint8_t* x8,
@@ -131,6 +141,11 @@ void orc_expert_fmt(int32_t h, int32_t inter, int32_t fmt, const uint8_t* x8,
  * normed [m,H] bf16, x8 [m,H], x8s [m,H/32], logits [m,E], ids [m,k],
  * wts [m,k], out_f64 [m,H] (the sum before its bf16 rounding), out [m,H] bf16.
  * Returns 0, or -1 on bad dimensions / allocation failure. */
+/* One token's output from its k picked experts' outputs y_routed [k][H]
+ * (weights wts [k], selection order) and the shared expert's y_shared [H]:
+ * out_f64 [H] the sum in double, out [H] its bf16 (either may be NULL). */
+void orc_combine(int32_t k, int32_t h, const double* wts, const double* y_routed,
+                 const double* y_shared, double* out_f64, uint16_t* out);
 int32_t orc_layer(const orc_dims* d, int32_t m, const uint16_t* x,
                   const uint16_t* norm_w, const uint16_t* gate_w,
                   const float* bias, const uint8_t* w13, const uint8_t* w13_s,

@@ -1,10 +1,12 @@
 """Parity of the HIP path with the oracle, through the C ABI.
 
 Bars: bit-exact for the normed bf16 rows, the MXFP8 activation bytes and
-codes, the picked experts and the plan; |gpu - ref| <= 1e-2 + 2e-2 |ref| for
-the bf16 output (ref: the oracle's double-precision sum before its rounding);
-routing weights within 1e-6 relative.  The SiLU*up intermediate is compared
-to the oracle's by fraction of equal bytes (its accumulation order differs).
+codes, the picked experts and the plan (up to near-ties of the biased score,
+tests/routing_check.py); routing weights within 1e-6 relative; every byte and
+code of the SiLU*up intermediate one of the roundings the arithmetic allows
+(tests/a8_check.py); |gpu - ref| <= 1e-2 + 2e-2 |ref| for the bf16 output
+(ref: the oracle's double-precision sum before its rounding), plus the part
+an allowed different rounding of the intermediate can move each element.
 """
 import numpy as np
 import pytest
@@ -12,6 +14,9 @@ import torch
 
 import oracle
 import synth
+from concurrent.futures import ThreadPoolExecutor
+
+from tests import a8_check
 from tests import data
 from tests import gpu_util as gu
 from tests import routing_check
@@ -101,9 +106,62 @@ def _check_layer(cfg, handle, inp, w, out, rows_ref=None, o=None):
     if o is None:
         o = oracle.layer_parallel(dims, inp, w, rows, workers=data.WORKERS)
     keep = [i for i, t in enumerate(rows) if t not in ties]
+    # the intermediate: every GPU byte must be the oracle's or, where the
+    # oracle's value lies within the arithmetic's error of a rounding
+    # midpoint, the other correct rounding (tests/a8_check.py); the output is
+    # then held to the bar against the oracle's down projection and combine
+    # of those bytes.  With no differing byte that reference is the oracle's
+    # own output.
+    ref, nb, nc = _reference_out(cfg, handle, o, w, [rows[i] for i in keep], keep, ids, row)
     got = gu.out_f64(out)[rows][keep]
-    gu.assert_out_close(got, o["out_f64"][keep], what=cfg["name"])
+    gu.assert_out_close(got, ref, what=cfg["name"])
+    plain = np.abs(got - o["out_f64"][keep]) > 1e-2 + 2e-2 * np.abs(o["out_f64"][keep])
+    print(f"[{cfg['name']}] intermediate bytes differing from the oracle's: {nb}, codes: {nc}; "
+          f"output elements beyond the bar against the oracle's own intermediate: {int(plain.sum())}",
+          flush=True)
     return r, o
+
+
+def _reference_out(cfg, handle, o, w, toks, idx, ids, row):
+    """For token rows `toks` (o's rows `idx`): checks every SiLU*up byte and
+    code of the GPU run against the roundings the arithmetic allows, then
+    returns the oracle's output [len(toks), H] computed from those bytes
+    (its down projection of each expert's intermediate and its combine),
+    with the counts of bytes and codes that differ from the oracle's."""
+    m, H, K = cfg["m"], cfg["hidden"], cfg["topk"]
+    I, Is = cfg["inter"], cfg["shared_inter"]
+    Imax = max(I, Is)
+    fmt = data.routed_of(cfg)
+    a8 = gu.tap(handle, "a8").reshape(-1, Imax)
+    a8s = gu.tap(handle, "a8s").reshape(-1, Imax // 32)
+
+    def one(job):
+        t, i = job
+        ys = np.empty((K, H))
+        nb = nc = 0
+        for j in range(K + 1):
+            if j < K:
+                e = int(ids[t, j])
+                w13, w13s, w2, w2s, f, Kv, gr = (w["w13"][e], w["w13_s"][e], w["w2"][e], w["w2_s"][e],
+                                                 fmt, I, int(row[t, j]))
+            else:
+                w13, w13s, w2, w2s, f, Kv, gr = w["sgu"], w["sgu_s"], w["sw2"], w["sw2_s"], "e4m3", Is, m * K + t
+            up = oracle.expert_up(o["x8"][i], o["x8s"][i], w13, w13s, f)
+            a8_g, a8s_g = a8[gr, :Kv], a8s[gr, :Kv // 32]
+            a8_check.check_row(a8_check.ambiguity(up), a8_g, a8s_g)
+            db, dc = a8_check.differing(up, a8_g, a8s_g)
+            nb, nc = nb + db, nc + dc
+            y = oracle.expert_down(a8_g, a8s_g, w2, w2s, f)
+            if j < K:
+                ys[j] = y
+            else:
+                ysh = y
+        return oracle.combine(o["wts"][i], ys, ysh), nb, nc
+
+    with ThreadPoolExecutor(max_workers=data.WORKERS) as ex:
+        res = list(ex.map(one, list(zip(toks, idx))))
+    ref = np.stack([r_[0] for r_ in res]) if res else np.zeros((0, H))
+    return ref, sum(r_[1] for r_ in res), sum(r_[2] for r_ in res)
 
 
 def _bf16_f64(bits):
@@ -133,22 +191,7 @@ def test_parity_small(cfg):
     try:
         out = gu.run(h, cfg, dinp, dw)
         torch.cuda.synchronize()
-        r, o = _check_layer(cfg, h, inp, w, out)
-        # the intermediate: nearly all bytes equal (fp32 vs double accumulation)
-        a8 = gu.tap(h, "a8")
-        Imax = max(cfg["inter"], cfg["shared_inter"])
-        a8 = a8.reshape(-1, Imax)
-        counts, row = oracle.plan(r["ids"], cfg["experts"])
-        same = tot = 0
-        for t in range(min(cfg["m"], 4)):
-            for j in range(cfg["topk"]):
-                e = r["ids"][t, j]
-                ref = oracle.expert(o["x8"][t], o["x8s"][t], w["w13"][e], w["w13_s"][e],
-                                    w["w2"][e], w["w2_s"][e], fmt=data.routed_of(cfg))["a8"]
-                got = a8[row[t, j], :cfg["inter"]]
-                same += int((got == ref).sum())
-                tot += ref.size
-        assert same >= 0.995 * tot, f"a8 equal bytes {same}/{tot}"
+        _check_layer(cfg, h, inp, w, out)
     finally:
         mdl.destroy(h)
 
@@ -182,18 +225,7 @@ def test_parity_with_widely_varying_block_codes():
     try:
         out = gu.run(h, cfg, dinp, dw)
         torch.cuda.synchronize()
-        r, o = _check_layer(cfg, h, inp, w, out)
-        # the intermediate of every (token, pick) nearly byte-identical
-        a8 = gu.tap(h, "a8").reshape(-1, I)
-        a8s = gu.tap(h, "a8s").reshape(-1, I // 32)
-        counts, row = oracle.plan(r["ids"], E)
-        for t in range(6):
-            for j in range(4):
-                e = r["ids"][t, j]
-                ref = oracle.expert(o["x8"][t], o["x8s"][t], w["w13"][e], w["w13_s"][e],
-                                    w["w2"][e], w["w2_s"][e])
-                assert (a8[row[t, j]] == ref["a8"]).mean() >= 0.99, (t, j)
-                assert (a8s[row[t, j]] == ref["a8s"]).mean() >= 0.85, (t, j)
+        _check_layer(cfg, h, inp, w, out)
     finally:
         mdl.destroy(h)
 
