@@ -161,6 +161,38 @@ int moe_decode_run(moe_decode_handle plan, int32_t m, const void* d_x,
                    const void* d_sgu, const void* d_sgu_s, const void* d_sw2,
                    const void* d_sw2_s, void* d_out, void* stream);
 
+/* The run for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): no plan, and no
+ * allocation of any kind -- neither device nor host memory, nor a library
+ * routine that allocates.  The same step as moe_decode_run with the same
+ * kernels and output bits, on a plan-less scratch: one file-scope device
+ * array of MOE_DECODE_NOALLOC_SCRATCH_BYTES per GPU the library runs on,
+ * held until the process ends (its address is looked up once per device, on
+ * the first call made with that device current).
+ *   dims      as for moe_decode_plan (validated the same way); m <= max_tokens
+ *   d_*       as for moe_decode_run
+ *   d_status  u32 on the device: the bits moe_decode_status documents are
+ *             ORed into it; the caller zeroes it and reads it after the
+ *             step's work completes
+ * The step's scratch is laid out for its m rows (not max_tokens'); a step
+ * whose scratch would exceed the array returns MOE_DECODE_EINVAL (at
+ * H = 5120, E = 256, top-8, I = Is = 2048 every m <= 48 fits).  Every call on
+ * a GPU shares that GPU's array and leaves its contents there: two calls
+ * whose work overlaps on one GPU (two streams, or two threads) race and give
+ * wrong results; the caller serialises them.  Each step also launches the
+ * seam kernel, which clears the array's hand-off words left by the previous
+ * call.  Errors: EINVAL for bad dims, m, pointers or size, EHIP on a
+ * runtime error (nothing is enqueued after an argument error). */
+#define MOE_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_decode_run_noalloc(const moe_decode_dims* dims, int32_t m,
+                           const void* d_x, const void* d_norm_w,
+                           const void* d_gate_w, const float* d_bias,
+                           const void* d_w13, const void* d_w13_s,
+                           const void* d_w2, const void* d_w2_s,
+                           const void* d_sgu, const void* d_sgu_s,
+                           const void* d_sw2, const void* d_sw2_s,
+                           void* d_out, uint32_t* d_status, void* stream);
+
 /* Views of the last run's intermediates inside the plan's scratch (device
  * pointers, valid until the next run or destroy; read them after the run's
  * work completes).  Shapes use the last run's m; P = m * k pairs, R = P + m

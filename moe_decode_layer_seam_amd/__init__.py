@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_scratch_bytes.restype = ctypes.c_size_t
         L.moe_decode_run.argtypes = [_P, ctypes.c_int32] + [_P] * 14
         L.moe_decode_run.restype = ctypes.c_int
+        L.moe_decode_run_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32] + [_P] * 15
+        L.moe_decode_run_noalloc.restype = ctypes.c_int
         L.moe_decode_inspect.argtypes = [_P, ctypes.c_int32, ctypes.POINTER(_P),
                                          ctypes.POINTER(ctypes.c_size_t)]
         L.moe_decode_inspect.restype = ctypes.c_int
@@ -107,7 +109,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run",
+EXPORTS = ("moe_decode_plan", "moe_decode_scratch_bytes", "moe_decode_run", "moe_decode_run_noalloc",
            "moe_decode_inspect", "moe_decode_status", "moe_decode_timing", "moe_decode_timing_read",
            "moe_decode_timeline", "moe_decode_timeline_read",
            "moe_decode_destroy", "moe_decode_quantize_weight",
@@ -198,6 +200,43 @@ def run(handle: int, dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s,
     ]
     rc = lib().moe_decode_run(handle, m, *ptrs, _stream_ptr(stream))
     _check(rc, "moe_decode_run", handle)
+
+
+def run_noalloc(dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s, sgu, sgu_s, sw2, sw2_s,
+                out, status, max_tokens: int = MAX_TOKENS, rms_eps: float = 1e-6,
+                routed_scale: float = 1.0, schedule: str = "launches", stream=None) -> None:
+    """moe_decode_run_noalloc: the step without a plan or any allocation.
+    dims as for `run` (plus the layer's hidden..shared_inter); status an
+    int32 (or uint32) tensor of one element on the GPU, which the kernels'
+    status bits are ORed into (the caller zeroes it)."""
+    H, E, K, I, Is = dims["hidden"], dims["experts"], dims["topk"], dims["inter"], dims["shared_inter"]
+    routed = dims.get("routed", "e4m3")
+    fp4 = routed == "mxfp4"
+    m = x.shape[0]
+    d = Dims(H, E, K, I, Is, max_tokens, rms_eps, routed_scale, ROUTED[routed], SCHEDULES[schedule])
+
+    def q(t, name, shape):
+        dt = torch.float8_e4m3fn if t.dtype == torch.float8_e4m3fn else torch.uint8
+        return _tensor(t, name, shape, dt)
+
+    ptrs = [
+        _tensor(x, "x", (m, H), torch.bfloat16),
+        _tensor(norm_w, "norm_w", (H,), torch.bfloat16),
+        _tensor(gate_w, "gate_w", (E, H), torch.bfloat16),
+        _tensor(bias, "bias", (E,), torch.float32),
+        *((_tensor(w13, "w13", (E, 2 * I, H // 2), torch.uint8),
+           _tensor(w13_s, "w13_s", (E,) + fp4_codes_shape(2 * I, H), torch.uint8),
+           _tensor(w2, "w2", (E, H, I // 2), torch.uint8),
+           _tensor(w2_s, "w2_s", (E,) + fp4_codes_shape(H, I), torch.uint8)) if fp4 else
+          (q(w13, "w13", (E, 2 * I, H)), _tensor(w13_s, "w13_s", (E, 2 * I // 32, H // 32), torch.uint8),
+           q(w2, "w2", (E, H, I)), _tensor(w2_s, "w2_s", (E, H // 32, I // 32), torch.uint8))),
+        q(sgu, "sgu", (2 * Is, H)), _tensor(sgu_s, "sgu_s", (2 * Is // 32, H // 32), torch.uint8),
+        q(sw2, "sw2", (H, Is)), _tensor(sw2_s, "sw2_s", (H // 32, Is // 32), torch.uint8),
+        _tensor(out, "out", (m, H), torch.bfloat16),
+    ]
+    st = _tensor(status, "status", (1,), status.dtype)
+    rc = lib().moe_decode_run_noalloc(ctypes.byref(d), m, *ptrs, st, _stream_ptr(stream))
+    _check(rc, "moe_decode_run_noalloc")
 
 
 def run_ptrs(handle: int, m: int, ptrs, stream=None) -> int:

@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -124,6 +125,214 @@ namespace moe {
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 }  // namespace moe
 
+namespace {
+
+// Byte offsets of the scratch regions of one layout, each 256-byte aligned.
+struct Layout {
+  size_t normed, x8, x8s, logits, ids, wts, counts, pair, tok, roww, rowout, vs, hdr, a8, a8s;
+  size_t sync, status, tl, part13, part2, bytes;
+  size_t nsync, lbox;  // words of the hand-off region; the logit box's first word
+  int act_stride;
+};
+
+// The layout for d.Mx token rows: GEMM sum planes sized for every step
+// width up to d.Mx (one [R(m)][width] fp32 plane, or one per K segment for
+// the widths that run in split mode); `timeline`: room for the stamps.
+Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool timeline) {
+  Layout L{};
+  const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = Mx * K + Mx;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off = align_up(off + n);
+    return o;
+  };
+  L.normed = take(Mx * H * 2), L.x8 = take(Mx * H), L.x8s = take(Mx * H / 32);
+  L.logits = take(Mx * E * 8), L.ids = take(Mx * K * 4), L.wts = take(Mx * K * 4);
+  L.counts = take(E * 4), L.pair = take(Mx * K * 4), L.tok = take(R * 4), L.roww = take(R * 4);
+  L.rowout = take(R * 4);
+  L.vs = take((size_t)max_vs * 16), L.hdr = take(16);
+  L.a8 = take(R * d.Imax), L.a8s = take(R * d.Imax / 32);
+  // the hand-off words, zeroed by the seam launch: the route launch's arrival
+  // counter (word 0), from word 64 the fused launch's ready words and act
+  // groups' unit counts, then the boxes of the w13 launch that routes: the
+  // pick box, then (from an even word) the logit box
+  L.act_stride = d.Imax / kActCols;
+  L.lbox = (64 + (size_t)max_vs + (size_t)max_vs * L.act_stride + kPickBox + 1) & ~(size_t)1;
+  L.nsync = L.lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
+  L.sync = take(L.nsync * 4);
+  L.status = take(4);
+  L.tl = timeline ? take((size_t)kKernels * kTlBlocks * kTlPoints * 8) : 0;
+  size_t part13 = 0, part2 = 0;
+  const size_t nseg13 = (H / 128 + kSegSteps - 1) / kSegSteps;
+  const size_t nseg2 = (d.Imax / 128 + kSegSteps - 1) / kSegSteps;
+  for (int mm = 1; mm <= d.Mx; ++mm) {
+    const size_t Rm = (size_t)mm * (K + 1);
+    const size_t a = (gemm_split(d, mm, grid13 * gemm_waves(true), true) ? nseg13 : 1) * Rm * 2 * d.Imax * 4;
+    const size_t c = (gemm_split(d, mm, grid2 * gemm_waves(false), false) ? nseg2 : 1) * Rm * H * 4;
+    part13 = a > part13 ? a : part13;
+    part2 = c > part2 ? c : part2;
+  }
+  L.part13 = take(part13), L.part2 = take(part2);
+  L.bytes = off;
+  return L;
+}
+
+// The kernels' view of a layout at device address b.
+Scratch scratch_at(char* b, const Layout& L, const LayerDims& d, int max_vs) {
+  Scratch s{};
+  s.normed = reinterpret_cast<uint16_t*>(b + L.normed);
+  s.x8 = reinterpret_cast<uint8_t*>(b + L.x8);
+  s.x8s = reinterpret_cast<uint8_t*>(b + L.x8s);
+  s.logits = reinterpret_cast<double*>(b + L.logits);
+  s.ids = reinterpret_cast<int32_t*>(b + L.ids);
+  s.wts = reinterpret_cast<float*>(b + L.wts);
+  s.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  s.pair_row = reinterpret_cast<int32_t*>(b + L.pair);
+  s.row_tok = reinterpret_cast<int32_t*>(b + L.tok);
+  s.row_w = reinterpret_cast<float*>(b + L.roww);
+  s.row_out = reinterpret_cast<int32_t*>(b + L.rowout);
+  s.vslots = reinterpret_cast<int4*>(b + L.vs);
+  s.header = reinterpret_cast<int32_t*>(b + L.hdr);
+  s.a8 = reinterpret_cast<uint8_t*>(b + L.a8);
+  s.a8s = reinterpret_cast<uint8_t*>(b + L.a8s);
+  s.part13 = reinterpret_cast<float*>(b + L.part13);
+  s.part2 = reinterpret_cast<float*>(b + L.part2);
+  s.sync = reinterpret_cast<uint32_t*>(b + L.sync);
+  s.counter = s.sync;
+  s.status = reinterpret_cast<uint32_t*>(b + L.status);
+  s.ready = s.sync + 64;
+  s.act_cnt = s.ready + max_vs;
+  s.pick_box = s.act_cnt + (size_t)max_vs * L.act_stride;
+  s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + L.lbox) : nullptr;
+  s.nsync = (int)L.nsync;
+  s.act_stride = L.act_stride;
+  return s;
+}
+
+LayerDims dims_of(const moe_decode_dims* dims) {
+  LayerDims d{};
+  d.H = dims->hidden;
+  d.E = dims->experts;
+  d.K = dims->topk;
+  d.I = dims->inter;
+  d.Is = dims->shared_inter;
+  d.Imax = d.I > d.Is ? d.I : d.Is;
+  d.Mx = dims->max_tokens;
+  d.eps = dims->rms_eps;
+  d.routed_scale = dims->routed_scale;
+  d.rfmt = dims->routed_format;
+  return d;
+}
+
+// Whether every kernel variant fits a CU once (the expert GEMMs run one
+// block per CU).
+bool fits_cu(const LayerDims& d, int max_vs, bool fused) {
+  return gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, max_vs, true)) >= 1 &&
+         gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, max_vs, false)) >= 1 &&
+         (!fused || experts_blocks_per_cu(experts_lds_bytes(d, d.Mx, max_vs)) >= 1);
+}
+
+// The argument checks of a run (nothing is enqueued when one fails).
+const char* check_run(const LayerDims& d, int m, int max_m, const void* const* ptrs, int nptrs, const void* d_x,
+                      const void* d_out) {
+  if (m < 1 || m > max_m) return "m outside [1, max_tokens]";
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i])) return "null or misaligned (not 16-byte) pointer";
+  // out is written while x is still read by other blocks: no overlap
+  const uintptr_t xo = reinterpret_cast<uintptr_t>(d_x), oo = reinterpret_cast<uintptr_t>(d_out);
+  const uintptr_t n = (uintptr_t)m * d.H * 2;
+  if (xo < oo + n && oo < xo + n) return "out overlaps x";
+  return nullptr;
+}
+
+Inputs inputs_of(const void* d_x, const void* d_norm_w, const void* d_gate_w, const float* d_bias, const void* d_w13,
+                 const void* d_w13_s, const void* d_w2, const void* d_w2_s, const void* d_sgu, const void* d_sgu_s,
+                 const void* d_sw2, const void* d_sw2_s, void* d_out) {
+  Inputs in;
+  in.x = static_cast<const uint16_t*>(d_x);
+  in.norm_w = static_cast<const uint16_t*>(d_norm_w);
+  in.gate_w = static_cast<const uint16_t*>(d_gate_w);
+  in.bias = d_bias;
+  in.w13 = static_cast<const uint8_t*>(d_w13);
+  in.w13_s = static_cast<const uint8_t*>(d_w13_s);
+  in.w2 = static_cast<const uint8_t*>(d_w2);
+  in.w2_s = static_cast<const uint8_t*>(d_w2_s);
+  in.sgu = static_cast<const uint8_t*>(d_sgu);
+  in.sgu_s = static_cast<const uint8_t*>(d_sgu_s);
+  in.sw2 = static_cast<const uint8_t*>(d_sw2);
+  in.sw2_s = static_cast<const uint8_t*>(d_sw2_s);
+  in.out = static_cast<uint16_t*>(d_out);
+  return in;
+}
+
+// One step's launches on st.  seam_always: launch the seam even where the
+// w13 launch runs it itself (the seam launch zeroes the hand-off words).
+// boxes_dirty (may be null): set while a w13 launch that routes has run
+// without the act launch that clears its boxes.  ts (may be null): the
+// run's timing events; last_grid (may be null): the launches' grids.
+hipError_t enqueue(const LayerDims& d, int m, const Inputs& in, const Scratch& sc, int grid13, int grid2, int max_vs,
+                   bool fused, bool seam_always, bool* boxes_dirty, TimingSet* ts, int* last_grid, hipStream_t st,
+                   const char** what) {
+  const bool route13 = !fused && route_in_w13(d, m, grid13);
+  const bool seam = !route13 || seam_always || (boxes_dirty && *boxes_dirty);
+  if (last_grid) {
+    last_grid[0] = seam ? seam_blocks(d, m) : 0;
+    last_grid[1] = logits_blocks(d, m);
+    last_grid[2] = m;
+    last_grid[3] = grid13;
+    last_grid[4] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
+    last_grid[5] = grid2;
+    last_grid[6] = d.H / 64 * m;
+    last_grid[7] = grid13;
+  }
+  auto ev = [&](int k) {
+    KernelEvents r;
+    if (ts) {
+      r.start = ts->ev[2 * k], r.stop = ts->ev[2 * k + 1];
+      ts->launched |= 1u << k;
+    }
+    return r;
+  };
+  hipError_t e;
+  if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return *what = "seam launch", e;
+  if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
+    return *what = "logits launch", e;
+  // the fused launch reads the route launch's plan; the w13 launch of the
+  // launches schedule builds its own from the stored picks
+  if (!route13 && (e = launch_route(d, m, in, sc, fused, st, ev(2))) != hipSuccess)
+    return *what = "route launch", e;
+  if (fused) {
+    if ((e = launch_experts(d, m, in, sc, grid13, max_vs, st, ev(7))) != hipSuccess)
+      return *what = "experts launch", e;
+  } else {
+    if (route13 && boxes_dirty) *boxes_dirty = true;
+    if ((e = launch_w13(d, m, in, sc, grid13, max_vs, route13, st, ev(3))) != hipSuccess)
+      return *what = "w13 launch", e;
+    if ((e = launch_act(d, m, sc, grid13, st, ev(4))) != hipSuccess) return *what = "act launch", e;
+    if (boxes_dirty) *boxes_dirty = false;
+    if ((e = launch_w2(d, m, in, sc, grid2, max_vs, st, ev(5))) != hipSuccess) return *what = "w2 launch", e;
+  }
+  if ((e = launch_combine(d, m, in, sc, grid2, st, ev(6))) != hipSuccess) return *what = "combine launch", e;
+  return hipSuccess;
+}
+
+// The scratch of moe_decode_run_noalloc: one array per GPU the library runs
+// on, held until the process ends.  Its name is a host-side stand-in; host
+// code uses the device address hipGetSymbolAddress gives, kept per device.
+constexpr size_t kNoAllocBytes = MOE_DECODE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+struct NoAllocDevice {
+  char* ptr = nullptr;  // the array's device address on this device
+  int cus = 0;
+};
+NoAllocDevice g_noalloc[kMaxDevices];
+std::mutex g_noalloc_mu;
+
+}  // namespace
+
 extern "C" {
 
 int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle* out) {
@@ -143,16 +352,7 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   auto* p = new (std::nothrow) moe_decode_plan_s();
   if (!p) return MOE_DECODE_ENOMEM;
   LayerDims& d = p->d;
-  d.H = dims->hidden;
-  d.E = dims->experts;
-  d.K = dims->topk;
-  d.I = dims->inter;
-  d.Is = dims->shared_inter;
-  d.Imax = d.I > d.Is ? d.I : d.Is;
-  d.Mx = dims->max_tokens;
-  d.eps = dims->rms_eps;
-  d.routed_scale = dims->routed_scale;
-  d.rfmt = dims->routed_format;
+  d = dims_of(dims);
   p->fused = dims->schedule == MOE_DECODE_SCHEDULE_FUSED;
   p->max_vs = max_vslots(d.Mx, d.E, d.K);
   p->R = d.Mx * d.K + d.Mx;
@@ -167,54 +367,14 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
     delete p;
     return rc;
   }
-  // the expert GEMMs run one block per CU; every variant must fit once
-  if (gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, p->max_vs, true)) < 1 ||
-      gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, p->max_vs, false)) < 1 ||
-      (p->fused && experts_blocks_per_cu(experts_lds_bytes(d, d.Mx, p->max_vs)) < 1)) {
+  if (!fits_cu(d, p->max_vs, p->fused)) {
     p->err = g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
     delete p;
     return MOE_DECODE_EINVAL;
   }
   p->grid13 = p->grid2 = p->cus;
-
-  // scratch layout, every region 256-byte aligned
-  const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = p->R;
-  size_t off = 0;
-  auto take = [&](size_t n) {
-    size_t o = off;
-    off = align_up(off + n);
-    return o;
-  };
-  const size_t o_normed = take(Mx * H * 2), o_x8 = take(Mx * H), o_x8s = take(Mx * H / 32);
-  const size_t o_logits = take(Mx * E * 8), o_ids = take(Mx * K * 4), o_wts = take(Mx * K * 4);
-  const size_t o_counts = take(E * 4), o_pair = take(Mx * K * 4), o_tok = take(R * 4), o_roww = take(R * 4);
-  const size_t o_rowout = take(R * 4);
-  const size_t o_vs = take((size_t)p->max_vs * 16), o_hdr = take(16), o_ctr = take(4);
-  const size_t o_a8 = take(R * d.Imax), o_a8s = take(R * d.Imax / 32);
-  // counters of the fused launch (from word 64): the slots' ready words,
-  // the act groups' unit counts
-  const int act_stride = d.Imax / kActCols;
-  // ... and the boxes of the w13 launch that routes: the pick box, then
-  // (from an even word) the logit box
-  const size_t o_lbox = (64 + (size_t)p->max_vs + (size_t)p->max_vs * act_stride + kPickBox + 1) & ~(size_t)1;
-  const size_t nsync = o_lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
-  const size_t o_sync = take(nsync * 4);
-  const size_t o_status = take(4);
-  const size_t o_tl = take((size_t)kKernels * kTlBlocks * kTlPoints * 8);
-  // GEMM sum planes: one [R(m)][width] fp32 plane, or one per K segment for
-  // the step sizes that run in split mode
-  size_t part13 = 0, part2 = 0;
-  const size_t nseg13 = (H / 128 + kSegSteps - 1) / kSegSteps;
-  const size_t nseg2 = (d.Imax / 128 + kSegSteps - 1) / kSegSteps;
-  for (int mm = 1; mm <= d.Mx; ++mm) {
-    const size_t Rm = (size_t)mm * (K + 1);
-    const size_t a = (gemm_split(d, mm, p->grid13 * gemm_waves(true), true) ? nseg13 : 1) * Rm * 2 * d.Imax * 4;
-    const size_t c = (gemm_split(d, mm, p->grid2 * gemm_waves(false), false) ? nseg2 : 1) * Rm * H * 4;
-    part13 = a > part13 ? a : part13;
-    part2 = c > part2 ? c : part2;
-  }
-  const size_t o_part13 = take(part13), o_part2 = take(part2);
-  p->bytes = off;
+  const Layout L = make_layout(d, p->max_vs, p->grid13, p->grid2, true);
+  p->bytes = L.bytes;
   if ((e = hipMalloc(&p->base, p->bytes)) != hipSuccess) {
     hip_fail(p, e, "hipMalloc");
     delete p;
@@ -227,35 +387,8 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
     return rc;
   }
   char* b = static_cast<char*>(p->base);
-  Scratch& s = p->s;
-  s.normed = reinterpret_cast<uint16_t*>(b + o_normed);
-  s.x8 = reinterpret_cast<uint8_t*>(b + o_x8);
-  s.x8s = reinterpret_cast<uint8_t*>(b + o_x8s);
-  s.logits = reinterpret_cast<double*>(b + o_logits);
-  s.ids = reinterpret_cast<int32_t*>(b + o_ids);
-  s.wts = reinterpret_cast<float*>(b + o_wts);
-  s.counts = reinterpret_cast<int32_t*>(b + o_counts);
-  s.pair_row = reinterpret_cast<int32_t*>(b + o_pair);
-  s.row_tok = reinterpret_cast<int32_t*>(b + o_tok);
-  s.row_w = reinterpret_cast<float*>(b + o_roww);
-  s.row_out = reinterpret_cast<int32_t*>(b + o_rowout);
-  s.vslots = reinterpret_cast<int4*>(b + o_vs);
-  s.header = reinterpret_cast<int32_t*>(b + o_hdr);
-  s.counter = reinterpret_cast<uint32_t*>(b + o_ctr);
-  s.a8 = reinterpret_cast<uint8_t*>(b + o_a8);
-  s.a8s = reinterpret_cast<uint8_t*>(b + o_a8s);
-  p->tl_base = reinterpret_cast<uint64_t*>(b + o_tl);
-  s.part13 = reinterpret_cast<float*>(b + o_part13);
-  s.part2 = reinterpret_cast<float*>(b + o_part2);
-  s.sync = reinterpret_cast<uint32_t*>(b + o_sync);
-  s.status = reinterpret_cast<uint32_t*>(b + o_status);
-  s.ready = s.sync + 64;
-  s.act_cnt = s.ready + p->max_vs;
-  s.pick_box = s.act_cnt + (size_t)p->max_vs * act_stride;
-  s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + o_lbox) : nullptr;
-  s.nsync = (int)nsync;
-  s.act_stride = act_stride;
-  s.tl_seam = s.tl_logits = s.tl_route = s.tl_w13 = s.tl_act = s.tl_w2 = s.tl_combine = s.tl_experts = nullptr;
+  p->s = scratch_at(b, L, d, p->max_vs);
+  p->tl_base = reinterpret_cast<uint64_t*>(b + L.tl);
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -268,42 +401,15 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
                    const void* d_sw2_s, void* d_out, void* stream) {
   if (!p) return MOE_DECODE_EINVAL;
   const LayerDims& d = p->d;
-  if (m < 1 || m > d.Mx) {
-    p->err = "m outside [1, max_tokens]";
-    return MOE_DECODE_EINVAL;
-  }
   const void* ptrs[] = {d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s,
                         d_sgu, d_sgu_s, d_sw2, d_sw2_s, d_out};
-  for (const void* q : ptrs)
-    if (!aligned16(q)) {
-      p->err = "null or misaligned (not 16-byte) pointer";
-      return MOE_DECODE_EINVAL;
-    }
-  {
-    // out is written while x is still read by other blocks: no overlap
-    const uintptr_t xo = reinterpret_cast<uintptr_t>(d_x), oo = reinterpret_cast<uintptr_t>(d_out);
-    const uintptr_t n = (uintptr_t)m * d.H * 2;
-    if (xo < oo + n && oo < xo + n) {
-      p->err = "out overlaps x";
-      return MOE_DECODE_EINVAL;
-    }
+  if (const char* why = check_run(d, m, d.Mx, ptrs, 13, d_x, d_out)) {
+    p->err = why;
+    return MOE_DECODE_EINVAL;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Inputs in;
-  in.x = static_cast<const uint16_t*>(d_x);
-  in.norm_w = static_cast<const uint16_t*>(d_norm_w);
-  in.gate_w = static_cast<const uint16_t*>(d_gate_w);
-  in.bias = d_bias;
-  in.w13 = static_cast<const uint8_t*>(d_w13);
-  in.w13_s = static_cast<const uint8_t*>(d_w13_s);
-  in.w2 = static_cast<const uint8_t*>(d_w2);
-  in.w2_s = static_cast<const uint8_t*>(d_w2_s);
-  in.sgu = static_cast<const uint8_t*>(d_sgu);
-  in.sgu_s = static_cast<const uint8_t*>(d_sgu_s);
-  in.sw2 = static_cast<const uint8_t*>(d_sw2);
-  in.sw2_s = static_cast<const uint8_t*>(d_sw2_s);
-  in.out = static_cast<uint16_t*>(d_out);
-
+  const Inputs in = inputs_of(d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s, d_sgu, d_sgu_s, d_sw2,
+                              d_sw2_s, d_out);
   TimingSet* ts = nullptr;
   if (p->timing) {
     if (p->ring_used == kTimingRing) fold_timing(p);
@@ -322,50 +428,79 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     sc.tl_combine = tl[6];
     sc.tl_experts = tl[7];
   }
-  // the w13 launch that routes runs the seam itself; the seam launch runs
-  // then only to zero the boxes after a run that stopped between the w13
-  // and act launches (act zeroes them for the next run)
-  const bool route13 = !p->fused && route_in_w13(d, m, p->grid13);
-  const bool seam = !route13 || p->boxes_dirty;
-  p->last_grid[0] = seam ? seam_blocks(d, m) : 0;
-  p->last_grid[1] = logits_blocks(d, m);
-  p->last_grid[2] = m;
-  p->last_grid[3] = p->grid13;
-  p->last_grid[4] = (d.Imax + kThreads - 1) / kThreads * (m * d.K + m);
-  p->last_grid[5] = p->grid2;
-  p->last_grid[6] = d.H / 64 * m;
-  p->last_grid[7] = p->grid13;
-  hipError_t e;
-  auto ev = [&](int k) {
-    KernelEvents r;
-    if (ts) {
-      r.start = ts->ev[2 * k], r.stop = ts->ev[2 * k + 1];
-      ts->launched |= 1u << k;
-    }
-    return r;
-  };
-  if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return hip_fail(p, e, "seam launch");
-  if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
-    return hip_fail(p, e, "logits launch");
-  // the fused launch reads the route launch's plan; the w13 launch of the
-  // launches schedule builds its own from the stored picks
-  if (!route13 && (e = launch_route(d, m, in, sc, p->fused, st, ev(2))) != hipSuccess)
-    return hip_fail(p, e, "route launch");
-  if (p->fused) {
-    if ((e = launch_experts(d, m, in, sc, p->grid13, p->max_vs, st, ev(7))) != hipSuccess)
-      return hip_fail(p, e, "experts launch");
-  } else {
-    if (route13) p->boxes_dirty = true;
-    if ((e = launch_w13(d, m, in, sc, p->grid13, p->max_vs, route13, st, ev(3))) != hipSuccess)
-      return hip_fail(p, e, "w13 launch");
-    if ((e = launch_act(d, m, sc, p->grid13, st, ev(4))) != hipSuccess) return hip_fail(p, e, "act launch");
-    p->boxes_dirty = false;
-    if ((e = launch_w2(d, m, in, sc, p->grid2, p->max_vs, st, ev(5))) != hipSuccess)
-      return hip_fail(p, e, "w2 launch");
-  }
-  if ((e = launch_combine(d, m, in, sc, p->grid2, st, ev(6))) != hipSuccess)
-    return hip_fail(p, e, "combine launch");
+  const char* what = "";
+  hipError_t e = enqueue(d, m, in, sc, p->grid13, p->grid2, p->max_vs, p->fused, false, &p->boxes_dirty, ts,
+                         p->last_grid, st, &what);
+  if (e != hipSuccess) return hip_fail(p, e, what);
   p->last_m = m;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_run_noalloc(const moe_decode_dims* dims, int32_t m, const void* d_x, const void* d_norm_w,
+                           const void* d_gate_w, const float* d_bias, const void* d_w13, const void* d_w13_s,
+                           const void* d_w2, const void* d_w2_s, const void* d_sgu, const void* d_sgu_s,
+                           const void* d_sw2, const void* d_sw2_s, void* d_out, uint32_t* d_status, void* stream) {
+  if (!valid_dims(dims)) {
+    g_last_error = "invalid dimensions";
+    return MOE_DECODE_EINVAL;
+  }
+  LayerDims d = dims_of(dims);
+  const void* ptrs[] = {d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s,
+                        d_sgu, d_sgu_s, d_sw2, d_sw2_s, d_out};
+  if (const char* why = check_run(d, m, d.Mx, ptrs, 13, d_x, d_out)) {
+    g_last_error = why;
+    return MOE_DECODE_EINVAL;
+  }
+  if (d_status == nullptr || reinterpret_cast<uintptr_t>(d_status) % 4) {
+    g_last_error = "null or misaligned status word";
+    return MOE_DECODE_EINVAL;
+  }
+  // this step's layout only: its rows, not max_tokens'
+  d.Mx = m;
+  const bool fused = dims->schedule == MOE_DECODE_SCHEDULE_FUSED;
+  const int max_vs = max_vslots(d.Mx, d.E, d.K);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "device index beyond the no-alloc table";
+    return MOE_DECODE_EINVAL;
+  }
+  NoAllocDevice nd;
+  {
+    // once per device, with it current: the array's address on this device
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (g_noalloc[dev].ptr == nullptr) {
+      void* ptr = nullptr;
+      if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+        return hip_fail(nullptr, e, "hipGetSymbolAddress");
+      int cus = 0;
+      if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return hip_fail(nullptr, e, "hipDeviceGetAttribute");
+      g_noalloc[dev].ptr = static_cast<char*>(ptr);
+      g_noalloc[dev].cus = cus;
+    }
+    nd = g_noalloc[dev];
+  }
+  if (!fits_cu(d, max_vs, fused)) {
+    g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
+    return MOE_DECODE_EINVAL;
+  }
+  const Layout L = make_layout(d, max_vs, nd.cus, nd.cus, false);
+  if (L.bytes > kNoAllocBytes) {
+    g_last_error = "the step's scratch exceeds MOE_DECODE_NOALLOC_SCRATCH_BYTES";
+    return MOE_DECODE_EINVAL;
+  }
+  Scratch sc = scratch_at(nd.ptr, L, d, max_vs);
+  sc.status = d_status;
+  const Inputs in = inputs_of(d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s, d_sgu, d_sgu_s, d_sw2,
+                              d_sw2_s, d_out);
+  // the seam launch runs in every step: it zeroes the hand-off words, which
+  // the array holds from whatever call used it last
+  const char* what = "";
+  e = enqueue(d, m, in, sc, nd.cus, nd.cus, max_vs, fused, true, nullptr, nullptr, nullptr,
+              static_cast<hipStream_t>(stream), &what);
+  if (e != hipSuccess) return hip_fail(nullptr, e, what);
   return MOE_DECODE_OK;
 }
 
