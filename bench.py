@@ -45,13 +45,13 @@ def expert_bytes(H: int, I: int, fmt: str = "e4m3") -> dict:
     return {"w13": w13, "w2": w2}
 
 
-def w13_input_bytes(m: int, H: int, E: int, K: int, schedule: str = "launches") -> int:
-    """Algorithmic bytes the w13 launch reads besides the expert weights.
-    Steps of up to 4 tokens (the launches schedule, E <= 256, H <= 8192, at
-    most 64 pairs) run the seam and the router in that launch: it reads the
-    bf16 rows, the norm weight, the router's gate rows and bias.  Otherwise
-    it reads the MXFP8 rows and their codes."""
-    if schedule == "launches" and m <= 4 and m * K <= 64 and E <= 256 and H <= 8192:
+def w13_input_bytes(m: int, H: int, E: int, K: int) -> int:
+    """Algorithmic bytes the w13 launch (or the persistent launch) reads
+    besides the expert weights.  Steps of up to 4 tokens (E <= 256, H <= 8192,
+    at most 64 pairs) run the seam and the router in that launch: it reads
+    the bf16 rows, the norm weight, the router's gate rows and bias.
+    Otherwise it reads the MXFP8 rows and their codes."""
+    if m <= 4 and m * K <= 64 and E <= 256 and H <= 8192:
         return 2 * m * H + 2 * H + 2 * E * H + 4 * E
     return m * (H + H // 32)
 
@@ -318,7 +318,6 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
     # the plan a caller makes for this decode width
     h = mdl.plan(H, E, K, I, Is, m, cfg["rms_eps"], cfg["routed_scale"], routed=routed,
                  schedule=args.schedule)
-    fused = args.schedule == "fused"
     try:
         def step(c):
             w = wsets[c]
@@ -416,7 +415,7 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
             step(i % copies)
         torch.cuda.synchronize()
         kern = {}
-        for k in ("seam", "logits", "route") + (("experts",) if fused else ("w13", "act", "w2")) + ("combine",):
+        for k in mdl.KERNELS:
             tot, runs = mdl.timing_read(h, k)
             if runs:
                 kern[k] = tot / runs
@@ -432,19 +431,21 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
     tiles = int(sum(-(-int(c) // 16) for c in counts if c > 0)) + -(-m // 16)
     row_occupancy = (m * K + m) / (16 * tiles)
 
-    # algorithmic bytes per launch of the dominant kernel (the fused expert
-    # launch, else w13): every active expert's weights and codes (shared
-    # expert included) and the rows they are multiplied with (MXFP8, or at
-    # m <= 4 the bf16 rows, norm weight and router weights the launch's own
-    # seam and router read)
+    # algorithmic bytes per launch of the dominant kernel (the persistent
+    # launch where it ran, else w13): every active expert's weights and codes
+    # (shared expert included) and the rows they are multiplied with (MXFP8,
+    # or at m <= 4 the bf16 rows, norm weight and router weights the launch's
+    # own seam and router read); w2 also reads the SiLU*up intermediate,
+    # which the persistent launch makes itself
     steps_U = [U[i % copies] for i in range(args.steps)]
     avg_U = sum(steps_U) / len(steps_U)
-    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + w13_input_bytes(m, H, E, K, args.schedule)
+    w13_bytes = avg_U * eb["w13"] + ebs["w13"] + w13_input_bytes(m, H, E, K)
     expert_step_bytes = avg_U * (eb["w13"] + eb["w2"]) + ebs["w13"] + ebs["w2"]
-    w2_bytes = avg_U * eb["w2"] + ebs["w2"] + (m * K + m) * (max(I, Is) + max(I, Is) // 32)
-    if fused:
-        dom, dom_bytes = "experts", w13_bytes + w2_bytes
-        kernel_gbs = {"experts": dom_bytes / (kern["experts"] * 1e-3) / 1e9}
+    a8_bytes = (m * K + m) * (max(I, Is) + max(I, Is) // 32)
+    w2_bytes = avg_U * eb["w2"] + ebs["w2"] + a8_bytes
+    if "persistent" in kern:
+        dom, dom_bytes = "persistent", w13_bytes + w2_bytes - a8_bytes
+        kernel_gbs = {"persistent": dom_bytes / (kern["persistent"] * 1e-3) / 1e9}
     else:
         dom, dom_bytes = "w13", w13_bytes
         kernel_gbs = {"w13": w13_bytes / (kern["w13"] * 1e-3) / 1e9,
@@ -495,8 +496,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="oracle seconds per workload")
     ap.add_argument("--routed", choices=("e4m3", "mxfp4"), default="e4m3",
                     help="routed experts' weight format (the shared expert is E4M3)")
-    ap.add_argument("--schedule", choices=("launches", "fused"), default="launches",
-                    help="expert GEMMs as one fused launch or as w13, act and w2 launches")
+    ap.add_argument("--schedule", choices=("auto", "launches", "persistent"), default="auto",
+                    help="auto: the library's fastest (the short launches); launches: the short "
+                         "launches for every step; persistent: the persistent launch for the small "
+                         "steps it covers")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the upstream-seam timing and the read probe")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

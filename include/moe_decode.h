@@ -64,19 +64,26 @@ extern "C" {
                                      the pages' A8W4 routed experts
                                      (MonoLayerWeights.check, fp4x2) */
 
-/* How a run schedules the expert GEMMs.  LAUNCHES (the default): w13, the
- * SiLU*up requantisation (act) and w2 as three launches.  FUSED: the three
- * in one launch of one block per CU, each w2 work unit waiting on
- * device-scope counters for its expert's a8 instead of on a launch boundary
- * (the pages' persistent MoE launch with device counters: [layer] run_ffn,
- * build_mono_ffn; [device] atomic_add_dev).  Both give the same output bits.
- * FUSED assumes that all its blocks can be resident at once (no concurrent
- * work holds CUs for its whole duration); a wait that runs past 100 ms flags
- * the run (moe_decode_status) and goes on.  On MI355X it is the slower
- * of the two: a hand-off between CUs through device memory waits behind the
- * weight stream's queued reads, which costs more than a launch boundary. */
-#define MOE_DECODE_SCHEDULE_LAUNCHES 0
-#define MOE_DECODE_SCHEDULE_FUSED 1
+/* How runs are scheduled.  LAUNCHES: the short launches (seam, logits,
+ * route, w13, SiLU * up, w2, combine; steps of up to 4 rows route inside
+ * w13).  PERSISTENT: steps of at most 4 rows whose layer the persistent
+ * launch covers run the seam, the router, w13, SiLU * up and w2 in one
+ * launch of one block per CU, then the combine launch (the pages'
+ * persistent MoE launch whose phases hand off through device counters:
+ * [layer] run_ffn, build_mono_ffn; [device] atomic_add_dev); other steps run
+ * the short launches.  The persistent launch cuts every active expert's
+ * intermediate into one slice per XCD, so each hand-off stays in one XCD's
+ * L2.  It covers E4M3 routed experts whose I and Is are 2048 or 4096, with
+ * the other conditions of the w13 launch that routes (below); the plan
+ * checks that the device deals a launch's blocks to its XCDs round-robin
+ * (from any first XCD), else every step runs the short launches.  It
+ * assumes that all its blocks are resident at once; a wait past 100 ms sets
+ * a status bit (moe_decode_status).  AUTO (the default): the schedule that
+ * runs a step fastest on MI355X, today the short launches at every width.
+ * Every schedule gives a token the same output bits. */
+#define MOE_DECODE_SCHEDULE_AUTO 0
+#define MOE_DECODE_SCHEDULE_LAUNCHES 1
+#define MOE_DECODE_SCHEDULE_PERSISTENT 2
 
 /* Layer dimensions, fixed when the plan is made.
  *   hidden        H, a multiple of 128 (the scaled MFMA's K step), <= 16384
@@ -88,7 +95,7 @@ extern "C" {
  *   rms_eps       RMSNorm epsilon (added to mean(x^2) in double precision)
  *   routed_scale  factor applied to the renormalised routing weights
  *   routed_format MOE_DECODE_ROUTED_E4M3 or MOE_DECODE_ROUTED_MXFP4
- *   schedule      MOE_DECODE_SCHEDULE_LAUNCHES or MOE_DECODE_SCHEDULE_FUSED */
+ *   schedule      MOE_DECODE_SCHEDULE_AUTO, _LAUNCHES or _PERSISTENT */
 typedef struct moe_decode_dims {
   int32_t hidden;
   int32_t experts;
@@ -231,9 +238,10 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * A kernel that waits on other blocks of its launch (the hand-offs of the
  * pages' persistent launch through device-scope words, [device]
  * atomic_add_dev; [layer] run_ffn) gives up after 100 ms and sets a bit; the
- * run's output is then not valid.  Bits: 1 a wait of the fused expert launch
- * for a slot's a8; 2 a wait of the w13 launch that routes (m <= 4) for the
- * logits or the picks.  The bits are sticky: no kernel clears them, so a
+ * run's output is then not valid.  Bits: 1 a wait of the persistent launch
+ * for a slot's a8; 2 a wait of a launch that routes (m <= 4) for the logits
+ * or the picks; 4 blocks of the persistent launch whose indices agree mod
+ * the XCD count ran on different XCDs (their hand-offs then crossed XCDs).  The bits are sticky: no kernel clears them, so a
  * check after many runs (a graph replayed many times) covers all of them.
  * moe_decode_status synchronises `stream`, copies the word to *h_status and,
  * when `clear` is nonzero, zeroes it.  Not during stream capture
@@ -248,8 +256,8 @@ int moe_decode_status(moe_decode_handle plan, void* stream, uint32_t* h_status,
  * moe_decode_timing(plan, 1) starts recording (and clears the totals), 0
  * stops.  While on, moe_decode_run must not be captured into a graph.
  * moe_decode_timing_read sums the elapsed milliseconds of kernel `kernel` (0
- * seam, 1 logits, 2 route, 3 w13, 4 act, 5 w2, 6 combine, 7 experts: the
- * fused w13 + act + w2 launch) over the recorded
+ * seam, 1 logits, 2 route, 3 w13, 4 act, 5 w2, 6 combine, 7 the persistent
+ * launch) over the recorded
  * runs that launched it, and sets *runs to their number; it synchronises
  * with the recorded events.  (Steps of m <= 4 rows compute the logits inside
  * the seam launch and do not launch `logits`; with the launches schedule they
@@ -266,15 +274,16 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   route: 0 start, 5 scores computed, 1 groups sorted, 6 lists merged,
  *          2 picks stored, 3 last block admitted, 4 plan written (3-4 only
  *          in the last block; 3 not with one token)
- *   w13, w2, experts: 0 start, 3 + w: wave w of the block done, 1 end;
- *          w13 that routes also 2: its seam done (the route block's
- *          route points are stored as route's, block = token)
+ *   w13, w2, persistent: 0 start, 3 + w: wave w of the block done, 1 end;
+ *          w13 that routes and the persistent launch also 2: their seam
+ *          done (the route block's route points are stored as route's,
+ *          block = token)
  *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.
  * Unwritten points keep stale values.  moe_decode_timeline_read copies the
  * last run's records of kernel `kernel` (0 seam, 1 logits, 2 route, 3 w13,
- * 4 act, 5 w2, 6 combine, 7 experts) as
+ * 4 act, 5 w2, 6 combine, 7 persistent) as
  * u64 [blocks][8] into h_out (n entries available), sets *blocks, and
  * synchronises the device. */
 int moe_decode_timeline(moe_decode_handle plan, int32_t on);

@@ -27,13 +27,14 @@ MAX_TOKENS = 48
 TAPS = {"normed": 0, "x8": 1, "x8s": 2, "logits": 3, "topk_ids": 4, "topk_w": 5,
         "counts": 6, "pair_row": 7, "row_tok": 8, "a8": 9, "a8s": 10, "status": 11}
 KERNELS = {"seam": 0, "logits": 1, "route": 2, "w13": 3, "act": 4, "w2": 5, "combine": 6,
-           "experts": 7}
+           "persistent": 7}
 
 
 # routed expert weight formats (moe_decode.h MOE_DECODE_ROUTED_*)
 ROUTED = {"e4m3": 0, "mxfp4": 1}
-# expert GEMM schedules (MOE_DECODE_SCHEDULE_*)
-SCHEDULES = {"launches": 0, "fused": 1}
+# schedules (MOE_DECODE_SCHEDULE_*): the fastest (today the short launches),
+# the short launches always, or the persistent launch where it covers a step
+SCHEDULES = {"auto": 0, "launches": 1, "persistent": 2}
 
 
 class Dims(ctypes.Structure):
@@ -144,10 +145,12 @@ def _check(rc: int, what: str, handle=None) -> None:
 def plan(hidden: int, experts: int, topk: int, inter: int, shared_inter: int,
          max_tokens: int = MAX_TOKENS, rms_eps: float = 1e-6,
          routed_scale: float = 1.0, stream=None, routed: str = "e4m3",
-         schedule: str = "launches") -> int:
+         schedule: str = "auto") -> int:
     """moe_decode_plan: returns an opaque handle (int).  routed: the routed
-    experts' weight format, "e4m3" or "mxfp4"; schedule: "launches" (w13,
-    act and w2 as three launches) or "fused" (one launch)."""
+    experts' weight format, "e4m3" or "mxfp4"; schedule: "auto" (the
+    fastest: today the short launches), "launches" (the short launches) or
+    "persistent" (the persistent launch for the small steps it covers, the
+    short launches otherwise)."""
     d = Dims(hidden, experts, topk, inter, shared_inter, max_tokens, rms_eps, routed_scale,
              ROUTED[routed], SCHEDULES[schedule])
     h = _P()
@@ -204,7 +207,7 @@ def run(handle: int, dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s,
 
 def run_noalloc(dims: dict, x, norm_w, gate_w, bias, w13, w13_s, w2, w2_s, sgu, sgu_s, sw2, sw2_s,
                 out, status, max_tokens: int = MAX_TOKENS, rms_eps: float = 1e-6,
-                routed_scale: float = 1.0, schedule: str = "launches", stream=None) -> None:
+                routed_scale: float = 1.0, schedule: str = "auto", stream=None) -> None:
     """moe_decode_run_noalloc: the step without a plan or any allocation.
     dims as for `run` (plus the layer's hidden..shared_inter); status an
     int32 (or uint32) tensor of one element on the GPU, which the kernels'

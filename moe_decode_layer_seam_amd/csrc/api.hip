@@ -52,8 +52,8 @@ struct moe_decode_plan_s {
   Scratch s{};
   int last_m = 0;
   int last_grid[kKernels] = {};
-  bool boxes_dirty = false;  // a w13 launch that routes ran without the act launch after it
-  bool fused = false;  // MOE_DECODE_SCHEDULE_FUSED
+  bool boxes_dirty = false;  // a launch that routes ran without the launch after it that clears its boxes
+  bool persistent = false;   // the persistent launch serves the steps it covers (checked dispatch)
   bool timeline = false;
   uint64_t* tl_base = nullptr;  // [kKernels][kTlBlocks][kTlPoints]
   std::string err = "no error";
@@ -87,7 +87,9 @@ bool valid_dims(const moe_decode_dims* d) {
   if (!std::isfinite(d->rms_eps) || d->rms_eps < 0.0f) return false;
   if (!std::isfinite(d->routed_scale)) return false;
   if (d->routed_format != MOE_DECODE_ROUTED_E4M3 && d->routed_format != MOE_DECODE_ROUTED_MXFP4) return false;
-  if (d->schedule != MOE_DECODE_SCHEDULE_FUSED && d->schedule != MOE_DECODE_SCHEDULE_LAUNCHES) return false;
+  if (d->schedule != MOE_DECODE_SCHEDULE_AUTO && d->schedule != MOE_DECODE_SCHEDULE_LAUNCHES &&
+      d->schedule != MOE_DECODE_SCHEDULE_PERSISTENT)
+    return false;
   return true;
 }
 
@@ -137,8 +139,9 @@ struct Layout {
 
 // The layout for d.Mx token rows: GEMM sum planes sized for every step
 // width up to d.Mx (one [R(m)][width] fp32 plane, or one per K segment for
-// the widths that run in split mode); `timeline`: room for the stamps.
-Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool timeline) {
+// the widths that run in split mode or in the persistent launch, where
+// `persistent` says it may serve them); `timeline`: room for the stamps.
+Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool timeline, bool persistent) {
   Layout L{};
   const size_t Mx = d.Mx, H = d.H, E = d.E, K = d.K, R = Mx * K + Mx;
   size_t off = 0;
@@ -154,22 +157,24 @@ Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool t
   L.vs = take((size_t)max_vs * 16), L.hdr = take(16);
   L.a8 = take(R * d.Imax), L.a8s = take(R * d.Imax / 32);
   // the hand-off words, zeroed by the seam launch: the route launch's arrival
-  // counter (word 0), from word 64 the fused launch's ready words and act
-  // groups' unit counts, then the boxes of the w13 launch that routes: the
-  // pick box, then (from an even word) the logit box
+  // counter (word 0), the XCC id + 1 seen by the persistent launch's blocks
+  // of each index mod kXcds (words 8..15), from word 64 its ready words (per
+  // slot and XCD) and act groups' unit counts, then the boxes of the
+  // launches that route: the pick box, then (from an even word) the logit box
   L.act_stride = d.Imax / kActCols;
-  L.lbox = (64 + (size_t)max_vs + (size_t)max_vs * L.act_stride + kPickBox + 1) & ~(size_t)1;
+  L.lbox = (64 + (size_t)max_vs * kXcds + (size_t)max_vs * L.act_stride + kPickBox + 1) & ~(size_t)1;
   L.nsync = L.lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   L.sync = take(L.nsync * 4);
   L.status = take(4);
   L.tl = timeline ? take((size_t)kKernels * kTlBlocks * kTlPoints * 8) : 0;
   size_t part13 = 0, part2 = 0;
   const size_t nseg13 = (H / 128 + kSegSteps - 1) / kSegSteps;
-  const size_t nseg2 = (d.Imax / 128 + kSegSteps - 1) / kSegSteps;
+  const size_t nseg2 = (size_t)w2_planes(d);
   for (int mm = 1; mm <= d.Mx; ++mm) {
     const size_t Rm = (size_t)mm * (K + 1);
-    const size_t a = (gemm_split(d, mm, grid13 * gemm_waves(true), true) ? nseg13 : 1) * Rm * 2 * d.Imax * 4;
-    const size_t c = (gemm_split(d, mm, grid2 * gemm_waves(false), false) ? nseg2 : 1) * Rm * H * 4;
+    const bool xcd = persistent && xcd_applies(d, mm, grid13);
+    const size_t a = (xcd || gemm_split(d, mm, grid13 * gemm_waves(true), true) ? nseg13 : 1) * Rm * 2 * d.Imax * 4;
+    const size_t c = (xcd || gemm_split(d, mm, grid2 * gemm_waves(false), false) ? nseg2 : 1) * Rm * H * 4;
     part13 = a > part13 ? a : part13;
     part2 = c > part2 ? c : part2;
   }
@@ -202,7 +207,7 @@ Scratch scratch_at(char* b, const Layout& L, const LayerDims& d, int max_vs) {
   s.counter = s.sync;
   s.status = reinterpret_cast<uint32_t*>(b + L.status);
   s.ready = s.sync + 64;
-  s.act_cnt = s.ready + max_vs;
+  s.act_cnt = s.ready + (size_t)max_vs * kXcds;
   s.pick_box = s.act_cnt + (size_t)max_vs * L.act_stride;
   s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + L.lbox) : nullptr;
   s.nsync = (int)L.nsync;
@@ -225,12 +230,11 @@ LayerDims dims_of(const moe_decode_dims* dims) {
   return d;
 }
 
-// Whether every kernel variant fits a CU once (the expert GEMMs run one
-// block per CU).
-bool fits_cu(const LayerDims& d, int max_vs, bool fused) {
+// Whether every GEMM variant fits a CU once (the expert GEMMs run one block
+// per CU).
+bool fits_cu(const LayerDims& d, int max_vs) {
   return gemm_blocks_per_cu(true, gemm_lds_bytes(d, d.Mx, max_vs, true)) >= 1 &&
-         gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, max_vs, false)) >= 1 &&
-         (!fused || experts_blocks_per_cu(experts_lds_bytes(d, d.Mx, max_vs)) >= 1);
+         gemm_blocks_per_cu(false, gemm_lds_bytes(d, d.Mx, max_vs, false)) >= 1;
 }
 
 // The argument checks of a run (nothing is enqueued when one fails).
@@ -266,15 +270,17 @@ Inputs inputs_of(const void* d_x, const void* d_norm_w, const void* d_gate_w, co
   return in;
 }
 
-// One step's launches on st.  seam_always: launch the seam even where the
-// w13 launch runs it itself (the seam launch zeroes the hand-off words).
-// boxes_dirty (may be null): set while a w13 launch that routes has run
-// without the act launch that clears its boxes.  ts (may be null): the
+// One step's launches on st.  persistent: the persistent launch may serve
+// the step (if it covers it).  seam_always: launch the seam even where a
+// later launch runs it itself (the seam launch zeroes the hand-off words).
+// boxes_dirty (may be null): set while a launch that routes has run
+// without the launch after it that clears its boxes.  ts (may be null): the
 // run's timing events; last_grid (may be null): the launches' grids.
 hipError_t enqueue(const LayerDims& d, int m, const Inputs& in, const Scratch& sc, int grid13, int grid2, int max_vs,
-                   bool fused, bool seam_always, bool* boxes_dirty, TimingSet* ts, int* last_grid, hipStream_t st,
-                   const char** what) {
-  const bool route13 = !fused && route_in_w13(d, m, grid13);
+                   bool persistent, bool seam_always, bool* boxes_dirty, TimingSet* ts, int* last_grid,
+                   hipStream_t st, const char** what) {
+  const bool fused = persistent && xcd_applies(d, m, grid13);
+  const bool route13 = fused || route_in_w13(d, m, grid13);
   const bool seam = !route13 || seam_always || (boxes_dirty && *boxes_dirty);
   if (last_grid) {
     last_grid[0] = seam ? seam_blocks(d, m) : 0;
@@ -298,22 +304,22 @@ hipError_t enqueue(const LayerDims& d, int m, const Inputs& in, const Scratch& s
   if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return *what = "seam launch", e;
   if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
     return *what = "logits launch", e;
-  // the fused launch reads the route launch's plan; the w13 launch of the
-  // launches schedule builds its own from the stored picks
-  if (!route13 && (e = launch_route(d, m, in, sc, fused, st, ev(2))) != hipSuccess)
+  // the launches that route build their own plan from the stored picks
+  if (!route13 && (e = launch_route(d, m, in, sc, false, st, ev(2))) != hipSuccess)
     return *what = "route launch", e;
+  if (route13 && boxes_dirty) *boxes_dirty = true;
   if (fused) {
-    if ((e = launch_experts(d, m, in, sc, grid13, max_vs, st, ev(7))) != hipSuccess)
-      return *what = "experts launch", e;
+    if ((e = launch_xcd(d, m, in, sc, grid13, max_vs, st, ev(7))) != hipSuccess)
+      return *what = "persistent launch", e;
   } else {
-    if (route13 && boxes_dirty) *boxes_dirty = true;
     if ((e = launch_w13(d, m, in, sc, grid13, max_vs, route13, st, ev(3))) != hipSuccess)
       return *what = "w13 launch", e;
     if ((e = launch_act(d, m, sc, grid13, st, ev(4))) != hipSuccess) return *what = "act launch", e;
     if (boxes_dirty) *boxes_dirty = false;
     if ((e = launch_w2(d, m, in, sc, grid2, max_vs, st, ev(5))) != hipSuccess) return *what = "w2 launch", e;
   }
-  if ((e = launch_combine(d, m, in, sc, grid2, st, ev(6))) != hipSuccess) return *what = "combine launch", e;
+  if ((e = launch_combine(d, m, in, sc, grid2, fused, st, ev(6))) != hipSuccess) return *what = "combine launch", e;
+  if (fused && boxes_dirty) *boxes_dirty = false;
   return hipSuccess;
 }
 
@@ -353,7 +359,6 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   if (!p) return MOE_DECODE_ENOMEM;
   LayerDims& d = p->d;
   d = dims_of(dims);
-  p->fused = dims->schedule == MOE_DECODE_SCHEDULE_FUSED;
   p->max_vs = max_vslots(d.Mx, d.E, d.K);
   p->R = d.Mx * d.K + d.Mx;
 
@@ -367,13 +372,14 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
     delete p;
     return rc;
   }
-  if (!fits_cu(d, p->max_vs, p->fused)) {
+  if (!fits_cu(d, p->max_vs)) {
     p->err = g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
     delete p;
     return MOE_DECODE_EINVAL;
   }
   p->grid13 = p->grid2 = p->cus;
-  const Layout L = make_layout(d, p->max_vs, p->grid13, p->grid2, true);
+  const Layout L = make_layout(d, p->max_vs, p->grid13, p->grid2, true,
+                               dims->schedule == MOE_DECODE_SCHEDULE_PERSISTENT);
   p->bytes = L.bytes;
   if ((e = hipMalloc(&p->base, p->bytes)) != hipSuccess) {
     hip_fail(p, e, "hipMalloc");
@@ -389,6 +395,31 @@ int moe_decode_plan(const moe_decode_dims* dims, void* stream, moe_decode_handle
   char* b = static_cast<char*>(p->base);
   p->s = scratch_at(b, L, d, p->max_vs);
   p->tl_base = reinterpret_cast<uint64_t*>(b + L.tl);
+  // the persistent launch serves the steps it covers if its blocks fit a CU
+  // and the device deals a launch's blocks to the XCDs round-robin, from
+  // whichever XCD the previous launch left off at (checked here with a probe
+  // launch that stores each block's XCC id into the scratch, then zeroed
+  // again): then the blocks with one index mod kXcds share an XCD
+  if (dims->schedule == MOE_DECODE_SCHEDULE_PERSISTENT && p->grid13 % kXcds == 0 && p->grid13 <= 4096 &&
+      xcd_blocks_per_cu(xcd_lds_bytes(d, d.Mx < kRouteRows ? d.Mx : kRouteRows, p->max_vs)) >= 1 &&
+      p->bytes >= (size_t)p->grid13 * 4) {
+    std::vector<uint32_t> ids((size_t)p->grid13);
+    uint32_t* dev_ids = reinterpret_cast<uint32_t*>(b);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((e = probe_xcc(p->grid13, dev_ids, st)) != hipSuccess ||
+        (e = hipMemcpyAsync(ids.data(), dev_ids, ids.size() * 4, hipMemcpyDeviceToHost, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess ||
+        (e = hipMemsetAsync(dev_ids, 0, ids.size() * 4, st)) != hipSuccess ||
+        (e = hipStreamSynchronize(st)) != hipSuccess) {
+      int rc = hip_fail(p, e, "dispatch probe");
+      (void)hipFree(p->base);
+      delete p;
+      return rc;
+    }
+    bool rr = true;
+    for (size_t i = 0; i < ids.size(); ++i) rr = rr && ids[i] == (ids[0] + (uint32_t)i) % kXcds;
+    p->persistent = rr;
+  }
   *out = p;
   return MOE_DECODE_OK;
 }
@@ -429,7 +460,7 @@ int moe_decode_run(moe_decode_handle p, int32_t m, const void* d_x, const void* 
     sc.tl_experts = tl[7];
   }
   const char* what = "";
-  hipError_t e = enqueue(d, m, in, sc, p->grid13, p->grid2, p->max_vs, p->fused, false, &p->boxes_dirty, ts,
+  hipError_t e = enqueue(d, m, in, sc, p->grid13, p->grid2, p->max_vs, p->persistent, false, &p->boxes_dirty, ts,
                          p->last_grid, st, &what);
   if (e != hipSuccess) return hip_fail(p, e, what);
   p->last_m = m;
@@ -457,7 +488,6 @@ int moe_decode_run_noalloc(const moe_decode_dims* dims, int32_t m, const void* d
   }
   // this step's layout only: its rows, not max_tokens'
   d.Mx = m;
-  const bool fused = dims->schedule == MOE_DECODE_SCHEDULE_FUSED;
   const int max_vs = max_vslots(d.Mx, d.E, d.K);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -482,11 +512,11 @@ int moe_decode_run_noalloc(const moe_decode_dims* dims, int32_t m, const void* d
     }
     nd = g_noalloc[dev];
   }
-  if (!fits_cu(d, max_vs, fused)) {
+  if (!fits_cu(d, max_vs)) {
     g_last_error = "the expert GEMM blocks do not fit a CU for these dimensions";
     return MOE_DECODE_EINVAL;
   }
-  const Layout L = make_layout(d, max_vs, nd.cus, nd.cus, false);
+  const Layout L = make_layout(d, max_vs, nd.cus, nd.cus, false, false);
   if (L.bytes > kNoAllocBytes) {
     g_last_error = "the step's scratch exceeds MOE_DECODE_NOALLOC_SCRATCH_BYTES";
     return MOE_DECODE_EINVAL;
@@ -496,9 +526,12 @@ int moe_decode_run_noalloc(const moe_decode_dims* dims, int32_t m, const void* d
   const Inputs in = inputs_of(d_x, d_norm_w, d_gate_w, d_bias, d_w13, d_w13_s, d_w2, d_w2_s, d_sgu, d_sgu_s, d_sw2,
                               d_sw2_s, d_out);
   // the seam launch runs in every step: it zeroes the hand-off words, which
-  // the array holds from whatever call used it last
+  // the array holds from whatever call used it last.  The short launches
+  // serve every step here: the persistent launch needs the dispatch check a
+  // plan makes (which synchronises, and may not run under capture); a
+  // token's output bits are the same either way.
   const char* what = "";
-  e = enqueue(d, m, in, sc, nd.cus, nd.cus, max_vs, fused, true, nullptr, nullptr, nullptr,
+  e = enqueue(d, m, in, sc, nd.cus, nd.cus, max_vs, false, true, nullptr, nullptr, nullptr,
               static_cast<hipStream_t>(stream), &what);
   if (e != hipSuccess) return hip_fail(nullptr, e, what);
   return MOE_DECODE_OK;

@@ -41,6 +41,7 @@ namespace {
 struct Geo {
   int tiles;  // 16-row weight tiles
   int K;      // bytes per weight row (the contraction length)
+  int seg;    // K steps per segment
   int nseg;   // K segments
 };
 
@@ -50,7 +51,8 @@ __device__ __forceinline__ Geo geo(const LayerDims& d, bool shared) {
   Geo g;
   g.tiles = W13 ? 2 * Kv / 16 : d.H / 16;
   g.K = W13 ? d.H : Kv;
-  g.nseg = (g.K / 128 + kSegSteps - 1) / kSegSteps;
+  g.seg = W13 ? kSegSteps : w2_seg_steps(Kv, !shared && d.rfmt == MOE_DECODE_ROUTED_MXFP4);
+  g.nseg = (g.K / 128 + g.seg - 1) / g.seg;
   return g;
 }
 
@@ -74,7 +76,7 @@ struct Step {
 struct UnitOps {
   rsrc_t w, ws, a, as;
   uint32_t wsoff, wlane, row8, tstride, ssoff, sstride, slane, alane, aslane;
-  int row0, c, col0, nsteps;
+  int row0, c, col0, nsteps, seg;
   int fp4;  // weights as E2M1 pairs with per-row 32-column codes, blocked
 };
 
@@ -109,6 +111,7 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
   u.c = slot.z;
   u.col0 = 16 * TT * tgroup;
   u.nsteps = G.K / 128;
+  u.seg = G.seg;
   u.w = make_rsrc(W, (uint32_t)N * rowb);
   u.ws = make_rsrc(WS, u.fp4 ? (uint32_t)G.tiles * G.nseg * 256 : (uint32_t)(N / 32) * (G.K / 32));
   u.wsoff = (uint32_t)u.col0 * rowb;
@@ -166,22 +169,23 @@ __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st)
     const uint32_t ao = ok ? u.alane + kw : kNoRow;
     f.alo = bload16a<AUX>(u.a, ao, 0);
     f.ahi = bload16a<AUX>(u.a, ao + 64, 0);
-    f.sa = bload8a<AUX>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+    f.sa = bload8a<code_aux(AUX)>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
   }
 }
 
-// One segment's sums for the TT tiles, in bursts of BS K steps: a burst's
-// loads are all issued before its first MFMA.  Each tile's MFMAs run in K
-// order whatever BS is.
-template <int TT, int BS, int AUX, bool ALDS>
+// One segment's sums for the TT tiles (SEG K steps), in bursts of BS K
+// steps: a burst's loads are all issued before its first MFMA.  Each tile's
+// MFMAs run in K order whatever BS is.
+template <int TT, int BS, int AUX, bool ALDS, int SEG>
 __device__ __forceinline__ void segment_sum(v4f (&acc)[TT], const UnitOps& u, int seg) {
+  static_assert(SEG % BS == 0, "bursts tile the segment");
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int b0 = 0; b0 < kSegSteps; b0 += BS) {
+  for (int b0 = 0; b0 < SEG; b0 += BS) {
     Step<TT> f[BS];
 #pragma unroll
-    for (int q = 0; q < BS; ++q) load_step<TT, AUX, ALDS>(f[q], u, seg * kSegSteps + b0 + q);
+    for (int q = 0; q < BS; ++q) load_step<TT, AUX, ALDS>(f[q], u, seg * SEG + b0 + q);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < BS; ++q) {
@@ -229,7 +233,7 @@ __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int
   if constexpr (ALDS)
     c.a = ok && u.aslane != kNoRow ? lds32(u.aslane - g + 16 * seg + 4 * g) : 0u;
   else
-    c.a = bload32a<AUX>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
+    c.a = bload32a<code_aux(AUX)>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
 }
 
 template <int TT>
@@ -295,11 +299,28 @@ __device__ __forceinline__ void segment_sum_fp4(v4f (&acc)[TT], const UnitOps& u
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// E4M3 weights: the segment sums of [s0, s1) added in segment order.  BSO:
+// K steps per load burst (0: 2 for 8-tile units, else the whole segment).
+template <int TT, int AUX, bool ALDS, int SEG, int BSO>
+__device__ __forceinline__ void unit_sums_e4m3(v4f (&tot)[TT], const UnitOps& ops, int s0, int s1) {
+  constexpr int BS = BSO ? BSO : TT >= 8 ? 2 : SEG;  // K steps per load burst
+  segment_sum<TT, BS, AUX, ALDS, SEG>(tot, ops, s0);
+  for (int sg = s0 + 1; sg < s1; ++sg) {
+    v4f p[TT];
+    segment_sum<TT, BS, AUX, ALDS, SEG>(p, ops, sg);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
+  }
+}
+
 // The unit's sums over its segments [s0, s1), added in segment order; each
-// segment's sum starts from zero.
-template <int TT, int AUX, bool ALDS = false>
+// segment's sum starts from zero.  BSO: the E4M3 load burst (K steps; 0: by
+// tile count).  The burst only sets how many loads are in flight: each
+// tile's MFMAs run in K order whatever it is, so the sums do not change.
+template <int TT, int AUX, bool ALDS = false, int BSO = 0>
 __device__ __forceinline__ void unit_sums(v4f (&tot)[TT], const UnitOps& ops, int s0, int s1, int g, int j) {
-  constexpr int BS = TT >= 8 ? 2 : kSegSteps;  // K steps per load burst
   if (ops.fp4) {
     segment_sum_fp4<TT, AUX, ALDS>(tot, ops, s0, g, j);
     for (int sg = s0 + 1; sg < s1; ++sg) {
@@ -310,16 +331,10 @@ __device__ __forceinline__ void unit_sums(v4f (&tot)[TT], const UnitOps& ops, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
     }
+  } else if (ops.seg == 2) {
+    unit_sums_e4m3<TT, AUX, ALDS, 2, BSO>(tot, ops, s0, s1);
   } else {
-    segment_sum<TT, BS, AUX, ALDS>(tot, ops, s0);
-    for (int sg = s0 + 1; sg < s1; ++sg) {
-      v4f p[TT];
-      segment_sum<TT, BS, AUX, ALDS>(p, ops, sg);
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tot[t][q] = tot[t][q] + p[t][q];
-    }
+    unit_sums_e4m3<TT, AUX, ALDS, kSegSteps, BSO>(tot, ops, s0, s1);
   }
 }
 
@@ -387,7 +402,6 @@ __device__ __forceinline__ void unit_decode(const UnitMap& um, uint32_t u, int& 
 __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B, uint32_t b) {
   return i * B + ((i & 1u) ? B - 1u - b : b);
 }
-__device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B) { return unit_turn(i, B, blockIdx.x); }
 
 // Longest wait for the plan before the run is flagged (status) and the wave
 // goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
@@ -399,8 +413,9 @@ constexpr uint64_t kPlanWaitTicks = 10000000ull;
 // carries the tag, then sorts the picks into the plan's rows (small_rows:
 // the same rows and slots as the router's plan).  On a timeout the status
 // word is set and no routed slot is staged.
+// s_out (may be null): also each routed row's w2 output row, its pair.
 __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap,
-                           int* s_plan, int* s_nvs, int lane) {
+                           int* s_plan, int* s_nvs, int lane, int* s_out = nullptr) {
   int st = 0;
   if (lane == 0) st = atomicCAS(s_plan, 0, 1);
   st = __builtin_amdgcn_readfirstlane(st);
@@ -424,6 +439,7 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
     const SmallRows q = small_rows((int)(w & 0x3FFu), n, d.K, lane);
     const int nR = min(q.nR, vs_cap - nS);
     if (q.valid) s_tok[lane] = q.t;
+    if (q.valid && s_out) s_out[lane] = q.p;
     if (q.first && q.ri < nR) s_vs[nS + q.ri] = make_int4(q.e, lane, q.cnt, 0);
     if (lane == 0) *s_nvs = nS + nR;
     wait_memory();  // the LDS writes are done
@@ -669,6 +685,25 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   stamp(tl, kTlPoints, 1);
 }
 
+// a = SiLU(gate) * up of row r, column col (one lane each, 32 consecutive
+// columns in 32 consecutive lanes), and its MXFP8: the code of the 32
+// columns' amax, the byte of a scaled by 2^(127 - code).  THROUGH: the code
+// is written through to memory (read back with code_aux(kScL2)).
+template <bool THROUGH = false>
+__device__ __forceinline__ void act_store(const LayerDims& d, const Scratch& s, int r, int col, float hg, float hu) {
+  const float a = hg / (1.0f + __expf(-hg)) * hu;
+  const float amax = group_max(fabsf(a), 32);
+  const int code = e8m0_code(amax);
+  s.a8[(size_t)r * d.Imax + col] = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
+  if ((col & 31) == 0) {
+    uint8_t* cp = s.a8s + (size_t)r * (d.Imax / 32) + col / 32;
+    if constexpr (THROUGH)
+      __hip_atomic_store(cp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *cp = (uint8_t)code;
+  }
+}
+
 // SiLU(gate) * up of row r (blockIdx.y), columns blockIdx.x * 256 + tid, and
 // the MXFP8 of each 32 columns (one lane group of 32 per code).  The NSEG
 // bound makes every load unconditional (planes past the run's count are read
@@ -702,11 +737,7 @@ __global__ __launch_bounds__(kThreads) void act_kernel(LayerDims d, Scratch s, i
     hg = sg < nseg ? hg + vg[sg] : hg;
     hu = sg < nseg ? hu + vu[sg] : hu;
   }
-  const float a = hg / (1.0f + __expf(-hg)) * hu;
-  const float amax = group_max(fabsf(a), 32);
-  const int code = e8m0_code(amax);
-  s.a8[(size_t)r * d.Imax + c] = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
-  if ((c & 31) == 0) s.a8s[(size_t)r * (d.Imax / 32) + c / 32] = (uint8_t)code;
+  act_store(d, s, r, c, hg, hu);
   stamp(s.tl_act, kTlPoints, 1);
 }
 
@@ -731,15 +762,25 @@ __device__ __forceinline__ float row_sum(const float* p, size_t plane, int nseg)
 // NSEG bounds the run's segment counts; every load is unconditional (picks
 // past k and planes past the count re-read valid addresses and are not
 // added), so a lane's loads are all in flight at once.
+// clear: also zero the hand-off words of the persistent launch (from word 1
+// of the sync region: XCC ids, ready words, act counts, the boxes) for the
+// next step; word 0, the route blocks' arrival counter, resets itself.
 template <int NSEG>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, Inputs in, Scratch s, int m,
-                                                                  int split) {
+                                                                  int split, int clear) {
   const int t = blockIdx.y, n = blockIdx.x * kCombineThreads + threadIdx.x;
   stamp(s.tl_combine, kTlPoints, 0);
+  if (clear) {
+    const uint32_t nthr = gridDim.x * gridDim.y * kCombineThreads;
+    for (uint32_t w = 1 + (blockIdx.y * gridDim.x + blockIdx.x) * kCombineThreads + threadIdx.x;
+         w < (uint32_t)s.nsync; w += nthr)
+      s.sync[w] = 0u;
+  }
   if (n >= d.H) return;
   const int P = m * d.K;
-  const int nseg_r = split ? (d.I / 128 + kSegSteps - 1) / kSegSteps : 1;
-  const int nseg_s = split ? (d.Is / 128 + kSegSteps - 1) / kSegSteps : 1;
+  const int seg_r = w2_seg_steps(d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), seg_s = w2_seg_steps(d.Is, false);
+  const int nseg_r = split ? (d.I / 128 + seg_r - 1) / seg_r : 1;
+  const int nseg_s = split ? (d.Is / 128 + seg_s - 1) / seg_s : 1;
   const size_t plane = (size_t)(m * d.K + m) * d.H;
   const float ysh = row_sum<NSEG>(s.part2 + (size_t)(P + t) * d.H + n, plane, nseg_s);
   float acc = 0.0f;
@@ -759,74 +800,92 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, I
   stamp(s.tl_combine, kTlPoints, 1);
 }
 
+// Tiles per unit and waves per block (one block per CU) of each GEMM and
+// mode.  More tiles per unit share one activation fragment among more weight
+// tiles and keep more weight bytes in flight per wave; fewer tiles give more
+// units to balance at small m.  Each tile's sums are the same whichever
+// variant runs it.  Whole-mode w13 units take 4 tiles: a block's 25-26
+// units of 8 tiles (655 KB each at H = 5120) left one wave streaming the
+// last unit alone for up to 40 us after its block's other waves ended.
+// Split-mode w2 units take 8 tiles where a w2 segment is 2 K steps, so a
+// unit still streams 32 KB.
+constexpr int kTT13 = 4;       // w13 units, both modes
+constexpr int kTT2Whole = 8;   // whole-mode w2 units
+constexpr int kTT2Split = 4;   // split-mode w2 units over 4-step segments
+constexpr int kGemmWaves = 8;  // waves per block of either GEMM
+// K steps per load burst of the persistent launch's units (w13, w2): 16 KB
+// a wave.  Its hand-offs make round trips through the memory queues that the
+// weight stream fills; smaller bursts keep those queues short.
+constexpr int kXcdBurst13 = 2;
+constexpr int kXcdBurst2 = 1;
+
 // ===========================================================================
-// The fused expert launch: w13, act and w2 in one grid of one block per CU.
+// The persistent launch of a step of at most kRouteRows tokens: the seam,
+// the router, w13, SiLU * up and w2 in one launch of one block per CU, cut by
+// XCD.  The dispatcher deals a launch's blocks to the XCDs round-robin
+// (from where the previous launch left off), so the blocks with index x mod
+// kXcds share one XCD: the plan checks that on the device, and each block
+// checks it against the others.  Those blocks take slice x of every active
+// expert's intermediate: gate rows [x S, (x + 1) S) and up rows
+// [Kv + x S, ...) of w13 (S = Kv / kXcds), and the same S columns of w2.
+// So each hand-off of an expert -- its w13 sums to its SiLU * up, its a8 to
+// its w2 units -- stays inside one XCD's L2, which every CU of the XCD
+// shares: the sums and a8 are stored and completed (written through to the
+// L2) and counted by atomics performed there (no sc1); the counts are read
+// by atomics too, and the data (sc0) only by CUs that have not read those
+// lines before in the launch, so their own caches hold no copy of them.  A
+// hand-off through device memory would
+// queue behind the weight stream; one through the L2 does not.  Nothing
+// crosses XCDs until the launch ends: the combine launch adds the slices'
+// w2 sums (plane x holds slice x) in slice order, which is the w2 segment
+// order of every other step width (w2 segments are S = 256 columns here).
 //
-// Units are numbered w13 first, then w2, and dealt to the blocks as in the
-// separate GEMMs; a block's waves take its units in increasing order.  The
-// act of a slot is split into groups of 64 columns of a; the w13 unit that
-// completes a group (a device-scope count of its units) computes that
-// group's a8 and counts it on the slot's ready word, and a w2 unit waits
-// for the ready word of its slot before it loads a8.  No w13 unit waits, and
-// a wave holds at most w2 units while it waits, so with every block resident
-// the waits always end.  The w13 sums and a8 cross CUs with the coherent
-// policy; a unit's sums are counted when the wave's next unit is done (its
-// stores are complete by then, so counting them costs no wait), or before a
-// w2 unit.  Each tile, act group and output is computed with the same
-// arithmetic, in the same order, as by the separate launches.
+// The units of an XCD are dealt over its blocks (the m route blocks, rank 0
+// of XCDs 0..m-1, take none) in this order: the shared expert's w13 (tile
+// groups of 64 rows in the slice, times the H segments), then, once the
+// picks are in, every routed slot's w13, the shared expert's w2 (tile
+// groups of 128 output rows over the slice) and every routed slot's w2.
+// The w13 unit that completes the count of an act group (64 columns: a
+// gate and an up tile group, every H segment) computes the group's a8 from
+// the summed planes with the act launch's arithmetic and counts the group
+// on its slot's ready word for the XCD; a w2 unit waits until that word
+// holds the slice's groups (one wave of a block polls, wait_slot).  A wave
+// counts a w13 unit once its next unit's loads have returned (its stores
+// are complete by then, so the count waits for nothing but the atomic), and
+// always before it waits itself; a block's waves take its units in deal
+// order.  So with every block resident each wait ends.
 // ===========================================================================
 
-// Longest wait for a slot's a8 before the run is flagged (status) and the
-// wave goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
-constexpr uint64_t kWaitTicks = 10000000ull;
-
-// SiLU(gate) * up of act group q of a slot (columns [64 q, +64) of a, lane =
-// column) for its c rows from row0, from the w13 sums of nseg planes added in
-// plane order, then MXFP8 of each 32 columns: act_kernel's arithmetic.
-__device__ __forceinline__ void finish_row(const LayerDims& d, const Scratch& s, int r, int col, int lane,
-                                           float hg, float hu) {
-  const float a = hg / (1.0f + __expf(-hg)) * hu;
-  const float amax = group_max(fabsf(a), 32);
-  const int code = e8m0_code(amax);
-  const uint8_t byte = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
-  __hip_atomic_store(&s.a8[(size_t)r * d.Imax + col], byte, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((lane & 31) == 0)
-    __hip_atomic_store(&s.a8s[(size_t)r * (d.Imax / 32) + col / 32], (uint8_t)code, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float ld_l2(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kScL2));
 }
 
-__device__ void finish_act(const LayerDims& d, const Scratch& s, int m, int row0, int c, int Kv, int q, int nseg,
-                           int lane) {
-  const size_t width = 2 * (size_t)d.Imax;
-  const size_t plane = (size_t)(m * d.K + m) * width;
+// Counts w13 unit (slot v, act group q) on the XCD's L2; the unit that
+// completes the group computes its a8 (rows of the slot, 64 columns, lane =
+// column) and counts the group on ready word v * kXcds + x.
+__device__ void count_w13(const LayerDims& d, const Scratch& s, int m, const int4& slot, int v, int q, int x,
+                          uint32_t expect, int nseg, int lane) {
+  uint32_t old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(&s.act_cnt[(size_t)v * s.act_stride + q], 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+  if (old + 1u != expect) return;
+  const int Kv = slot.x < 0 ? d.Is : d.I;
+  const uint32_t width = 2u * (uint32_t)d.Imax;
+  const uint32_t plane = (uint32_t)(m * d.K + m) * width;
+  const rsrc_t pr = make_rsrc(s.part13, (uint32_t)nseg * plane * 4u);
   const int col = kActCols * q + lane;
-  if (nseg == 1) {
-    // whole-mode sums: one plane; eight rows' loads in flight at once
-    for (int i0 = 0; i0 < c; i0 += 8) {
-      float vg[8], vu[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k < c ? i0 + k : c - 1;
-        const float* p = s.part13 + (size_t)(row0 + i) * width + col;
-        vg[k] = load_coherent(p);
-        vu[k] = load_coherent(p + Kv);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (i0 + k < c) finish_row(d, s, row0 + i0 + k, col, lane, vg[k], vu[k]);
-    }
-    return;
-  }
-  for (int i = 0; i < c; ++i) {
-    const float* p = s.part13 + (size_t)(row0 + i) * width + col;
+  for (int i = 0; i < slot.z; ++i) {
+    const uint32_t o = ((uint32_t)(slot.y + i) * width + (uint32_t)col) * 4u;
+    float vg[16], vu[16];
     float hg = 0.0f, hu = 0.0f;
     for (int s0 = 0; s0 < nseg; s0 += 16) {
-      float vg[16], vu[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int sg = s0 + k < nseg ? s0 + k : nseg - 1;
-        vg[k] = load_coherent(p + (size_t)sg * plane);
-        vu[k] = load_coherent(p + (size_t)sg * plane + Kv);
+        vg[k] = ld_l2(pr, o + (uint32_t)sg * plane * 4u);
+        vu[k] = ld_l2(pr, o + ((uint32_t)sg * plane + (uint32_t)Kv) * 4u);
       }
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -836,176 +895,251 @@ __device__ void finish_act(const LayerDims& d, const Scratch& s, int m, int row0
         }
       }
     }
-    finish_row(d, s, row0 + i, col, lane, hg, hu);
+    act_store<true>(d, s, slot.y + i, col, hg, hu);
   }
+  wait_memory();  // the a8 bytes are in the L2, the codes in memory
+  if (lane == 0)
+    (void)__hip_atomic_fetch_add(&s.ready[(size_t)v * kXcds + x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Counts w13 unit (slot v, tile group tg) on the act groups its rows belong
-// to; the unit that completes a group computes it and counts it on the
-// slot's ready word.  The unit's sums must be stored and complete.
-template <int TT13>
-__device__ __forceinline__ void arrive13(const LayerDims& d, const Scratch& s, int m, const int4& slot, int v, int tg,
-                                         uint32_t expect, int nseg, int lane) {
-  constexpr int G = TT13 * 16 / kActCols;  // act groups per tile group
-  const int Kv = slot.x < 0 ? d.Is : d.I;
-  int r0 = 16 * TT13 * tg;
-  if (r0 >= Kv) r0 -= Kv;  // up rows: the same columns of a as the gate rows
-  const int q0 = r0 / kActCols;
-  uint32_t old[G];
-#pragma unroll
-  for (int k = 0; k < G; ++k) old[k] = 0;
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < G; ++k) old[k] = count_arrival(&s.act_cnt[(size_t)v * s.act_stride + q0 + k]);
-  }
-#pragma unroll
-  for (int k = 0; k < G; ++k) {
-    if ((uint32_t)__builtin_amdgcn_readlane((int)old[k], 0) + 1u == expect) {
-      finish_act(d, s, m, slot.y, slot.z, Kv, q0 + k, nseg, lane);
-      wait_memory();
-      if (lane == 0) (void)count_arrival(&s.ready[v]);
-    }
-  }
+// The count in a ready word, read in the XCD's L2.  A load, even at
+// workgroup scope, may be served by this CU's own cache, which would keep
+// the first value it saw; an atomic is performed in the L2.  An atomic that
+// changes nothing (adding 0) is compiled into a load, so the read sets bit
+// 31, which the counts (a slice's act groups) never reach, and masks it
+// off.  The combine launch zeroes the words for the next step.
+constexpr uint32_t kPeekBit = 0x80000000u;
+__device__ __forceinline__ uint32_t peek_l2(uint32_t* p) {
+  return __hip_atomic_fetch_or(p, kPeekBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & ~kPeekBit;
 }
 
-// Waits until slot v's ready word reaches want (seen: a value read earlier).
-__device__ __forceinline__ void wait_ready(const Scratch& s, int v, uint32_t want, uint32_t seen, int lane) {
-  if (seen >= want) return;
+// The slots whose a8 slice this XCD has completed, as seen by a block: one
+// bit per slot in the block's LDS.  A wave that needs slot v and finds its
+// bit clear takes the block's poll lock (the others sleep and re-read the
+// mask), then reads every slot's ready word at once (lane = slot) until
+// slot v's is complete, publishing each poll's mask.  So a block puts one
+// wave's reads on the L2, not one per waiting wave: a few hundred waves
+// spinning on one word would queue behind each other there, and hold up
+// the counts and the a8 that end the wait.  Counts only grow, so a mask
+// never loses a bit.  100 ms bound: then the status word is flagged and the
+// bit set, and the waves go on.
+struct SlotWait {
+  uint64_t* mask;   // LDS: slots complete on this XCD
+  uint32_t* lock;   // LDS: 1 while a wave of the block polls
+  int nvs, x;
+  uint32_t want_s, want_r;  // act groups of a slice: shared slot 0, routed
+};
+
+__device__ void wait_slot(const Scratch& s, const SlotWait& w, int v, int lane) {
+  const uint64_t bit = 1ull << v;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    __builtin_amdgcn_s_sleep(1);
-    const uint32_t now = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(&s.ready[v]));
-    if (now >= want) return;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+  while (!(__hip_atomic_load(w.mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & bit)) {
+    uint32_t got = 0;
+    if (lane == 0)
+      got = __hip_atomic_exchange(w.lock, 1u, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u ? 1u : 0u;
+    if (__builtin_amdgcn_readfirstlane((int)got)) {
+      while (true) {
+        uint32_t c = 0;
+        if (lane < w.nvs) c = peek_l2(&s.ready[(size_t)lane * kXcds + w.x]);
+        const uint64_t in = __ballot(lane < w.nvs && c >= (lane == 0 ? w.want_s : w.want_r));
+        bool done = (in & bit) != 0ull;
+        if (!done && __builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
+          if (lane == 0) flag_status(s.status, kStatusA8Wait);
+          done = true;
+        }
+        if (lane == 0)
+          (void)__hip_atomic_fetch_or(w.mask, done ? (in | bit) : in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (done) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) __hip_atomic_store(w.lock, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(4);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * kPlanWaitTicks) {
       if (lane == 0) flag_status(s.status, kStatusA8Wait);
       return;
     }
   }
 }
 
-template <int TT13, int TT2, int NW>
+template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
-void experts_kernel(LayerDims d, Inputs in, Scratch s, int m, int split13, int split2) {
+void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
+  constexpr int TT13 = kTT13, TT2 = 8;
   unsigned char* lds_raw = dyn_lds;
-  __shared__ uint32_t s_next;
+  __shared__ uint32_t s_next, s_plock;
+  __shared__ uint64_t s_ready;
+  __shared__ int s_plan, s_nvs;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
   stamp(s.tl_experts, kTlPoints, 0);
-  const UnitMap um13 = unit_map<true, TT13>(d, s, split13);
-  const UnitMap um2 = unit_map<false, TT2>(d, s, split2);
-  const int R = m * d.K + m;
-  int4* s_vs = reinterpret_cast<int4*>(lds_raw);
-  int* s_tok = reinterpret_cast<int*>(s_vs + um13.nvs);  // row -> token (w13's activation rows)
-  int* s_out = s_tok + R;                                 // row -> the row of its w2 sums
-  for (int i = tid; i < um13.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
-  for (int i = tid; i < R; i += NW * 64) {
-    s_tok[i] = s.row_tok[i];
-    s_out[i] = s.row_out[i];
+  const int b = blockIdx.x, x = b % kXcds, rank = b / kXcds;
+  if (tid == 0) {
+    // every block with index x mod kXcds must run on one XCD: the first of
+    // them records its XCC id, the others compare
+    const uint32_t id = (__builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xF) + 1u;
+    uint32_t prev = 0;
+    if (!__hip_atomic_compare_exchange_strong(&s.sync[8 + x], &prev, id, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) &&
+        prev != id)
+      flag_status(s.status, kStatusXcdMap);
   }
-  if (tid == 0) s_next = 0;
+  const int R = m * d.K + m, P = m * d.K;
+  // LDS: the slots, row -> token, row -> w2 output row, then the MXFP8 rows
+  const uint32_t x8o = ((uint32_t)vs_cap * 16 + (uint32_t)R * 8 + 15u) & ~15u;
+  const uint32_t xso = x8o + (uint32_t)(m * d.H);
+  seam_rows(d, m, in, s, x8o, xso);
+  stamp(s.tl_experts, kTlPoints, 2);
+  if (b < m) {
+    __shared__ RouteLds L;
+    (void)route_block<1>(d, m, b, m, in.bias, s, L, s.pick_box, s.logit_box);
+    return;
+  }
+  int4* s_vs = reinterpret_cast<int4*>(lds_raw);
+  int* s_tok = reinterpret_cast<int*>(s_vs + vs_cap);
+  int* s_out = s_tok + R;
+  constexpr int nS = 1;  // m <= kRouteRows rows: one shared slot
+  if (tid == 0) {
+    s_vs[0] = make_int4(-1, P, m, 0);
+    s_plan = 0;
+    s_next = 0;
+    s_plock = 0;
+    s_ready = 0;
+  }
+  if (tid < m) {
+    s_tok[P + tid] = tid;
+    s_out[P + tid] = P + tid;
+  }
   __syncthreads();
 
-  const int nseg13 = split13 ? um13.nseg_r : 1;  // w13's K is H for every slot
-  const uint32_t expect = 2u * (uint32_t)nseg13;  // gate and up units per act group
-  const size_t width13 = 2 * (size_t)d.Imax, plane13 = (size_t)R * width13;
-  const size_t plane2 = (size_t)R * d.H;
-  const uint32_t n13 = um13.total, total = n13 + um2.total;
-  const uint32_t B = gridDim.x, turns = (total + B - 1) / B;
-  int pv = -1, ptg = 0;  // the w13 unit whose sums are stored but not yet counted
-  uint32_t seen = 0;     // the ready word of this unit's slot, read during the previous unit
+  // this block's share of its XCD's units
+  const int r0 = x < m ? 1 : 0;
+  const uint32_t Bw = (uint32_t)(gridDim.x / kXcds - r0), rw = (uint32_t)(rank - r0);
+  const int Ss = d.Is / kXcds, Sr = d.I / kXcds;
+  const int nseg13 = (d.H / 128 + kSegSteps - 1) / kSegSteps;
+  const uint32_t u13s = (uint32_t)(2 * Ss / 64 * nseg13), u13r = (uint32_t)(2 * Sr / 64 * nseg13);
+  const uint32_t u2 = (uint32_t)(d.H / (16 * TT2));
+  const uint32_t expect13 = 2u * (uint32_t)nseg13;
+  // turns: the shared w13 units (phase A), then, once the picks are in, one
+  // list of every routed w13 unit (C), the shared w2 units (B) and the
+  // routed w2 units (D), slot by slot.  Each w2 unit comes after every w13
+  // unit of the XCD has been dealt, so by the time a wave takes it the
+  // slot's a8 is mostly complete: the shared expert's long before, the
+  // first routed slots a whole turn of the XCD's waves earlier.
+  const uint32_t tA = (u13s + Bw - 1) / Bw;
+  uint32_t nC = 0, nPost = 0, tP = 0;
+  bool planned = false;
+  const uint32_t width13 = 2u * (uint32_t)d.Imax;
+  const size_t plane13 = (size_t)R * width13, plane2 = (size_t)R * d.H;
+  SlotWait sw{&s_ready, &s_plock, 0, x, (uint32_t)(Ss / 64), (uint32_t)(Sr / 64)};
+  int pend_v = -1, pend_q = 0;  // a w13 unit whose sums are stored but not yet counted
   uint32_t i = wave;
-  while (i < turns) {
-    const uint32_t u = unit_turn(i, B);
-    if (u >= total) break;  // the last turn has no unit for this block
+  while (true) {
+    int ph;
+    uint32_t u, units;
+    if (i < tA) {
+      ph = 0, u = unit_turn(i, Bw, rw), units = u13s;
+    } else {
+      if (!planned) {
+        // the routed units need the picks: count first, then wait
+        if (pend_v >= 0) {
+          wait_memory();
+          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
+          pend_v = -1;
+        }
+        stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out);
+        const int nvs = __builtin_amdgcn_readfirstlane(s_nvs);
+        sw.nvs = nvs;
+        nC = (uint32_t)(nvs - nS) * u13r;
+        nPost = nC + u2 + (uint32_t)(nvs - nS) * u2;
+        tP = (nPost + Bw - 1) / Bw;
+        planned = true;
+      }
+      if (i >= tA + tP) break;
+      const uint32_t gu = unit_turn(i - tA, Bw, rw);
+      if (gu < nC) {
+        ph = 2, u = gu, units = nC;
+      } else if (gu < nC + u2) {
+        ph = 1, u = gu - nC, units = u2;
+      } else {
+        ph = 3, u = gu - nC - u2, units = nPost - nC - u2;
+      }
+    }
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const uint32_t inext = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
-    // read the next unit's ready word now: it is in by the time that unit starts
-    uint32_t seen_next = 0;
-    {
-      const uint32_t un = unit_turn(inext, B);
-      if (inext < turns && un < total && un >= n13) {
-        int vn, tgn, a0, a1;
-        unit_decode(um2, un - n13, vn, tgn, a0, a1);
-        seen_next = load_coherent(&s.ready[vn]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (u < n13) {
-      int v, tg, s0, s1;
-      unit_decode(um13, u, v, tg, s0, s1);
-      const UnitOps ops = unit_ops<true, TT13>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j);
-      v4f tot[TT13];
-      unit_sums<TT13, 0>(tot, ops, s0, s1, g, j);
-      if (pv >= 0) {
-        wait_memory();
-        arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
-      }
-      float* dst = s.part13 + (size_t)(split13 ? s0 : 0) * plane13 + ops.col0 + j;
+    if (u < units) {
+      if (ph == 0 || ph == 2) {
+        // w13: slot, tile group in the slice (gate groups, then up groups),
+        // H segment
+        const uint32_t per = ph == 0 ? u13s : u13r;
+        const int v = ph == 0 ? 0 : nS + (int)(u / per);
+        const uint32_t uu = u % per;
+        const int tg = (int)(uu / (uint32_t)nseg13), seg = (int)(uu % (uint32_t)nseg13);
+        const int4 slot = s_vs[v];
+        const int S = ph == 0 ? Ss : Sr, Kv = ph == 0 ? d.Is : d.I;
+        const int gps = S / 64;  // act groups (and gate tile groups) per slice
+        const int q = x * gps + (tg % gps);
+        const int tgroup = tg < gps ? q : (Kv / 64 + q);
+        const UnitOps ops = unit_ops<true, TT13, true>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
+        v4f tot[TT13];
+        unit_sums<TT13, 0, true, kXcdBurst13>(tot, ops, seg, seg + 1, g, j);
+        if (pend_v >= 0) {
+          wait_memory();
+          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
+        }
+        float* dst = s.part13 + (size_t)seg * plane13 + ops.col0 + j;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * g + q < ops.c) {
-          const size_t r = (size_t)(ops.row0 + 4 * g + q);
+        for (int qq = 0; qq < 4; ++qq) {
+          if (4 * g + qq < ops.c) {
+            const size_t r = (size_t)(ops.row0 + 4 * g + qq);
 #pragma unroll
-          for (int t = 0; t < TT13; ++t) store_coherent(&dst[r * width13 + 16 * t], tot[t][q]);
+            for (int t = 0; t < TT13; ++t) dst[r * width13 + 16 * t] = tot[t][qq];
+          }
+        }
+        pend_v = v, pend_q = q;
+      } else {
+        // w2: slot, tile group of output rows, over the slice's K steps
+        const int v = ph == 1 ? 0 : nS + (int)(u / u2);
+        const int tg = (int)(u % u2);
+        if (pend_v >= 0) {
+          wait_memory();
+          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
+          pend_v = -1;
+        }
+        const int4 slot = s_vs[v];
+        wait_slot(s, sw, v, lane);
+        const UnitOps ops = unit_ops<false, TT2>(slot, tg, d, in, s, s_out, m, R, g, j);
+        v4f tot[TT2];
+        unit_sums<TT2, kScL2, false, kXcdBurst2>(tot, ops, x, x + 1, g, j);
+        float* dst = s.part2 + (size_t)x * plane2 + ops.col0 + j;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          if (4 * g + qq < ops.c) {
+            const size_t orow = (size_t)s_out[ops.row0 + 4 * g + qq];
+#pragma unroll
+            for (int t = 0; t < TT2; ++t) dst[orow * d.H + 16 * t] = tot[t][qq];
+          }
         }
       }
-      pv = v;
-      ptg = tg;
-    } else {
-      if (pv >= 0) {
-        wait_memory();
-        arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
-        pv = -1;
-      }
-      int v, tg, s0, s1;
-      unit_decode(um2, u - n13, v, tg, s0, s1);
-      const int4 slot = s_vs[v];
-      wait_ready(s, v, (uint32_t)((slot.x < 0 ? d.Is : d.I) / kActCols), seen, lane);
-      const UnitOps ops = unit_ops<false, TT2>(slot, tg, d, in, s, s_out, m, R, g, j);
-      v4f tot[TT2];
-      unit_sums<TT2, kCoherent>(tot, ops, s0, s1, g, j);
-      float* dst = s.part2 + (size_t)(split2 ? s0 : 0) * plane2 + ops.col0 + j;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (4 * g + q < ops.c) {
-          const size_t orow = (size_t)s_out[ops.row0 + 4 * g + q];
-#pragma unroll
-          for (int t = 0; t < TT2; ++t) dst[orow * d.H + 16 * t] = tot[t][q];
-        }
-      }
     }
-    seen = (uint32_t)__builtin_amdgcn_readfirstlane((int)seen_next);
-    i = inext;
+    i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
-  if (pv >= 0) {
+  if (pend_v >= 0) {
     wait_memory();
-    arrive13<TT13>(d, s, m, s_vs[pv], pv, ptg, expect, nseg13, lane);
+    count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
   }
   stamp_wave(s.tl_experts, kTlPoints, 3 + (wave & 3));
   __syncthreads();
   stamp(s.tl_experts, kTlPoints, 1);
 }
 
-// Tiles per unit and waves per block (one block per CU) of each GEMM and
-// mode.  More tiles per unit share one activation fragment among more weight
-// tiles and keep more weight bytes in flight per wave; fewer tiles give more
-// units to balance at small m.  Each tile's sums are the same whichever
-// variant runs it.  Whole-mode w13 units take 4 tiles: a block's 25-26
-// units of 8 tiles (655 KB each at H = 5120) left one wave streaming the
-// last unit alone for up to 40 us after its block's other waves ended.
-#ifndef MOE_W13_WHOLE
-#define MOE_W13_WHOLE 4, 8
-#endif
-#ifndef MOE_W13_SPLIT
-#define MOE_W13_SPLIT 4, 8
-#endif
-#ifndef MOE_W2_WHOLE
-#define MOE_W2_WHOLE 8, 8
-#endif
-#ifndef MOE_W2_SPLIT
-#define MOE_W2_SPLIT 4, 8
-#endif
+// Where the blocks of a launch run: block b stores its XCC id at out[b].
+// Launched like the persistent launch (one block of 512 threads per CU).
+__global__ __launch_bounds__(512) void xcc_probe_kernel(uint32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xF;
+}
+
 
 // ROUTE: and the MXFP8 rows of at most kRouteRows tokens
 template <bool W13>
@@ -1034,7 +1168,53 @@ int occupancy_t(size_t lds) {
 }  // namespace
 
 // Nominal waves per block of each GEMM, for the split decision.
-int gemm_waves(bool w13) { return w13 ? 8 : 8; }
+int gemm_waves(bool) { return kGemmWaves; }
+
+// The persistent launch's dynamic LDS: slots, row -> token and row -> output
+// row, then the MXFP8 rows.
+size_t xcd_lds_bytes(const LayerDims& d, int m, int max_vs) {
+  const size_t base = ((size_t)max_vs * 16 + (size_t)(m * d.K + m) * 8 + 15) & ~(size_t)15;
+  const size_t mr = m < kRouteRows ? m : kRouteRows;
+  return base + mr * d.H + mr * (d.H / 32);
+}
+
+int xcd_blocks_per_cu(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, xcd_kernel<kGemmWaves>, kGemmWaves * 64, lds) != hipSuccess)
+    return 0;
+  return n;
+}
+
+// Whether the persistent launch covers a step: one that routes inside the
+// w13 launch, E4M3 routed experts, and intermediates that cut into kXcds
+// slices that are each one w2 segment.
+bool xcd_applies(const LayerDims& d, int m, int grid) {
+  auto slice_ok = [](int Kv) {
+    return Kv % (kXcds * 128) == 0 && Kv / (kXcds * 128) == w2_seg_steps(Kv, false);
+  };
+  // a step's slots (the shared one and at most m k routed) fit a wave's
+  // lanes: the slot wait reads them lane by lane
+  const bool slots_ok = 1 + std::min(m * d.K, d.E) <= 64;
+  return route_in_w13(d, m, grid) && d.rfmt == MOE_DECODE_ROUTED_E4M3 && slice_ok(d.I) && slice_ok(d.Is) &&
+         grid % kXcds == 0 && grid / kXcds > 1 && m < kXcds && slots_ok;
+}
+
+hipError_t launch_xcd(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                      hipStream_t st, const KernelEvents& ev) {
+  return launch_kernel(xcd_kernel<kGemmWaves>, dim3(grid), dim3(kGemmWaves * 64),
+                       (uint32_t)xcd_lds_bytes(d, m, max_vs), st, ev, d, in, s, m, max_vs);
+}
+
+hipError_t probe_xcc(int grid, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(grid), dim3(512), 0, st, out);
+  return hipGetLastError();
+}
+
+// Tiles per split-mode w2 unit: 8 where a w2 segment is 2 K steps.
+int w2_split_tiles(const LayerDims& d) {
+  const bool fp4 = d.rfmt == MOE_DECODE_ROUTED_MXFP4;
+  return (w2_seg_steps(d.I, fp4) == 2 || w2_seg_steps(d.Is, false) == 2) ? 8 : kTT2Split;
+}
 
 template <int TT, int NW>
 constexpr int unit_tiles() { return TT; }
@@ -1057,7 +1237,7 @@ bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
   if (w13) {
     if (m <= kRouteRows) return true;
     const double distinct = d.E * (1.0 - std::pow(1.0 - (double)d.K / d.E, m));
-    const double units = (distinct + shared) * (2.0 * d.Imax / 16 / unit_tiles<MOE_W13_WHOLE>());
+    const double units = (distinct + shared) * (2.0 * d.Imax / 16 / unit_tiles<kTT13, kGemmWaves>());
     return units < 0.9 * waves;
   }
   const int pairs = m * d.K;
@@ -1071,8 +1251,8 @@ hipError_t launch_w13(const LayerDims& d, int m, const Inputs& in, const Scratch
   // the launch that routes: 4 tiles per unit in either mode (registers for
   // its seam)
   if (route) return launch_gemm_t<true, 4, 8, true>(d, m, in, s, grid, max_vs, split ? 1 : 0, st, ev);
-  if (split) return launch_gemm_t<true, MOE_W13_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
-  return launch_gemm_t<true, MOE_W13_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
+  if (split) return launch_gemm_t<true, kTT13, kGemmWaves>(d, m, in, s, grid, max_vs, 1, st, ev);
+  return launch_gemm_t<true, kTT13, kGemmWaves>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
 
 hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid, hipStream_t st,
@@ -1088,39 +1268,25 @@ hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid,
 
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                      hipStream_t st, const KernelEvents& ev) {
-  if (gemm_split(d, m, grid * gemm_waves(false), false))
-    return launch_gemm_t<false, MOE_W2_SPLIT>(d, m, in, s, grid, max_vs, 1, st, ev);
-  return launch_gemm_t<false, MOE_W2_WHOLE>(d, m, in, s, grid, max_vs, 0, st, ev);
+  if (gemm_split(d, m, grid * gemm_waves(false), false)) {
+    if (w2_split_tiles(d) == 8) return launch_gemm_t<false, 8, kGemmWaves>(d, m, in, s, grid, max_vs, 1, st, ev);
+    return launch_gemm_t<false, kTT2Split, kGemmWaves>(d, m, in, s, grid, max_vs, 1, st, ev);
+  }
+  return launch_gemm_t<false, kTT2Whole, kGemmWaves>(d, m, in, s, grid, max_vs, 0, st, ev);
 }
 
 hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
-                          hipStream_t st, const KernelEvents& ev) {
-  const int split = gemm_split(d, m, w2_grid * gemm_waves(false), false) ? 1 : 0;
+                          bool persistent, hipStream_t st, const KernelEvents& ev) {
+  // after the persistent launch: its slice planes, and its hand-off words
+  // to clear
+  const bool clear = persistent;
+  const int split = persistent || gemm_split(d, m, w2_grid * gemm_waves(false), false) ? 1 : 0;
   const dim3 grid(d.H / kCombineThreads, m), block(kCombineThreads);
-  const int nseg = split ? (d.Imax / 128 + kSegSteps - 1) / kSegSteps : 1;
-  if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, block, 0, st, ev, d, in, s, m, split);
-  if (nseg <= 4) return launch_kernel(combine_kernel<4>, grid, block, 0, st, ev, d, in, s, m, split);
-  if (nseg <= 8) return launch_kernel(combine_kernel<8>, grid, block, 0, st, ev, d, in, s, m, split);
-  return launch_kernel(combine_kernel<16>, grid, block, 0, st, ev, d, in, s, m, split);
-}
-
-size_t experts_lds(const LayerDims& d, int m, int max_vs) {
-  return (size_t)max_vs * 16 + (size_t)(m * d.K + m) * 8;
-}
-
-template <int TT13, int TT2>
-hipError_t launch_experts_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
-                            int split13, int split2, hipStream_t st, const KernelEvents& ev) {
-  return launch_kernel(experts_kernel<TT13, TT2, 8>, dim3(grid), dim3(8 * 64), (uint32_t)experts_lds(d, m, max_vs),
-                       st, ev, d, in, s, m, split13, split2);
-}
-
-template <int TT13, int TT2>
-int experts_occupancy_t(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, experts_kernel<TT13, TT2, 8>, 8 * 64, lds) != hipSuccess)
-    return 0;
-  return n;
+  const int nseg = split ? w2_planes(d) : 1;
+  if (nseg <= 1) return launch_kernel(combine_kernel<1>, grid, block, 0, st, ev, d, in, s, m, split, clear ? 1 : 0);
+  if (nseg <= 4) return launch_kernel(combine_kernel<4>, grid, block, 0, st, ev, d, in, s, m, split, clear ? 1 : 0);
+  if (nseg <= 8) return launch_kernel(combine_kernel<8>, grid, block, 0, st, ev, d, in, s, m, split, clear ? 1 : 0);
+  return launch_kernel(combine_kernel<16>, grid, block, 0, st, ev, d, in, s, m, split, clear ? 1 : 0);
 }
 
 // Blocks per CU that every variant of the GEMM fits (one block per CU is
@@ -1128,38 +1294,18 @@ int experts_occupancy_t(size_t lds) {
 int gemm_blocks_per_cu(bool w13, size_t lds) {
   int a, b;
   if (w13) {
-    a = occupancy_t<true, MOE_W13_WHOLE>(lds);
-    b = occupancy_t<true, MOE_W13_SPLIT>(lds);
+    a = occupancy_t<true, kTT13, kGemmWaves>(lds);
+    b = occupancy_t<true, kTT13, kGemmWaves>(lds);
     const int c = occupancy_t<true, 4, 8, true>(lds);
     a = c < a ? c : a;
   } else {
-    a = occupancy_t<false, MOE_W2_WHOLE>(lds);
-    b = occupancy_t<false, MOE_W2_SPLIT>(lds);
+    a = occupancy_t<false, kTT2Whole, kGemmWaves>(lds);
+    b = occupancy_t<false, kTT2Split, kGemmWaves>(lds);
+    const int c = occupancy_t<false, 8, kGemmWaves>(lds);
+    b = c < b ? c : b;
   }
   return a < b ? a : b;
 }
-
-// The fused launch: split-mode GEMMs take 4 tiles per unit, whole-mode 8,
-// as in the separate launches.
-hipError_t launch_experts(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
-                          hipStream_t st, const KernelEvents& ev) {
-  const int waves = grid * 8;
-  const int sp13 = gemm_split(d, m, waves, true) ? 1 : 0, sp2 = gemm_split(d, m, waves, false) ? 1 : 0;
-  if (sp13 && sp2) return launch_experts_t<4, 4>(d, m, in, s, grid, max_vs, 1, 1, st, ev);
-  if (sp13) return launch_experts_t<4, 8>(d, m, in, s, grid, max_vs, 1, 0, st, ev);
-  if (sp2) return launch_experts_t<8, 4>(d, m, in, s, grid, max_vs, 0, 1, st, ev);
-  return launch_experts_t<8, 8>(d, m, in, s, grid, max_vs, 0, 0, st, ev);
-}
-
-int experts_blocks_per_cu(size_t lds) {
-  const int o[4] = {experts_occupancy_t<4, 4>(lds), experts_occupancy_t<4, 8>(lds), experts_occupancy_t<8, 4>(lds),
-                    experts_occupancy_t<8, 8>(lds)};
-  int n = o[0];
-  for (int k = 1; k < 4; ++k) n = o[k] < n ? o[k] : n;
-  return n;
-}
-
-size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs) { return experts_lds(d, m, max_vs); }
 
 size_t gemm_lds_bytes(const LayerDims& d, int m, int max_vs, bool w13) {
   if (!w13) return gemm_lds<false>(d, m, max_vs);

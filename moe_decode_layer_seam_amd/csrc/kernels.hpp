@@ -40,20 +40,21 @@ struct Scratch {
   int32_t* row_out;   // [R] the row of its w2 sums: pair t k + j, or P + t for the shared row
   int4* vslots;       // [VS] {expert (-1: shared), first row, rows (<= 16), 0}
   int32_t* header;    // [4] {virtual slots, shared virtual slots, routed virtual slots, m}
-  uint32_t* counter;  // arrival counter of the seam blocks (zero between runs)
+  uint32_t* counter;  // arrival counter of the route blocks (sync word 0)
   uint8_t* a8;        // [R, Imax] E4M3 SiLU*up intermediate
   uint8_t* a8s;       // [R, Imax/32] E8M0
   float* part13;       // [planes][R][2 Imax] fp32 w13 sums (per K segment in split mode)
   float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
-  // Counters of the fused expert launch, nsync words from `sync`, zeroed by
-  // the seam launch of every run: per virtual slot the act groups whose a8
-  // is stored (ready), and per slot and 64-column act group the w13 units
-  // counted (act_cnt).
+  // The hand-off words, nsync from `sync`, zeroed by the seam launch (and
+  // after the persistent launch by the combine launch): the route launch's
+  // arrival counter (word 0); per virtual slot and XCD the act groups whose
+  // a8 is stored (ready); per slot and 64-column act group the w13 units
+  // counted (act_cnt); the boxes.
   uint32_t* sync;
   // The run's status word, in its own 256 bytes: bits set by a wait that
   // timed out (kStatus*); sticky across runs until the host clears it.
   uint32_t* status;
-  uint32_t* ready;     // [max_vs]
+  uint32_t* ready;     // [max_vs][kXcds]
   uint32_t* act_cnt;   // [max_vs][act_stride]
   uint32_t* pick_box;  // [kPickBox] the picks, for the w13 launch that routes (tagged words)
   uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
@@ -70,14 +71,35 @@ struct Scratch {
   uint64_t* tl_experts;
 };
 
-// Status bits: a wait of the fused expert launch for a slot's a8; a wait of
-// the w13 launch that routes for the logits or the picks.
+// Status bits: a wait of the persistent launch for a slot's a8; a wait of
+// the w13 launch that routes (or of the persistent launch) for the logits
+// or the picks; blocks of the persistent launch with one index mod kXcds
+// on different XCDs.
 constexpr uint32_t kStatusA8Wait = 1u;
 constexpr uint32_t kStatusRouteWait = 2u;
+constexpr uint32_t kStatusXcdMap = 4u;
 
-constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, experts (fused)
+constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, persistent
 constexpr int kActCols = 64;     // columns of a per act group of the fused launch
-constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment
+constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment (w13; w2: w2_seg_steps)
+
+// The persistent launch of small steps cuts the intermediate of every expert
+// into kXcds slices, one per XCD.
+constexpr int kXcds = 8;
+// K steps of 128 per segment of a w2 contraction of length Kv (I or Is):
+// 2 (256 columns) where Kv is kXcds slices of 256, so that those slices are
+// the segments; else kSegSteps.  E2M1 weights keep kSegSteps: their codes
+// are blocked by 512 columns.
+__host__ __device__ inline int w2_seg_steps(int Kv, bool fp4) {
+  return (!fp4 && Kv == kXcds * 256) ? 2 : kSegSteps;
+}
+// Segments of w2 (its sum planes in split mode): the larger of the routed
+// and the shared expert's counts.
+inline int w2_planes(const LayerDims& d) {
+  const int sr = w2_seg_steps(d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), ss = w2_seg_steps(d.Is, false);
+  const int nr = (d.I / 128 + sr - 1) / sr, ns = (d.Is / 128 + ss - 1) / ss;
+  return nr > ns ? nr : ns;
+}
 
 constexpr int kTlPoints = 8;     // stamps per block and kernel
 constexpr int kTlBlocks = 1024;  // blocks recorded per kernel (kTlBlockCap)
@@ -187,15 +209,21 @@ hipError_t launch_act(const LayerDims& d, int m, const Scratch& s, int w13_grid,
                       const KernelEvents& ev);
 hipError_t launch_w2(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
                      hipStream_t st, const KernelEvents& ev);
+// persistent: after the persistent launch (its w2 slice planes; also clear
+// its hand-off words for the next step)
 hipError_t launch_combine(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int w2_grid,
-                          hipStream_t st, const KernelEvents& ev);
-// w13, act and w2 in one launch of `grid` blocks (one per CU, all resident
-// at once): each w2 unit waits for its slot's a8, which the last w13 unit of
-// each act group computes.
-hipError_t launch_experts(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
-                          hipStream_t st, const KernelEvents& ev);
-int experts_blocks_per_cu(size_t lds);
-size_t experts_lds_bytes(const LayerDims& d, int m, int max_vs);
+                          bool persistent, hipStream_t st, const KernelEvents& ev);
+// The persistent launch of a step of at most kRouteRows rows (seam, router,
+// w13, SiLU * up and w2), cut by XCD: whether it covers a step, its launch,
+// its dynamic LDS and occupancy.  probe_xcc: block b of a grid of `grid`
+// blocks of 512 threads stores its XCC id at out[b] (the plan checks that
+// blocks are dealt to the XCDs round-robin).
+bool xcd_applies(const LayerDims& d, int m, int grid);
+hipError_t launch_xcd(const LayerDims& d, int m, const Inputs& in, const Scratch& s, int grid, int max_vs,
+                      hipStream_t st, const KernelEvents& ev);
+size_t xcd_lds_bytes(const LayerDims& d, int m, int max_vs);
+int xcd_blocks_per_cu(size_t lds);
+hipError_t probe_xcc(int grid, uint32_t* out, hipStream_t st);
 // Whether a step of m rows runs the GEMM (w13 or w2) in split mode on
 // `waves` waves, the occupancy of its kernel and its dynamic LDS bytes.
 bool gemm_split(const LayerDims& d, int m, int waves, bool w13);

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     dict(topk=0), dict(topk=9, experts=8), dict(topk=33, experts=64), dict(inter=96),
     dict(shared_inter=0), dict(max_tokens=0), dict(max_tokens=49), dict(rms_eps=-1.0),
     dict(rms_eps=float("nan")), dict(routed_scale=float("inf")), dict(routed_format=2),
-    dict(routed_format=-1), dict(schedule=2), dict(schedule=-1),
+    dict(routed_format=-1), dict(schedule=3), dict(schedule=-1),
 ])
 def test_plan_rejects_invalid_dims(bad):
     d = dict(hidden=256, experts=8, topk=2, inter=128, shared_inter=128, max_tokens=4,

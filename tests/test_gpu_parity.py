@@ -30,6 +30,8 @@ def _cfg(m, H, E, K, I, Is, **kw):
     c = dict(name=f"m{m}_h{H}_e{E}_k{K}_i{I}_is{Is}", m=m, hidden=H, experts=E, topk=K,
              inter=I, shared_inter=Is, rms_eps=1e-6, routed_scale=1.0)
     c.update(kw)
+    if "schedule" in kw:
+        c["name"] += "_" + kw["schedule"]
     return c
 
 
@@ -52,10 +54,17 @@ SMALL = [
     _cfg(2, 256, 300, 8, 128, 128),
     _cfg(4, 256, 64, 20, 128, 128),
     _cfg(2, 8320, 16, 2, 128, 128),
+    # m <= 4 with I and Is of 2048 or 4096: the persistent launch, cut by XCD
+    # (ragged H and E, I != Is, k = 1)
+    _cfg(1, 256, 64, 6, 2048, 2048, schedule="persistent"),
+    _cfg(4, 640, 100, 8, 2048, 4096, schedule="persistent"),
+    _cfg(3, 512, 256, 8, 4096, 2048, schedule="persistent"),
+    _cfg(2, 384, 16, 1, 2048, 2048, schedule="persistent"),
 ]
 
 
-def _plan_for(cfg, max_tokens=None, schedule="launches"):
+def _plan_for(cfg, max_tokens=None, schedule=None):
+    schedule = schedule or cfg.get("schedule", "auto")
     return mdl.plan(cfg["hidden"], cfg["experts"], cfg["topk"], cfg["inter"],
                     cfg["shared_inter"], max_tokens or cfg["m"], cfg["rms_eps"],
                     cfg["routed_scale"], routed=data.routed_of(cfg), schedule=schedule)
@@ -264,9 +273,11 @@ def test_concentrated_routing_splits_slots():
         mdl.destroy(h)
 
 
-@pytest.mark.parametrize("schedule", ["launches", "fused"])
-def test_runs_are_deterministic_and_plan_reusable_across_m(schedule):
-    cfg = _cfg(48, 512, 256, 8, 256, 256)
+@pytest.mark.parametrize("schedule,inter", [("launches", 256), ("persistent", 2048)])
+def test_runs_are_deterministic_and_plan_reusable_across_m(schedule, inter):
+    # auto at I = 2048: steps of up to 4 rows run the persistent launch, the
+    # others the short launches, and a token's bits are the same in either
+    cfg = _cfg(48, 512, 256, 8, inter, inter)
     inp, w = data.build_layer(10, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
     h = _plan_for(cfg, schedule=schedule)
@@ -319,9 +330,11 @@ def test_whole_and_split_units_give_the_same_bits():
 
 # m = 3: the launches schedule runs the seam and the router inside the w13
 # launch, whose hand-off boxes the act launch clears for the next replay
-@pytest.mark.parametrize("schedule,m", [("launches", 16), ("fused", 16), ("launches", 3)])
-def test_graph_capture_replays_match_eager(schedule, m):
-    cfg = _cfg(m, 512, 64, 6, 256, 128)
+@pytest.mark.parametrize("schedule,m,inter", [("launches", 16, 256), ("launches", 3, 256), ("persistent", 3, 2048)])
+def test_graph_capture_replays_match_eager(schedule, m, inter):
+    # ("auto", 3, 2048): the persistent launch and the combine launch that
+    # clears its hand-off words for the next replay
+    cfg = _cfg(m, 512, 64, 6, inter, 2048 if inter == 2048 else 128)
     inp, w = data.build_layer(11, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
     h = _plan_for(cfg, schedule=schedule)
@@ -381,42 +394,46 @@ def _gpu_weights(cfg, seed):
     return out
 
 
-# (w13 mode, w2 mode) of the fused launch on 256 CUs: split/split at small
-# sizes and m <= 4 of the full layer, whole/whole at m = 8 and 48,
-# split/whole for 48 rows at I = 256, whole/split where I is much larger
-# than H
-SCHEDULE_CASES = [
-    _cfg(13, 640, 100, 8, 128, 256),
-    dict(synth.WORKLOADS[1], m=8, name="dsv41_m8"),
-    synth.WORKLOADS[3],
-    synth.WORKLOADS[6],
-    _cfg(40, 256, 64, 4, 8192, 128),
-    dict(synth.WORKLOADS[1], routed="mxfp4", name="dsv41_m1_fp4"),
-    dict(synth.WORKLOADS[3], routed="mxfp4", name="dsv41_m48_fp4"),
+# steps the persistent launch covers: the full layer at 1, 3 and 4 rows, a
+# shape with Is = 4096, and 2 rows at k = 1
+PERSISTENT_CASES = [
+    dict(synth.WORKLOADS[1], name="dsv41_m1"),
+    dict(synth.WORKLOADS[1], m=3, name="dsv41_m3"),
+    dict(synth.WORKLOADS[1], m=4, name="dsv41_m4"),
+    _cfg(4, 640, 100, 8, 2048, 4096),
+    _cfg(2, 384, 16, 1, 2048, 2048),
 ]
 
 
-@pytest.mark.parametrize("cfg", SCHEDULE_CASES, ids=lambda c: c["name"])
-def test_fused_launch_matches_separate_launches_bit_for_bit(cfg):
-    """The fused expert launch runs the separate launches' arithmetic in the
-    same order: output and intermediate bytes are identical."""
+@pytest.mark.parametrize("cfg", PERSISTENT_CASES, ids=lambda c: c["name"])
+def test_persistent_launch_matches_the_short_launches_bit_for_bit(cfg):
+    """The persistent launch runs the short launches'
+    arithmetic in the same order -- w2 segments are its XCD slices -- so the
+    intermediate and the output are the same bytes; and it ran (its timing
+    event recorded a dispatch)."""
     m, H, E = cfg["m"], cfg["hidden"], cfg["experts"]
     dw = _gpu_weights(cfg, 31)
     inp = synth.small_inputs(5, m, H, E)
     dinp = gu.inputs_dev(inp)
     got = {}
-    for schedule in ("launches", "fused"):
-        h = _plan_for(cfg, max_tokens=48, schedule=schedule)
+    for schedule in ("launches", "persistent"):
+        h = _plan_for(cfg, max_tokens=m, schedule=schedule)
         try:
+            mdl.timing(h, True)
             outs = [gu.run(h, cfg, dinp, dw).clone() for _ in range(2)]
             torch.cuda.synchronize()
+            _, runs = mdl.timing_read(h, "persistent")
+            mdl.timing(h, False)
+            assert runs == (2 if schedule == "persistent" else 0), (schedule, runs)
             assert mdl.status(h) == 0
-            got[schedule] = (outs, gu.tap(h, "a8"), gu.tap(h, "a8s"))
+            rows = m * cfg["topk"] + m
+            got[schedule] = (outs, gu.tap(h, "a8")[:rows * max(cfg["inter"], cfg["shared_inter"])],
+                             gu.tap(h, "a8s"))
         finally:
             mdl.destroy(h)
-    (o_l, a8_l, a8s_l), (o_f, a8_f, a8s_f) = got["launches"], got["fused"]
-    assert np.array_equal(a8_l, a8_f) and np.array_equal(a8s_l, a8s_f)
-    for a, b in zip(o_l + o_f[1:], o_f):
+    (o_l, a8_l, a8s_l), (o_p, a8_p, a8s_p) = got["launches"], got["persistent"]
+    assert np.array_equal(a8_l, a8_p) and np.array_equal(a8s_l, a8s_p)
+    for a, b in zip(o_l + o_p[1:], o_p):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
