@@ -80,7 +80,10 @@ extern "C" {
  * assumes that all its blocks are resident at once; a wait past 100 ms sets
  * a status bit (moe_decode_status).  AUTO (the default): the schedule that
  * runs a step fastest on MI355X, today the short launches at every width.
- * Every schedule gives a token the same output bits. */
+ * Within one plan a token's output bits do not depend on the step's width.
+ * Plans of the persistent schedule add w2 over 256-column segments where I
+ * or Is is 2048 (its XCD slices), other plans over 512-column ones, so the
+ * two can differ in the rounding of those sums. */
 #define MOE_DECODE_SCHEDULE_AUTO 0
 #define MOE_DECODE_SCHEDULE_LAUNCHES 1
 #define MOE_DECODE_SCHEDULE_PERSISTENT 2

@@ -227,6 +227,7 @@ LayerDims dims_of(const moe_decode_dims* dims) {
   d.eps = dims->rms_eps;
   d.routed_scale = dims->routed_scale;
   d.rfmt = dims->routed_format;
+  d.xslices = dims->schedule == MOE_DECODE_SCHEDULE_PERSISTENT ? 1 : 0;
   return d;
 }
 

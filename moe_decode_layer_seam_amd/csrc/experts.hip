@@ -51,7 +51,7 @@ __device__ __forceinline__ Geo geo(const LayerDims& d, bool shared) {
   Geo g;
   g.tiles = W13 ? 2 * Kv / 16 : d.H / 16;
   g.K = W13 ? d.H : Kv;
-  g.seg = W13 ? kSegSteps : w2_seg_steps(Kv, !shared && d.rfmt == MOE_DECODE_ROUTED_MXFP4);
+  g.seg = W13 ? kSegSteps : w2_seg_steps(d, Kv, !shared && d.rfmt == MOE_DECODE_ROUTED_MXFP4);
   g.nseg = (g.K / 128 + g.seg - 1) / g.seg;
   return g;
 }
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LayerDims d, I
   }
   if (n >= d.H) return;
   const int P = m * d.K;
-  const int seg_r = w2_seg_steps(d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), seg_s = w2_seg_steps(d.Is, false);
+  const int seg_r = w2_seg_steps(d, d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), seg_s = w2_seg_steps(d, d.Is, false);
   const int nseg_r = split ? (d.I / 128 + seg_r - 1) / seg_r : 1;
   const int nseg_s = split ? (d.Is / 128 + seg_s - 1) / seg_s : 1;
   const size_t plane = (size_t)(m * d.K + m) * d.H;
@@ -1189,8 +1189,8 @@ int xcd_blocks_per_cu(size_t lds) {
 // w13 launch, E4M3 routed experts, and intermediates that cut into kXcds
 // slices that are each one w2 segment.
 bool xcd_applies(const LayerDims& d, int m, int grid) {
-  auto slice_ok = [](int Kv) {
-    return Kv % (kXcds * 128) == 0 && Kv / (kXcds * 128) == w2_seg_steps(Kv, false);
+  auto slice_ok = [&d](int Kv) {
+    return Kv % (kXcds * 128) == 0 && Kv / (kXcds * 128) == w2_seg_steps(d, Kv, false);
   };
   // a step's slots (the shared one and at most m k routed) fit a wave's
   // lanes: the slot wait reads them lane by lane
@@ -1213,7 +1213,7 @@ hipError_t probe_xcc(int grid, uint32_t* out, hipStream_t st) {
 // Tiles per split-mode w2 unit: 8 where a w2 segment is 2 K steps.
 int w2_split_tiles(const LayerDims& d) {
   const bool fp4 = d.rfmt == MOE_DECODE_ROUTED_MXFP4;
-  return (w2_seg_steps(d.I, fp4) == 2 || w2_seg_steps(d.Is, false) == 2) ? 8 : kTT2Split;
+  return (w2_seg_steps(d, d.I, fp4) == 2 || w2_seg_steps(d, d.Is, false) == 2) ? 8 : kTT2Split;
 }
 
 template <int TT, int NW>

@@ -23,6 +23,7 @@ struct LayerDims {
   int H, E, K, I, Is, Imax, Mx;
   float eps, routed_scale;
   int rfmt;  // routed expert weights: MOE_DECODE_ROUTED_E4M3 or _MXFP4
+  int xslices;  // plans of the persistent schedule: w2 segments are its XCD slices
 };
 
 // The plan's device scratch, laid out for Mx token rows.
@@ -87,16 +88,18 @@ constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment (w13; w2: w2
 // into kXcds slices, one per XCD.
 constexpr int kXcds = 8;
 // K steps of 128 per segment of a w2 contraction of length Kv (I or Is):
-// 2 (256 columns) where Kv is kXcds slices of 256, so that those slices are
-// the segments; else kSegSteps.  E2M1 weights keep kSegSteps: their codes
-// are blocked by 512 columns.
-__host__ __device__ inline int w2_seg_steps(int Kv, bool fp4) {
-  return (!fp4 && Kv == kXcds * 256) ? 2 : kSegSteps;
+// in plans of the persistent schedule, 2 (256 columns) where Kv is kXcds
+// slices of 256, so that those slices are the segments and every step of
+// the plan sums w2 in the same order; else kSegSteps (segments of 512
+// columns read longer runs of each weight row).  E2M1 weights keep
+// kSegSteps: their codes are blocked by 512 columns.
+__host__ __device__ inline int w2_seg_steps(const LayerDims& d, int Kv, bool fp4) {
+  return (d.xslices && !fp4 && Kv == kXcds * 256) ? 2 : kSegSteps;
 }
 // Segments of w2 (its sum planes in split mode): the larger of the routed
 // and the shared expert's counts.
 inline int w2_planes(const LayerDims& d) {
-  const int sr = w2_seg_steps(d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), ss = w2_seg_steps(d.Is, false);
+  const int sr = w2_seg_steps(d, d.I, d.rfmt == MOE_DECODE_ROUTED_MXFP4), ss = w2_seg_steps(d, d.Is, false);
   const int nr = (d.I / 128 + sr - 1) / sr, ns = (d.Is / 128 + ss - 1) / ss;
   return nr > ns ? nr : ns;
 }

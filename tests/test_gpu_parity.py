@@ -275,8 +275,9 @@ def test_concentrated_routing_splits_slots():
 
 @pytest.mark.parametrize("schedule,inter", [("launches", 256), ("persistent", 2048)])
 def test_runs_are_deterministic_and_plan_reusable_across_m(schedule, inter):
-    # auto at I = 2048: steps of up to 4 rows run the persistent launch, the
-    # others the short launches, and a token's bits are the same in either
+    # persistent at I = 2048: steps of up to 4 rows run the persistent
+    # launch, the others the short launches, and a token's bits are the same
+    # in either
     cfg = _cfg(48, 512, 256, 8, inter, inter)
     inp, w = data.build_layer(10, cfg)
     dinp, dw = gu.inputs_dev(inp), gu.weights_dev(w)
@@ -407,34 +408,31 @@ PERSISTENT_CASES = [
 
 @pytest.mark.parametrize("cfg", PERSISTENT_CASES, ids=lambda c: c["name"])
 def test_persistent_launch_matches_the_short_launches_bit_for_bit(cfg):
-    """The persistent launch runs the short launches'
-    arithmetic in the same order -- w2 segments are its XCD slices -- so the
-    intermediate and the output are the same bytes; and it ran (its timing
-    event recorded a dispatch)."""
+    """In a plan of the persistent schedule, a step of m <= 4 rows runs the
+    persistent launch (its timing event records the dispatches) and a step of
+    5 rows the short launches, with the same arithmetic in the same order --
+    the w2 segments are the XCD slices -- so the m rows come out the same
+    bytes in either."""
     m, H, E = cfg["m"], cfg["hidden"], cfg["experts"]
     dw = _gpu_weights(cfg, 31)
-    inp = synth.small_inputs(5, m, H, E)
-    dinp = gu.inputs_dev(inp)
-    got = {}
-    for schedule in ("launches", "persistent"):
-        h = _plan_for(cfg, max_tokens=m, schedule=schedule)
-        try:
-            mdl.timing(h, True)
-            outs = [gu.run(h, cfg, dinp, dw).clone() for _ in range(2)]
-            torch.cuda.synchronize()
-            _, runs = mdl.timing_read(h, "persistent")
-            mdl.timing(h, False)
-            assert runs == (2 if schedule == "persistent" else 0), (schedule, runs)
-            assert mdl.status(h) == 0
-            rows = m * cfg["topk"] + m
-            got[schedule] = (outs, gu.tap(h, "a8")[:rows * max(cfg["inter"], cfg["shared_inter"])],
-                             gu.tap(h, "a8s"))
-        finally:
-            mdl.destroy(h)
-    (o_l, a8_l, a8s_l), (o_p, a8_p, a8s_p) = got["launches"], got["persistent"]
-    assert np.array_equal(a8_l, a8_p) and np.array_equal(a8s_l, a8s_p)
-    for a, b in zip(o_l + o_p[1:], o_p):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    dinp = gu.inputs_dev(synth.small_inputs(5, 5, H, E))
+    h = _plan_for(cfg, max_tokens=5, schedule="persistent")
+    try:
+        mdl.timing(h, True)
+        outs = [gu.run(h, cfg, dinp, dw, x=dinp["x"][:m].contiguous()).clone() for _ in range(2)]
+        torch.cuda.synchronize()
+        _, runs = mdl.timing_read(h, "persistent")
+        assert runs == 2, runs
+        five = gu.run(h, cfg, dinp, dw).clone()
+        torch.cuda.synchronize()
+        _, runs = mdl.timing_read(h, "persistent")
+        assert runs == 2, runs  # the 5-row step ran the short launches
+        mdl.timing(h, False)
+        assert mdl.status(h) == 0
+    finally:
+        mdl.destroy(h)
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), five[:m].view(torch.int16))
 
 
 def test_quantize_weight_matches_oracle():
@@ -539,14 +537,14 @@ def _full_layer(key, seed=0):
     return _FULL[want]
 
 
-def _run_full(cfg, key, seed=0, rows_ref=None):
+def _run_full(cfg, key, seed=0, rows_ref=None, schedule=None):
     """One step at full size planned exactly as bench.py plans it (max_tokens
     = m), every output row (or rows_ref) checked against the oracle."""
     inp_all, w, dinp_all, dw = _full_layer(key, seed)
     m = cfg["m"]
     inp = dict(inp_all, x=inp_all["x"][:m])
     dinp = dict(dinp_all, x=dinp_all["x"][:m].contiguous())
-    h = _plan_for(cfg, max_tokens=m)
+    h = _plan_for(cfg, max_tokens=m, schedule=schedule)
     try:
         out = gu.run(h, cfg, dinp, dw)
         torch.cuda.synchronize()
@@ -577,6 +575,14 @@ def test_parity_tensor_parallel_share(idx):
 @pytest.mark.parametrize("idx", [1, 2, 3])
 def test_parity_full_size(idx):
     _run_full(synth.WORKLOADS[idx], "dsv41")
+
+
+@pytest.mark.parametrize("idx", [1])
+def test_parity_full_size_persistent(idx):
+    """The persistent launch at full size, planned as bench.py plans it, against
+    the oracle."""
+    _run_full(dict(synth.WORKLOADS[idx], name=synth.WORKLOADS[idx]["name"] + "_persistent"), "dsv41",
+              schedule="persistent")
 
 
 def test_parity_full_size_m1_on_a_48_row_plan():
