@@ -813,10 +813,10 @@ constexpr int kTT13 = 4;       // w13 units, both modes
 constexpr int kTT2Whole = 8;   // whole-mode w2 units
 constexpr int kTT2Split = 4;   // split-mode w2 units over 4-step segments
 constexpr int kGemmWaves = 8;  // waves per block of either GEMM
-// K steps per load burst of the persistent launch's units (w13, w2): 16 KB
-// a wave.  Its hand-offs make round trips through the memory queues that the
+// K steps per load burst of the persistent launch's units (w13, w2): 8 and
+// 16 KB a wave.  Its hand-offs make round trips through the memory queues that the
 // weight stream fills; smaller bursts keep those queues short.
-constexpr int kXcdBurst13 = 2;
+constexpr int kXcdBurst13 = 1;
 constexpr int kXcdBurst2 = 1;
 
 // ===========================================================================
@@ -850,10 +850,9 @@ constexpr int kXcdBurst2 = 1;
 // the summed planes with the act launch's arithmetic and counts the group
 // on its slot's ready word for the XCD; a w2 unit waits until that word
 // holds the slice's groups (one wave of a block polls, wait_slot).  A wave
-// counts a w13 unit once its next unit's loads have returned (its stores
-// are complete by then, so the count waits for nothing but the atomic), and
-// always before it waits itself; a block's waves take its units in deal
-// order.  So with every block resident each wait ends.
+// counts each w13 unit as soon as its stores complete, so it never waits
+// while holding an uncounted unit.  So with every block resident each wait
+// ends.
 // ===========================================================================
 
 __device__ __forceinline__ float ld_l2(rsrc_t r, uint32_t off) {
@@ -1033,7 +1032,6 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
   const uint32_t width13 = 2u * (uint32_t)d.Imax;
   const size_t plane13 = (size_t)R * width13, plane2 = (size_t)R * d.H;
   SlotWait sw{&s_ready, &s_plock, 0, x, (uint32_t)(Ss / 64), (uint32_t)(Sr / 64)};
-  int pend_v = -1, pend_q = 0;  // a w13 unit whose sums are stored but not yet counted
   uint32_t i = wave;
   while (true) {
     int ph;
@@ -1042,12 +1040,6 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
       ph = 0, u = unit_turn(i, Bw, rw), units = u13s;
     } else {
       if (!planned) {
-        // the routed units need the picks: count first, then wait
-        if (pend_v >= 0) {
-          wait_memory();
-          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
-          pend_v = -1;
-        }
         stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out);
         const int nvs = __builtin_amdgcn_readfirstlane(s_nvs);
         sw.nvs = nvs;
@@ -1084,10 +1076,6 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
         const UnitOps ops = unit_ops<true, TT13, true>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
         v4f tot[TT13];
         unit_sums<TT13, 0, true, kXcdBurst13>(tot, ops, seg, seg + 1, g, j);
-        if (pend_v >= 0) {
-          wait_memory();
-          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
-        }
         float* dst = s.part13 + (size_t)seg * plane13 + ops.col0 + j;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
@@ -1097,16 +1085,15 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
             for (int t = 0; t < TT13; ++t) dst[r * width13 + 16 * t] = tot[t][qq];
           }
         }
-        pend_v = v, pend_q = q;
+        // counted as soon as its sums are in the L2: the wave waits for its
+        // stores and the count, while the CU's other waves keep the weight
+        // stream's bytes in flight
+        wait_memory();
+        count_w13(d, s, m, slot, v, q, x, expect13, nseg13, lane);
       } else {
         // w2: slot, tile group of output rows, over the slice's K steps
         const int v = ph == 1 ? 0 : nS + (int)(u / u2);
         const int tg = (int)(u % u2);
-        if (pend_v >= 0) {
-          wait_memory();
-          count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
-          pend_v = -1;
-        }
         const int4 slot = s_vs[v];
         wait_slot(s, sw, v, lane);
         const UnitOps ops = unit_ops<false, TT2>(slot, tg, d, in, s, s_out, m, R, g, j);
@@ -1124,10 +1111,6 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
       }
     }
     i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
-  }
-  if (pend_v >= 0) {
-    wait_memory();
-    count_w13(d, s, m, s_vs[pend_v], pend_v, pend_q, x, expect13, nseg13, lane);
   }
   stamp_wave(s.tl_experts, kTlPoints, 3 + (wave & 3));
   __syncthreads();
