@@ -581,6 +581,36 @@ __device__ void seam_rows(const LayerDims& d, int m, const Inputs& in, const Scr
 // c are not stored.  Split units store their segment sums in plane s0 of
 // `part`, whole units the tiles' totals in plane 0.  Part planes are
 // [R][width] fp32, R = m (k + 1).
+// One unit of the GEMM: TT tiles of tile group tgroup (in units of TT
+// tiles) of a slot over segments [s0, s1).  w13 sums go to the slot's rows,
+// w2 sums to the rows' output rows (plane s0 in split mode, else plane 0).
+template <bool W13, int TT, bool ROUTE>
+__device__ __forceinline__ void run_unit(const int4& slot, int tgroup, int s0, int s1, bool split, const LayerDims& d,
+                                         const Inputs& in, const Scratch& s, const int* s_tok, int m, int R, int g,
+                                         int j, uint32_t x8o, uint32_t xso, float* part, size_t plane, int width) {
+  const UnitOps ops = unit_ops<W13, TT, ROUTE>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
+  v4f tot[TT];
+  unit_sums<TT, 0, ROUTE>(tot, ops, s0, s1, g, j);
+  float* dst = part + (size_t)(split ? s0 : 0) * plane + ops.col0 + j;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (4 * g + q < ops.c) {
+      const int r = ops.row0 + 4 * g + q;
+      const size_t orow = (size_t)(W13 ? r : s_tok[r]);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) dst[orow * width + 16 * t] = tot[t][q];
+    }
+  }
+}
+
+// The first turn dealt as half units: the units of a run's last, partial
+// row of B (fewer than B) are cut in two halves of TT / 2 tiles (the same
+// sums: tiles are independent), dealt one per block, so every block streams
+// about the same bytes (w2 at 48 rows: 326 -> 320 us).  ~0u: no halves.
+__device__ __forceinline__ uint32_t half_row(uint32_t total, uint32_t B, int TT) {
+  return (TT >= 4 && total % B != 0) ? total / B : 0xFFFFFFFFu;
+}
+
 template <bool W13, int TT, int NW, bool ROUTE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)))
 void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap) {
@@ -647,36 +677,48 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
   const uint32_t nroute = ROUTE ? (uint32_t)m : 0u;
   const uint32_t B = gridDim.x - nroute, b = blockIdx.x - nroute;
   bool planned = !ROUTE;
+  // the launch that routes keeps whole units to the end: a second unit
+  // body there spilled registers and slowed it more than the tail gained
+  uint32_t hrow = ROUTE ? 0xFFFFFFFFu : half_row(um.total, B, TT);
   // first unit by wave index, the rest from the block's counter; the next
   // index is fetched while the current unit streams
   uint32_t i = wave;
   while (true) {
-    const uint32_t u = unit_turn(i, B, b);
-    if (u >= um.total) {
-      // past the shared expert's units: the routed ones need the picks
-      if (planned) break;
-      stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
-      um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
-      planned = true;
-      if (u >= um.total) break;  // the last turn has no unit for this block
+    uint32_t u;
+    int half = -1;
+    if constexpr (ROUTE) {
+      u = unit_turn(i, B, b);
+      if (u >= um.total) {
+        // past the shared expert's units: the routed ones need the picks
+        if (planned) break;
+        stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
+        um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
+        planned = true;
+        if (u >= um.total) break;  // the last turn has no unit for this block
+      }
+    } else if (i < hrow) {
+      u = unit_turn(i, B, b);
+      if (u >= um.total) break;
+    } else {
+      const uint32_t h = unit_turn(i - hrow, B, b);
+      if (h >= 2u * (um.total - hrow * B)) break;
+      u = hrow * B + h / 2u;
+      half = (int)(h & 1u);
     }
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int v, tg, s0, s1;
     unit_decode(um, u, v, tg, s0, s1);
-    const UnitOps ops = unit_ops<W13, TT, ROUTE>(s_vs[v], tg, d, in, s, s_tok, m, R, g, j, x8o, xso);
-    v4f tot[TT];
-    unit_sums<TT, 0, ROUTE>(tot, ops, s0, s1, g, j);
-    // w13 sums go to the slot's rows; w2 sums to the rows' output rows
-    float* dst = part + (size_t)(um.split ? s0 : 0) * plane + ops.col0 + j;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (4 * g + q < ops.c) {
-        const int r = ops.row0 + 4 * g + q;
-        const size_t orow = (size_t)(W13 ? r : s_tok[r]);
-#pragma unroll
-        for (int t = 0; t < TT; ++t) dst[orow * width + 16 * t] = tot[t][q];
-      }
+    if constexpr (TT >= 4 && !ROUTE) {
+      if (half >= 0)
+        run_unit<W13, TT / 2, ROUTE>(s_vs[v], 2 * tg + half, s0, s1, um.split, d, in, s, s_tok, m, R, g, j, x8o,
+                                     xso, part, plane, width);
+      else
+        run_unit<W13, TT, ROUTE>(s_vs[v], tg, s0, s1, um.split, d, in, s, s_tok, m, R, g, j, x8o, xso, part, plane,
+                                 width);
+    } else {
+      run_unit<W13, TT, ROUTE>(s_vs[v], tg, s0, s1, um.split, d, in, s, s_tok, m, R, g, j, x8o, xso, part, plane,
+                               width);
     }
     i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
