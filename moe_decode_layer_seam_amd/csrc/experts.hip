@@ -590,7 +590,10 @@ __device__ __forceinline__ void run_unit(const int4& slot, int tgroup, int s0, i
                                          int j, uint32_t x8o, uint32_t xso, float* part, size_t plane, int width) {
   const UnitOps ops = unit_ops<W13, TT, ROUTE>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
   v4f tot[TT];
-  unit_sums<TT, 0, ROUTE>(tot, ops, s0, s1, g, j);
+  // the launch that routes loads 2 K steps (16 KB) a burst: its blocks' pick
+  // polls then wait behind less, and it holds 204 VGPRs without spilling
+  // (m = 1: 65.6 -> 64.5 us; 1-step bursts took 66.3)
+  unit_sums<TT, 0, ROUTE, ROUTE ? 2 : 0>(tot, ops, s0, s1, g, j);
   float* dst = part + (size_t)(split ? s0 : 0) * plane + ops.col0 + j;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
