@@ -664,8 +664,10 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
     const int nvs = plan_block<NW>(d, m, s, s_vs, s_tok, reinterpret_cast<uint32_t*>(lds_raw + x8o), blockIdx.x == 0);
     um = unit_map_n<W13, TT>(d, nvs, (m + kTokTile - 1) / kTokTile, split);
   } else {
+    // the whole slot table (vs_cap entries, allocated for the plan's widest
+    // step) beside the header's load, instead of after it
+    for (int i = tid; i < vs_cap; i += NW * 64) s_vs[i] = s.vslots[i];
     um = unit_map<W13, TT>(d, s, split);
-    for (int i = tid; i < um.nvs; i += NW * 64) s_vs[i] = s.vslots[i];
     for (int i = tid; i < R; i += NW * 64) s_tok[i] = s.row_out[i];
   }
   if (tid == 0) s_next = 0;
