@@ -240,7 +240,10 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
 /* The plan's status word: 0 while every run since the last clear was valid.
  * A kernel that waits on other blocks of its launch (the hand-offs of the
  * pages' persistent launch through device-scope words, [device]
- * atomic_add_dev; [layer] run_ffn) gives up after 100 ms and sets a bit; the
+ * atomic_add_dev; [layer] run_ffn) gives up after 100 ms (or after
+ * MOE_DECODE_WAIT_LIMIT_US microseconds when that environment variable is
+ * set as a plan is made, or a no-alloc run starts: a low value makes the
+ * waits give up at once, to check this path) and sets a bit; the
  * run's output is then not valid.  Bits: 1 a wait of the persistent launch
  * for a slot's a8; 2 a wait of a launch that routes (m <= 4) for the logits
  * or the picks; 4 blocks of the persistent launch whose indices agree mod

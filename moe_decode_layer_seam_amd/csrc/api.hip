@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -184,8 +185,21 @@ Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool t
 }
 
 // The kernels' view of a layout at device address b.
+// The bound of the waits inside a launch: MOE_DECODE_WAIT_LIMIT_US (whole
+// microseconds) when set, else kWaitTicks.  A small bound makes the waits
+// give up at once (their status bits report it): a way to check that path.
+uint64_t wait_ticks_from_env() {
+  const char* v = std::getenv("MOE_DECODE_WAIT_LIMIT_US");
+  if (!v || !*v) return kWaitTicks;
+  char* end = nullptr;
+  const unsigned long long us = std::strtoull(v, &end, 10);
+  if (!end || *end || us > kWaitTicks / 100) return kWaitTicks;
+  return (uint64_t)us * 100;
+}
+
 Scratch scratch_at(char* b, const Layout& L, const LayerDims& d, int max_vs) {
   Scratch s{};
+  s.wait_ticks = wait_ticks_from_env();
   s.normed = reinterpret_cast<uint16_t*>(b + L.normed);
   s.x8 = reinterpret_cast<uint8_t*>(b + L.x8);
   s.x8s = reinterpret_cast<uint8_t*>(b + L.x8s);

@@ -403,10 +403,6 @@ __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B, uint32_t b
   return i * B + ((i & 1u) ? B - 1u - b : b);
 }
 
-// Longest wait for the plan before the run is flagged (status) and the wave
-// goes on: 100 ms of the 100 MHz device clock, far beyond a real wait.
-constexpr uint64_t kPlanWaitTicks = 10000000ull;
-
 // The routed slots of a w13 launch that routes in its first blocks, built in
 // the block's LDS by the first wave that needs them (the others wait for
 // that wave): the wave reads the pick box until every pick of the step
@@ -414,8 +410,11 @@ constexpr uint64_t kPlanWaitTicks = 10000000ull;
 // the same rows and slots as the router's plan).  On a timeout the status
 // word is set and no routed slot is staged.
 // s_out (may be null): also each routed row's w2 output row, its pair.
-__device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap,
-                           int* s_plan, int* s_nvs, int lane, int* s_out = nullptr) {
+// Returns the slots the calling wave may use: the staged ones, or only the
+// nS shared ones when it gave up waiting for the staging wave (whose LDS
+// writes it then must not read).
+__device__ int stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap,
+                          int* s_plan, int* s_nvs, int lane, int* s_out = nullptr) {
   int st = 0;
   if (lane == 0) st = atomicCAS(s_plan, 0, 1);
   st = __builtin_amdgcn_readfirstlane(st);
@@ -429,7 +428,7 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
         in = true;
         break;
       }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > s.wait_ticks) {
         if (lane == 0) flag_status(s.status, kStatusRouteWait);
         break;
       }
@@ -444,15 +443,16 @@ __device__ void stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int
     if (lane == 0) *s_nvs = nS + nR;
     wait_memory();  // the LDS writes are done
     if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else {
-    while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * kPlanWaitTicks) {
-        if (lane == 0) flag_status(s.status, kStatusRouteWait);
-        break;
-      }
+    return nS + nR;
+  }
+  while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
+    __builtin_amdgcn_s_sleep(1);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * s.wait_ticks) {
+      if (lane == 0) flag_status(s.status, kStatusRouteWait);
+      return nS;
     }
   }
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(s_nvs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 
 // The seam of the w13 launch that routes (m <= kRouteRows rows, H <= 8192),
@@ -696,8 +696,8 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
       if (u >= um.total) {
         // past the shared expert's units: the routed ones need the picks
         if (planned) break;
-        stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
-        um = unit_map_n<W13, TT>(d, __builtin_amdgcn_readfirstlane(s_nvs), um.nS, split);
+        const int nvs = stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
+        um = unit_map_n<W13, TT>(d, nvs, um.nS, split);
         planned = true;
         if (u >= um.total) break;  // the last turn has no unit for this block
       }
@@ -989,7 +989,7 @@ __device__ void wait_slot(const Scratch& s, const SlotWait& w, int v, int lane) 
         if (lane < w.nvs) c = peek_l2(&s.ready[(size_t)lane * kXcds + w.x]);
         const uint64_t in = __ballot(lane < w.nvs && c >= (lane == 0 ? w.want_s : w.want_r));
         bool done = (in & bit) != 0ull;
-        if (!done && __builtin_amdgcn_s_memrealtime() - t0 > kPlanWaitTicks) {
+        if (!done && __builtin_amdgcn_s_memrealtime() - t0 > s.wait_ticks) {
           if (lane == 0) flag_status(s.status, kStatusA8Wait);
           done = true;
         }
@@ -1002,7 +1002,7 @@ __device__ void wait_slot(const Scratch& s, const SlotWait& w, int v, int lane) 
       return;
     }
     __builtin_amdgcn_s_sleep(4);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * kPlanWaitTicks) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * s.wait_ticks) {
       if (lane == 0) flag_status(s.status, kStatusA8Wait);
       return;
     }
@@ -1087,8 +1087,7 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
       ph = 0, u = unit_turn(i, Bw, rw), units = u13s;
     } else {
       if (!planned) {
-        stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out);
-        const int nvs = __builtin_amdgcn_readfirstlane(s_nvs);
+        const int nvs = stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out);
         sw.nvs = nvs;
         nC = (uint32_t)(nvs - nS) * u13r;
         nPost = nC + u2 + (uint32_t)(nvs - nS) * u2;

@@ -61,6 +61,10 @@ struct Scratch {
   uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
   int nsync;
   int act_stride;      // Imax / 64
+  // The longest a wait inside a launch spins (100 MHz device-clock ticks)
+  // before it sets its status bit and goes on: kWaitTicks, or
+  // MOE_DECODE_WAIT_LIMIT_US from the environment.
+  uint64_t wait_ticks;
   // timeline records [block][kTlPoints] of each kernel (nullptr: off)
   uint64_t* tl_seam;
   uint64_t* tl_logits;
@@ -79,6 +83,8 @@ struct Scratch {
 constexpr uint32_t kStatusA8Wait = 1u;
 constexpr uint32_t kStatusRouteWait = 2u;
 constexpr uint32_t kStatusXcdMap = 4u;
+// 100 ms of the 100 MHz device clock: far beyond any real wait.
+constexpr uint64_t kWaitTicks = 10000000ull;
 
 constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, persistent
 constexpr int kActCols = 64;     // columns of a per act group of the fused launch

@@ -414,15 +414,14 @@ __device__ __forceinline__ void merge64(uint64_t& a, uint64_t c, int lane) {
 // keys of expert groups w, w + 4, ... (GPW groups of 64) and merges them;
 // wave 0 merges the four waves' lists, and its lanes [0, k) hold the picks
 // in selection order.
-// Longest wait for a logit of the logit box before the run is flagged
-// (status 2) and the logit taken as 0: 100 ms of the 100 MHz device clock.
-constexpr uint64_t kLogitWaitTicks = 10000000ull;
+// A logit of the logit box that does not arrive within s.wait_ticks (100 ms
+// unless set lower) flags the run (status 2) and is taken as 0.
 
 // The logit at w of the logit box, once it is in.
 __device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s, uint64_t t0) {
   uint64_t v;
   while ((v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0ull) {
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kLogitWaitTicks) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > s.wait_ticks) {
       flag_status(s.status, kStatusRouteWait);
       return 0.0;
     }
