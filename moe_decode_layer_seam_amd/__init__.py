@@ -2,11 +2,15 @@
 
 Argument marshalling only -- every step of the layer runs in the HIP kernels
 of ``libmoe_decode.so`` (declared in ``include/moe_decode.h``).  The functions
-keep the C names without the ``moe_decode_`` prefix: ``plan``, ``run``,
-``inspect``, ``timing``, ``timing_read``, ``destroy``, ``quantize_weight``,
-``quantize_weight_fp4``, ``strerror``.  Tensors are torch tensors on the GPU (torch supplies device
-memory and streams); shapes, dtypes and contiguity are checked here before
-the pointers cross the boundary, because the kernels' loads are unchecked.
+keep the C names without the ``moe_decode_`` prefix: ``plan``,
+``scratch_bytes``, ``run``, ``run_noalloc``, ``inspect``, ``status``,
+``timing``, ``timing_read``, ``timeline``, ``timeline_read``, ``destroy``,
+``quantize_weight``, ``quantize_weight_fp4``, ``hc_fold``, ``attn_x8``,
+``read_probe``, ``strerror``, ``last_hip_error`` (``run_ptrs`` and
+``inspect_tensor`` are thin variants of ``run`` and ``inspect``).  Tensors are
+torch tensors on the GPU (torch supplies device memory and streams); shapes,
+dtypes and contiguity are checked here before the pointers cross the
+boundary, because the kernels' loads are unchecked.
 
 There is no fallback: if the library is missing this module raises.
 """

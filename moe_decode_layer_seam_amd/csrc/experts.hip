@@ -1245,9 +1245,6 @@ int w2_split_tiles(const LayerDims& d) {
   return (w2_seg_steps(d, d.I, fp4) == 2 || w2_seg_steps(d, d.Is, false) == 2) ? 8 : kTT2Split;
 }
 
-template <int TT, int NW>
-constexpr int unit_tiles() { return TT; }
-
 // Split mode when whole units would leave waves without one.  w13: the
 // expected slots of a step under uniform routing (E (1 - (1 - K/E)^m)
 // distinct experts, plus the shared expert's slots) times the whole units
@@ -1266,7 +1263,7 @@ bool gemm_split(const LayerDims& d, int m, int waves, bool w13) {
   if (w13) {
     if (m <= kRouteRows) return true;
     const double distinct = d.E * (1.0 - std::pow(1.0 - (double)d.K / d.E, m));
-    const double units = (distinct + shared) * (2.0 * d.Imax / 16 / unit_tiles<kTT13, kGemmWaves>());
+    const double units = (distinct + shared) * (2.0 * d.Imax / 16 / kTT13);
     return units < 0.9 * waves;
   }
   const int pairs = m * d.K;
@@ -1324,9 +1321,7 @@ int gemm_blocks_per_cu(bool w13, size_t lds) {
   int a, b;
   if (w13) {
     a = occupancy_t<true, kTT13, kGemmWaves>(lds);
-    b = occupancy_t<true, kTT13, kGemmWaves>(lds);
-    const int c = occupancy_t<true, 4, 8, true>(lds);
-    a = c < a ? c : a;
+    b = occupancy_t<true, 4, 8, true>(lds);
   } else {
     a = occupancy_t<false, kTT2Whole, kGemmWaves>(lds);
     b = occupancy_t<false, kTT2Split, kGemmWaves>(lds);
