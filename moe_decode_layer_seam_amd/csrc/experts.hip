@@ -87,7 +87,13 @@ template <bool W13, int TT, bool ALDS = false>
 __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const LayerDims& d, const Inputs& in,
                                             const Scratch& s, const int* s_tok, int m, int R, int g, int j,
                                             uint32_t x8o = 0, uint32_t xso = 0) {
-  const int ex = slot.x;
+  // A unit is one wave's: its slot and tile group are the same in every
+  // lane.  Read as such, the weight and code descriptors built from them
+  // stay in scalar registers; where the compiler could not prove it (slots
+  // read back from the LDS), every buffer load went into a loop over the
+  // lanes' distinct descriptors.
+  const int ex = __builtin_amdgcn_readfirstlane(slot.x);
+  tgroup = __builtin_amdgcn_readfirstlane(tgroup);
   const bool shared = ex < 0;
   const Geo G = geo<W13>(d, shared);
   const int N = 16 * G.tiles;
@@ -107,8 +113,8 @@ __device__ __forceinline__ UnitOps unit_ops(const int4& slot, int tgroup, const 
     WS = shared ? in.sw2_s : in.w2_s + (size_t)ex * (u.fp4 ? (size_t)(d.H / 16) * G.nseg * 256
                                                          : (size_t)(d.H / 32) * (d.I / 32));
   }
-  u.row0 = slot.y;
-  u.c = slot.z;
+  u.row0 = __builtin_amdgcn_readfirstlane(slot.y);
+  u.c = __builtin_amdgcn_readfirstlane(slot.z);
   u.col0 = 16 * TT * tgroup;
   u.nsteps = G.K / 128;
   u.seg = G.seg;
