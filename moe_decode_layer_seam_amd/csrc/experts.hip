@@ -418,7 +418,10 @@ __device__ __forceinline__ uint32_t unit_turn(uint32_t i, uint32_t B, uint32_t b
 // s_out (may be null): also each routed row's w2 output row, its pair.
 // Returns the slots the calling wave may use: the staged ones, or only the
 // nS shared ones when it gave up waiting for the staging wave (whose LDS
-// writes it then must not read).
+// writes it then must not read).  The count is the same in every lane of
+// the wave; it is returned (and taken by the callers) through
+// readfirstlane, since the unit map and the deal derived from it otherwise
+// compile to per-lane arithmetic and branches.
 __device__ int stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int* s_tok, int nS, int P, int vs_cap,
                           int* s_plan, int* s_nvs, int lane, int* s_out = nullptr) {
   int st = 0;
@@ -449,7 +452,7 @@ __device__ int stage_plan(const LayerDims& d, const Scratch& s, int4* s_vs, int*
     if (lane == 0) *s_nvs = nS + nR;
     wait_memory();  // the LDS writes are done
     if (lane == 0) __hip_atomic_store(s_plan, 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return nS + nR;
+    return __builtin_amdgcn_readfirstlane(nS + nR);
   }
   while (__hip_atomic_load(s_plan, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
     __builtin_amdgcn_s_sleep(1);
@@ -702,7 +705,7 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
       if (u >= um.total) {
         // past the shared expert's units: the routed ones need the picks
         if (planned) break;
-        const int nvs = stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane);
+        const int nvs = __builtin_amdgcn_readfirstlane(stage_plan(d, s, s_vs, s_tok, um.nS, P, vs_cap, &s_plan, &s_nvs, lane));
         um = unit_map_n<W13, TT>(d, nvs, um.nS, split);
         planned = true;
         if (u >= um.total) break;  // the last turn has no unit for this block
@@ -1093,7 +1096,7 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
       ph = 0, u = unit_turn(i, Bw, rw), units = u13s;
     } else {
       if (!planned) {
-        const int nvs = stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out);
+        const int nvs = __builtin_amdgcn_readfirstlane(stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out));
         sw.nvs = nvs;
         nC = (uint32_t)(nvs - nS) * u13r;
         nPost = nC + u2 + (uint32_t)(nvs - nS) * u2;
