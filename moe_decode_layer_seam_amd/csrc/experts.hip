@@ -600,8 +600,8 @@ __device__ __forceinline__ void run_unit(const int4& slot, int tgroup, int s0, i
   const UnitOps ops = unit_ops<W13, TT, ROUTE>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
   v4f tot[TT];
   // the launch that routes loads 2 K steps (16 KB) a burst: its blocks' pick
-  // polls then wait behind less, and it holds 204 VGPRs without spilling
-  // (m = 1: 65.6 -> 64.5 us; 1-step bursts took 66.3)
+  // polls then wait behind less (m = 1: 4-step bursts 63.4-63.7 us against
+  // 63.1-63.2, 1-step bursts slower still)
   unit_sums<TT, 0, ROUTE, ROUTE ? 2 : 0>(tot, ops, s0, s1, g, j);
   float* dst = part + (size_t)(split ? s0 : 0) * plane + ops.col0 + j;
 #pragma unroll
