@@ -11,9 +11,12 @@ consecutive steps (as a decode graph holds many layers).  To keep the 256 MB
 last-level cache from serving the expert weights, the steps rotate over
 several device copies of the whole weight set, each with its own input rows
 (so each copy picks its own experts); a labelled cache-warm figure repeats one
-copy.  After the timed region the same steps run eagerly, each kernel's
-dispatch recording its own start/stop HIP events on the run's stream, which
-gives the dominant kernel's average duration for the roofline.
+copy.  Right before the timed region the steps are warmed up in the same
+mode for --warmup steps and at least --warmup-s seconds, so that the GPU's
+clocks have settled after the graph capture.  After the timed region the
+same steps run eagerly, each kernel's dispatch recording its own start/stop
+HIP events on the run's stream, which gives the dominant kernel's average
+duration for the roofline.
 
 Output: one JSON line (rank 0).  `python bench.py --gpus N` with N > 1 exits:
 the benchmark measures one GPU.
@@ -367,6 +370,23 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
                 for i in range(n):
                     step(i % copies)
 
+        # warm-up in the timed mode, right before the timed region: the
+        # --warmup steps, extended to --warmup-s seconds of steps.  The GPU's
+        # clocks drop while the host captures the graphs; timed right after,
+        # one token ran 61.9-63.6 us a step and the draft layer 193 us, against
+        # 60.0-60.9 and 186.6 us once they had settled (a second of steps;
+        # three seconds gave the same)
+        t_wu = time.perf_counter()
+        wu_steps = 0
+        chunk = 8 * (G if graphs else copies)
+        while wu_steps < args.warmup or time.perf_counter() - t_wu < args.warmup_s:
+            run_steps(chunk)
+            wu_steps += chunk
+            torch.cuda.synchronize()
+        wu_s = time.perf_counter() - t_wu
+        if mdl.status(h):
+            raise InvalidRun(f"{cfg['name']}: a wait timed out in the warm-up replays")
+
         # ---- timed region
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
         torch.cuda.synchronize()
@@ -396,7 +416,11 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
                     for i in range(G):
                         step(0)
             torch.cuda.current_stream().wait_stream(st)
-            gw.replay()
+            t_w = time.perf_counter()
+            while time.perf_counter() - t_w < args.warmup_s:  # as before the timed region
+                for _ in range(8):
+                    gw.replay()
+                torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = max(1, args.steps // G)
             e0.record()
@@ -465,6 +489,8 @@ def bench_config(cfg: dict, args, wsets: list, xs_all: list, small: dict) -> dic
         "median_batch_us_per_layer": batch_us[len(batch_us) // 2],
         "cache_warm_us_per_layer": warm_us,
         "steps_per_graph": G if args.mode == "graph" else None,
+        "warmup_steps": wu_steps,
+        "warmup_s": wu_s,
         "weight_copies": copies,
         "mfma_row_occupancy": row_occupancy,
         "expert_hbm_frac": expert_step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
@@ -486,6 +512,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-s", type=float, default=1.0,
+                    help="warm-up before each timed region lasts at least this long (seconds)")
     ap.add_argument("--configs", default="1,2,3,4",
                     help="workload indices, the first one the headline (0 tiny; 1-3 the layer at "
                          "M = 1, 16, 48; 4 the draft layer; 5-6 the eight-way tensor-parallel share)")
