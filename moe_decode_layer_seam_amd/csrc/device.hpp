@@ -357,13 +357,11 @@ __device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t voff, uint32_t sof
 // ---------------------------------------------------------------------------
 constexpr int kCoherent = 16;  // sc1
 // Activations a launch made itself and handed over inside one XCD (the
-// persistent launch's a8): values with sc0, from the XCD's L2 (the reading
-// CU has not read those lines before); their E8M0 codes with sc1, past the
-// reading CU's cache -- a code row of 64 bytes shares its cache line with
-// its neighbour row, which the CU may have read while this row's codes were
-// still being written.  The codes are written through (store_code_through).
+// persistent launch's a8, values and codes): with sc0, from the XCD's L2.
+// They are read only after a barrier of the XCD's blocks that follows every
+// store of them, by CUs that have not read those lines before in the launch,
+// so no CU's own cache holds a stale copy.
 constexpr int kScL2 = 1;  // sc0
-__host__ __device__ constexpr int code_aux(int aux) { return aux == kScL2 ? kCoherent : aux; }
 
 template <int AUX>
 __device__ __forceinline__ u32x4 bload16a(rsrc_t r, uint32_t voff, uint32_t soff) {

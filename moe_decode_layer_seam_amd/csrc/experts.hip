@@ -175,7 +175,7 @@ __device__ __forceinline__ void load_step(Step<TT>& f, const UnitOps& u, int st)
     const uint32_t ao = ok ? u.alane + kw : kNoRow;
     f.alo = bload16a<AUX>(u.a, ao, 0);
     f.ahi = bload16a<AUX>(u.a, ao + 64, 0);
-    f.sa = bload8a<code_aux(AUX)>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
+    f.sa = bload8a<AUX>(u.as, ok ? u.aslane + 4 * st : kNoRow, 0);
   }
 }
 
@@ -239,7 +239,7 @@ __device__ __forceinline__ void load_codes4(Codes4<TT>& c, const UnitOps& u, int
   if constexpr (ALDS)
     c.a = ok && u.aslane != kNoRow ? lds32(u.aslane - g + 16 * seg + 4 * g) : 0u;
   else
-    c.a = bload32a<code_aux(AUX)>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
+    c.a = bload32a<AUX>(u.as, ok ? u.aslane - g + 16 * seg + 4 * g : kNoRow, 0);
 }
 
 template <int TT>
@@ -743,21 +743,13 @@ void gemm_kernel(LayerDims d, Inputs in, Scratch s, int m, int split, int vs_cap
 
 // a = SiLU(gate) * up of row r, column col (one lane each, 32 consecutive
 // columns in 32 consecutive lanes), and its MXFP8: the code of the 32
-// columns' amax, the byte of a scaled by 2^(127 - code).  THROUGH: the code
-// is written through to memory (read back with code_aux(kScL2)).
-template <bool THROUGH = false>
+// columns' amax, the byte of a scaled by 2^(127 - code).
 __device__ __forceinline__ void act_store(const LayerDims& d, const Scratch& s, int r, int col, float hg, float hu) {
   const float a = hg / (1.0f + __expf(-hg)) * hu;
   const float amax = group_max(fabsf(a), 32);
   const int code = e8m0_code(amax);
   s.a8[(size_t)r * d.Imax + col] = (uint8_t)(fp8x2(a * mx_mul(code), 0.0f) & 0xFF);
-  if ((col & 31) == 0) {
-    uint8_t* cp = s.a8s + (size_t)r * (d.Imax / 32) + col / 32;
-    if constexpr (THROUGH)
-      __hip_atomic_store(cp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      *cp = (uint8_t)code;
-  }
+  if ((col & 31) == 0) s.a8s[(size_t)r * (d.Imax / 32) + col / 32] = (uint8_t)code;
 }
 
 // SiLU(gate) * up of row r (blockIdx.y), columns blockIdx.x * 256 + tid, and
@@ -869,11 +861,11 @@ constexpr int kTT13 = 4;       // w13 units, both modes
 constexpr int kTT2Whole = 8;   // whole-mode w2 units
 constexpr int kTT2Split = 4;   // split-mode w2 units over 4-step segments
 constexpr int kGemmWaves = 8;  // waves per block of either GEMM
-// K steps per load burst of the persistent launch's units (w13, w2): 8 and
-// 16 KB a wave.  Its hand-offs make round trips through the memory queues that the
-// weight stream fills; smaller bursts keep those queues short.
-constexpr int kXcdBurst13 = 1;
-constexpr int kXcdBurst2 = 1;
+// K steps per load burst of the persistent launch's units (w13, w2): 16 KB
+// a wave for w13 (as in the w13 launch that routes, whose pick polls then
+// queue behind less), a whole 256-column w2 slice for w2.
+constexpr int kXcdBurst13 = 2;
+constexpr int kXcdBurst2 = 2;
 
 // ===========================================================================
 // The persistent launch of a step of at most kRouteRows tokens: the seam,
@@ -884,48 +876,37 @@ constexpr int kXcdBurst2 = 1;
 // checks it against the others.  Those blocks take slice x of every active
 // expert's intermediate: gate rows [x S, (x + 1) S) and up rows
 // [Kv + x S, ...) of w13 (S = Kv / kXcds), and the same S columns of w2.
-// So each hand-off of an expert -- its w13 sums to its SiLU * up, its a8 to
-// its w2 units -- stays inside one XCD's L2, which every CU of the XCD
-// shares: the sums and a8 are stored and completed (written through to the
-// L2) and counted by atomics performed there (no sc1); the counts are read
-// by atomics too, and the data (sc0) only by CUs that have not read those
-// lines before in the launch, so their own caches hold no copy of them.  A
-// hand-off through device memory would
-// queue behind the weight stream; one through the L2 does not.  Nothing
-// crosses XCDs until the launch ends: the combine launch adds the slices'
-// w2 sums (plane x holds slice x) in slice order, which is the w2 segment
-// order of every other step width (w2 segments are S = 256 columns here).
+// So every hand-off -- the w13 sums to SiLU * up, the a8 to w2 -- stays
+// inside one XCD's L2, which every CU of the XCD shares.  Nothing crosses
+// XCDs until the launch ends: the combine launch adds the slices' w2 sums
+// (plane x holds slice x) in slice order, which is the w2 segment order of
+// every other step width (w2 segments are S = 256 columns here).
 //
-// The units of an XCD are dealt over its blocks (the m route blocks, rank 0
-// of XCDs 0..m-1, take none) in this order: the shared expert's w13 (tile
-// groups of 64 rows in the slice, times the H segments), then, once the
-// picks are in, every routed slot's w13, the shared expert's w2 (tile
-// groups of 128 output rows over the slice) and every routed slot's w2.
-// The w13 unit that completes the count of an act group (64 columns: a
-// gate and an up tile group, every H segment) computes the group's a8 from
-// the summed planes with the act launch's arithmetic and counts the group
-// on its slot's ready word for the XCD; a w2 unit waits until that word
-// holds the slice's groups (one wave of a block polls, wait_slot).  A wave
-// counts each w13 unit as soon as its stores complete, so it never waits
-// while holding an uncounted unit.  So with every block resident each wait
-// ends.
+// Each XCD runs three phases, its blocks meeting at a barrier between them
+// (an arrival count performed in the XCD's L2):
+//   1. w13: the shared expert's units (tile groups of 64 rows in the slice,
+//      times the H segments), then, once the picks are in, every routed
+//      slot's, dealt over the XCD's blocks (the m route blocks, rank 0 of
+//      XCDs 0..m-1, take none);
+//   2. SiLU * up: the slice's act groups (slot, 64 columns), one a wave,
+//      with the act launch's arithmetic on the summed planes;
+//   3. w2: the shared expert's units (tile groups of 128 output rows over
+//      the slice), then every routed slot's.
+// The sums and a8 are stored and completed before a block arrives, and read
+// after the barrier by loads that reach the L2 (sc0; the a8 codes, which
+// share cache lines between rows, are written through and read with sc1).
+// Per-slot counts that let w2 units start before the whole w13 phase ended
+// were measured slower: each hand-off then queued behind the weight stream.
 // ===========================================================================
 
 __device__ __forceinline__ float ld_l2(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kScL2));
 }
 
-// Counts w13 unit (slot v, act group q) on the XCD's L2; the unit that
-// completes the group computes its a8 (rows of the slot, 64 columns, lane =
-// column) and counts the group on ready word v * kXcds + x.
-__device__ void count_w13(const LayerDims& d, const Scratch& s, int m, const int4& slot, int v, int q, int x,
-                          uint32_t expect, int nseg, int lane) {
-  uint32_t old = 0;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(&s.act_cnt[(size_t)v * s.act_stride + q], 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-  old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
-  if (old + 1u != expect) return;
+// The a8 of act group q (64 columns, lane = column) of slot `slot` from the
+// w13 sums of its nseg planes, every row of the slot.
+__device__ void act_group(const LayerDims& d, const Scratch& s, int m, const int4& slot, int q, int nseg,
+                          int lane) {
   const int Kv = slot.x < 0 ? d.Is : d.I;
   const uint32_t width = 2u * (uint32_t)d.Imax;
   const uint32_t plane = (uint32_t)(m * d.K + m) * width;
@@ -950,72 +931,43 @@ __device__ void count_w13(const LayerDims& d, const Scratch& s, int m, const int
         }
       }
     }
-    act_store<true>(d, s, slot.y + i, col, hg, hu);
+    act_store(d, s, slot.y + i, col, hg, hu);
   }
-  wait_memory();  // the a8 bytes are in the L2, the codes in memory
-  if (lane == 0)
-    (void)__hip_atomic_fetch_add(&s.ready[(size_t)v * kXcds + x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// The count in a ready word, read in the XCD's L2.  A load, even at
+// The count in an arrival word, read in the XCD's L2.  A load, even at
 // workgroup scope, may be served by this CU's own cache, which would keep
 // the first value it saw; an atomic is performed in the L2.  An atomic that
 // changes nothing (adding 0) is compiled into a load, so the read sets bit
-// 31, which the counts (a slice's act groups) never reach, and masks it
-// off.  The combine launch zeroes the words for the next step.
+// 31, which the counts never reach, and masks it off.  The combine launch
+// zeroes the words for the next step.
 constexpr uint32_t kPeekBit = 0x80000000u;
 __device__ __forceinline__ uint32_t peek_l2(uint32_t* p) {
   return __hip_atomic_fetch_or(p, kPeekBit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & ~kPeekBit;
 }
 
-// The slots whose a8 slice this XCD has completed, as seen by a block: one
-// bit per slot in the block's LDS.  A wave that needs slot v and finds its
-// bit clear takes the block's poll lock (the others sleep and re-read the
-// mask), then reads every slot's ready word at once (lane = slot) until
-// slot v's is complete, publishing each poll's mask.  So a block puts one
-// wave's reads on the L2, not one per waiting wave: a few hundred waves
-// spinning on one word would queue behind each other there, and hold up
-// the counts and the a8 that end the wait.  Counts only grow, so a mask
-// never loses a bit.  100 ms bound: then the status word is flagged and the
-// bit set, and the waves go on.
-struct SlotWait {
-  uint64_t* mask;   // LDS: slots complete on this XCD
-  uint32_t* lock;   // LDS: 1 while a wave of the block polls
-  int nvs, x;
-  uint32_t want_s, want_r;  // act groups of a slice: shared slot 0, routed
-};
-
-__device__ void wait_slot(const Scratch& s, const SlotWait& w, int v, int lane) {
-  const uint64_t bit = 1ull << v;
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (!(__hip_atomic_load(w.mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & bit)) {
-    uint32_t got = 0;
-    if (lane == 0)
-      got = __hip_atomic_exchange(w.lock, 1u, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u ? 1u : 0u;
-    if (__builtin_amdgcn_readfirstlane((int)got)) {
-      while (true) {
-        uint32_t c = 0;
-        if (lane < w.nvs) c = peek_l2(&s.ready[(size_t)lane * kXcds + w.x]);
-        const uint64_t in = __ballot(lane < w.nvs && c >= (lane == 0 ? w.want_s : w.want_r));
-        bool done = (in & bit) != 0ull;
-        if (!done && __builtin_amdgcn_s_memrealtime() - t0 > s.wait_ticks) {
-          if (lane == 0) flag_status(s.status, kStatusA8Wait);
-          done = true;
-        }
-        if (lane == 0)
-          (void)__hip_atomic_fetch_or(w.mask, done ? (in | bit) : in, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (done) break;
-        __builtin_amdgcn_s_sleep(8);
+// Barrier of the `blocks` blocks of one XCD on arrival word w: every wave's
+// stores completed, the block counted once, and wave 0 reads the word until
+// it holds every block.  A wait past s.wait_ticks sets the status word (the
+// block then goes on).  Called by every thread of the block.
+__device__ void xcd_barrier(uint32_t* w, uint32_t blocks, const Scratch& s, int tid) {
+  wait_memory();
+  __syncthreads();
+  if (tid < 64) {
+    if (tid == 0) (void)__hip_atomic_fetch_add(w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      uint32_t c = 0;
+      if (tid == 0) c = peek_l2(w);
+      if (__builtin_amdgcn_readfirstlane((int)c) >= (int)blocks) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > s.wait_ticks) {
+        if (tid == 0) flag_status(s.status, kStatusA8Wait);
+        break;
       }
-      if (lane == 0) __hip_atomic_store(w.lock, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(4);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > 2 * s.wait_ticks) {
-      if (lane == 0) flag_status(s.status, kStatusA8Wait);
-      return;
+      __builtin_amdgcn_s_sleep(2);
     }
   }
+  __syncthreads();
 }
 
 template <int NW>
@@ -1023,23 +975,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4)
 void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
   constexpr int TT13 = kTT13, TT2 = 8;
   unsigned char* lds_raw = dyn_lds;
-  __shared__ uint32_t s_next, s_plock;
-  __shared__ uint64_t s_ready;
+  __shared__ uint32_t s_next;
   __shared__ int s_plan, s_nvs;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, j = lane & 15;
   stamp(s.tl_experts, kTlPoints, 0);
   const int b = blockIdx.x, x = b % kXcds, rank = b / kXcds;
-  if (tid == 0) {
-    // every block with index x mod kXcds must run on one XCD: the first of
-    // them records its XCC id, the others compare
-    const uint32_t id = (__builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xF) + 1u;
-    uint32_t prev = 0;
-    if (!__hip_atomic_compare_exchange_strong(&s.sync[8 + x], &prev, id, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) &&
-        prev != id)
-      flag_status(s.status, kStatusXcdMap);
-  }
   const int R = m * d.K + m, P = m * d.K;
   // LDS: the slots, row -> token, row -> w2 output row, then the MXFP8 rows
   const uint32_t x8o = ((uint32_t)vs_cap * 16 + (uint32_t)R * 8 + 15u) & ~15u;
@@ -1059,8 +1000,6 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
     s_vs[0] = make_int4(-1, P, m, 0);
     s_plan = 0;
     s_next = 0;
-    s_plock = 0;
-    s_ready = 0;
   }
   if (tid < m) {
     s_tok[P + tid] = tid;
@@ -1075,100 +1014,116 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
   const int nseg13 = (d.H / 128 + kSegSteps - 1) / kSegSteps;
   const uint32_t u13s = (uint32_t)(2 * Ss / 64 * nseg13), u13r = (uint32_t)(2 * Sr / 64 * nseg13);
   const uint32_t u2 = (uint32_t)(d.H / (16 * TT2));
-  const uint32_t expect13 = 2u * (uint32_t)nseg13;
-  // turns: the shared w13 units (phase A), then, once the picks are in, one
-  // list of every routed w13 unit (C), the shared w2 units (B) and the
-  // routed w2 units (D), slot by slot.  Each w2 unit comes after every w13
-  // unit of the XCD has been dealt, so by the time a wave takes it the
-  // slot's a8 is mostly complete: the shared expert's long before, the
-  // first routed slots a whole turn of the XCD's waves earlier.
-  const uint32_t tA = (u13s + Bw - 1) / Bw;
-  uint32_t nC = 0, nPost = 0, tP = 0;
-  bool planned = false;
   const uint32_t width13 = 2u * (uint32_t)d.Imax;
   const size_t plane13 = (size_t)R * width13, plane2 = (size_t)R * d.H;
-  SlotWait sw{&s_ready, &s_plock, 0, x, (uint32_t)(Ss / 64), (uint32_t)(Sr / 64)};
+
+  // phase 1, w13: the shared expert's turns, then (once the picks are in)
+  // the routed slots' turns
+  const uint32_t tA = (u13s + Bw - 1) / Bw;
+  uint32_t nC = 0, tC = 0;
+  int nvs = nS;
+  bool planned = false;
   uint32_t i = wave;
   while (true) {
-    int ph;
     uint32_t u, units;
+    bool shared;
     if (i < tA) {
-      ph = 0, u = unit_turn(i, Bw, rw), units = u13s;
+      u = unit_turn(i, Bw, rw), units = u13s, shared = true;
     } else {
       if (!planned) {
-        const int nvs = __builtin_amdgcn_readfirstlane(stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out));
-        sw.nvs = nvs;
+        nvs = __builtin_amdgcn_readfirstlane(
+            stage_plan(d, s, s_vs, s_tok, nS, P, vs_cap, &s_plan, &s_nvs, lane, s_out));
         nC = (uint32_t)(nvs - nS) * u13r;
-        nPost = nC + u2 + (uint32_t)(nvs - nS) * u2;
-        tP = (nPost + Bw - 1) / Bw;
+        tC = (nC + Bw - 1) / Bw;
         planned = true;
       }
-      if (i >= tA + tP) break;
-      const uint32_t gu = unit_turn(i - tA, Bw, rw);
-      if (gu < nC) {
-        ph = 2, u = gu, units = nC;
-      } else if (gu < nC + u2) {
-        ph = 1, u = gu - nC, units = u2;
-      } else {
-        ph = 3, u = gu - nC - u2, units = nPost - nC - u2;
-      }
+      if (i >= tA + tC) break;
+      u = unit_turn(i - tA, Bw, rw), units = nC, shared = false;
     }
     uint32_t nx = 0;
     if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (u < units) {
-      if (ph == 0 || ph == 2) {
-        // w13: slot, tile group in the slice (gate groups, then up groups),
-        // H segment
-        const uint32_t per = ph == 0 ? u13s : u13r;
-        const int v = ph == 0 ? 0 : nS + (int)(u / per);
-        const uint32_t uu = u % per;
-        const int tg = (int)(uu / (uint32_t)nseg13), seg = (int)(uu % (uint32_t)nseg13);
-        const int4 slot = s_vs[v];
-        const int S = ph == 0 ? Ss : Sr, Kv = ph == 0 ? d.Is : d.I;
-        const int gps = S / 64;  // act groups (and gate tile groups) per slice
-        const int q = x * gps + (tg % gps);
-        const int tgroup = tg < gps ? q : (Kv / 64 + q);
-        const UnitOps ops = unit_ops<true, TT13, true>(slot, tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
-        v4f tot[TT13];
-        unit_sums<TT13, 0, true, kXcdBurst13>(tot, ops, seg, seg + 1, g, j);
-        float* dst = s.part13 + (size_t)seg * plane13 + ops.col0 + j;
+      // slot, tile group in the slice (gate groups, then up groups), H segment
+      const uint32_t per = shared ? u13s : u13r;
+      const int v = shared ? 0 : nS + (int)(u / per);
+      const uint32_t uu = u % per;
+      const int tg = (int)(uu / (uint32_t)nseg13), seg = (int)(uu % (uint32_t)nseg13);
+      const int S = shared ? Ss : Sr, Kv = shared ? d.Is : d.I;
+      const int gps = S / 64;  // act groups (and gate tile groups) per slice
+      const int q = x * gps + (tg % gps);
+      const int tgroup = tg < gps ? q : (Kv / 64 + q);
+      const UnitOps ops = unit_ops<true, TT13, true>(s_vs[v], tgroup, d, in, s, s_tok, m, R, g, j, x8o, xso);
+      v4f tot[TT13];
+      unit_sums<TT13, 0, true, kXcdBurst13>(tot, ops, seg, seg + 1, g, j);
+      float* dst = s.part13 + (size_t)seg * plane13 + ops.col0 + j;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          if (4 * g + qq < ops.c) {
-            const size_t r = (size_t)(ops.row0 + 4 * g + qq);
+      for (int qq = 0; qq < 4; ++qq) {
+        if (4 * g + qq < ops.c) {
+          const size_t r = (size_t)(ops.row0 + 4 * g + qq);
 #pragma unroll
-            for (int t = 0; t < TT13; ++t) dst[r * width13 + 16 * t] = tot[t][qq];
-          }
-        }
-        // counted as soon as its sums are in the L2: the wave waits for its
-        // stores and the count, while the CU's other waves keep the weight
-        // stream's bytes in flight
-        wait_memory();
-        count_w13(d, s, m, slot, v, q, x, expect13, nseg13, lane);
-      } else {
-        // w2: slot, tile group of output rows, over the slice's K steps
-        const int v = ph == 1 ? 0 : nS + (int)(u / u2);
-        const int tg = (int)(u % u2);
-        const int4 slot = s_vs[v];
-        wait_slot(s, sw, v, lane);
-        const UnitOps ops = unit_ops<false, TT2>(slot, tg, d, in, s, s_out, m, R, g, j);
-        v4f tot[TT2];
-        unit_sums<TT2, kScL2, false, kXcdBurst2>(tot, ops, x, x + 1, g, j);
-        float* dst = s.part2 + (size_t)x * plane2 + ops.col0 + j;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          if (4 * g + qq < ops.c) {
-            const size_t orow = (size_t)s_out[ops.row0 + 4 * g + qq];
-#pragma unroll
-            for (int t = 0; t < TT2; ++t) dst[orow * d.H + 16 * t] = tot[t][qq];
-          }
+          for (int t = 0; t < TT13; ++t) dst[r * width13 + 16 * t] = tot[t][qq];
         }
       }
     }
     i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
   }
-  stamp_wave(s.tl_experts, kTlPoints, 3 + (wave & 3));
+  // (every wave leaves the loop through the routed turns, so it has read
+  // the slot count)
+  stamp(s.tl_experts, kTlPoints, 3);
+  xcd_barrier(&s.sync[kXcdBarrier1 + x], Bw, s, tid);
+
+  // phase 2, SiLU * up: act group k of the slice (the shared slot's gps_s,
+  // then gps_r per routed slot), one a wave
+  const int gps_s = Ss / kActCols, gps_r = Sr / kActCols;
+  const uint32_t nact = (uint32_t)(gps_s + (nvs - nS) * gps_r);
+  for (uint32_t k = (uint32_t)wave * Bw + rw; k < nact; k += (uint32_t)NW * Bw) {
+    const bool shared = k < (uint32_t)gps_s;
+    const int v = shared ? 0 : nS + (int)((k - gps_s) / (uint32_t)gps_r);
+    const int ql = shared ? (int)k : (int)((k - gps_s) % (uint32_t)gps_r);
+    act_group(d, s, m, s_vs[v], x * (shared ? gps_s : gps_r) + ql, nseg13, lane);
+  }
+  if (tid == 0) s_next = 0;
+  stamp(s.tl_experts, kTlPoints, 4);
+  xcd_barrier(&s.sync[kXcdBarrier2 + x], Bw, s, tid);
+
+  // phase 3, w2: slot, tile group of output rows, over the slice's K steps
+  const uint32_t n2 = (uint32_t)nvs * u2, t2 = (n2 + Bw - 1) / Bw;
+  i = wave;
+  while (i < t2) {
+    const uint32_t u = unit_turn(i, Bw, rw);
+    uint32_t nx = 0;
+    if (lane == 0) nx = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (u < n2) {
+      const int v = (int)(u / u2), tg = (int)(u % u2);
+      const UnitOps ops = unit_ops<false, TT2>(s_vs[v], tg, d, in, s, s_out, m, R, g, j);
+      v4f tot[TT2];
+      unit_sums<TT2, kScL2, false, kXcdBurst2>(tot, ops, x, x + 1, g, j);
+      float* dst = s.part2 + (size_t)x * plane2 + ops.col0 + j;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        if (4 * g + qq < ops.c) {
+          const size_t orow = (size_t)s_out[ops.row0 + 4 * g + qq];
+#pragma unroll
+          for (int t = 0; t < TT2; ++t) dst[orow * d.H + 16 * t] = tot[t][qq];
+        }
+      }
+    }
+    i = NW + (uint32_t)__builtin_amdgcn_readfirstlane((int)nx);
+  }
+  stamp_wave(s.tl_experts, kTlPoints, 5 + (wave & 1));
   __syncthreads();
+  if (tid == 0) {
+    // every block with index x mod kXcds must have run on one XCD: the first
+    // of them records its XCC id, the others compare (at the end, so the
+    // round trip does not delay the seam; a block on another XCD would have
+    // timed out at the barriers)
+    const uint32_t id = (__builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xF) + 1u;
+    uint32_t prev = 0;
+    if (!__hip_atomic_compare_exchange_strong(&s.sync[8 + x], &prev, id, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) &&
+        prev != id)
+      flag_status(s.status, kStatusXcdMap);
+  }
   stamp(s.tl_experts, kTlPoints, 1);
 }
 

@@ -48,19 +48,16 @@ struct Scratch {
   float* part2;        // [planes][R][H] fp32 w2 sums (per K segment in split mode)
   // The hand-off words, nsync from `sync`, zeroed by the seam launch (and
   // after the persistent launch by the combine launch): the route launch's
-  // arrival counter (word 0); per virtual slot and XCD the act groups whose
-  // a8 is stored (ready); per slot and 64-column act group the w13 units
-  // counted (act_cnt); the boxes.
+  // arrival counter (word 0); the persistent launch's XCC ids (words 8..15)
+  // and barrier counts (kXcdBarrier1, kXcdBarrier2, one word per XCD); the
+  // boxes.
   uint32_t* sync;
   // The run's status word, in its own 256 bytes: bits set by a wait that
   // timed out (kStatus*); sticky across runs until the host clears it.
   uint32_t* status;
-  uint32_t* ready;     // [max_vs][kXcds]
-  uint32_t* act_cnt;   // [max_vs][act_stride]
   uint32_t* pick_box;  // [kPickBox] the picks, for the w13 launch that routes (tagged words)
   uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
   int nsync;
-  int act_stride;      // Imax / 64
   // The longest a wait inside a launch spins (100 MHz device-clock ticks)
   // before it sets its status bit and goes on: kWaitTicks, or
   // MOE_DECODE_WAIT_LIMIT_US from the environment.
@@ -87,7 +84,9 @@ constexpr uint32_t kStatusXcdMap = 4u;
 constexpr uint64_t kWaitTicks = 10000000ull;
 
 constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, persistent
-constexpr int kActCols = 64;     // columns of a per act group of the fused launch
+constexpr int kActCols = 64;     // columns of an act group of the persistent launch
+constexpr int kXcdBarrier1 = 16; // sync words of the persistent launch's barriers (+ XCD)
+constexpr int kXcdBarrier2 = 24;
 constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment (w13; w2: w2_seg_steps)
 
 // The persistent launch of small steps cuts the intermediate of every expert
