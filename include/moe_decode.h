@@ -72,8 +72,9 @@ extern "C" {
  * persistent MoE launch whose phases hand off through device counters:
  * [layer] run_ffn, build_mono_ffn; [device] atomic_add_dev); other steps run
  * the short launches.  The persistent launch cuts every active expert's
- * intermediate into one slice per XCD, so each hand-off stays in one XCD's
- * L2.  It covers E4M3 routed experts whose I and Is are 2048 or 4096, with
+ * intermediate into one slice per XCD, and each XCD's blocks meet at a
+ * barrier (a count in that XCD's L2) between w13, SiLU * up and w2, so
+ * each hand-off stays in one XCD's L2.  It covers E4M3 routed experts whose I and Is are 2048 or 4096, with
  * the other conditions of the w13 launch that routes (below); the plan
  * checks that the device deals a launch's blocks to its XCDs round-robin
  * (from any first XCD), else every step runs the short launches.  It
@@ -244,10 +245,12 @@ int moe_decode_inspect(moe_decode_handle plan, int32_t tap,
  * MOE_DECODE_WAIT_LIMIT_US microseconds when that environment variable is
  * set as a plan is made, or a no-alloc run starts: a low value makes the
  * waits give up at once, to check this path) and sets a bit; the
- * run's output is then not valid.  Bits: 1 a wait of the persistent launch
- * for a slot's a8; 2 a wait of a launch that routes (m <= 4) for the logits
- * or the picks; 4 blocks of the persistent launch whose indices agree mod
- * the XCD count ran on different XCDs (their hand-offs then crossed XCDs).  The bits are sticky: no kernel clears them, so a
+ * run's output is then not valid.  Bits: 1 a barrier of the persistent
+ * launch (between its w13, SiLU * up and w2 phases); 2 a wait of a launch
+ * that routes (m <= 4) for the logits or the picks; 4 blocks of the
+ * persistent launch whose indices agree mod the XCD count ran on different
+ * XCDs (their hand-offs then crossed XCDs).  The bits are sticky: no kernel
+ * clears them, so a
  * check after many runs (a graph replayed many times) covers all of them.
  * moe_decode_status synchronises `stream`, copies the word to *h_status and,
  * when `clear` is nonzero, zeroes it.  Not during stream capture
@@ -280,10 +283,12 @@ int moe_decode_timing_read(moe_decode_handle plan, int32_t kernel,
  *   route: 0 start, 5 scores computed, 1 groups sorted, 6 lists merged,
  *          2 picks stored, 3 last block admitted, 4 plan written (3-4 only
  *          in the last block; 3 not with one token)
- *   w13, w2, persistent: 0 start, 3 + w: wave w of the block done, 1 end;
- *          w13 that routes and the persistent launch also 2: their seam
- *          done (the route block's route points are stored as route's,
- *          block = token)
+ *   w13, w2: 0 start, 3 + w: wave w of the block done, 1 end; w13 that
+ *          routes also 2: its seam done (the route block's route points
+ *          are stored as route's, block = token)
+ *   persistent: 0 start, 2 seam done, 3 w13 phase done (wave 0), 4 SiLU *
+ *          up phase done (wave 0), 5 and 6 the w2 phase done (the last
+ *          even and the last odd wave to store), 1 end
  *   act, combine: 0 start, 1 end (thread 0's part)
  * Point 7 of every record holds where the block ran (XCC id << 32 | the
  * HW_ID register).  Blocks past the first 1024 of a launch are not recorded.

@@ -2,7 +2,8 @@
 
 The launches that route inside w13 (and the persistent launch) wait on other
 blocks of the same launch: for the router's logits, for the picks and, in
-the persistent launch, for a slot's a8.  Each wait is bounded; one that runs
+the persistent launch, at the barriers of an XCD's blocks between its w13,
+SiLU * up and w2 phases.  Each wait is bounded; one that runs
 past its bound sets a bit of the plan's sticky status word and the wave goes
 on, so the run's output is not valid but nothing hangs.  A plan made while
 MOE_DECODE_WAIT_LIMIT_US is 0 has every such wait give up at its first
@@ -29,7 +30,7 @@ pytestmark = pytest.mark.gpu
 # of the persistent schedule run the persistent launch
 CFG = dict(name="status_m1", m=1, hidden=256, experts=64, topk=6, inter=2048, shared_inter=2048,
            rms_eps=1e-6, routed_scale=1.0)
-ROUTE_WAIT, A8_WAIT = 2, 1
+ROUTE_WAIT, XCD_BARRIER = 2, 1
 
 
 def _plan(schedule):
@@ -57,7 +58,7 @@ def test_waits_that_give_up_set_the_status_word(schedule):
         torch.cuda.synchronize()
         st = mdl.status(h)
         assert st & ROUTE_WAIT, f"no wait for the logits or the picks gave up (status {st})"
-        assert st & ~(ROUTE_WAIT | A8_WAIT) == 0, f"unexpected status bits {st}"
+        assert st & ~(ROUTE_WAIT | XCD_BARRIER) == 0, f"unexpected status bits {st}"
         assert mdl.status(h) == 0, "reading the status word did not clear it"
     finally:
         mdl.destroy(h)
