@@ -158,10 +158,10 @@ Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool t
   L.a8 = take(R * d.Imax), L.a8s = take(R * d.Imax / 32);
   // the hand-off words, zeroed by the seam launch: the route launch's arrival
   // counter (word 0), the XCC id + 1 seen by the persistent launch's blocks
-  // of each index mod kXcds (words 8..15), that launch's two barrier counts
-  // per XCD (words 16..31), then from word 64 the boxes of the launches that
-  // route: the pick box, then (from an even word) the logit box
-  L.lbox = (64 + (size_t)kPickBox + 1) & ~(size_t)1;
+  // of each index mod kXcds (words 8..15), from word 64 that launch's two
+  // barrier counts per XCD (a cache line each), then the boxes of the
+  // launches that route: the pick box, then (from an even word) the logit box
+  L.lbox = (kXcdBarrierBase + kXcdBarrierWords + (size_t)kPickBox + 1) & ~(size_t)1;
   L.nsync = L.lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   L.sync = take(L.nsync * 4);
   L.status = take(4);
@@ -218,7 +218,7 @@ Scratch scratch_at(char* b, const Layout& L, const LayerDims& d, int max_vs) {
   s.sync = reinterpret_cast<uint32_t*>(b + L.sync);
   s.counter = s.sync;
   s.status = reinterpret_cast<uint32_t*>(b + L.status);
-  s.pick_box = s.sync + 64;
+  s.pick_box = s.sync + kXcdBarrierBase + kXcdBarrierWords;
   s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + L.lbox) : nullptr;
   s.nsync = (int)L.nsync;
   return s;

@@ -1070,7 +1070,7 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
   // (every wave leaves the loop through the routed turns, so it has read
   // the slot count)
   stamp(s.tl_experts, kTlPoints, 3);
-  xcd_barrier(&s.sync[kXcdBarrier1 + x], Bw, s, tid);
+  xcd_barrier(&s.sync[kXcdBarrierBase + x * kXcdBarrierStride], Bw, s, tid);
 
   // phase 2, SiLU * up: act group k of the slice (the shared slot's gps_s,
   // then gps_r per routed slot), one a wave
@@ -1084,7 +1084,7 @@ void xcd_kernel(LayerDims d, Inputs in, Scratch s, int m, int vs_cap) {
   }
   if (tid == 0) s_next = 0;
   stamp(s.tl_experts, kTlPoints, 4);
-  xcd_barrier(&s.sync[kXcdBarrier2 + x], Bw, s, tid);
+  xcd_barrier(&s.sync[kXcdBarrierBase + (kXcds + x) * kXcdBarrierStride], Bw, s, tid);
 
   // phase 3, w2: slot, tile group of output rows, over the slice's K steps
   const uint32_t n2 = (uint32_t)nvs * u2, t2 = (n2 + Bw - 1) / Bw;

@@ -49,7 +49,7 @@ struct Scratch {
   // The hand-off words, nsync from `sync`, zeroed by the seam launch (and
   // after the persistent launch by the combine launch): the route launch's
   // arrival counter (word 0); the persistent launch's XCC ids (words 8..15)
-  // and barrier counts (kXcdBarrier1, kXcdBarrier2, one word per XCD); the
+  // and barrier counts (from kXcdBarrierBase, one cache line each); the
   // boxes.
   uint32_t* sync;
   // The run's status word, in its own 256 bytes: bits set by a wait that
@@ -85,8 +85,13 @@ constexpr uint64_t kWaitTicks = 10000000ull;
 
 constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, persistent
 constexpr int kActCols = 64;     // columns of an act group of the persistent launch
-constexpr int kXcdBarrier1 = 16; // sync words of the persistent launch's barriers (+ XCD)
-constexpr int kXcdBarrier2 = 24;
+// The persistent launch's barrier counts: barrier b (0, 1) of XCD x in sync
+// word kXcdBarrierBase + (b * kXcds + x) * kXcdBarrierStride, each in a cache
+// line of its own.  With the sixteen words in one line, atomics of
+// different XCDs on that line held each barrier up for 4-8 us.
+constexpr int kXcdBarrierBase = 64;
+constexpr int kXcdBarrierStride = 32;  // 128 bytes
+constexpr int kXcdBarrierWords = 2 * 8 * kXcdBarrierStride;
 constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment (w13; w2: w2_seg_steps)
 
 // The persistent launch of small steps cuts the intermediate of every expert
