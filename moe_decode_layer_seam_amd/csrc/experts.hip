@@ -1185,8 +1185,8 @@ bool xcd_applies(const LayerDims& d, int m, int grid) {
   auto slice_ok = [&d](int Kv) {
     return Kv % (kXcds * 128) == 0 && Kv / (kXcds * 128) == w2_seg_steps(d, Kv, false);
   };
-  // a step's slots (the shared one and at most m k routed) fit a wave's
-  // lanes: the slot wait reads them lane by lane
+  // a step's slots (the shared one and at most m k routed) number at most
+  // 64, the range the launch is measured and tested on
   const bool slots_ok = 1 + std::min(m * d.K, d.E) <= 64;
   return route_in_w13(d, m, grid) && d.rfmt == MOE_DECODE_ROUTED_E4M3 && slice_ok(d.I) && slice_ok(d.Is) &&
          grid % kXcds == 0 && grid / kXcds > 1 && m < kXcds && slots_ok;

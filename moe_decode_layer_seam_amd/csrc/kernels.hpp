@@ -85,18 +85,18 @@ constexpr uint64_t kWaitTicks = 10000000ull;
 
 constexpr int kKernels = 8;      // seam, logits, route, w13, act, w2, combine, persistent
 constexpr int kActCols = 64;     // columns of an act group of the persistent launch
-// The persistent launch's barrier counts: barrier b (0, 1) of XCD x in sync
-// word kXcdBarrierBase + (b * kXcds + x) * kXcdBarrierStride, each in a cache
-// line of its own.  With the sixteen words in one line, atomics of
-// different XCDs on that line held each barrier up for 4-8 us.
-constexpr int kXcdBarrierBase = 64;
-constexpr int kXcdBarrierStride = 32;  // 128 bytes
-constexpr int kXcdBarrierWords = 2 * 8 * kXcdBarrierStride;
 constexpr int kSegSteps = 4;     // K steps of 128 per GEMM segment (w13; w2: w2_seg_steps)
 
 // The persistent launch of small steps cuts the intermediate of every expert
 // into kXcds slices, one per XCD.
 constexpr int kXcds = 8;
+// Its barrier counts: barrier b (0, 1) of XCD x in sync word
+// kXcdBarrierBase + (b * kXcds + x) * kXcdBarrierStride, each in a cache line
+// of its own.  With the sixteen words in one line, atomics of different
+// XCDs on that line held each barrier up for 4-8 us.
+constexpr int kXcdBarrierBase = 64;
+constexpr int kXcdBarrierStride = 32;  // 128 bytes
+constexpr int kXcdBarrierWords = 2 * kXcds * kXcdBarrierStride;
 // K steps of 128 per segment of a w2 contraction of length Kv (I or Is):
 // in plans of the persistent schedule, 2 (256 columns) where Kv is kXcds
 // slices of 256, so that those slices are the segments and every step of
