@@ -873,8 +873,8 @@ constexpr int kXcdBurst2 = 2;
 // XCD.  The dispatcher deals a launch's blocks to the XCDs round-robin
 // (from where the previous launch left off), so the blocks with index x mod
 // kXcds share one XCD: the plan checks that on the device, and each block
-// checks it against the others.  Those blocks take slice x of every active
-// expert's intermediate: gate rows [x S, (x + 1) S) and up rows
+// checks it against the others at its end.  Those blocks take slice x of
+// every active expert's intermediate: gate rows [x S, (x + 1) S) and up rows
 // [Kv + x S, ...) of w13 (S = Kv / kXcds), and the same S columns of w2.
 // So every hand-off -- the w13 sums to SiLU * up, the a8 to w2 -- stays
 // inside one XCD's L2, which every CU of the XCD shares.  Nothing crosses
@@ -892,11 +892,12 @@ constexpr int kXcdBurst2 = 2;
 //      with the act launch's arithmetic on the summed planes;
 //   3. w2: the shared expert's units (tile groups of 128 output rows over
 //      the slice), then every routed slot's.
-// The sums and a8 are stored and completed before a block arrives, and read
-// after the barrier by loads that reach the L2 (sc0; the a8 codes, which
-// share cache lines between rows, are written through and read with sc1).
-// Per-slot counts that let w2 units start before the whole w13 phase ended
-// were measured slower: each hand-off then queued behind the weight stream.
+// The sums and a8 (values and codes) are stored and completed before a
+// block arrives, and read after the barrier by loads that reach the L2
+// (sc0) from CUs that have not read those lines before in the launch.
+// Each barrier's count sits in a cache line of its own.  Per-slot counts
+// that let w2 units start before the whole w13 phase ended were measured
+// slower: each hand-off then queued behind the weight stream.
 // ===========================================================================
 
 __device__ __forceinline__ float ld_l2(rsrc_t r, uint32_t off) {
