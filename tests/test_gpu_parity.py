@@ -578,11 +578,12 @@ def test_parity_full_size(idx):
 
 
 @pytest.mark.parametrize("idx", [1])
-def test_parity_full_size_persistent(idx):
-    """The persistent launch at full size, planned as bench.py plans it, against
-    the oracle."""
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_parity_full_size_persistent(idx, seed):
+    """The persistent launch at full size, planned as bench.py plans it (and
+    as its persistent figure plans it), against the oracle, on three seeds."""
     _run_full(dict(synth.WORKLOADS[idx], name=synth.WORKLOADS[idx]["name"] + "_persistent"), "dsv41",
-              schedule="persistent")
+              seed=seed, schedule="persistent")
 
 
 def test_parity_full_size_m1_on_a_48_row_plan():
