@@ -161,7 +161,7 @@ Layout make_layout(const LayerDims& d, int max_vs, int grid13, int grid2, bool t
   // of each index mod kXcds (words 8..15), from word 64 that launch's two
   // barrier counts per XCD (a cache line each), then the boxes of the
   // launches that route: the pick box, then (from an even word) the logit box
-  L.lbox = (kXcdBarrierBase + kXcdBarrierWords + (size_t)kPickBox + 1) & ~(size_t)1;
+  L.lbox = (kTileCntBase + kTileCntWords + (size_t)kPickBox + 1) & ~(size_t)1;
   L.nsync = L.lbox + (d.E <= 256 ? (size_t)2 * kRouteRows * d.E : 0);
   L.sync = take(L.nsync * 4);
   L.status = take(4);
@@ -218,7 +218,8 @@ Scratch scratch_at(char* b, const Layout& L, const LayerDims& d, int max_vs) {
   s.sync = reinterpret_cast<uint32_t*>(b + L.sync);
   s.counter = s.sync;
   s.status = reinterpret_cast<uint32_t*>(b + L.status);
-  s.pick_box = s.sync + kXcdBarrierBase + kXcdBarrierWords;
+  s.tile_cnt = s.sync + kTileCntBase;
+  s.pick_box = s.sync + kTileCntBase + kTileCntWords;
   s.logit_box = d.E <= 256 ? reinterpret_cast<uint64_t*>(s.sync + L.lbox) : nullptr;
   s.nsync = (int)L.nsync;
   return s;
@@ -312,10 +313,13 @@ hipError_t enqueue(const LayerDims& d, int m, const Inputs& in, const Scratch& s
   };
   hipError_t e;
   if (seam && (e = launch_seam(d, m, in, sc, st, ev(0))) != hipSuccess) return *what = "seam launch", e;
-  if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, st, ev(1))) != hipSuccess)
+  // with one sort group (E <= 64) the logits launch routes each 4-row tile
+  // in its last block, and no route launch runs
+  const bool route_logits = !route13 && !seam_fused(m) && d.E <= 64;
+  if (!seam_fused(m) && (e = launch_logits(d, m, in, sc, route_logits, st, ev(1))) != hipSuccess)
     return *what = "logits launch", e;
   // the launches that route build their own plan from the stored picks
-  if (!route13 && (e = launch_route(d, m, in, sc, false, st, ev(2))) != hipSuccess)
+  if (!route13 && !route_logits && (e = launch_route(d, m, in, sc, false, st, ev(2))) != hipSuccess)
     return *what = "route launch", e;
   if (route13 && boxes_dirty) *boxes_dirty = true;
   if (fused) {

@@ -55,6 +55,7 @@ struct Scratch {
   // The run's status word, in its own 256 bytes: bits set by a wait that
   // timed out (kStatus*); sticky across runs until the host clears it.
   uint32_t* status;
+  uint32_t* tile_cnt;  // arrivals of the logits launch's blocks per 4-row tile (kTileCntStride apart)
   uint32_t* pick_box;  // [kPickBox] the picks, for the w13 launch that routes (tagged words)
   uint64_t* logit_box; // [kRouteRows][E] its router logits (tagged; E <= 256)
   int nsync;
@@ -97,6 +98,12 @@ constexpr int kXcds = 8;
 constexpr int kXcdBarrierBase = 64;
 constexpr int kXcdBarrierStride = 32;  // 128 bytes
 constexpr int kXcdBarrierWords = 2 * kXcds * kXcdBarrierStride;
+// The logits launch that routes (E <= 64, above four rows): one arrival
+// count per 4-row tile, each in a cache line of its own, after the barrier
+// words.
+constexpr int kTileCntBase = kXcdBarrierBase + kXcdBarrierWords;
+constexpr int kTileCntStride = 32;
+constexpr int kTileCntWords = (48 + 3) / 4 * kTileCntStride;
 // K steps of 128 per segment of a w2 contraction of length Kv (I or Is):
 // in plans of the persistent schedule, 2 (256 columns) where Kv is kXcds
 // slices of 256, so that those slices are the segments and every step of
@@ -208,7 +215,7 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, h
 // Launchers; each returns the hipError_t of its launch.
 hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
                        const KernelEvents& ev);
-hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, bool route, hipStream_t st,
                          const KernelEvents& ev);
 // plan: the route launch also builds the plan (last block to finish); else
 // the w13 launch builds it from the stored picks.

@@ -430,6 +430,35 @@ __device__ __forceinline__ double take_logit(const uint64_t* w, const Scratch& s
   return __longlong_as_double((long long)(v ^ kLogitTag));
 }
 
+// One token's picks by one wave, for at most 64 experts (one sort group):
+// the logits read device-coherently from s.logits (other blocks stored them
+// through), then route_block's selection keys, network and weights, so the
+// ids and weights are route_block's bits.  The picks are stored
+// device-coherent for the w13 launch's plan.
+__device__ void route_wave(const LayerDims& d, int t, const float* __restrict__ bias, const Scratch& s, int lane) {
+  const int E = d.E, K = d.K;
+  uint64_t k[1] = {0ull};  // below every real expert's key
+  double sg = 0.0;
+  if (lane < E) {
+    const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t*>(s.logits) + (size_t)t * E + lane,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const double lg = __longlong_as_double((long long)bits);
+    sg = 1.0 / (1.0 + exp(-lg));
+    const double bb = sg + (double)bias[lane];
+    k[0] = select_key((bb == bb) ? bb : -INFINITY, lane);  // a NaN score ranks last
+  }
+  sort64<1>(k, lane);
+  const int e = 1023 - (int)(k[0] & 0x3FF);
+  const double sge = __shfl(sg, e & 63, 64);
+  const double sgk = lane < K ? sge : 0.0;
+  const double ssum = wave_sum(sgk);
+  if (lane < K) {
+    const float w = (float)((double)d.routed_scale * sgk / ssum);
+    __hip_atomic_store(&s.ids[t * K + lane], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&s.wts[t * K + lane], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <int GPW>
 __device__ bool route_block(const LayerDims& d, int m, int t, int nblocks, const float* __restrict__ bias,
                             const Scratch& s, RouteLds& L, uint32_t* pbox = nullptr,

@@ -180,7 +180,7 @@ constexpr int seam_tb() {
 // [EPB es, +EPB) and rows [TB ts, +TB).  Every logit is summed exactly as in
 // seam_kernel (a thread's columns in the same order, the same wave sum, the
 // waves in order), so both paths give the same bits.
-template <int EPB, int CPT, int TB>
+template <int EPB, int CPT, int TB, bool ROUTE>
 __global__ __launch_bounds__(kSeamThreads) void logits_kernel(LayerDims d, int m, Inputs in, Scratch s) {
   __shared__ double red_lg[TB][EPB][kSeamWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -254,7 +254,29 @@ __global__ __launch_bounds__(kSeamThreads) void logits_kernel(LayerDims d, int m
       double v = red_lg[tt][e][0];
 #pragma unroll
       for (int w = 1; w < kSeamWaves; ++w) v += red_lg[tt][e][w];
-      s.logits[(size_t)(t0 + tt) * E + e0 + e] = v;
+      if constexpr (ROUTE)  // read by the tile's last block: stored through
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(s.logits) + (size_t)(t0 + tt) * E + e0 + e,
+                           (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        s.logits[(size_t)(t0 + tt) * E + e0 + e] = v;
+    }
+  }
+  if constexpr (ROUTE) {
+    // the tile's last block to arrive (its blocks' logits stored and
+    // completed before each counts itself) routes the tile's rows, one wave
+    // a row; it then zeroes the count for the next step
+    __shared__ int s_last;
+    wait_memory();
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t* cnt = s.tile_cnt + (size_t)blockIdx.y * kTileCntStride;
+      s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u;
+    }
+    __syncthreads();
+    if (s_last) {
+      if (wave < nt) route_wave(d, t0 + wave, in.bias, s, lane);
+      if (tid == 0) __hip_atomic_store(s.tile_cnt + (size_t)blockIdx.y * kTileCntStride, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   stamp(s.tl_logits, kTlPoints, 1);
@@ -284,12 +306,15 @@ hipError_t launch_seam_epb(const LayerDims& d, int m, const Inputs& in, const Sc
 // takes 9.5 us at m = 48 and 4.5 us at m = 16; tiles of 8 x 4, 4 x 8 or
 // 8 x 2 took 12 and 4.7-6.3 us.  A logit is summed in the same tree
 // whatever the tile.
+// route: the launch also routes the rows (one sort group, E <= 64).
 template <int CPT>
-hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+hipError_t launch_logits_t(const LayerDims& d, int m, const Inputs& in, const Scratch& s, bool route, hipStream_t st,
                            const KernelEvents& ev) {
   constexpr int TB = 4, EPB = CPT <= 2 ? 4 : 2;
   const dim3 grid((d.E + EPB - 1) / EPB, (m + TB - 1) / TB);
-  return launch_kernel(logits_kernel<EPB, CPT, TB>, grid, dim3(kSeamThreads), 0, st, ev, d, m, in, s);
+  if (route)
+    return launch_kernel(logits_kernel<EPB, CPT, TB, true>, grid, dim3(kSeamThreads), 0, st, ev, d, m, in, s);
+  return launch_kernel(logits_kernel<EPB, CPT, TB, false>, grid, dim3(kSeamThreads), 0, st, ev, d, m, in, s);
 }
 
 // ===========================================================================
@@ -315,13 +340,13 @@ hipError_t launch_seam(const LayerDims& d, int m, const Inputs& in, const Scratc
   return launch_seam_epb<8, true>(d, m, in, s, st, ev);
 }
 
-hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, hipStream_t st,
+hipError_t launch_logits(const LayerDims& d, int m, const Inputs& in, const Scratch& s, bool route, hipStream_t st,
                          const KernelEvents& ev) {
   switch (seam_cpt(d.H)) {
-    case 1: return launch_logits_t<1>(d, m, in, s, st, ev);
-    case 2: return launch_logits_t<2>(d, m, in, s, st, ev);
-    case 3: return launch_logits_t<3>(d, m, in, s, st, ev);
-    default: return launch_logits_t<4>(d, m, in, s, st, ev);
+    case 1: return launch_logits_t<1>(d, m, in, s, route, st, ev);
+    case 2: return launch_logits_t<2>(d, m, in, s, route, st, ev);
+    case 3: return launch_logits_t<3>(d, m, in, s, route, st, ev);
+    default: return launch_logits_t<4>(d, m, in, s, route, st, ev);
   }
 }
 
